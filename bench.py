@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Benchmark: attention-layer forward tokens/s on one MI355X.
+
+Default workload: Laplacian Nystrom attention, PVT stage-1 shape
+(B=8, H=1, 56x56 grid -> N=3136 tokens, d=64, 8x8 average-pool landmarks ->
+m=49, lambda=2*sqrt(d)=16, eps=1e-3, 20 Newton-Schulz steps), fp32 I/O,
+synthetic seeded inputs N(0,1)/sqrt(d)*4 already resident in HBM.
+
+One step = one lapattn_forward call over the whole batch (landmark pool,
+solver, kernel maps, W reduction, output).  Prints one JSON line on stdout;
+progress goes to stderr.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X published peaks used as roofline denominators.
+PEAK_HBM_GBS = 8000.0
+PEAK_FP32_VALU_TFLOPS = 157.3
+PEAK_FP32_MFMA_TFLOPS = 157.3
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """Timing events from the HIP runtime (the library records them on the
+    stream each stage runs on, which torch.cuda.Event cannot follow)."""
+
+    def __init__(self):
+        self.rt = ctypes.CDLL("libamdhip64.so")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                ctypes.c_void_p, ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.owned = []
+
+    def create(self, n):
+        arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            ev = ctypes.c_void_p()
+            if self.rt.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            arr[i] = ev.value
+            self.owned.append(ev.value)
+        return arr
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.rt.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def close(self):
+        for ev in self.owned:
+            self.rt.hipEventDestroy(ev)
+        self.owned = []
+
+
+def stage_work(w):
+    """Algorithmic work per launch of each stage."""
+    BH, N, d, m = w.heads, w.N, w.d, w.m
+    e = 2 if w.dtype == "bf16" else 4
+    maps_pairs = BH * (1 if w.shared_qk else 2) * N * m * d
+    return {
+        # bytes: read K once, write L
+        "pool": {"bytes": BH * (N * d * e + m * d * 4)},
+        # flops: A pairs (3/pair) + 2 m^3 multiply-adds per NS step (4 m^3 flops)
+        "solver": {"flops": BH * (3 * m * m * d + 4 * m ** 3 * w.iters)},
+        # flops: 3 per coordinate pair (sub, |.|, add) or (sub, square, add)
+        "maps": {"flops": 3 * maps_pairs, "pairs": maps_pairs,
+                 "bytes": BH * ((1 if w.shared_qk else 2) * N * d * e
+                                + (1 if w.shared_qk else 2) * m * N * 4)},
+        # bytes: read K_LK (fp32) and V, write W
+        "w": {"bytes": BH * (m * N * 4 + N * d * e + m * d * 4)},
+        # bytes: read K_QL (fp32), write O
+        "out": {"bytes": BH * (m * N * 4 + N * d * e)},
+    }
+
+
+def cpu_baseline(w, inputs, seconds):
+    """The fp64 oracle on the host, one thread, over whole heads of the same
+    workload until `seconds` of CPU time have been spent."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while True:
+            bh = heads[done % len(heads)]
+            oracle.forward_workload(w, inputs, heads=[bh])
+            done += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    tokens = done * w.N
+    return {
+        "value": tokens / el,
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{done} whole heads of {w.name} (N={w.N} tokens each, "
+                  f"round-robin over its {len(heads)} heads), fp64 NumPy, "
+                  f"BLAS limited to 1 thread, {el:.1f} s",
+        "numpy": np.__version__,
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--serial", action="store_true", help="single-stream launch plan")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported: this build runs on one "
+              "GPU only (heads are independent, so B*H would shard across GPUs with no "
+              "exchange; see DESIGN.md).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from nystr_linear_attention_amd import _lib, api
+    from nystr_linear_attention_amd import workloads as wl
+
+    w = wl.BY_NAME[args.workload] if args.workload else wl.HEADLINE
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    log(f"[bench] workload {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} m={w.m} "
+        f"kernel={w.kernel} dtype={w.dtype} iters={w.iters}")
+    x = wl.make_inputs(w)
+
+    def to_dev(a):
+        if w.dtype == wl.BF16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    q = to_dev(x["q"])
+    k = q if w.shared_qk else to_dev(x["k"])
+    v = to_dev(x["v"])
+    out = torch.empty_like(q)
+    desc = api.make_desc(w.B, w.H, w.grid_h, w.grid_w, w.d, w.pool_h, w.pool_w,
+                         w.kernel, q.dtype, serial=args.serial)
+    ws = api.alloc_workspace(desc, dev)
+    lib = _lib.lib()
+    api.init()
+    stream = torch.cuda.current_stream().cuda_stream
+    call = (ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(), w.lam, w.eps,
+            w.iters, out.data_ptr(), ws.data_ptr(), ws.numel(), stream)
+
+    def step():
+        st = lib.lapattn_forward(*call)
+        if st != 0:
+            raise _lib.LapattnError(st, _lib.strerror(st))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} done")
+
+    # Timed region: K steps; the library records per-stage HIP events on the
+    # stream each stage runs on (one event set per step, read afterwards).
+    hip = HipEvents()
+    nev = 2 * len(_lib.STAGES)
+    evsets = [hip.create(nev) for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(args.steps):
+        lib.lapattn_set_stage_events(evsets[i], nev)
+        step()
+    t1.record()
+    lib.lapattn_set_stage_events(None, 0)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    stage_ms = {}
+    for s, name in enumerate(_lib.STAGES):
+        vals = [hip.elapsed_ms(evs[2 * s], evs[2 * s + 1]) for evs in evsets]
+        stage_ms[name] = sum(vals) / len(vals)
+    hip.close()
+    log(f"[bench] timed {args.steps} steps: {ms_step * 1e3:.2f} us/step; stages (us): "
+        + ", ".join(f"{n}={t * 1e3:.2f}" for n, t in stage_ms.items()))
+
+    # Second pass without the per-stage events, for reference.
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_plain = t0.elapsed_time(t1) / args.steps
+    log(f"[bench] same steps without stage events: {ms_plain * 1e3:.2f} us/step")
+
+    tokens = w.B * w.N
+    value = tokens / (ms_step * 1e-3)
+    work = stage_work(w)
+    t_maps = stage_ms["maps"] * 1e-3
+    ach = work["maps"]["flops"] / t_maps / 1e12
+    roofline = {
+        "kernel": "maps (K_QL and K_LK kernel maps, FP32 VALU)",
+        "bound": "alu",
+        "achieved": round(ach, 3),
+        "peak": PEAK_FP32_VALU_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(ach / PEAK_FP32_VALU_TFLOPS, 4),
+        "traffic": None,
+    }
+    stages = {}
+    for name, t in stage_ms.items():
+        e = {"us": round(t * 1e3, 3)}
+        if "bytes" in work[name] and name != "maps":
+            e["GB/s"] = round(work[name]["bytes"] / (t * 1e-3) / 1e9, 1)
+            e["hbm_frac"] = round(e["GB/s"] / PEAK_HBM_GBS, 4)
+        if "flops" in work[name]:
+            e["TFLOP/s"] = round(work[name]["flops"] / (t * 1e-3) / 1e12, 3)
+        stages[name] = e
+
+    res = {
+        "metric": "attention-layer tokens/sec (fwd) at N=3136,d=64,m=49; % FP32 VALU peak of L1 stage",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if w.dtype == wl.F32 else "bf16 I/O, f32 compute",
+        "data": "synthetic (seeded N(0,1)/sqrt(d)*4 inputs, resident in HBM)",
+        "config": {
+            "workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "m": w.m,
+            "pool": f"{w.pool_h}x{w.pool_w}", "lambda": w.lam, "eps": w.eps,
+            "iters": w.iters, "kernel": w.kernel,
+            "launch": "serial" if args.serial else "overlapped (solver on side stream)",
+        },
+        "roofline": roofline,
+        "stages": stages,
+        "ms_per_step_without_stage_events": round(ms_plain, 5),
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline: oracle for ~{args.cpu_seconds:.0f} s")
+        res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

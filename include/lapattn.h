@@ -1,0 +1,174 @@
+/*
+ * lapattn.h -- Nystrom-approximated, softmax-free kernel attention (forward)
+ * for AMD Instinct MI355X (gfx950).  Plain C ABI: no C++ types, no exceptions,
+ * no allocation inside the library's compute entry points.
+ *
+ * What one call computes, independently for every head (b, h):
+ *
+ *   L     = average pool of K over non-overlapping pool_h x pool_w windows of
+ *           the grid_h x grid_w token grid, windows in raster order
+ *           (SOFT review, "method": bottleneck tokens by average pooling;
+ *           LaplacianFormer summaries, Nystrom paragraph: landmark keys by
+ *           average pooling)                                         [m x d]
+ *   K_QL  = k(Q, L),  K_LK = k(L, K)                   [N x m], [m x N]
+ *           Laplacian k(x, y) = exp(-||x - y||_1 / lambda)
+ *           (LaplacianFormer summaries, kernel definition in the method
+ *           section);  Gaussian variant k(x, y) = exp(-||x - y||_2^2 / lambda)
+ *           (SOFT review, "method": symmetric kernel S = exp(Q (-) K); the
+ *           caller passes lambda = 2 sqrt(d) for SOFT's scale)
+ *   A     = k(L, L) + eps I   (diagonal perturbation that makes the landmark
+ *           matrix strictly positive definite; LaplacianFormer summaries,
+ *           Newton-Schulz paragraph)                                 [m x m]
+ *   X     = Newton-Schulz inverse of A: X_0 = alpha A,
+ *           X_{t+1} = 2 X_t - X_t A X_t, exactly `iters` steps,
+ *           alpha = 1 / (||A||_1 ||A||_inf)
+ *           (SOFT review, "method": the A_0 / A_{k+1} recursion)     [m x m]
+ *   O     = K_QL (X (K_LK V))   (SOFT review, "method": S_hat = P^T A^+ P,
+ *           applied to V with no further normalisation)              [N x d]
+ *
+ * Data layout.  Q, K, V and O are device pointers to [B, H, N, d] C-contiguous
+ * tensors, 16-byte aligned, N = grid_h * grid_w, token n = row * grid_w + col.  The element
+ * type is fp32 (LAPATTN_F32) or bf16 (LAPATTN_BF16) for all four; arithmetic
+ * is fp32 throughout and bf16 outputs are rounded to nearest even.
+ *
+ * Ownership.  The caller allocates and frees Q, K, V, O and the workspace.
+ * Compute entry points never allocate or free memory and never synchronise
+ * with the host: work is enqueued on `stream` (a hipStream_t passed as void*;
+ * NULL is the default stream) and the call returns after the enqueue.  K may
+ * be the same pointer as Q (the shared projection of the Gaussian variant);
+ * O must not overlap Q, K, V or the workspace.
+ *
+ * Errors.  Every entry point returning int returns LAPATTN_OK (0) or one of
+ * the negative codes below.  All argument checks run on the host before the
+ * first launch, so on an argument error nothing is enqueued.  Inputs are not
+ * scanned: NaN and Inf propagate to the output.
+ */
+#ifndef LAPATTN_H
+#define LAPATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LAPATTN_VERSION 1
+#define LAPATTN_MAX_LANDMARKS 64
+#define LAPATTN_MAX_ITERS 64
+
+typedef enum {
+  LAPATTN_KERNEL_LAPLACIAN = 0,   /* exp(-||x - y||_1 / lambda)   */
+  LAPATTN_KERNEL_GAUSSIAN = 1     /* exp(-||x - y||_2^2 / lambda) */
+} lapattn_kernel_t;
+
+typedef enum {
+  LAPATTN_F32 = 0,
+  LAPATTN_BF16 = 1
+} lapattn_dtype_t;
+
+/* Launch-plan flags (lapattn_desc_t.flags). */
+#define LAPATTN_FLAG_SERIAL 1u  /* run every stage on `stream` only; by default
+                                   the Newton-Schulz solver runs on a library-
+                                   owned side stream, overlapped with the
+                                   kernel-map stage, joined before the output */
+
+enum {
+  LAPATTN_OK = 0,
+  LAPATTN_ERR_NULL = -1,         /* a required pointer is NULL              */
+  LAPATTN_ERR_SHAPE = -2,        /* non-positive size, grid not divisible by
+                                    the pool, unsupported head dim d          */
+  LAPATTN_ERR_M_TOO_LARGE = -3,  /* m = (grid_h/pool_h)*(grid_w/pool_w) > 64 */
+  LAPATTN_ERR_PARAM = -4,        /* lambda <= 0 or not finite, eps < 0 or not
+                                    finite, iters outside [0, 64], bad kernel
+                                    or flags                                  */
+  LAPATTN_ERR_DTYPE = -5,        /* unknown dtype                             */
+  LAPATTN_ERR_ALIAS = -6,        /* O overlaps an input or the workspace      */
+  LAPATTN_ERR_WORKSPACE = -7,    /* workspace smaller than required / unaligned*/
+  LAPATTN_ERR_HIP = -8,          /* a HIP runtime call or launch failed       */
+  LAPATTN_ERR_ALIGN = -9         /* q, k, v or out not 16-byte aligned        */
+};
+
+/* Stages of one forward call, in launch order (for lapattn_set_stage_events). */
+#define LAPATTN_STAGE_POOL 0     /* landmark average pool                      */
+#define LAPATTN_STAGE_SOLVER 1   /* A = k(L,L) + eps I, alpha, Newton-Schulz  */
+#define LAPATTN_STAGE_MAPS 2     /* K_QL and K_LK kernel maps                  */
+#define LAPATTN_STAGE_W 3        /* W = K_LK V and the join Y = X W           */
+#define LAPATTN_STAGE_OUT 4      /* O = K_QL Y                                 */
+#define LAPATTN_NUM_STAGES 5
+
+typedef struct {
+  int32_t B, H;            /* batch and heads; every (b, h) is independent   */
+  int32_t grid_h, grid_w;  /* token grid; N = grid_h * grid_w                 */
+  int32_t d;               /* head dimension: 16, 32 or 64                    */
+  int32_t pool_h, pool_w;  /* average-pool window = stride; must divide grid  */
+  int32_t kernel;          /* lapattn_kernel_t                                */
+  int32_t dtype;           /* lapattn_dtype_t, for Q, K, V and O              */
+  uint32_t flags;          /* LAPATTN_FLAG_*                                  */
+} lapattn_desc_t;
+
+/* Library version (LAPATTN_VERSION). */
+int lapattn_version(void);
+
+/* Static text for a status code; never NULL. */
+const char* lapattn_strerror(int status);
+
+/* Validates a descriptor and the scalar parameters without touching any
+ * device.  Returns LAPATTN_OK or the error lapattn_forward would return for
+ * the same arguments (pointer checks aside). */
+int lapattn_check(const lapattn_desc_t* desc, float lambda, float eps, int32_t iters);
+
+/* Bytes of device workspace lapattn_forward needs for `desc` (256-byte
+ * aligned base required); 0 if the descriptor is invalid.  The size is linear
+ * in B*H*N. */
+size_t lapattn_workspace_bytes(const lapattn_desc_t* desc);
+
+/* Creates the library's per-device side stream on the current device ahead
+ * of time (otherwise it is created on the first overlapped call).  Safe to
+ * call more than once and from several threads. */
+int lapattn_init(void);
+
+/* O = K_QL (X (K_LK V)) per head, as defined at the top of this file.
+ *   q, k, v   device, [B, H, N, d], element type desc->dtype (k may equal q)
+ *   lambda    kernel length scale (> 0)
+ *   eps       diagonal perturbation of the landmark matrix (>= 0)
+ *   iters     Newton-Schulz steps, exact (0 .. 64), no early exit
+ *   out       device, [B, H, N, d], element type desc->dtype
+ *   workspace device scratch of lapattn_workspace_bytes(desc) bytes, 256-byte
+ *             aligned; its contents on entry are ignored
+ *   stream    hipStream_t (as void*) the work is ordered on
+ * Concurrent calls that share a workspace race; calls on different streams
+ * with different workspaces are independent. */
+int lapattn_forward(const lapattn_desc_t* desc, const void* q, const void* k,
+                    const void* v, float lambda, float eps, int32_t iters,
+                    void* out, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* lapattn_forward plus device copies of every intermediate, for stage-wise
+ * checking.  Each stage pointer may be NULL (not written).  All fp32:
+ *   L   [B, H, m, d]   landmarks
+ *   kql [B, H, N, m]   k(Q, L)
+ *   klk [B, H, m, N]   k(L, K)
+ *   a   [B, H, m, m]   k(L, L) + eps I
+ *   x   [B, H, m, m]   Newton-Schulz result after `iters` steps
+ *   w   [B, H, m, d]   K_LK V */
+int lapattn_forward_stages(const lapattn_desc_t* desc, const void* q,
+                           const void* k, const void* v, float lambda,
+                           float eps, int32_t iters, void* out,
+                           void* workspace, size_t workspace_bytes,
+                           void* stream, float* L, float* kql, float* klk,
+                           float* a, float* x, float* w);
+
+/* Profiling hook.  For the calling host thread, makes every later forward
+ * call record events[2*s] right before and events[2*s+1] right after the
+ * launch of stage s (LAPATTN_STAGE_*), on the stream that stage runs on.
+ * `events` holds 2 * LAPATTN_NUM_STAGES hipEvent_t handles (as void*) created
+ * by the caller with timing enabled, and must stay valid until the hook is
+ * cleared with (NULL, 0).  n must be 0 or 2 * LAPATTN_NUM_STAGES. */
+int lapattn_set_stage_events(void* const* events, int n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LAPATTN_H */

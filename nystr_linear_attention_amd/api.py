@@ -1,0 +1,125 @@
+"""PyTorch-facing binding of the C ABI: argument marshalling only.
+
+Tensors supply device pointers and the current HIP stream; every step of the
+computation runs in the library's kernels.  Names mirror the C entry points.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Dict, Optional
+
+import torch
+
+from . import _lib
+from ._lib import Desc
+
+_KERNELS = {"laplacian": _lib.KERNEL_LAPLACIAN, "gaussian": _lib.KERNEL_GAUSSIAN}
+_DTYPES = {torch.float32: _lib.DTYPE_F32, torch.bfloat16: _lib.DTYPE_BF16}
+
+
+def make_desc(B: int, H: int, grid_h: int, grid_w: int, d: int, pool_h: int,
+              pool_w: int, kernel: str = "laplacian", dtype=torch.float32,
+              serial: bool = False) -> Desc:
+    if kernel not in _KERNELS:
+        raise ValueError(f"kernel must be one of {sorted(_KERNELS)}")
+    if dtype not in _DTYPES:
+        raise ValueError("dtype must be torch.float32 or torch.bfloat16")
+    return Desc(B, H, grid_h, grid_w, d, pool_h, pool_w, _KERNELS[kernel],
+                _DTYPES[dtype], _lib.FLAG_SERIAL if serial else 0)
+
+
+def version() -> int:
+    return _lib.lib().lapattn_version()
+
+
+def init() -> None:
+    _lib.check(_lib.lib().lapattn_init())
+
+
+def check(desc: Desc, lam: float, eps: float, iters: int) -> int:
+    return _lib.lib().lapattn_check(ctypes.byref(desc), lam, eps, iters)
+
+
+def workspace_bytes(desc: Desc) -> int:
+    return int(_lib.lib().lapattn_workspace_bytes(ctypes.byref(desc)))
+
+
+def alloc_workspace(desc: Desc, device) -> torch.Tensor:
+    n = workspace_bytes(desc)
+    if n == 0:
+        raise ValueError("invalid descriptor")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _desc_for(q: torch.Tensor, grid_h: int, grid_w: int, pool_h: int, pool_w: int,
+              kernel: str, serial: bool) -> Desc:
+    if q.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    if N != grid_h * grid_w:
+        raise ValueError(f"N={N} does not match the {grid_h}x{grid_w} grid")
+    return make_desc(B, H, grid_h, grid_w, d, pool_h, pool_w, kernel, q.dtype, serial)
+
+
+def _check_io(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dtype != q.dtype or t.shape != q.shape:
+            raise ValueError("q, k and v must share shape and dtype")
+
+
+def _stream_ptr(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, grid_h: int,
+            grid_w: int, pool_h: int, pool_w: int, lam: float, eps: float,
+            iters: int, kernel: str = "laplacian", out: Optional[torch.Tensor] = None,
+            workspace: Optional[torch.Tensor] = None, serial: bool = False,
+            stream=None) -> torch.Tensor:
+    """O = K_QL (X (K_LK V)) per head; see include/lapattn.h."""
+    _check_io(q, k, v)
+    desc = _desc_for(q, grid_h, grid_w, pool_h, pool_w, kernel, serial)
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = alloc_workspace(desc, q.device)
+    st = _lib.lib().lapattn_forward(
+        ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(), lam, eps, iters,
+        out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream_ptr(stream))
+    _lib.check(st)
+    return out
+
+
+def forward_stages(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, grid_h: int,
+                   grid_w: int, pool_h: int, pool_w: int, lam: float, eps: float,
+                   iters: int, kernel: str = "laplacian", serial: bool = False,
+                   stream=None) -> Dict[str, torch.Tensor]:
+    """forward() plus fp32 copies of L, K_QL, K_LK, A, X and W."""
+    _check_io(q, k, v)
+    desc = _desc_for(q, grid_h, grid_w, pool_h, pool_w, kernel, serial)
+    B, H, N, d = q.shape
+    m = (grid_h // pool_h) * (grid_w // pool_w)
+    dev = q.device
+    f32 = torch.float32
+    res = {
+        "O": torch.empty_like(q),
+        "L": torch.empty(B, H, m, d, dtype=f32, device=dev),
+        "KQL": torch.empty(B, H, N, m, dtype=f32, device=dev),
+        "KLK": torch.empty(B, H, m, N, dtype=f32, device=dev),
+        "A": torch.empty(B, H, m, m, dtype=f32, device=dev),
+        "X": torch.empty(B, H, m, m, dtype=f32, device=dev),
+        "W": torch.empty(B, H, m, d, dtype=f32, device=dev),
+    }
+    ws = alloc_workspace(desc, dev)
+    st = _lib.lib().lapattn_forward_stages(
+        ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(), lam, eps, iters,
+        res["O"].data_ptr(), ws.data_ptr(), ws.numel(), _stream_ptr(stream),
+        res["L"].data_ptr(), res["KQL"].data_ptr(), res["KLK"].data_ptr(),
+        res["A"].data_ptr(), res["X"].data_ptr(), res["W"].data_ptr())
+    _lib.check(st)
+    return res

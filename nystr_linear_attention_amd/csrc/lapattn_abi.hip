@@ -1,0 +1,292 @@
+// C-ABI front end: argument validation, workspace plan, launch sequence.
+// The entry points are declared (with their contracts) in include/lapattn.h.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <mutex>
+
+#include "lapattn.h"
+#include "lapattn_internal.h"
+
+namespace lapattn {
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxDevices = 64;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int check_desc(const lapattn_desc_t* d) {
+  if (!d) return LAPATTN_ERR_NULL;
+  if (d->B <= 0 || d->H <= 0 || d->grid_h <= 0 || d->grid_w <= 0 || d->d <= 0 ||
+      d->pool_h <= 0 || d->pool_w <= 0)
+    return LAPATTN_ERR_SHAPE;
+  if (d->d != 16 && d->d != 32 && d->d != 64) return LAPATTN_ERR_SHAPE;
+  if (d->grid_h % d->pool_h || d->grid_w % d->pool_w) return LAPATTN_ERR_SHAPE;
+  const long long N = static_cast<long long>(d->grid_h) * d->grid_w;
+  const long long BH = static_cast<long long>(d->B) * d->H;
+  // Index arithmetic inside the kernels is 32-bit per head and per launch.
+  if (N > (1LL << 24) || BH > (1LL << 20) || BH * ((N + 63) / 64) * 16 > (1LL << 31))
+    return LAPATTN_ERR_SHAPE;
+  const long long m = static_cast<long long>(d->grid_h / d->pool_h) * (d->grid_w / d->pool_w);
+  if (m > LAPATTN_MAX_LANDMARKS) return LAPATTN_ERR_M_TOO_LARGE;
+  if (d->kernel != LAPATTN_KERNEL_LAPLACIAN && d->kernel != LAPATTN_KERNEL_GAUSSIAN)
+    return LAPATTN_ERR_PARAM;
+  if (d->dtype != LAPATTN_F32 && d->dtype != LAPATTN_BF16) return LAPATTN_ERR_DTYPE;
+  if (d->flags & ~LAPATTN_FLAG_SERIAL) return LAPATTN_ERR_PARAM;
+  return LAPATTN_OK;
+}
+
+int check_params(float lambda, float eps, int32_t iters) {
+  if (!std::isfinite(lambda) || !(lambda > 0.f)) return LAPATTN_ERR_PARAM;
+  if (!std::isfinite(eps) || eps < 0.f) return LAPATTN_ERR_PARAM;
+  if (iters < 0 || iters > LAPATTN_MAX_ITERS) return LAPATTN_ERR_PARAM;
+  return LAPATTN_OK;
+}
+
+Plan make_plan(const lapattn_desc_t* d) {
+  Plan p{};
+  p.B = d->B;
+  p.H = d->H;
+  p.gh = d->grid_h;
+  p.gw = d->grid_w;
+  p.D = d->d;
+  p.ph = d->pool_h;
+  p.pw = d->pool_w;
+  p.kernel = d->kernel;
+  p.bf16 = d->dtype == LAPATTN_BF16;
+  p.N = p.gh * p.gw;
+  p.m = (p.gh / p.ph) * (p.gw / p.pw);
+  p.BH = p.B * p.H;
+  p.nT = (p.N + 63) / 64;
+  p.ng = (p.m + 7) / 8;  // about 8 landmarks per wave-level work unit
+  // W partials: at most 32 chunks per head, at least 128 tokens per chunk.
+  int nC = (p.N + 127) / 128;
+  if (nC > 32) nC = 32;
+  int CH = (p.N + nC - 1) / nC;
+  CH = (CH + 15) / 16 * 16;
+  p.CH = CH;
+  p.nC = (p.N + CH - 1) / CH;
+
+  const size_t BH = static_cast<size_t>(p.BH);
+  const size_t f = sizeof(float);
+  size_t off = 0;
+  p.off_ctr = off;
+  off = align_up(off + BH * CTR_PER_HEAD * sizeof(unsigned));
+  p.off_L = off;
+  off = align_up(off + BH * p.m * p.D * f);
+  p.off_kqlt = off;
+  off = align_up(off + BH * p.m * p.N * f);
+  p.off_klkt = off;
+  off = align_up(off + BH * p.m * p.N * f);
+  p.off_wpart = off;
+  off = align_up(off + BH * p.nC * MP * p.D * f);
+  p.off_w = off;
+  off = align_up(off + BH * MP * p.D * f);
+  p.off_x = off;
+  off = align_up(off + BH * MP * MP * f);
+  p.off_y = off;
+  off = align_up(off + BH * MP * p.D * f);
+  p.total = off;
+  return p;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+// Per-device side stream and fork/join events for the overlapped plan.
+struct DeviceCtx {
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr;
+  hipEvent_t join = nullptr;
+  bool ready = false;
+};
+std::mutex g_mu[kMaxDevices];
+DeviceCtx g_ctx[kMaxDevices];
+
+int ensure_ctx(int dev) {
+  DeviceCtx& c = g_ctx[dev];
+  if (c.ready) return LAPATTN_OK;
+  if (hipStreamCreateWithFlags(&c.side, hipStreamNonBlocking) != hipSuccess) return LAPATTN_ERR_HIP;
+  if (hipEventCreateWithFlags(&c.fork, hipEventDisableTiming) != hipSuccess) return LAPATTN_ERR_HIP;
+  if (hipEventCreateWithFlags(&c.join, hipEventDisableTiming) != hipSuccess) return LAPATTN_ERR_HIP;
+  c.ready = true;
+  return LAPATTN_OK;
+}
+
+// Per-thread stage events (profiling hook).
+thread_local void* const* t_events = nullptr;
+
+inline bool mark(int slot, hipStream_t s) {
+  if (!t_events) return true;
+  return hipEventRecord(static_cast<hipEvent_t>(t_events[slot]), s) == hipSuccess;
+}
+
+// Launches one stage between its two profiling events.
+template <typename F>
+inline bool stage(int st, hipStream_t s, F&& launch) {
+  if (!mark(2 * st, s)) return false;
+  if (launch() != hipSuccess) return false;
+  return mark(2 * st + 1, s);
+}
+
+bool misaligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 != 0; }
+
+int run(const lapattn_desc_t* desc, const Args& a, void* workspace, size_t ws_bytes,
+        hipStream_t stream) {
+  const Plan p = make_plan(desc);
+  if (misaligned16(a.q) || misaligned16(a.k) || misaligned16(a.v) || misaligned16(a.out))
+    return LAPATTN_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return LAPATTN_ERR_WORKSPACE;
+  if (ws_bytes < p.total) return LAPATTN_ERR_WORKSPACE;
+  const size_t esize = p.bf16 ? 2 : 4;
+  const size_t io = static_cast<size_t>(p.BH) * p.N * p.D * esize;
+  if (overlaps(a.out, io, a.q, io) || overlaps(a.out, io, a.k, io) ||
+      overlaps(a.out, io, a.v, io) || overlaps(a.out, io, workspace, ws_bytes))
+    return LAPATTN_ERR_ALIAS;
+
+  char* ws = static_cast<char*>(workspace);
+  Buffers b;
+  b.ctr = reinterpret_cast<unsigned*>(ws + p.off_ctr);
+  b.L = reinterpret_cast<float*>(ws + p.off_L);
+  b.kqlt = reinterpret_cast<float*>(ws + p.off_kqlt);
+  b.klkt = reinterpret_cast<float*>(ws + p.off_klkt);
+  b.wpart = reinterpret_cast<float*>(ws + p.off_wpart);
+  b.w = reinterpret_cast<float*>(ws + p.off_w);
+  b.x = reinterpret_cast<float*>(ws + p.off_x);
+  b.y = reinterpret_cast<float*>(ws + p.off_y);
+
+  const bool serial = (desc->flags & LAPATTN_FLAG_SERIAL) != 0;
+  auto pool = [&] { return launch_pool(p, a, b, stream); };
+  auto maps = [&] { return launch_maps(p, a, b, stream); };
+  auto wred = [&] { return launch_w(p, a, b, 2, stream); };
+  auto out = [&] { return launch_out(p, a, b, stream); };
+  if (serial) {
+    auto ns = [&] { return launch_ns(p, a, b, 2, stream); };
+    if (!stage(LAPATTN_STAGE_POOL, stream, pool)) return LAPATTN_ERR_HIP;
+    if (!stage(LAPATTN_STAGE_SOLVER, stream, ns)) return LAPATTN_ERR_HIP;
+    if (!stage(LAPATTN_STAGE_MAPS, stream, maps)) return LAPATTN_ERR_HIP;
+    if (!stage(LAPATTN_STAGE_W, stream, wred)) return LAPATTN_ERR_HIP;
+    if (!stage(LAPATTN_STAGE_OUT, stream, out)) return LAPATTN_ERR_HIP;
+    if (launch_export(p, a, b, stream) != hipSuccess) return LAPATTN_ERR_HIP;
+    return LAPATTN_OK;
+  }
+
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LAPATTN_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_mu[dev]);
+  if (ensure_ctx(dev) != LAPATTN_OK) return LAPATTN_ERR_HIP;
+  DeviceCtx& c = g_ctx[dev];
+  auto ns = [&] { return launch_ns(p, a, b, 2, c.side); };
+  // stream: pool -> (fork) -> maps -> w -> (wait join) -> out
+  // side:           (wait fork) -> ns -> (join)
+  if (!stage(LAPATTN_STAGE_POOL, stream, pool)) return LAPATTN_ERR_HIP;
+  if (hipEventRecord(c.fork, stream) != hipSuccess) return LAPATTN_ERR_HIP;
+  if (hipStreamWaitEvent(c.side, c.fork, 0) != hipSuccess) return LAPATTN_ERR_HIP;
+  if (!stage(LAPATTN_STAGE_SOLVER, c.side, ns)) return LAPATTN_ERR_HIP;
+  if (hipEventRecord(c.join, c.side) != hipSuccess) return LAPATTN_ERR_HIP;
+  if (!stage(LAPATTN_STAGE_MAPS, stream, maps)) return LAPATTN_ERR_HIP;
+  if (!stage(LAPATTN_STAGE_W, stream, wred)) return LAPATTN_ERR_HIP;
+  if (hipStreamWaitEvent(stream, c.join, 0) != hipSuccess) return LAPATTN_ERR_HIP;
+  if (!stage(LAPATTN_STAGE_OUT, stream, out)) return LAPATTN_ERR_HIP;
+  if (launch_export(p, a, b, stream) != hipSuccess) return LAPATTN_ERR_HIP;
+  return LAPATTN_OK;
+}
+
+int forward_common(const lapattn_desc_t* desc, const void* q, const void* k, const void* v,
+                   float lambda, float eps, int32_t iters, void* out, void* workspace,
+                   size_t workspace_bytes, void* stream, float* L, float* kql, float* klk,
+                   float* am, float* x, float* w) {
+  int st = check_desc(desc);
+  if (st != LAPATTN_OK) return st;
+  st = check_params(lambda, eps, iters);
+  if (st != LAPATTN_OK) return st;
+  if (!q || !k || !v || !out || !workspace) return LAPATTN_ERR_NULL;
+  Args a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lambda = lambda;
+  a.eps = eps;
+  a.iters = iters;
+  a.shared_qk = (q == k) ? 1 : 0;
+  a.st_L = L;
+  a.st_kql = kql;
+  a.st_klk = klk;
+  a.st_a = am;
+  a.st_x = x;
+  a.st_w = w;
+  return run(desc, a, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+}  // namespace lapattn
+
+extern "C" {
+
+int lapattn_version(void) { return LAPATTN_VERSION; }
+
+const char* lapattn_strerror(int status) {
+  switch (status) {
+    case LAPATTN_OK: return "ok";
+    case LAPATTN_ERR_NULL: return "a required pointer is NULL";
+    case LAPATTN_ERR_SHAPE:
+      return "invalid shape: non-positive size, grid not divisible by pool, or head dim not in {16, 32, 64}";
+    case LAPATTN_ERR_M_TOO_LARGE: return "more than 64 landmarks";
+    case LAPATTN_ERR_PARAM: return "invalid parameter: lambda, eps, iters, kernel or flags";
+    case LAPATTN_ERR_DTYPE: return "unknown dtype";
+    case LAPATTN_ERR_ALIAS: return "output overlaps an input or the workspace";
+    case LAPATTN_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
+    case LAPATTN_ERR_HIP: return "HIP runtime or kernel launch failure";
+    case LAPATTN_ERR_ALIGN: return "q, k, v or out is not 16-byte aligned";
+  }
+  return "unknown status";
+}
+
+int lapattn_check(const lapattn_desc_t* desc, float lambda, float eps, int32_t iters) {
+  const int st = lapattn::check_desc(desc);
+  if (st != LAPATTN_OK) return st;
+  return lapattn::check_params(lambda, eps, iters);
+}
+
+size_t lapattn_workspace_bytes(const lapattn_desc_t* desc) {
+  if (lapattn::check_desc(desc) != LAPATTN_OK) return 0;
+  return lapattn::make_plan(desc).total;
+}
+
+int lapattn_set_stage_events(void* const* events, int n) {
+  if (n != 0 && n != 2 * LAPATTN_NUM_STAGES) return LAPATTN_ERR_PARAM;
+  if (n != 0 && !events) return LAPATTN_ERR_NULL;
+  lapattn::t_events = n ? events : nullptr;
+  return LAPATTN_OK;
+}
+
+int lapattn_init(void) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= lapattn::kMaxDevices)
+    return LAPATTN_ERR_HIP;
+  std::lock_guard<std::mutex> lock(lapattn::g_mu[dev]);
+  return lapattn::ensure_ctx(dev);
+}
+
+int lapattn_forward(const lapattn_desc_t* desc, const void* q, const void* k, const void* v,
+                    float lambda, float eps, int32_t iters, void* out, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return lapattn::forward_common(desc, q, k, v, lambda, eps, iters, out, workspace,
+                                 workspace_bytes, stream, nullptr, nullptr, nullptr, nullptr,
+                                 nullptr, nullptr);
+}
+
+int lapattn_forward_stages(const lapattn_desc_t* desc, const void* q, const void* k,
+                           const void* v, float lambda, float eps, int32_t iters, void* out,
+                           void* workspace, size_t workspace_bytes, void* stream, float* L,
+                           float* kql, float* klk, float* a, float* x, float* w) {
+  return lapattn::forward_common(desc, q, k, v, lambda, eps, iters, out, workspace,
+                                 workspace_bytes, stream, L, kql, klk, a, x, w);
+}
+
+}  // extern "C"

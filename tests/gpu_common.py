@@ -1,0 +1,56 @@
+"""Shared helpers for the GPU parity tests: move seeded inputs to the device,
+run the HIP path through the C ABI, and compare against the oracle."""
+import numpy as np
+import torch
+
+import oracle
+from nystr_linear_attention_amd import api
+from nystr_linear_attention_amd import workloads as wl
+
+# Tolerances on max|O_gpu - O_ref| / max|O_ref| per head (normwise max error).
+TOL_F32 = 2e-3
+TOL_BF16 = 2e-2
+
+
+def tol_for(w):
+    return TOL_BF16 if w.dtype == wl.BF16 else TOL_F32
+
+
+def to_device(a, dtype):
+    if dtype == wl.BF16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def device_inputs(w, x):
+    q = to_device(x["q"], w.dtype)
+    k = q if w.shared_qk else to_device(x["k"], w.dtype)
+    v = to_device(x["v"], w.dtype)
+    return q, k, v
+
+
+def run_gpu(w, x, serial=False, stages=False):
+    q, k, v = device_inputs(w, x)
+    kw = dict(grid_h=w.grid_h, grid_w=w.grid_w, pool_h=w.pool_h, pool_w=w.pool_w,
+              lam=w.lam, eps=w.eps, iters=w.iters, kernel=w.kernel, serial=serial)
+    if stages:
+        res = api.forward_stages(q, k, v, **kw)
+    else:
+        res = {"O": api.forward(q, k, v, **kw)}
+    torch.cuda.synchronize()
+    return {key: t.float().cpu().numpy().astype(np.float64) for key, t in res.items()}
+
+
+def normwise(a, b):
+    return float(np.abs(a - b).max() / max(np.abs(b).max(), 1e-300))
+
+
+def compare_output(w, x, got_O, heads=None):
+    ref = oracle.forward_workload(w, x, heads=heads)
+    worst = 0.0
+    for (b, h), r in ref.items():
+        err = normwise(got_O[b, h], r["O"])
+        worst = max(worst, err)
+        assert np.isfinite(got_O[b, h]).all(), f"non-finite output in head ({b},{h})"
+        assert err <= tol_for(w), f"{w.name} head ({b},{h}): normwise error {err:.3e}"
+    return worst

@@ -1,0 +1,137 @@
+"""C-ABI library: loads on the host, exports every declared symbol, and
+rejects every bad argument before any device work.  CPU only: the pointers
+below are never dereferenced because each call fails validation first."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from nystr_linear_attention_amd import _lib
+from nystr_linear_attention_amd._lib import Desc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lapattn.h")
+
+FAKE = 0x10000000  # never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lapattn_[a-z_]+)\s*\(", text)))
+
+
+def good_desc(**kw):
+    d = dict(B=2, H=3, grid_h=14, grid_w=14, d=32, pool_h=2, pool_w=2, kernel=0, dtype=0, flags=0)
+    d.update(kw)
+    return Desc(**d)
+
+
+def test_exports_every_declared_symbol():
+    lib = _lib.lib()
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS), names
+    for name in names:
+        assert hasattr(lib, name), f"{name} not exported"
+
+
+def test_version_and_strerror():
+    lib = _lib.lib()
+    assert lib.lapattn_version() == 1
+    for code in range(-9, 1):
+        s = _lib.strerror(code)
+        assert s and s != "unknown status"
+    assert _lib.strerror(-99) == "unknown status"
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(B=0), _lib.ERR_SHAPE),
+    (dict(H=-1), _lib.ERR_SHAPE),
+    (dict(grid_h=0), _lib.ERR_SHAPE),
+    (dict(d=48), _lib.ERR_SHAPE),
+    (dict(d=128), _lib.ERR_SHAPE),
+    (dict(pool_h=3), _lib.ERR_SHAPE),
+    (dict(pool_w=0), _lib.ERR_SHAPE),
+    (dict(grid_h=18, grid_w=18, pool_h=2, pool_w=2), _lib.ERR_M_TOO_LARGE),
+    (dict(kernel=2), _lib.ERR_PARAM),
+    (dict(dtype=7), _lib.ERR_DTYPE),
+    (dict(flags=4), _lib.ERR_PARAM),
+    (dict(), _lib.OK),
+    (dict(grid_h=16, grid_w=16, pool_h=2, pool_w=2), _lib.OK),
+])
+def test_descriptor_validation(kw, expect):
+    lib = _lib.lib()
+    assert lib.lapattn_check(ctypes.byref(good_desc(**kw)), 5.0, 1e-3, 20) == expect
+
+
+@pytest.mark.parametrize("lam,eps,iters,expect", [
+    (0.0, 1e-3, 20, _lib.ERR_PARAM),
+    (-1.0, 1e-3, 20, _lib.ERR_PARAM),
+    (float("nan"), 1e-3, 20, _lib.ERR_PARAM),
+    (float("inf"), 1e-3, 20, _lib.ERR_PARAM),
+    (4.0, -1e-3, 20, _lib.ERR_PARAM),
+    (4.0, float("nan"), 20, _lib.ERR_PARAM),
+    (4.0, 1e-3, -1, _lib.ERR_PARAM),
+    (4.0, 1e-3, 65, _lib.ERR_PARAM),
+    (4.0, 0.0, 0, _lib.OK),
+    (4.0, 1e-3, 64, _lib.OK),
+])
+def test_parameter_validation(lam, eps, iters, expect):
+    lib = _lib.lib()
+    assert lib.lapattn_check(ctypes.byref(good_desc()), lam, eps, iters) == expect
+
+
+def test_stage_event_hook_validation():
+    lib = _lib.lib()
+    assert lib.lapattn_set_stage_events(None, 0) == _lib.OK
+    assert lib.lapattn_set_stage_events(None, 10) == _lib.ERR_NULL
+    arr = (ctypes.c_void_p * 10)()
+    assert lib.lapattn_set_stage_events(arr, 3) == _lib.ERR_PARAM
+    assert lib.lapattn_set_stage_events(None, 0) == _lib.OK
+
+
+def test_null_desc():
+    lib = _lib.lib()
+    assert lib.lapattn_check(None, 1.0, 0.0, 1) == _lib.ERR_NULL
+    assert lib.lapattn_workspace_bytes(None) == 0
+
+
+def test_workspace_bytes_linear_in_tokens():
+    lib = _lib.lib()
+    assert lib.lapattn_workspace_bytes(ctypes.byref(good_desc(d=48))) == 0
+    a = lib.lapattn_workspace_bytes(ctypes.byref(good_desc(B=1, H=1, grid_h=56, grid_w=56, d=64, pool_h=8, pool_w=8)))
+    b = lib.lapattn_workspace_bytes(ctypes.byref(good_desc(B=8, H=1, grid_h=56, grid_w=56, d=64, pool_h=8, pool_w=8)))
+    assert a > 0 and 7.5 * a <= b <= 8.5 * a
+    # at least the two [m, N] kernel maps in fp32
+    assert a >= 2 * 49 * 3136 * 4
+
+
+def _fwd(desc, q=FAKE, k=FAKE + 0x1000000, v=FAKE + 0x2000000, out=FAKE + 0x3000000,
+         ws=FAKE + 0x4000000, wsb=1 << 30, lam=4.0, eps=1e-3, iters=20):
+    lib = _lib.lib()
+    return lib.lapattn_forward(ctypes.byref(desc), q, k, v, lam, eps, iters, out, ws, wsb, None)
+
+
+def test_forward_rejects_before_launch():
+    d = good_desc()
+    assert _fwd(d, q=None) == _lib.ERR_NULL
+    assert _fwd(d, v=None) == _lib.ERR_NULL
+    assert _fwd(d, out=None) == _lib.ERR_NULL
+    assert _fwd(d, ws=None) == _lib.ERR_NULL
+    assert _fwd(good_desc(B=0)) == _lib.ERR_SHAPE
+    assert _fwd(d, lam=-2.0) == _lib.ERR_PARAM
+    assert _fwd(d, iters=100) == _lib.ERR_PARAM
+    need = _lib.lib().lapattn_workspace_bytes(ctypes.byref(d))
+    assert _fwd(d, wsb=need - 1) == _lib.ERR_WORKSPACE
+    assert _fwd(d, ws=FAKE + 0x4000000 + 64) == _lib.ERR_WORKSPACE
+    io = 2 * 3 * 196 * 32 * 4
+    assert _fwd(d, out=FAKE + io // 2) == _lib.ERR_ALIAS          # overlaps q
+    assert _fwd(d, out=FAKE + 0x2000000 + 16) == _lib.ERR_ALIAS   # overlaps v
+    assert _fwd(d, out=FAKE + 0x4000000 + 256, wsb=need) == _lib.ERR_ALIAS  # inside workspace
+    assert _fwd(d, q=FAKE + 4) == _lib.ERR_ALIGN
+    assert _fwd(d, out=FAKE + 0x3000000 + 8) == _lib.ERR_ALIGN
+    st = _lib.lib().lapattn_forward_stages(ctypes.byref(d), FAKE, None, FAKE, 4.0, 1e-3, 20,
+                                           FAKE, FAKE, 1 << 30, None, None, None, None, None,
+                                           None, None)
+    assert st == _lib.ERR_NULL

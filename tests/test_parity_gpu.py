@@ -1,0 +1,100 @@
+"""Parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Bar: per head, max|O_gpu - O_ref| / max|O_ref| <= 2e-3 with fp32 I/O and
+<= 2e-2 with bf16 I/O (fp32 compute in both cases).  Stage checks use the
+bounds stated next to each one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_common import compare_output, normwise, run_gpu, tol_for
+from nystr_linear_attention_amd import api
+from nystr_linear_attention_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+def _print_case(w, extra=""):
+    print(f"\n[case] {w.name} B={w.B} H={w.H} N={w.N} d={w.d} m={w.m} "
+          f"kernel={w.kernel} dtype={w.dtype} iters={w.iters} {extra}", flush=True)
+
+
+@pytest.mark.parametrize("idx", range(len(wl.WORKLOADS)), ids=[w.name for w in wl.WORKLOADS])
+def test_full_size_workloads(idx):
+    """All heads of every reference workload, default (overlapped) launch plan."""
+    w = wl.WORKLOADS[idx]
+    _print_case(w)
+    x = wl.make_inputs(w)
+    got = run_gpu(w, x)
+    worst = compare_output(w, x, got["O"])
+    print(f"[case] worst normwise error {worst:.3e} (tol {tol_for(w):.0e})", flush=True)
+
+
+SMALL = [
+    wl.small_case(10, 14, 32, 2, 2, B=2, H=3),                    # ragged tiles, m=35
+    wl.small_case(9, 9, 16, 3, 3, B=1, H=2),                      # d=16, m=9
+    wl.small_case(4, 4, 16, 1, 1),                                # N=16 < one tile, m=16
+    wl.small_case(8, 8, 64, 1, 1, B=2),                           # m=64 (maximum), pool 1x1
+    wl.small_case(7, 9, 32, 7, 9, B=3),                           # m=1
+    wl.small_case(12, 12, 64, 2, 2, iters=0),                     # no NS steps
+    wl.small_case(12, 20, 32, 3, 4, kernel=wl.GAUSSIAN, B=2),     # Gaussian, Q != K
+    wl.small_case(16, 16, 64, 2, 2, shared_qk=True),              # Laplacian, Q = K
+    wl.small_case(10, 14, 64, 2, 2, dtype=wl.BF16, B=2, H=2),     # bf16, ragged
+    wl.small_case(24, 24, 64, 3, 3, qk_dist="student_t3", qk_scale=0.5, eps=1e-2, iters=30),
+    wl.small_case(40, 40, 64, 5, 5, B=1, H=1, iters=64),          # N=1600, max iters
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
+def test_small_and_edge_cases(w):
+    _print_case(w)
+    x = wl.make_inputs(w)
+    got = run_gpu(w, x)
+    compare_output(w, x, got["O"])
+
+
+STAGE_CASES = [wl.WORKLOADS[0], wl.small_case(10, 14, 32, 2, 2, B=2, H=1),
+               wl.small_case(12, 20, 32, 3, 4, kernel=wl.GAUSSIAN),
+               wl.small_case(8, 8, 64, 1, 1)]
+
+
+@pytest.mark.parametrize("w", STAGE_CASES, ids=[w.name for w in STAGE_CASES])
+def test_stages(w):
+    """Every intermediate against the oracle's same-named one."""
+    _print_case(w, "stages")
+    x = wl.make_inputs(w)
+    got = run_gpu(w, x, stages=True)
+    ref = oracle.forward_workload(w, x, stages=True)
+    for (b, h), r in ref.items():
+        assert normwise(got["L"][b, h], r["L"]) <= 1e-6, "landmarks"
+        for key, ref_key in (("KQL", "KQL"), ("KLK", "KLK"), ("A", "A")):
+            rel = np.abs(got[key][b, h] - r[ref_key]) / np.abs(r[ref_key])
+            assert rel.max() <= 1e-4, f"{key}: elementwise relative error {rel.max():.3e}"
+        assert normwise(got["X"][b, h], r["X"]) <= 2e-3, "Newton-Schulz result"
+        assert normwise(got["W"][b, h], r["W"]) <= 1e-5, "W = K_LK V"
+        assert normwise(got["O"][b, h], r["O"]) <= tol_for(w), "output"
+
+
+def test_serial_and_overlapped_plans_are_bitwise_equal():
+    w = wl.HEADLINE
+    _print_case(w, "serial vs overlapped")
+    x = wl.make_inputs(w)
+    a = run_gpu(w, x, serial=False)["O"]
+    b = run_gpu(w, x, serial=True)["O"]
+    c = run_gpu(w, x, serial=False)["O"]
+    assert np.array_equal(a, b) and np.array_equal(a, c)
+
+
+def test_device_errors_are_reported():
+    q = torch.zeros(1, 1, 196, 32, device="cuda")
+    with pytest.raises(ValueError):
+        api.forward(q, q, q, grid_h=14, grid_w=13, pool_h=2, pool_w=2, lam=1.0, eps=0.0, iters=1)
+    with pytest.raises(api._lib.LapattnError) as e:
+        api.forward(q, q, q, grid_h=14, grid_w=14, pool_h=2, pool_w=2, lam=-1.0, eps=0.0, iters=1)
+    assert e.value.status == api._lib.ERR_PARAM
+    with pytest.raises(api._lib.LapattnError) as e:
+        api.forward(q, q, q, grid_h=14, grid_w=14, pool_h=2, pool_w=2, lam=1.0, eps=0.0,
+                    iters=1, out=q)
+    assert e.value.status == api._lib.ERR_ALIAS
