@@ -73,18 +73,17 @@ def stage_work(w):
     """Algorithmic work per launch of each stage."""
     BH, N, d, m = w.heads, w.N, w.d, w.m
     e = 2 if w.dtype == "bf16" else 4
-    maps_pairs = BH * (1 if w.shared_qk else 2) * N * m * d
+    sides = 1 if w.shared_qk else 2
+    maps_pairs = BH * sides * N * m * d
     return {
         # bytes: read K once, write L
         "pool": {"bytes": BH * (N * d * e + m * d * 4)},
         # flops: A pairs (3/pair) + 2 m^3 multiply-adds per NS step (4 m^3 flops)
         "solver": {"flops": BH * (3 * m * m * d + 4 * m ** 3 * w.iters)},
-        # flops: 3 per coordinate pair (sub, |.|, add) or (sub, square, add)
+        # flops: 3 per coordinate pair (sub, |.|, add) or (sub, square, add);
+        # bytes: read the token rows of Q and K (once each) and V, write K_QL
         "maps": {"flops": 3 * maps_pairs, "pairs": maps_pairs,
-                 "bytes": BH * ((1 if w.shared_qk else 2) * N * d * e
-                                + (1 if w.shared_qk else 2) * m * N * 4)},
-        # bytes: read K_LK (fp32) and V, write W
-        "w": {"bytes": BH * (m * N * 4 + N * d * e + m * d * 4)},
+                 "bytes": BH * (sides * N * d * e + N * d * e + N * m * 4)},
         # bytes: read K_QL (fp32), write O
         "out": {"bytes": BH * (m * N * 4 + N * d * e)},
     }
@@ -255,7 +254,7 @@ def main(argv=None):
             "workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "m": w.m,
             "pool": f"{w.pool_h}x{w.pool_w}", "lambda": w.lam, "eps": w.eps,
             "iters": w.iters, "kernel": w.kernel,
-            "launch": "serial" if args.serial else "overlapped (solver on side stream)",
+            "launch": "serial (solver, then maps)" if args.serial else "fused (solver and map workgroups in one launch)",
         },
         "roofline": roofline,
         "stages": stages,

@@ -68,10 +68,12 @@ typedef enum {
 } lapattn_dtype_t;
 
 /* Launch-plan flags (lapattn_desc_t.flags). */
-#define LAPATTN_FLAG_SERIAL 1u  /* run every stage on `stream` only; by default
-                                   the Newton-Schulz solver runs on a library-
-                                   owned side stream, overlapped with the
-                                   kernel-map stage, joined before the output */
+#define LAPATTN_FLAG_SERIAL 1u  /* launch the Newton-Schulz solver and the
+                                   kernel-map/W stage as two kernels, one after
+                                   the other; by default one launch carries
+                                   both as separate workgroup roles, so the
+                                   solver overlaps the map stage.  Results are
+                                   bitwise identical either way. */
 
 enum {
   LAPATTN_OK = 0,
@@ -92,10 +94,9 @@ enum {
 /* Stages of one forward call, in launch order (for lapattn_set_stage_events). */
 #define LAPATTN_STAGE_POOL 0     /* landmark average pool                      */
 #define LAPATTN_STAGE_SOLVER 1   /* A = k(L,L) + eps I, alpha, Newton-Schulz  */
-#define LAPATTN_STAGE_MAPS 2     /* K_QL and K_LK kernel maps                  */
-#define LAPATTN_STAGE_W 3        /* W = K_LK V and the join Y = X W           */
-#define LAPATTN_STAGE_OUT 4      /* O = K_QL Y                                 */
-#define LAPATTN_NUM_STAGES 5
+#define LAPATTN_STAGE_MAPS 2     /* K_QL and K_LK maps, W = K_LK V, Y = X W   */
+#define LAPATTN_STAGE_OUT 3      /* O = K_QL Y                                 */
+#define LAPATTN_NUM_STAGES 4
 
 typedef struct {
   int32_t B, H;            /* batch and heads; every (b, h) is independent   */
@@ -123,9 +124,8 @@ int lapattn_check(const lapattn_desc_t* desc, float lambda, float eps, int32_t i
  * in B*H*N. */
 size_t lapattn_workspace_bytes(const lapattn_desc_t* desc);
 
-/* Creates the library's per-device side stream on the current device ahead
- * of time (otherwise it is created on the first overlapped call).  Safe to
- * call more than once and from several threads. */
+/* Checks that a HIP device is current.  The library keeps no per-device
+ * state, so this is optional; it exists so that callers can fail early. */
 int lapattn_init(void);
 
 /* O = K_QL (X (K_LK V)) per head, as defined at the top of this file.
@@ -161,7 +161,9 @@ int lapattn_forward_stages(const lapattn_desc_t* desc, const void* q,
 
 /* Profiling hook.  For the calling host thread, makes every later forward
  * call record events[2*s] right before and events[2*s+1] right after the
- * launch of stage s (LAPATTN_STAGE_*), on the stream that stage runs on.
+ * launch that carries stage s (LAPATTN_STAGE_*), on the caller's stream.  In
+ * the default plan the solver and map stages share one launch, so their two
+ * event pairs bracket the same launch.
  * `events` holds 2 * LAPATTN_NUM_STAGES hipEvent_t handles (as void*) created
  * by the caller with timing enabled, and must stay valid until the hook is
  * cleared with (NULL, 0).  n must be 0 or 2 * LAPATTN_NUM_STAGES. */

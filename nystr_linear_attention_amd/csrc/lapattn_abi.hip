@@ -4,7 +4,6 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
-#include <mutex>
 
 #include "lapattn.h"
 #include "lapattn_internal.h"
@@ -13,7 +12,6 @@ namespace lapattn {
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr int kMaxDevices = 64;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -59,15 +57,16 @@ Plan make_plan(const lapattn_desc_t* d) {
   p.N = p.gh * p.gw;
   p.m = (p.gh / p.ph) * (p.gw / p.pw);
   p.BH = p.B * p.H;
+  p.mpad = 16 * ((p.m + 15) / 16);
+  // Solver interior: whole 16x16 blocks; up to 4 border rows/columns go to
+  // VALU, otherwise the interior is padded up to the next block.
+  const int r = p.m % 16;
+  p.ns_mb = (r >= 1 && r <= 4) ? p.m / 16 : (p.m + 15) / 16;
   p.nT = (p.N + 63) / 64;
-  p.ng = (p.m + 7) / 8;  // about 8 landmarks per wave-level work unit
-  // W partials: at most 32 chunks per head, at least 128 tokens per chunk.
-  int nC = (p.N + 127) / 128;
-  if (nC > 32) nC = 32;
-  int CH = (p.N + nC - 1) / nC;
-  CH = (CH + 15) / 16 * 16;
-  p.CH = CH;
-  p.nC = (p.N + CH - 1) / CH;
+  // Key-side workgroups cover S tiles each so that a head has at most 32 W
+  // partials.
+  p.S = (p.nT + 31) / 32;
+  p.nP = (p.nT + p.S - 1) / p.S;
 
   const size_t BH = static_cast<size_t>(p.BH);
   const size_t f = sizeof(float);
@@ -76,18 +75,16 @@ Plan make_plan(const lapattn_desc_t* d) {
   off = align_up(off + BH * CTR_PER_HEAD * sizeof(unsigned));
   p.off_L = off;
   off = align_up(off + BH * p.m * p.D * f);
-  p.off_kqlt = off;
-  off = align_up(off + BH * p.m * p.N * f);
-  p.off_klkt = off;
-  off = align_up(off + BH * p.m * p.N * f);
+  p.off_kql = off;
+  off = align_up(off + BH * p.N * p.mpad * f);
   p.off_wpart = off;
-  off = align_up(off + BH * p.nC * MP * p.D * f);
-  p.off_w = off;
-  off = align_up(off + BH * MP * p.D * f);
+  off = align_up(off + BH * p.nP * p.D * MP * f);
+  p.off_wt = off;
+  off = align_up(off + BH * p.D * MP * f);
   p.off_x = off;
   off = align_up(off + BH * MP * MP * f);
-  p.off_y = off;
-  off = align_up(off + BH * MP * p.D * f);
+  p.off_yt = off;
+  off = align_up(off + BH * p.D * MP * f);
   p.total = off;
   return p;
 }
@@ -95,26 +92,6 @@ Plan make_plan(const lapattn_desc_t* d) {
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
   return x < y + nb && y < x + na;
-}
-
-// Per-device side stream and fork/join events for the overlapped plan.
-struct DeviceCtx {
-  hipStream_t side = nullptr;
-  hipEvent_t fork = nullptr;
-  hipEvent_t join = nullptr;
-  bool ready = false;
-};
-std::mutex g_mu[kMaxDevices];
-DeviceCtx g_ctx[kMaxDevices];
-
-int ensure_ctx(int dev) {
-  DeviceCtx& c = g_ctx[dev];
-  if (c.ready) return LAPATTN_OK;
-  if (hipStreamCreateWithFlags(&c.side, hipStreamNonBlocking) != hipSuccess) return LAPATTN_ERR_HIP;
-  if (hipEventCreateWithFlags(&c.fork, hipEventDisableTiming) != hipSuccess) return LAPATTN_ERR_HIP;
-  if (hipEventCreateWithFlags(&c.join, hipEventDisableTiming) != hipSuccess) return LAPATTN_ERR_HIP;
-  c.ready = true;
-  return LAPATTN_OK;
 }
 
 // Per-thread stage events (profiling hook).
@@ -152,47 +129,30 @@ int run(const lapattn_desc_t* desc, const Args& a, void* workspace, size_t ws_by
   Buffers b;
   b.ctr = reinterpret_cast<unsigned*>(ws + p.off_ctr);
   b.L = reinterpret_cast<float*>(ws + p.off_L);
-  b.kqlt = reinterpret_cast<float*>(ws + p.off_kqlt);
-  b.klkt = reinterpret_cast<float*>(ws + p.off_klkt);
+  b.kql = reinterpret_cast<float*>(ws + p.off_kql);
   b.wpart = reinterpret_cast<float*>(ws + p.off_wpart);
-  b.w = reinterpret_cast<float*>(ws + p.off_w);
+  b.wt = reinterpret_cast<float*>(ws + p.off_wt);
   b.x = reinterpret_cast<float*>(ws + p.off_x);
-  b.y = reinterpret_cast<float*>(ws + p.off_y);
+  b.yt = reinterpret_cast<float*>(ws + p.off_yt);
 
-  const bool serial = (desc->flags & LAPATTN_FLAG_SERIAL) != 0;
   auto pool = [&] { return launch_pool(p, a, b, stream); };
-  auto maps = [&] { return launch_maps(p, a, b, stream); };
-  auto wred = [&] { return launch_w(p, a, b, 2, stream); };
   auto out = [&] { return launch_out(p, a, b, stream); };
-  if (serial) {
-    auto ns = [&] { return launch_ns(p, a, b, 2, stream); };
-    if (!stage(LAPATTN_STAGE_POOL, stream, pool)) return LAPATTN_ERR_HIP;
-    if (!stage(LAPATTN_STAGE_SOLVER, stream, ns)) return LAPATTN_ERR_HIP;
-    if (!stage(LAPATTN_STAGE_MAPS, stream, maps)) return LAPATTN_ERR_HIP;
-    if (!stage(LAPATTN_STAGE_W, stream, wred)) return LAPATTN_ERR_HIP;
-    if (!stage(LAPATTN_STAGE_OUT, stream, out)) return LAPATTN_ERR_HIP;
-    if (launch_export(p, a, b, stream) != hipSuccess) return LAPATTN_ERR_HIP;
-    return LAPATTN_OK;
-  }
-
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LAPATTN_ERR_HIP;
-  std::lock_guard<std::mutex> lock(g_mu[dev]);
-  if (ensure_ctx(dev) != LAPATTN_OK) return LAPATTN_ERR_HIP;
-  DeviceCtx& c = g_ctx[dev];
-  auto ns = [&] { return launch_ns(p, a, b, 2, c.side); };
-  // stream: pool -> (fork) -> maps -> w -> (wait join) -> out
-  // side:           (wait fork) -> ns -> (join)
   if (!stage(LAPATTN_STAGE_POOL, stream, pool)) return LAPATTN_ERR_HIP;
-  if (hipEventRecord(c.fork, stream) != hipSuccess) return LAPATTN_ERR_HIP;
-  if (hipStreamWaitEvent(c.side, c.fork, 0) != hipSuccess) return LAPATTN_ERR_HIP;
-  if (!stage(LAPATTN_STAGE_SOLVER, c.side, ns)) return LAPATTN_ERR_HIP;
-  if (hipEventRecord(c.join, c.side) != hipSuccess) return LAPATTN_ERR_HIP;
-  if (!stage(LAPATTN_STAGE_MAPS, stream, maps)) return LAPATTN_ERR_HIP;
-  if (!stage(LAPATTN_STAGE_W, stream, wred)) return LAPATTN_ERR_HIP;
-  if (hipStreamWaitEvent(stream, c.join, 0) != hipSuccess) return LAPATTN_ERR_HIP;
+  if (desc->flags & LAPATTN_FLAG_SERIAL) {
+    auto solver = [&] { return launch_main(p, a, b, true, false, stream); };
+    auto maps = [&] { return launch_main(p, a, b, false, true, stream); };
+    if (!stage(LAPATTN_STAGE_SOLVER, stream, solver)) return LAPATTN_ERR_HIP;
+    if (!stage(LAPATTN_STAGE_MAPS, stream, maps)) return LAPATTN_ERR_HIP;
+  } else {
+    // One launch carries both roles: its event pairs for the solver and the
+    // map stage bracket the same launch.
+    if (!mark(2 * LAPATTN_STAGE_SOLVER, stream) || !mark(2 * LAPATTN_STAGE_MAPS, stream))
+      return LAPATTN_ERR_HIP;
+    if (launch_main(p, a, b, true, true, stream) != hipSuccess) return LAPATTN_ERR_HIP;
+    if (!mark(2 * LAPATTN_STAGE_SOLVER + 1, stream) || !mark(2 * LAPATTN_STAGE_MAPS + 1, stream))
+      return LAPATTN_ERR_HIP;
+  }
   if (!stage(LAPATTN_STAGE_OUT, stream, out)) return LAPATTN_ERR_HIP;
-  if (launch_export(p, a, b, stream) != hipSuccess) return LAPATTN_ERR_HIP;
   return LAPATTN_OK;
 }
 
@@ -267,10 +227,8 @@ int lapattn_set_stage_events(void* const* events, int n) {
 
 int lapattn_init(void) {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= lapattn::kMaxDevices)
-    return LAPATTN_ERR_HIP;
-  std::lock_guard<std::mutex> lock(lapattn::g_mu[dev]);
-  return lapattn::ensure_ctx(dev);
+  if (hipGetDevice(&dev) != hipSuccess) return LAPATTN_ERR_HIP;
+  return LAPATTN_OK;
 }
 
 int lapattn_forward(const lapattn_desc_t* desc, const void* q, const void* k, const void* v,

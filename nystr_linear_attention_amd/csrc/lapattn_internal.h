@@ -7,8 +7,8 @@
 
 namespace lapattn {
 
-// Landmarks are padded to MP rows/columns inside the solver and the small
-// contractions; padding rows and columns hold exact zeros.
+// Small per-head matrices (A, X, W^T, Y^T) are stored padded to MP columns;
+// padding holds exact zeros.
 constexpr int MP = 64;
 // Counters per head in the workspace: [0] W partials done, [1] join of the
 // solver and the W reduction.
@@ -19,24 +19,24 @@ struct Plan {
   int kernel;   // 0 Laplacian, 1 Gaussian
   int bf16;     // 0 fp32 I/O, 1 bf16 I/O
   int N, m, BH;
+  int mpad;     // 16 * ceil(m / 16): row length of the stored K_QL
+  int ns_mb;    // 16x16 MFMA blocks per side in the solver interior
   int nT;       // 64-token tiles per head
-  int ng;       // landmark groups per tile in the map stage
-  int CH;       // tokens per W-partial chunk (multiple of 16)
-  int nC;       // W-partial chunks per head
+  int S;        // tiles per key-side workgroup
+  int nP;       // key-side workgroups (= W partials) per head
   // workspace byte offsets
-  size_t off_ctr, off_L, off_kqlt, off_klkt, off_wpart, off_w, off_x, off_y;
+  size_t off_ctr, off_L, off_kql, off_wpart, off_wt, off_x, off_yt;
   size_t total;
 };
 
 struct Buffers {
   unsigned* ctr;
-  float* L;      // [BH][m][D]
-  float* kqlt;   // [BH][m][N]  k(q_n, l_j) at [j][n]
-  float* klkt;   // [BH][m][N]  k(l_j, k_n) at [j][n]
-  float* wpart;  // [BH][nC][MP][D]
-  float* w;      // [BH][MP][D]
-  float* x;      // [BH][MP][MP]
-  float* y;      // [BH][MP][D]
+  float* L;      // [BH][m][D]     landmarks
+  float* kql;    // [BH][N][mpad]  k(q_n, l_j), zero for j >= m
+  float* wpart;  // [BH][nP][D][MP] partial W^T
+  float* wt;     // [BH][D][MP]    W^T = (K_LK V)^T
+  float* x;      // [BH][MP][MP]   Newton-Schulz result (symmetric)
+  float* yt;     // [BH][D][MP]    Y^T = (X W)^T
 };
 
 struct Args {
@@ -56,11 +56,12 @@ struct Args {
   float* st_w;
 };
 
+// Stage launchers.  `with_solver` / `with_maps` select which workgroup roles
+// the main launch carries: both (one fused launch), or one each in two
+// launches.
 hipError_t launch_pool(const Plan& p, const Args& a, const Buffers& b, hipStream_t s);
-hipError_t launch_ns(const Plan& p, const Args& a, const Buffers& b, int join_target, hipStream_t s);
-hipError_t launch_maps(const Plan& p, const Args& a, const Buffers& b, hipStream_t s);
-hipError_t launch_w(const Plan& p, const Args& a, const Buffers& b, int join_target, hipStream_t s);
+hipError_t launch_main(const Plan& p, const Args& a, const Buffers& b, bool with_solver,
+                       bool with_maps, hipStream_t s);
 hipError_t launch_out(const Plan& p, const Args& a, const Buffers& b, hipStream_t s);
-hipError_t launch_export(const Plan& p, const Args& a, const Buffers& b, hipStream_t s);
 
 }  // namespace lapattn

@@ -1,14 +1,17 @@
 // HIP kernels for Nystrom kernel attention (forward) on gfx950.
 //
-// Stages (one head = one (b, h) pair, all heads batched in every launch):
-//   pool  : landmarks L = window means of K                   (HBM stream)
-//   ns    : A = k(L, L) + eps I, alpha, Newton-Schulz in LDS   (one CU per head,
-//           fp32 MFMA 16x16x4)
-//   maps  : K_QL^T, K_LK^T = exp(-dist(token, landmark)/lambda) (FP32 VALU; the
-//           landmark coordinates are wave-uniform scalar operands)
-//   w     : W = K_LK V as per-chunk partials on fp32 MFMA, deterministic
-//           last-block reduction, then the join that forms Y = X W
-//   out   : O = K_QL Y on fp32 MFMA, fp32 or bf16 (RNE) store
+// Three launches per forward call, all on the caller's stream:
+//   pool : landmarks L = window means of K                         (HBM stream)
+//   main : role-split workgroups
+//          - solver WGs (one per head, dispatched first, raised wave priority):
+//            A = k(L, L) + eps I, alpha, Newton-Schulz held in LDS, fp32 MFMA
+//          - map WGs: kernel values of 64 tokens against every landmark on
+//            FP32 VALU (landmark coordinates are wave-uniform scalar operands);
+//            query tiles store K_QL, key tiles contract K_LK V on fp32 MFMA
+//            into per-workgroup partials; the last key workgroup of a head sums
+//            them in fixed order, and whichever of {solver, W reduction} ends
+//            second forms Y = X W.
+//   out  : O = K_QL Y on fp32 MFMA, fp32 or bf16 (RNE) store.
 //
 // Pages behind each step: average-pool landmarks (SOFT review, "method";
 // LaplacianFormer summaries, Nystrom paragraph), Laplacian kernel
@@ -17,6 +20,12 @@
 // Newton-Schulz recursion A_0 = alpha A, A_{k+1} = 2 A_k - A_k A A_k
 // (LaplacianFormer summaries; SOFT review, "method"), S_hat = P^T A^+ P
 // (SOFT review, "method").
+//
+// MFMA operand convention used throughout (v_mfma_f32_16x16x4f32): for an
+// output block D[16][16] += sum_k A[i][k] B[k][j], lane l = 16*g + r supplies
+// A[r][k] and B[k][r] at sub-step s with k = KS*g + s (KS sub-steps), so each
+// lane reads KS *contiguous* k values of one row of A and one row of B^T.
+// The accumulator holds D[4g + i][r], i = 0..3.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -28,56 +37,11 @@ namespace {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-constexpr int LDA = MP + 1;   // LDS row stride of the 64x64 solver matrices
-constexpr int WG = 256;       // 4 wave64 per workgroup everywhere
-
-__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
-  return __uint_as_float(static_cast<uint32_t>(h) << 16);
-}
-
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
-}
-
-template <bool BF16>
-__device__ __forceinline__ float load_elem(const void* p, size_t i) {
-  if constexpr (BF16) {
-    return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
-  } else {
-    return static_cast<const float*>(p)[i];
-  }
-}
-
-// Loads D consecutive elements (one token row) into registers as fp32.
-template <int D, bool BF16>
-__device__ __forceinline__ void load_row(const void* base, size_t row, float* x) {
-  if constexpr (BF16) {
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + row * D);
-#pragma unroll
-    for (int i = 0; i < D / 8; ++i) {
-      uint4 u = p[i];
-      uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        x[8 * i + 2 * h] = __uint_as_float(w[h] << 16);
-        x[8 * i + 2 * h + 1] = __uint_as_float(w[h] & 0xffff0000u);
-      }
-    }
-  } else {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + row * D);
-#pragma unroll
-    for (int i = 0; i < D / 4; ++i) {
-      float4 u = p[i];
-      x[4 * i] = u.x;
-      x[4 * i + 1] = u.y;
-      x[4 * i + 2] = u.z;
-      x[4 * i + 3] = u.w;
-    }
-  }
-}
+constexpr int LS = 68;        // LDS row stride (floats) of 64-wide tiles: 16-B rows
+constexpr int WGM = 512;      // main kernel: 8 wave64
+constexpr int WGS = 256;      // pool / out kernels: 4 wave64
+constexpr int TILE = 64;      // tokens per map tile (one per lane)
+constexpr int NGRP = 8;       // landmark groups per map tile (one per wave)
 
 __device__ __forceinline__ f4 mfma4(float a, float b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -87,74 +51,82 @@ __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }
 
-// ---------------------------------------------------------------------------
-// pool: one workgroup per (landmark, head).  Thread (g, c) sums coordinate c
-// over every (WG/D)-th token of the window; a fixed-order LDS reduction
-// finishes the mean.  Workgroup (0, bh) also clears the head's counters.
-// ---------------------------------------------------------------------------
-template <int D, bool BF16>
-__global__ __launch_bounds__(WG) void pool_kernel(const void* __restrict__ K,
-                                                  float* __restrict__ L,
-                                                  unsigned* __restrict__ ctr,
-                                                  float* __restrict__ st_L, int gw,
-                                                  int ph, int pw, int m, int N) {
-  constexpr int G = WG / D;
-  __shared__ float part[WG];
-  const int j = blockIdx.x, bh = blockIdx.y;
-  const int tid = threadIdx.x, c = tid % D, g = tid / D;
-  const int mw = gw / pw;
-  const int R = j / mw, C = j % mw;
-  const int cnt = ph * pw;
-  float s = 0.f;
-  for (int t = g; t < cnt; t += G) {
-    const int n = (R * ph + t / pw) * gw + C * pw + t % pw;
-    s += load_elem<BF16>(K, (static_cast<size_t>(bh) * N + n) * D + c);
-  }
-  part[tid] = s;
-  __syncthreads();
-  if (g == 0) {
-    float acc = 0.f;
-#pragma unroll
-    for (int i = 0; i < G; ++i) acc += part[i * D + c];
-    const float mean = acc / static_cast<float>(cnt);
-    L[(static_cast<size_t>(bh) * m + j) * D + c] = mean;
-    if (st_L) st_L[(static_cast<size_t>(bh) * m + j) * D + c] = mean;
-  }
-  if (j == 0 && tid < CTR_PER_HEAD) ctr[bh * CTR_PER_HEAD + tid] = 0u;
+__device__ __forceinline__ f4 ld4(const float* p) { return *reinterpret_cast<const f4*>(p); }
+__device__ __forceinline__ void st4(float* p, f4 v) { *reinterpret_cast<f4*>(p) = v; }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
 }
 
-// ---------------------------------------------------------------------------
-// Y = X W for one head, all 256 threads: wave w computes rows 16w..16w+15.
-// X [MP][MP] and W [MP][D] are read from global memory (after an acquire).
-// ---------------------------------------------------------------------------
+// Four consecutive elements (16-B aligned for fp32, 8-B for bf16) as fp32.
+__device__ __forceinline__ f4 load4_io(const void* base, size_t idx, int bf16) {
+  if (bf16) {
+    const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + idx);
+    return f4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+              __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
+  }
+  return ld4(static_cast<const float*>(base) + idx);
+}
+
+__device__ __forceinline__ float load1_io(const void* base, size_t idx, int bf16) {
+  if (bf16) return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(base)[idx]) << 16);
+  return static_cast<const float*>(base)[idx];
+}
+
+// One token row of D elements into registers.
 template <int D>
-__device__ void compute_y(const float* __restrict__ X, const float* __restrict__ W,
-                          float* __restrict__ Y, int m) {
-  constexpr int CB = D / 16;
-  const int lane = threadIdx.x & 63, w = wave_id();
-  const int ksteps = (m + 3) >> 2;
-  f4 acc[CB];
+__device__ __forceinline__ void load_row(const void* base, size_t row, int bf16, float* x) {
+  if (bf16) {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + row * D);
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) acc[cb] = f4{0.f, 0.f, 0.f, 0.f};
-  for (int kk = 0; kk < ksteps; ++kk) {
-    const int kr = 4 * kk + (lane >> 4);
-    const float a = X[(16 * w + (lane & 15)) * MP + kr];
+    for (int i = 0; i < D / 8; ++i) {
+      const uint4 u = p[i];
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      const float b = W[kr * D + 16 * cb + (lane & 15)];
-      acc[cb] = mfma4(a, b, acc[cb]);
+      for (int h = 0; h < 4; ++h) {
+        x[8 * i + 2 * h] = __uint_as_float(w[h] << 16);
+        x[8 * i + 2 * h + 1] = __uint_as_float(w[h] & 0xffff0000u);
+      }
+    }
+  } else {
+    const f4* p = reinterpret_cast<const f4*>(static_cast<const float*>(base) + row * D);
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i) {
+      const f4 u = p[i];
+      x[4 * i] = u[0];
+      x[4 * i + 1] = u[1];
+      x[4 * i + 2] = u[2];
+      x[4 * i + 3] = u[3];
     }
   }
-#pragma unroll
-  for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      Y[(16 * w + 4 * (lane >> 4) + i) * D + 16 * cb + (lane & 15)] = acc[cb][i];
 }
 
-// Last-arrival join: returns true in every thread of the workgroup that
-// completes the count.  All prior global stores of the workgroup are released
-// before the increment and the winner acquires before returning.
+// Distance of a register-resident point to a wave-uniform point `l`
+// (scalar loads): L1 for KIND 0, squared L2 for KIND 1.  Two partial sums.
+template <int D, int KIND>
+__device__ __forceinline__ float dist_to(const float* x, const float* __restrict__ l) {
+  float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+  for (int k = 0; k < D; k += 2) {
+    const float t0 = x[k] - l[k];
+    const float t1 = x[k + 1] - l[k + 1];
+    if constexpr (KIND == 0) {
+      d0 += fabsf(t0);
+      d1 += fabsf(t1);
+    } else {
+      d0 = fmaf(t0, t0, d0);
+      d1 = fmaf(t1, t1, d1);
+    }
+  }
+  return d0 + d1;
+}
+
+// Last-arrival join: true in every thread of the workgroup that completes the
+// count.  Prior global stores are released before the increment; the winner
+// acquires before it returns.
 __device__ __forceinline__ bool arrive(unsigned* counter, unsigned target, int* flag_lds) {
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -168,364 +140,617 @@ __device__ __forceinline__ bool arrive(unsigned* counter, unsigned target, int* 
   return last;
 }
 
-// ---------------------------------------------------------------------------
-// ns: one workgroup per head.  A = k(L, L) + eps I is built in LDS, then
-// `iters` Newton-Schulz steps run on fp32 MFMA with every matrix held in LDS:
-//   T = A X_t        (A operand held in registers for the whole solve)
-//   X_{t+1} = 2 X_t - X_t T
-// Wave w owns block-row w (rows 16w..16w+15) of every product.
-// ---------------------------------------------------------------------------
-template <int D, int KIND>
-__global__ __launch_bounds__(WG) void ns_kernel(const float* __restrict__ Lw,
-                                                float* __restrict__ Xw,
-                                                const float* __restrict__ Ww,
-                                                float* __restrict__ Yw,
-                                                unsigned* __restrict__ ctr,
-                                                float* __restrict__ st_a,
-                                                float* __restrict__ st_x, int m,
-                                                float c_exp2, float eps, int iters,
-                                                int join_target) {
-  __shared__ float S0[MP * LDA];  // L, then T
-  __shared__ float S1[MP * LDA];  // A, then X buffer 1
-  __shared__ float S2[MP * LDA];  // X buffer 0
-  __shared__ float red[2 * WG];
-  __shared__ int flag;
-  const int bh = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
-  const int lr = lane & 15, lg = lane >> 4;
-  const int ksteps = (m + 3) >> 2;
-
-  // Landmarks -> LDS (row stride D+1), zero the A buffer.
-  const float* L = Lw + static_cast<size_t>(bh) * m * D;
-  for (int e = tid; e < m * D; e += WG) S0[(e / D) * (D + 1) + (e % D)] = L[e];
-  for (int e = tid; e < MP * LDA; e += WG) S1[e] = 0.f;
-  __syncthreads();
-
-  // A[i][j] for i <= j, mirrored: the distance is symmetric term by term.
-  for (int e = tid; e < m * m; e += WG) {
-    const int i = e / m, j = e - i * m;
-    if (i > j) continue;
-    const float* li = S0 + i * (D + 1);
-    const float* lj = S0 + j * (D + 1);
-    float d0 = 0.f, d1 = 0.f;
-#pragma unroll
-    for (int k = 0; k < D; k += 2) {
-      const float t0 = li[k] - lj[k];
-      const float t1 = li[k + 1] - lj[k + 1];
-      if constexpr (KIND == 0) {
-        d0 += fabsf(t0);
-        d1 += fabsf(t1);
-      } else {
-        d0 = fmaf(t0, t0, d0);
-        d1 = fmaf(t1, t1, d1);
-      }
-    }
-    float a = exp2f((d0 + d1) * c_exp2);
-    if (i == j) a += eps;
-    S1[i * LDA + j] = a;
-    S1[j * LDA + i] = a;
-  }
-  __syncthreads();
-
-  if (st_a) {
-    for (int e = tid; e < m * m; e += WG)
-      st_a[static_cast<size_t>(bh) * m * m + e] = S1[(e / m) * LDA + (e % m)];
-  }
-
-  // alpha = 1 / (max column abs-sum * max row abs-sum).
-  {
-    float cs = 0.f, rs = 0.f;
-    if (tid < m) {
-      for (int i = 0; i < m; ++i) {
-        cs += fabsf(S1[i * LDA + tid]);
-        rs += fabsf(S1[tid * LDA + i]);
-      }
-    }
-    red[tid] = cs;
-    red[WG + tid] = rs;
-  }
-  __syncthreads();
-  for (int s = WG / 2; s > 0; s >>= 1) {
-    if (tid < s) {
-      red[tid] = fmaxf(red[tid], red[tid + s]);
-      red[WG + tid] = fmaxf(red[WG + tid], red[WG + tid + s]);
-    }
-    __syncthreads();
-  }
-  const float alpha = 1.0f / (red[0] * red[WG]);
-
-  // A operand of T = A X (block-row w) stays in registers.
-  float a_reg[16];
-#pragma unroll
-  for (int kk = 0; kk < 16; ++kk) a_reg[kk] = S1[(16 * w + lr) * LDA + 4 * kk + lg];
-  // X_0 = alpha A, block-row w in accumulator layout.
-  f4 xr[4];
-#pragma unroll
-  for (int bj = 0; bj < 4; ++bj)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) xr[bj][i] = alpha * S1[(16 * w + 4 * lg + i) * LDA + 16 * bj + lr];
-#pragma unroll
-  for (int bj = 0; bj < 4; ++bj)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) S2[(16 * w + 4 * lg + i) * LDA + 16 * bj + lr] = xr[bj][i];
-  __syncthreads();
-
-  for (int t = 0; t < iters; ++t) {
-    float* Xc = (t & 1) ? S1 : S2;
-    float* Xn = (t & 1) ? S2 : S1;
-    // T = A X_t
-    f4 acc[4];
-#pragma unroll
-    for (int bj = 0; bj < 4; ++bj) acc[bj] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      if (kk < ksteps) {
-#pragma unroll
-        for (int bj = 0; bj < 4; ++bj) {
-          const float b = Xc[(4 * kk + lg) * LDA + 16 * bj + lr];
-          acc[bj] = mfma4(a_reg[kk], b, acc[bj]);
-        }
-      }
-    }
-#pragma unroll
-    for (int bj = 0; bj < 4; ++bj)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) S0[(16 * w + 4 * lg + i) * LDA + 16 * bj + lr] = acc[bj][i];
-    __syncthreads();
-    // X_{t+1} = 2 X_t - X_t T
-#pragma unroll
-    for (int bj = 0; bj < 4; ++bj) acc[bj] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      if (kk < ksteps) {
-        const float a = Xc[(16 * w + lr) * LDA + 4 * kk + lg];
-#pragma unroll
-        for (int bj = 0; bj < 4; ++bj) {
-          const float b = S0[(4 * kk + lg) * LDA + 16 * bj + lr];
-          acc[bj] = mfma4(a, b, acc[bj]);
-        }
-      }
-    }
-#pragma unroll
-    for (int bj = 0; bj < 4; ++bj)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        xr[bj][i] = 2.0f * xr[bj][i] - acc[bj][i];
-        Xn[(16 * w + 4 * lg + i) * LDA + 16 * bj + lr] = xr[bj][i];
-      }
-    __syncthreads();
-  }
-
-  float* X = Xw + static_cast<size_t>(bh) * MP * MP;
-#pragma unroll
-  for (int bj = 0; bj < 4; ++bj)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) X[(16 * w + 4 * lg + i) * MP + 16 * bj + lr] = xr[bj][i];
-  if (st_x) {
-#pragma unroll
-    for (int bj = 0; bj < 4; ++bj)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + 4 * lg + i, c = 16 * bj + lr;
-        if (r < m && c < m) st_x[static_cast<size_t>(bh) * m * m + r * m + c] = xr[bj][i];
-      }
-  }
-
-  if (arrive(&ctr[bh * CTR_PER_HEAD + 1], static_cast<unsigned>(join_target), &flag)) {
-    compute_y<D>(X, Ww + static_cast<size_t>(bh) * MP * D, Yw + static_cast<size_t>(bh) * MP * D, m);
-  }
-}
+struct MainArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* L;     // [BH][m][D]
+  float* kql;         // [BH][N][mpad]
+  float* wpart;       // [BH][nP][D][MP]
+  float* wt;          // [BH][D][MP]
+  float* xw;          // [BH][MP][MP]
+  float* yt;          // [BH][D][MP]
+  unsigned* ctr;
+  float* st_a;
+  float* st_x;
+  float* st_w;
+  float* st_kql;
+  float* st_klk;
+  int N, m, BH, nT, S, nP, mpad;
+  int ns_blocks;      // workgroups [0, ns_blocks) are solver workgroups
+  int nQ;             // query-tile workgroups per head (0 when Q == K)
+  int shared_qk;      // Q and K are the same tensor
+  int kind, bf16, iters;
+  float c_exp2, eps;
+};
 
 // ---------------------------------------------------------------------------
-// maps: each wave computes the kernel values of 64 tokens (one per lane, the
-// token's D coordinates in registers) against a group of landmarks.  The
-// landmark coordinates are wave-uniform and are read with scalar loads, so the
-// inner loop is two VALU operations per coordinate pair (sub, add with |.|
-// modifier; sub, fma for the Gaussian).  Results go to [m][N] rows so every
-// store is one coalesced 256-byte line per landmark.
-// Work unit u = (role, head, tile, group), group fastest.
+// Y^T = W^T X for one head (X symmetric): 8 waves, output blocks
+// (cb, rb), cb < D/16, rb < MBY; both operands are contiguous row reads.
 // ---------------------------------------------------------------------------
-template <int D, int KIND, bool BF16>
-__global__ __launch_bounds__(WG) void maps_kernel(const void* __restrict__ Q,
-                                                  const void* __restrict__ K,
-                                                  const float* __restrict__ Lw,
-                                                  float* __restrict__ kqlt,
-                                                  float* __restrict__ klkt, int N, int m,
-                                                  int nT, int ng, int nroles, int BH,
-                                                  float c_exp2) {
-  const int lane = threadIdx.x & 63;
-  const int u = blockIdx.x * (WG / 64) + wave_id();
-  const int total = nroles * BH * nT * ng;
-  if (u >= total) return;
-  const int g = u % ng;
-  const int r1 = u / ng;
-  const int t = r1 % nT;
-  const int r2 = r1 / nT;
-  const int bh = r2 % BH;
-  const int role = r2 / BH;  // 0: keys -> K_LK^T, 1: queries -> K_QL^T
-  const void* src = role == 0 ? K : Q;
-  float* dst = role == 0 ? klkt : kqlt;
-
-  const int n = t * 64 + lane;
-  const int nc = n < N ? n : N - 1;
-  float x[D];
-  load_row<D, BF16>(src, static_cast<size_t>(bh) * N + nc, x);
-
-  const int jb = (g * m) / ng, je = ((g + 1) * m) / ng;
-  const float* Lh = Lw + static_cast<size_t>(bh) * m * D;
-  float* out = dst + static_cast<size_t>(bh) * m * N + n;
-  for (int j = jb; j < je; ++j) {
-    const float* lj = Lh + j * D;
-    float d0 = 0.f, d1 = 0.f;
-#pragma unroll
-    for (int k = 0; k < D; k += 2) {
-      const float t0 = x[k] - lj[k];
-      const float t1 = x[k + 1] - lj[k + 1];
-      if constexpr (KIND == 0) {
-        d0 += fabsf(t0);
-        d1 += fabsf(t1);
-      } else {
-        d0 = fmaf(t0, t0, d0);
-        d1 = fmaf(t1, t1, d1);
-      }
-    }
-    const float kv = exp2f((d0 + d1) * c_exp2);
-    if (n < N) out[static_cast<size_t>(j) * N] = kv;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// w: W = K_LK V.  Workgroup (head, chunk) reduces CH tokens on fp32 MFMA
-// (wave w: landmark rows 16w..16w+15, all D columns) into a partial; the last
-// chunk of a head sums the partials in fixed order (deterministic), then
-// joins with the solver: whichever finishes second forms Y = X W.
-// Within a 16-token step, lane group g = lane/16 owns tokens 4g..4g+3 and MFMA
-// sub-step s consumes token 4g+s from both operands.
-// ---------------------------------------------------------------------------
-template <int D, bool BF16>
-__global__ __launch_bounds__(WG) void w_kernel(const float* __restrict__ klkt,
-                                               const void* __restrict__ V,
-                                               float* __restrict__ wpart,
-                                               float* __restrict__ Ww,
-                                               const float* __restrict__ Xw,
-                                               float* __restrict__ Yw,
-                                               unsigned* __restrict__ ctr,
-                                               float* __restrict__ st_w, int N, int m,
-                                               int CH, int nC, int join_target) {
-  constexpr int CB = D / 16;
-  __shared__ int flag;
-  const int bh = blockIdx.x / nC, ch = blockIdx.x % nC;
+template <int D, int MBY>
+__device__ void compute_yt(const float* __restrict__ wt, const float* __restrict__ X,
+                           float* __restrict__ yt) {
+  constexpr int KS = 4 * MBY;
+  constexpr int CBN = D / 16;
   const int lane = threadIdx.x & 63, w = wave_id();
   const int lr = lane & 15, lg = lane >> 4;
-  const int row = 16 * w + lr;
-  const bool row_ok = row < m;
-  const float* P = klkt + (static_cast<size_t>(bh) * m + (row_ok ? row : 0)) * N;
-  const size_t vbase = static_cast<size_t>(bh) * N;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int b = w + 8 * s;
+    if (b < CBN * MBY) {
+      const int cb = b % CBN, rb = b / CBN;
+      const float* ar = wt + (16 * cb + lr) * MP + KS * lg;
+      const float* br = X + (16 * rb + lr) * MP + KS * lg;
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < KS / 4; ++q) {
+        const f4 a4 = ld4(ar + 4 * q), b4 = ld4(br + 4 * q);
+        acc = mfma4(a4[0], b4[0], acc);
+        acc = mfma4(a4[1], b4[1], acc);
+        acc = mfma4(a4[2], b4[2], acc);
+        acc = mfma4(a4[3], b4[3], acc);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) yt[(16 * cb + 4 * lg + i) * MP + 16 * rb + lr] = acc[i];
+    }
+  }
+}
 
-  f4 acc[CB];
+template <int D>
+__device__ void compute_yt_any(const float* wt, const float* X, float* yt, int m) {
+  switch ((m + 15) >> 4) {
+    case 1: compute_yt<D, 1>(wt, X, yt); break;
+    case 2: compute_yt<D, 2>(wt, X, yt); break;
+    case 3: compute_yt<D, 3>(wt, X, yt); break;
+    default: compute_yt<D, 4>(wt, X, yt); break;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Solver role.  Matrices live in LDS (64 x LS floats, zero padded):
+//   A  (row-major; exactly symmetric by construction)
+//   XR (X_t row-major), XT (X_t transposed), TT (T transposed)
+//   phase 1: T = A X_t          operands: rows of A, rows of XT
+//   phase 2: X_{t+1} = 2 X_t - X_t T   operands: rows of XR, rows of TT
+// The recursion is evaluated as printed, with full (unsymmetrised)
+// products: forcing the iterates symmetric turns the quadratic error
+// contraction of the Newton step into a linear map with gain up to
+// (1 + cond(A)) / 2, which diverges near convergence for ill-conditioned A.
+// With m = 16*MB + r, r <= 4, the interior 16MB x 16MB blocks run on MFMA and
+// the r border rows/columns on VALU (rank-r update of the interior blocks
+// plus border dot products); when m % 16 > 4 the interior is padded up to
+// whole blocks and r = 0.
+// ---------------------------------------------------------------------------
+template <int MB>
+struct SolverGeom {
+  static constexpr int NBLK = MB * MB;            // interior 16x16 blocks
+  static constexpr int KS = 4 * MB;               // MFMA sub-steps per block
+  static constexpr int NBQ = 4 * MB + 1;          // float4 reads per border dot
+  // waves [BW0, 8) share the border entries (fewest interior blocks)
+  static constexpr int BW0 = MB == 0 ? 0 : (MB == 2 ? 4 : 1);
+};
+
+// Border entry e -> (a, b): Z[a][b] with b a border column (a < m) or a a
+// border row (b < 16 MB).
+template <int MB>
+__device__ __forceinline__ void border_ab(int e, int m, int r, int& a, int& b) {
+  a = e % m;
+  b = 16 * MB + e / m;
+  if constexpr (MB > 0) {
+    if (e >= r * m) {
+      const int e2 = e - r * m;
+      a = 16 * MB + e2 / (16 * MB);
+      b = e2 % (16 * MB);
+    }
+  }
+}
+
+// Interior blocks of Z = Lm R, with Lm given by rows and R by the rows of
+// R^T (Rt), in accumulator layout, for the blocks owned by wave w.
+template <int MB>
+__device__ __forceinline__ void solver_product(const float* Lm, const float* Rt, int w, int lane,
+                                               bool has_border, f4 acc[2]) {
+  using G = SolverGeom<MB>;
+  const int lr = lane & 15, lg = lane >> 4;
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) acc[cb] = f4{0.f, 0.f, 0.f, 0.f};
-  const int n_beg = ch * CH;
-  const int n_end = min(n_beg + CH, N);
-  for (int n0 = n_beg; n0 < n_end; n0 += 16) {
-    const int nt = n0 + 4 * lg;
-    float pa[4];
+  for (int s = 0; s < 2; ++s) {
+    const int b = w + 8 * s;
+    acc[s] = f4{0.f, 0.f, 0.f, 0.f};
+    if (b < G::NBLK) {
+      const int bi = b / (MB > 0 ? MB : 1), bj = b % (MB > 0 ? MB : 1);
+      const float* ar = Lm + (16 * bi + lr) * LS + G::KS * lg;
+      const float* br = Rt + (16 * bj + lr) * LS + G::KS * lg;
+      f4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 4; ++s) pa[s] = (row_ok && nt + s < n_end) ? P[nt + s] : 0.f;
+      for (int q = 0; q < G::KS / 4; ++q) {
+        const f4 a4 = ld4(ar + 4 * q), b4 = ld4(br + 4 * q);
+        c = mfma4(a4[0], b4[0], c);
+        c = mfma4(a4[1], b4[1], c);
+        c = mfma4(a4[2], b4[2], c);
+        c = mfma4(a4[3], b4[3], c);
+      }
+      if (MB < 4 && has_border) {
+        // k in [16 MB, 16 MB + 4); padding beyond m is zero
+        const f4 rb = ld4(Rt + (16 * bj + lr) * LS + 16 * MB);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int nv = nt + s;
-      const bool ok = nv < n_end;
+        for (int i = 0; i < 4; ++i) {
+          const f4 la = ld4(Lm + (16 * bi + 4 * lg + i) * LS + 16 * MB);
+          c[i] = fmaf(la[0], rb[0], fmaf(la[1], rb[1], fmaf(la[2], rb[2], fmaf(la[3], rb[3], c[i]))));
+        }
+      }
+      acc[s] = c;
+    }
+  }
+}
+
+template <int D, int MB>
+__device__ void solver_role(const MainArgs& a, int bh, float* smem, int* flag) {
+  using G = SolverGeom<MB>;
+  float* A = smem;
+  float* XR = smem + MP * LS;
+  float* XT = smem + 2 * MP * LS;
+  float* TT = smem + 3 * MP * LS;
+  float* red = smem + 4 * MP * LS;  // 4 scalars
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
+  const int lr = lane & 15, lg = lane >> 4;
+  const int m = a.m;
+  __builtin_amdgcn_s_setprio(3);
+
+  for (int e = tid; e < 4 * MP * LS; e += WGM) smem[e] = 0.f;
+  __syncthreads();
+  // landmarks -> TT (scratch), rows of D floats at stride LS
+  const float* Lh = a.L + static_cast<size_t>(bh) * m * D;
+  for (int e = tid; e < m * (D / 4); e += WGM) {
+    const int rr = e / (D / 4), c4 = e % (D / 4);
+    st4(TT + rr * LS + 4 * c4, ld4(Lh + rr * D + 4 * c4));
+  }
+  __syncthreads();
+
+  // A[i][j], i <= j, mirrored (the distance is symmetric term by term).
+  const int npairs = m * (m + 1) / 2;
+  for (int p = tid; p < npairs; p += WGM) {
+    int i = 0, rem = p;
+    while (rem >= m - i) {
+      rem -= m - i;
+      ++i;
+    }
+    const int j = i + rem;
+    const float* li = TT + i * LS;
+    const float* lj = TT + j * LS;
+    float d0 = 0.f, d1 = 0.f;
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const float b = ok ? load_elem<BF16>(V, (vbase + nv) * D + 16 * cb + lr) : 0.f;
-        acc[cb] = mfma4(pa[s], b, acc[cb]);
+    for (int q = 0; q < D / 4; ++q) {
+      const f4 u = ld4(li + 4 * q), v = ld4(lj + 4 * q);
+#pragma unroll
+      for (int h = 0; h < 4; h += 2) {
+        const float t0 = u[h] - v[h], t1 = u[h + 1] - v[h + 1];
+        if (a.kind == 0) {
+          d0 += fabsf(t0);
+          d1 += fabsf(t1);
+        } else {
+          d0 = fmaf(t0, t0, d0);
+          d1 = fmaf(t1, t1, d1);
+        }
+      }
+    }
+    float av = exp2f((d0 + d1) * a.c_exp2);
+    if (i == j) av += a.eps;
+    A[i * LS + j] = av;
+    A[j * LS + i] = av;
+  }
+  __syncthreads();
+  if (a.st_a) {
+    for (int e = tid; e < m * m; e += WGM)
+      a.st_a[static_cast<size_t>(bh) * m * m + e] = A[(e / m) * LS + (e % m)];
+  }
+  // alpha = 1 / (max column abs-sum * max row abs-sum); wave 0 rows, wave 1 columns.
+  if (w < 2) {
+    float sum = 0.f;
+    if (lane < m) {
+      for (int j = 0; j < m; ++j) sum += fabsf(w == 0 ? A[lane * LS + j] : A[j * LS + lane]);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) sum = fmaxf(sum, __shfl_xor(sum, o));
+    if (lane == 0) red[w] = sum;
+  }
+  __syncthreads();
+  const float alpha = 1.0f / (red[0] * red[1]);
+  // X_0 = alpha A in both layouts (A is exactly symmetric); TT back to zero.
+  for (int e = tid; e < MP * LS; e += WGM) {
+    const float x0 = alpha * A[e];
+    XR[e] = x0;
+    XT[e] = x0;
+    TT[e] = 0.f;
+  }
+  __syncthreads();
+
+  const int r = m > 16 * MB ? m - 16 * MB : 0;  // border width (0 when padded)
+  const bool has_border = r > 0;
+  const int nbe = r * m + r * 16 * MB;           // border entries
+  const int nl = 64 * (8 - G::BW0);
+
+  // Own entries of X_t in registers (interior accumulator layout, border).
+  f4 xr[2];
+  float xb[2];
+  int ba[2], bb[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int b = w + 8 * s;
+    xr[s] = f4{0.f, 0.f, 0.f, 0.f};
+    if (b < G::NBLK) {
+      const int bi = b / (MB > 0 ? MB : 1), bj = b % (MB > 0 ? MB : 1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xr[s][i] = XR[(16 * bi + 4 * lg + i) * LS + 16 * bj + lr];
+    }
+    xb[s] = 0.f;
+    ba[s] = -1;
+    bb[s] = 0;
+    if (has_border && w >= G::BW0) {
+      const int e = tid - 64 * G::BW0 + nl * s;
+      if (e < nbe) {
+        border_ab<MB>(e, m, r, ba[s], bb[s]);
+        xb[s] = XR[ba[s] * LS + bb[s]];
       }
     }
   }
-  float* part = wpart + (static_cast<size_t>(bh) * nC + ch) * MP * D;
-#pragma unroll
-  for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) part[(16 * w + 4 * lg + i) * D + 16 * cb + lr] = acc[cb][i];
 
-  if (!arrive(&ctr[bh * CTR_PER_HEAD + 0], static_cast<unsigned>(nC), &flag)) return;
-
-  // Last chunk of this head: W = sum of partials, chunk order 0..nC-1.
-  const float* pbase = wpart + static_cast<size_t>(bh) * nC * MP * D;
-  float* W = Ww + static_cast<size_t>(bh) * MP * D;
-  for (int e = threadIdx.x; e < MP * D; e += WG) {
-    const int r = e / D;
-    float s = 0.f;
-    if (r < m) {
-      for (int c = 0; c < nC; ++c) s += pbase[static_cast<size_t>(c) * MP * D + e];
-      if (st_w) st_w[(static_cast<size_t>(bh) * m + r) * D + (e % D)] = s;
+  for (int t = 0; t < a.iters; ++t) {
+    f4 acc[2];
+    // phase 1: T = A X_t, stored transposed
+    solver_product<MB>(A, XT, w, lane, has_border, acc);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int b = w + 8 * s;
+      if (b < G::NBLK) {
+        const int bi = b / (MB > 0 ? MB : 1), bj = b % (MB > 0 ? MB : 1);
+        st4(TT + (16 * bj + lr) * LS + 16 * bi + 4 * lg, acc[s]);
+      }
+      if (ba[s] >= 0) {
+        const float* ra = A + ba[s] * LS;
+        const float* rb = XT + bb[s] * LS;
+        float d = 0.f;
+#pragma unroll
+        for (int q = 0; q < G::NBQ; ++q) {
+          const f4 a4 = ld4(ra + 4 * q), b4 = ld4(rb + 4 * q);
+          d = fmaf(a4[0], b4[0], fmaf(a4[1], b4[1], fmaf(a4[2], b4[2], fmaf(a4[3], b4[3], d))));
+        }
+        TT[bb[s] * LS + ba[s]] = d;
+      }
     }
-    W[e] = s;
+    __syncthreads();
+    // phase 2: X_{t+1} = 2 X_t - X_t T
+    solver_product<MB>(XR, TT, w, lane, has_border, acc);
+    float xbn[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      xbn[s] = xb[s];
+      if (ba[s] >= 0) {
+        const float* ra = XR + ba[s] * LS;
+        const float* rb = TT + bb[s] * LS;
+        float d = 0.f;
+#pragma unroll
+        for (int q = 0; q < G::NBQ; ++q) {
+          const f4 a4 = ld4(ra + 4 * q), b4 = ld4(rb + 4 * q);
+          d = fmaf(a4[0], b4[0], fmaf(a4[1], b4[1], fmaf(a4[2], b4[2], fmaf(a4[3], b4[3], d))));
+        }
+        xbn[s] = 2.0f * xb[s] - d;
+      }
+    }
+    __syncthreads();  // every read of XR / TT of this step is done
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int b = w + 8 * s;
+      if (b < G::NBLK) {
+        const int bi = b / (MB > 0 ? MB : 1), bj = b % (MB > 0 ? MB : 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          xr[s][i] = 2.0f * xr[s][i] - acc[s][i];
+          XR[(16 * bi + 4 * lg + i) * LS + 16 * bj + lr] = xr[s][i];
+        }
+        st4(XT + (16 * bj + lr) * LS + 16 * bi + 4 * lg, xr[s]);
+      }
+      if (ba[s] >= 0) {
+        xb[s] = xbn[s];
+        XR[ba[s] * LS + bb[s]] = xb[s];
+        XT[bb[s] * LS + ba[s]] = xb[s];
+      }
+    }
+    __syncthreads();
   }
-  if (arrive(&ctr[bh * CTR_PER_HEAD + 1], static_cast<unsigned>(join_target), &flag)) {
-    compute_y<D>(Xw + static_cast<size_t>(bh) * MP * MP, W, Yw + static_cast<size_t>(bh) * MP * D, m);
+
+  float* Xg = a.xw + static_cast<size_t>(bh) * MP * MP;
+  for (int e = tid; e < MP * (MP / 4); e += WGM) {
+    const int row = e / (MP / 4), c4 = e % (MP / 4);
+    st4(Xg + row * MP + 4 * c4, ld4(XR + row * LS + 4 * c4));
   }
+  if (a.st_x) {
+    for (int e = tid; e < m * m; e += WGM)
+      a.st_x[static_cast<size_t>(bh) * m * m + e] = XR[(e / m) * LS + (e % m)];
+  }
+  if (arrive(&a.ctr[bh * CTR_PER_HEAD + 1], 2u, flag)) {
+    compute_yt_any<D>(a.wt + static_cast<size_t>(bh) * D * MP, Xg,
+                      a.yt + static_cast<size_t>(bh) * D * MP, m);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Map role.  Workgroup = one head and S consecutive 64-token tiles of either
+// the keys (key role: W partial; also K_QL when Q == K) or the queries (query
+// role: K_QL rows).  Wave g computes landmarks [g m / 8, (g+1) m / 8) for the
+// 64 tokens of the tile (lane = token); the tile's kernel values meet in LDS.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ void map_role(const MainArgs& a, int b, float* smem, int* flag) {
+  constexpr int CBN = D / 16;
+  float* PJ = smem;                // [64 landmarks][LS]: P[j][token]
+  float* PT = smem + MP * LS;      // [64 tokens][LS]:    P[j] of token at [token][j]
+  float* VT = smem + 2 * MP * LS;  // [D][LS]:            V[token][c] at [c][token]
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
+  const int lr = lane & 15, lg = lane >> 4;
+  const int m = a.m, N = a.N;
+  const int nK = a.nP;
+  const bool key_role = b < a.BH * nK;
+  int bh, t_beg, t_end;
+  if (key_role) {
+    bh = b / nK;
+    const int kw = b % nK;
+    t_beg = kw * a.S;
+    t_end = min(t_beg + a.S, a.nT);
+  } else {
+    const int bq = b - a.BH * nK;
+    bh = bq / a.nQ;
+    t_beg = bq % a.nQ;
+    t_end = t_beg + 1;
+  }
+  const bool store_kql = !key_role || a.shared_qk;
+  const void* src = key_role ? a.k : a.q;
+  const int mby = (m + 15) >> 4;
+  const int nwb = CBN * mby;  // W output blocks
+
+  // padding rows / columns j in [m, 64) stay zero for the whole workgroup
+  for (int e = tid; e < MP * LS; e += WGM) {
+    PJ[e] = 0.f;
+    PT[e] = 0.f;
+  }
+  __syncthreads();
+
+  const int jb = (w * m) / NGRP, je = ((w + 1) * m) / NGRP;
+  const float* Lh = a.L + static_cast<size_t>(bh) * m * D;
+  f4 wacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+
+  for (int t = t_beg; t < t_end; ++t) {
+    const int n = t * TILE + lane;
+    const bool valid = n < N;
+    float x[D];
+    load_row<D>(src, static_cast<size_t>(bh) * N + (valid ? n : N - 1), a.bf16, x);
+    if (key_role) {
+      // V tile -> VT[c][token]; thread (c, token group of 8)
+      const int c = tid % D, tg = tid / D;
+      constexpr int TPT = TILE * D / WGM;  // tokens per thread
+#pragma unroll
+      for (int u = 0; u < TPT; ++u) {
+        const int tok = tg * TPT + u;
+        const int nv = t * TILE + tok;
+        VT[c * LS + tok] = nv < N ? load1_io(a.v, (static_cast<size_t>(bh) * N + nv) * D + c, a.bf16) : 0.f;
+      }
+    }
+    for (int j = jb; j < je; ++j) {
+      const float dist = a.kind == 0 ? dist_to<D, 0>(x, Lh + j * D) : dist_to<D, 1>(x, Lh + j * D);
+      const float kv = valid ? exp2f(dist * a.c_exp2) : 0.f;
+      PJ[j * LS + lane] = kv;
+      PT[lane * LS + j] = kv;
+    }
+    __syncthreads();
+    if (store_kql) {
+      // 64 rows of mpad floats, contiguous in global memory
+      const int q4 = a.mpad / 4;
+      float* dst = a.kql + (static_cast<size_t>(bh) * N + t * TILE) * a.mpad;
+      for (int e = tid; e < TILE * q4; e += WGM) {
+        const int tok = e / q4, c4 = e % q4;
+        if (t * TILE + tok < N) st4(dst + tok * a.mpad + 4 * c4, ld4(PT + tok * LS + 4 * c4));
+      }
+      if (a.st_kql) {
+        for (int e = tid; e < TILE * m; e += WGM) {
+          const int tok = e / m, j = e % m;
+          if (t * TILE + tok < N)
+            a.st_kql[(static_cast<size_t>(bh) * N + t * TILE + tok) * m + j] = PT[tok * LS + j];
+        }
+      }
+    }
+    if (key_role) {
+      if (a.st_klk) {
+        for (int e = tid; e < m * TILE; e += WGM) {
+          const int j = e / TILE, tok = e % TILE;
+          if (t * TILE + tok < N)
+            a.st_klk[(static_cast<size_t>(bh) * m + j) * N + t * TILE + tok] = PJ[j * LS + tok];
+        }
+      }
+      // W^T[c][j] += sum_token V^T[c][token] P[j][token]
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int blk = w + 8 * s;
+        if (blk < nwb) {
+          const int cb = blk % CBN, jbk = blk / CBN;
+          const float* ar = VT + (16 * cb + lr) * LS + 16 * lg;
+          const float* br = PJ + (16 * jbk + lr) * LS + 16 * lg;
+          f4 c = wacc[s];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f4 a4 = ld4(ar + 4 * q), b4 = ld4(br + 4 * q);
+            c = mfma4(a4[0], b4[0], c);
+            c = mfma4(a4[1], b4[1], c);
+            c = mfma4(a4[2], b4[2], c);
+            c = mfma4(a4[3], b4[3], c);
+          }
+          wacc[s] = c;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (!key_role) return;
+
+  const int kw = b % nK;
+  float* part = a.wpart + (static_cast<size_t>(bh) * nK + kw) * D * MP;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int blk = w + 8 * s;
+    if (blk < nwb) {
+      const int cb = blk % CBN, jbk = blk / CBN;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part[(16 * cb + 4 * lg + i) * MP + 16 * jbk + lr] = wacc[s][i];
+    }
+  }
+  if (!arrive(&a.ctr[bh * CTR_PER_HEAD + 0], static_cast<unsigned>(nK), flag)) return;
+
+  // Last key workgroup of the head: W^T = sum of partials in order 0..nK-1.
+  const float* pb = a.wpart + static_cast<size_t>(bh) * nK * D * MP;
+  float* wt = a.wt + static_cast<size_t>(bh) * D * MP;
+  for (int e4 = tid; e4 < D * MP / 4; e4 += WGM) {
+    const int c = (4 * e4) / MP, j0 = (4 * e4) % MP;
+    f4 s = {0.f, 0.f, 0.f, 0.f};
+    int p = 0;
+    for (; p + 4 <= nK; p += 4) {
+      const f4 v0 = ld4(pb + static_cast<size_t>(p) * D * MP + 4 * e4);
+      const f4 v1 = ld4(pb + static_cast<size_t>(p + 1) * D * MP + 4 * e4);
+      const f4 v2 = ld4(pb + static_cast<size_t>(p + 2) * D * MP + 4 * e4);
+      const f4 v3 = ld4(pb + static_cast<size_t>(p + 3) * D * MP + 4 * e4);
+      s += v0;
+      s += v1;
+      s += v2;
+      s += v3;
+    }
+    for (; p < nK; ++p) s += ld4(pb + static_cast<size_t>(p) * D * MP + 4 * e4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (j0 + i >= m) s[i] = 0.f;
+      else if (a.st_w) a.st_w[(static_cast<size_t>(bh) * m + j0 + i) * D + c] = s[i];
+    }
+    st4(wt + 4 * e4, s);
+  }
+  if (arrive(&a.ctr[bh * CTR_PER_HEAD + 1], 2u, flag)) {
+    compute_yt_any<D>(wt, a.xw + static_cast<size_t>(bh) * MP * MP,
+                      a.yt + static_cast<size_t>(bh) * D * MP, m);
+  }
+}
+
+template <int D, int MB>
+__global__ __launch_bounds__(WGM) void main_kernel(MainArgs a) {
+  __shared__ __attribute__((aligned(16))) float smem[4 * MP * LS + 4];
+  __shared__ int flag;
+  const int b = blockIdx.x;
+  if (b < a.ns_blocks) {
+    solver_role<D, MB>(a, b, smem, &flag);
+  } else {
+    map_role<D>(a, b - a.ns_blocks, smem, &flag);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// pool: one workgroup per (landmark, head).  Thread (g, c4) sums a float4
+// column chunk over every G-th token of the window (loads issued 4 at a
+// time); a fixed-order LDS reduction over g finishes the mean.  Workgroup
+// (0, bh) also clears the head's counters.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(WGS) void pool_kernel(const void* __restrict__ K, int bf16,
+                                                   float* __restrict__ L,
+                                                   unsigned* __restrict__ ctr,
+                                                   float* __restrict__ st_L, int gw, int ph,
+                                                   int pw, int m, int N) {
+  constexpr int C4 = D / 4;
+  constexpr int G = WGS / C4;
+  __shared__ f4 part[WGS];
+  const int j = blockIdx.x, bh = blockIdx.y;
+  const int tid = threadIdx.x, c4 = tid % C4, g = tid / C4;
+  const int mw = gw / pw;
+  const int R = j / mw, C = j % mw;
+  const int cnt = ph * pw;
+  const size_t base = static_cast<size_t>(bh) * N;
+  f4 s = {0.f, 0.f, 0.f, 0.f};
+  for (int t0 = g; t0 < cnt; t0 += 4 * G) {
+    f4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = t0 + u * G;
+      v[u] = f4{0.f, 0.f, 0.f, 0.f};
+      if (t < cnt) {
+        const int n = (R * ph + t / pw) * gw + C * pw + t % pw;
+        v[u] = load4_io(K, (base + n) * D + 4 * c4, bf16);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) s += v[u];
+  }
+  part[tid] = s;
+  __syncthreads();
+  if (tid < C4) {
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < G; ++i) acc += part[i * C4 + tid];
+    const f4 mean = acc / static_cast<float>(cnt);
+    float* dst = L + (static_cast<size_t>(bh) * m + j) * D + 4 * tid;
+    st4(dst, mean);
+    if (st_L) st4(st_L + (static_cast<size_t>(bh) * m + j) * D + 4 * tid, mean);
+  }
+  if (j == 0 && tid < CTR_PER_HEAD) ctr[bh * CTR_PER_HEAD + tid] = 0u;
 }
 
 // ---------------------------------------------------------------------------
 // out: O = K_QL Y.  Workgroup = (head, 64 tokens); wave w computes tokens
-// 16w..16w+15 of the tile against all D columns, contraction over landmarks.
+// 16w..16w+15 of the tile against all D columns, contraction over KS*4 =
+// 16 ceil(m/16) landmarks (zero padded).
 // ---------------------------------------------------------------------------
-template <int D, bool BF16>
-__global__ __launch_bounds__(WG) void out_kernel(const float* __restrict__ kqlt,
-                                                 const float* __restrict__ Yw,
-                                                 void* __restrict__ O, int N, int m,
-                                                 int nT) {
-  constexpr int CB = D / 16;
+template <int D, int KS>
+__global__ __launch_bounds__(WGS) void out_kernel(const float* __restrict__ kql,
+                                                  const float* __restrict__ yt,
+                                                  void* __restrict__ O, int bf16, int N,
+                                                  int mpad, int nT) {
+  constexpr int CBN = D / 16;
   const int bh = blockIdx.x / nT, t = blockIdx.x % nT;
   const int lane = threadIdx.x & 63, w = wave_id();
   const int lr = lane & 15, lg = lane >> 4;
-  const int nb = t * 64 + 16 * w;
-  const int na = nb + lr;
-  const bool na_ok = na < N;
-  const float* P = kqlt + static_cast<size_t>(bh) * m * N + (na_ok ? na : 0);
-  const float* Y = Yw + static_cast<size_t>(bh) * MP * D;
-  const int ksteps = (m + 3) >> 2;
-  f4 acc[CB];
+  const int tok = t * TILE + 16 * w + lr;
+  const int tokc = tok < N ? tok : N - 1;
+  const float* ar = kql + (static_cast<size_t>(bh) * N + tokc) * mpad + KS * lg;
+  float av[KS];
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) acc[cb] = f4{0.f, 0.f, 0.f, 0.f};
-  for (int kk = 0; kk < ksteps; ++kk) {
-    const int j = 4 * kk + lg;
-    const float a = (na_ok && j < m) ? P[static_cast<size_t>(j) * N] : 0.f;
+  for (int q = 0; q < KS / 4; ++q) {
+    const f4 u = ld4(ar + 4 * q);
+    av[4 * q] = u[0];
+    av[4 * q + 1] = u[1];
+    av[4 * q + 2] = u[2];
+    av[4 * q + 3] = u[3];
+  }
+  f4 acc[CBN];
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) acc[cb] = mfma4(a, Y[j * D + 16 * cb + lr], acc[cb]);
+  for (int cb = 0; cb < CBN; ++cb) {
+    const float* br = yt + (static_cast<size_t>(bh) * D + 16 * cb + lr) * MP + KS * lg;
+    f4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < KS / 4; ++q) {
+      const f4 b4 = ld4(br + 4 * q);
+      c = mfma4(av[4 * q], b4[0], c);
+      c = mfma4(av[4 * q + 1], b4[1], c);
+      c = mfma4(av[4 * q + 2], b4[2], c);
+      c = mfma4(av[4 * q + 3], b4[3], c);
+    }
+    acc[cb] = c;
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int n = nb + 4 * lg + i;
+    const int n = t * TILE + 16 * w + 4 * lg + i;
     if (n < N) {
       const size_t o = (static_cast<size_t>(bh) * N + n) * D + lr;
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        if constexpr (BF16) {
+      for (int cb = 0; cb < CBN; ++cb) {
+        if (bf16) {
           static_cast<uint16_t*>(O)[o + 16 * cb] = f32_to_bf16_rne(acc[cb][i]);
         } else {
           static_cast<float*>(O)[o + 16 * cb] = acc[cb][i];
         }
       }
     }
-  }
-}
-
-// Stage export: K_QL in [N][m] layout and K_LK in [m][N] layout.
-__global__ __launch_bounds__(WG) void export_kernel(const float* __restrict__ kqlt,
-                                                    const float* __restrict__ klkt,
-                                                    float* __restrict__ st_kql,
-                                                    float* __restrict__ st_klk, int N,
-                                                    int m, size_t total) {
-  for (size_t e = blockIdx.x * static_cast<size_t>(WG) + threadIdx.x; e < total;
-       e += static_cast<size_t>(gridDim.x) * WG) {
-    const size_t bh = e / (static_cast<size_t>(m) * N);
-    const size_t r = e % (static_cast<size_t>(m) * N);
-    const size_t j = r / N, n = r % N;
-    if (st_klk) st_klk[e] = klkt[e];
-    if (st_kql) st_kql[(bh * N + n) * m + j] = kqlt[e];
   }
 }
 
@@ -536,65 +761,46 @@ inline float exp2_scale(float lambda) {
 
 template <int D>
 hipError_t launch_pool_d(const Plan& p, const Args& a, const Buffers& b, hipStream_t s) {
-  dim3 grid(p.m, p.BH);
-  if (p.bf16)
-    hipLaunchKernelGGL((pool_kernel<D, true>), grid, dim3(WG), 0, s, a.k, b.L, b.ctr, a.st_L,
-                       p.gw, p.ph, p.pw, p.m, p.N);
-  else
-    hipLaunchKernelGGL((pool_kernel<D, false>), grid, dim3(WG), 0, s, a.k, b.L, b.ctr, a.st_L,
-                       p.gw, p.ph, p.pw, p.m, p.N);
+  hipLaunchKernelGGL((pool_kernel<D>), dim3(p.m, p.BH), dim3(WGS), 0, s, a.k, p.bf16, b.L, b.ctr,
+                     a.st_L, p.gw, p.ph, p.pw, p.m, p.N);
+  return hipGetLastError();
+}
+
+template <int D, int MB>
+hipError_t launch_main_dm(const Plan& p, const MainArgs& ma, unsigned grid, hipStream_t s) {
+  hipLaunchKernelGGL((main_kernel<D, MB>), dim3(grid), dim3(WGM), 0, s, ma);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_ns_d(const Plan& p, const Args& a, const Buffers& b, int jt, hipStream_t s) {
-  const float c = exp2_scale(a.lambda);
-  if (p.kernel == 0)
-    hipLaunchKernelGGL((ns_kernel<D, 0>), dim3(p.BH), dim3(WG), 0, s, b.L, b.x, b.w, b.y, b.ctr,
-                       a.st_a, a.st_x, p.m, c, a.eps, a.iters, jt);
-  else
-    hipLaunchKernelGGL((ns_kernel<D, 1>), dim3(p.BH), dim3(WG), 0, s, b.L, b.x, b.w, b.y, b.ctr,
-                       a.st_a, a.st_x, p.m, c, a.eps, a.iters, jt);
-  return hipGetLastError();
-}
-
-template <int D, int KIND>
-hipError_t launch_maps_dk(const Plan& p, const Args& a, const Buffers& b, hipStream_t s) {
-  const int nroles = a.shared_qk ? 1 : 2;
-  const long units = static_cast<long>(nroles) * p.BH * p.nT * p.ng;
-  const unsigned blocks = static_cast<unsigned>((units + 3) / 4);
-  const float c = exp2_scale(a.lambda);
-  if (p.bf16)
-    hipLaunchKernelGGL((maps_kernel<D, KIND, true>), dim3(blocks), dim3(WG), 0, s, a.q, a.k, b.L,
-                       b.kqlt, b.klkt, p.N, p.m, p.nT, p.ng, nroles, p.BH, c);
-  else
-    hipLaunchKernelGGL((maps_kernel<D, KIND, false>), dim3(blocks), dim3(WG), 0, s, a.q, a.k, b.L,
-                       b.kqlt, b.klkt, p.N, p.m, p.nT, p.ng, nroles, p.BH, c);
-  return hipGetLastError();
-}
-
-template <int D>
-hipError_t launch_w_d(const Plan& p, const Args& a, const Buffers& b, int jt, hipStream_t s) {
-  dim3 grid(p.BH * p.nC);
-  if (p.bf16)
-    hipLaunchKernelGGL((w_kernel<D, true>), grid, dim3(WG), 0, s, b.klkt, a.v, b.wpart, b.w, b.x,
-                       b.y, b.ctr, a.st_w, p.N, p.m, p.CH, p.nC, jt);
-  else
-    hipLaunchKernelGGL((w_kernel<D, false>), grid, dim3(WG), 0, s, b.klkt, a.v, b.wpart, b.w, b.x,
-                       b.y, b.ctr, a.st_w, p.N, p.m, p.CH, p.nC, jt);
-  return hipGetLastError();
+hipError_t launch_main_d(const Plan& p, const MainArgs& ma, unsigned grid, hipStream_t s) {
+  switch (p.ns_mb) {
+    case 0: return launch_main_dm<D, 0>(p, ma, grid, s);
+    case 1: return launch_main_dm<D, 1>(p, ma, grid, s);
+    case 2: return launch_main_dm<D, 2>(p, ma, grid, s);
+    case 3: return launch_main_dm<D, 3>(p, ma, grid, s);
+    case 4: return launch_main_dm<D, 4>(p, ma, grid, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int D>
 hipError_t launch_out_d(const Plan& p, const Args& a, const Buffers& b, hipStream_t s) {
-  const float* kql = a.shared_qk ? b.klkt : b.kqlt;
-  dim3 grid(p.BH * p.nT);
-  if (p.bf16)
-    hipLaunchKernelGGL((out_kernel<D, true>), grid, dim3(WG), 0, s, kql, b.y, a.out, p.N, p.m,
-                       p.nT);
-  else
-    hipLaunchKernelGGL((out_kernel<D, false>), grid, dim3(WG), 0, s, kql, b.y, a.out, p.N, p.m,
-                       p.nT);
+  const dim3 grid(p.BH * p.nT);
+  switch (p.mpad / 16) {
+    case 1:
+      hipLaunchKernelGGL((out_kernel<D, 4>), grid, dim3(WGS), 0, s, b.kql, b.yt, a.out, p.bf16, p.N, p.mpad, p.nT);
+      break;
+    case 2:
+      hipLaunchKernelGGL((out_kernel<D, 8>), grid, dim3(WGS), 0, s, b.kql, b.yt, a.out, p.bf16, p.N, p.mpad, p.nT);
+      break;
+    case 3:
+      hipLaunchKernelGGL((out_kernel<D, 12>), grid, dim3(WGS), 0, s, b.kql, b.yt, a.out, p.bf16, p.N, p.mpad, p.nT);
+      break;
+    default:
+      hipLaunchKernelGGL((out_kernel<D, 16>), grid, dim3(WGS), 0, s, b.kql, b.yt, a.out, p.bf16, p.N, p.mpad, p.nT);
+      break;
+  }
   return hipGetLastError();
 }
 
@@ -609,30 +815,46 @@ hipError_t launch_pool(const Plan& p, const Args& a, const Buffers& b, hipStream
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_ns(const Plan& p, const Args& a, const Buffers& b, int jt, hipStream_t s) {
+hipError_t launch_main(const Plan& p, const Args& a, const Buffers& b, bool with_solver,
+                       bool with_maps, hipStream_t s) {
+  MainArgs ma{};
+  ma.q = a.q;
+  ma.k = a.k;
+  ma.v = a.v;
+  ma.L = b.L;
+  ma.kql = b.kql;
+  ma.wpart = b.wpart;
+  ma.wt = b.wt;
+  ma.xw = b.x;
+  ma.yt = b.yt;
+  ma.ctr = b.ctr;
+  ma.st_a = a.st_a;
+  ma.st_x = a.st_x;
+  ma.st_w = a.st_w;
+  ma.st_kql = a.st_kql;
+  ma.st_klk = a.st_klk;
+  ma.N = p.N;
+  ma.m = p.m;
+  ma.BH = p.BH;
+  ma.nT = p.nT;
+  ma.S = p.S;
+  ma.nP = p.nP;
+  ma.mpad = p.mpad;
+  ma.shared_qk = a.shared_qk;
+  ma.nQ = a.shared_qk ? 0 : p.nT;
+  ma.kind = p.kernel;
+  ma.bf16 = p.bf16;
+  ma.iters = a.iters;
+  ma.c_exp2 = exp2_scale(a.lambda);
+  ma.eps = a.eps;
+  ma.ns_blocks = with_solver ? p.BH : 0;
+  const long map_wgs = with_maps ? static_cast<long>(p.BH) * (p.nP + ma.nQ) : 0;
+  const unsigned grid = static_cast<unsigned>(ma.ns_blocks + map_wgs);
+  if (grid == 0) return hipSuccess;
   switch (p.D) {
-    case 16: return launch_ns_d<16>(p, a, b, jt, s);
-    case 32: return launch_ns_d<32>(p, a, b, jt, s);
-    case 64: return launch_ns_d<64>(p, a, b, jt, s);
-  }
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_maps(const Plan& p, const Args& a, const Buffers& b, hipStream_t s) {
-  const bool gauss = p.kernel != 0;
-  switch (p.D) {
-    case 16: return gauss ? launch_maps_dk<16, 1>(p, a, b, s) : launch_maps_dk<16, 0>(p, a, b, s);
-    case 32: return gauss ? launch_maps_dk<32, 1>(p, a, b, s) : launch_maps_dk<32, 0>(p, a, b, s);
-    case 64: return gauss ? launch_maps_dk<64, 1>(p, a, b, s) : launch_maps_dk<64, 0>(p, a, b, s);
-  }
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_w(const Plan& p, const Args& a, const Buffers& b, int jt, hipStream_t s) {
-  switch (p.D) {
-    case 16: return launch_w_d<16>(p, a, b, jt, s);
-    case 32: return launch_w_d<32>(p, a, b, jt, s);
-    case 64: return launch_w_d<64>(p, a, b, jt, s);
+    case 16: return launch_main_d<16>(p, ma, grid, s);
+    case 32: return launch_main_d<32>(p, ma, grid, s);
+    case 64: return launch_main_d<64>(p, ma, grid, s);
   }
   return hipErrorInvalidValue;
 }
@@ -644,16 +866,6 @@ hipError_t launch_out(const Plan& p, const Args& a, const Buffers& b, hipStream_
     case 64: return launch_out_d<64>(p, a, b, s);
   }
   return hipErrorInvalidValue;
-}
-
-hipError_t launch_export(const Plan& p, const Args& a, const Buffers& b, hipStream_t s) {
-  if (!a.st_kql && !a.st_klk) return hipSuccess;
-  const float* kql = a.shared_qk ? b.klkt : b.kqlt;
-  const size_t total = static_cast<size_t>(p.BH) * p.m * p.N;
-  const unsigned blocks = static_cast<unsigned>((total + WG - 1) / WG < 4096 ? (total + WG - 1) / WG : 4096);
-  hipLaunchKernelGGL(export_kernel, dim3(blocks), dim3(WG), 0, s, kql, b.klkt, a.st_kql, a.st_klk,
-                     p.N, p.m, total);
-  return hipGetLastError();
 }
 
 }  // namespace lapattn

@@ -85,7 +85,7 @@ def test_parameter_validation(lam, eps, iters, expect):
 def test_stage_event_hook_validation():
     lib = _lib.lib()
     assert lib.lapattn_set_stage_events(None, 0) == _lib.OK
-    assert lib.lapattn_set_stage_events(None, 10) == _lib.ERR_NULL
+    assert lib.lapattn_set_stage_events(None, 2 * len(_lib.STAGES)) == _lib.ERR_NULL
     arr = (ctypes.c_void_p * 10)()
     assert lib.lapattn_set_stage_events(arr, 3) == _lib.ERR_PARAM
     assert lib.lapattn_set_stage_events(None, 0) == _lib.OK

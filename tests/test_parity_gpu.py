@@ -77,9 +77,9 @@ def test_stages(w):
         assert normwise(got["O"][b, h], r["O"]) <= tol_for(w), "output"
 
 
-def test_serial_and_overlapped_plans_are_bitwise_equal():
+def test_serial_and_fused_plans_are_bitwise_equal():
     w = wl.HEADLINE
-    _print_case(w, "serial vs overlapped")
+    _print_case(w, "serial vs fused")
     x = wl.make_inputs(w)
     a = run_gpu(w, x, serial=False)["O"]
     b = run_gpu(w, x, serial=True)["O"]
