@@ -84,6 +84,8 @@ def stage_work(w):
         # bytes: read the token rows of Q and K (once each) and V, write K_QL
         "maps": {"flops": 3 * maps_pairs, "pairs": maps_pairs,
                  "bytes": BH * (sides * N * d * e + N * d * e + N * m * 4)},
+        # bytes: read the W^T partials and X, write Y^T
+        "y": {},
         # bytes: read K_QL (fp32), write O
         "out": {"bytes": BH * (m * N * 4 + N * d * e)},
     }

@@ -94,9 +94,10 @@ enum {
 /* Stages of one forward call, in launch order (for lapattn_set_stage_events). */
 #define LAPATTN_STAGE_POOL 0     /* landmark average pool                      */
 #define LAPATTN_STAGE_SOLVER 1   /* A = k(L,L) + eps I, alpha, Newton-Schulz  */
-#define LAPATTN_STAGE_MAPS 2     /* K_QL and K_LK maps, W = K_LK V, Y = X W   */
-#define LAPATTN_STAGE_OUT 3      /* O = K_QL Y                                 */
-#define LAPATTN_NUM_STAGES 4
+#define LAPATTN_STAGE_MAPS 2     /* K_QL and K_LK maps, partials of K_LK V    */
+#define LAPATTN_STAGE_Y 3        /* W = K_LK V (sum of partials), Y = X W     */
+#define LAPATTN_STAGE_OUT 4      /* O = K_QL Y                                 */
+#define LAPATTN_NUM_STAGES 5
 
 typedef struct {
   int32_t B, H;            /* batch and heads; every (b, h) is independent   */

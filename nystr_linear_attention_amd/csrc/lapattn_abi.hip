@@ -71,16 +71,12 @@ Plan make_plan(const lapattn_desc_t* d) {
   const size_t BH = static_cast<size_t>(p.BH);
   const size_t f = sizeof(float);
   size_t off = 0;
-  p.off_ctr = off;
-  off = align_up(off + BH * CTR_PER_HEAD * sizeof(unsigned));
   p.off_L = off;
   off = align_up(off + BH * p.m * p.D * f);
   p.off_kql = off;
   off = align_up(off + BH * p.N * p.mpad * f);
   p.off_wpart = off;
   off = align_up(off + BH * p.nP * p.D * MP * f);
-  p.off_wt = off;
-  off = align_up(off + BH * p.D * MP * f);
   p.off_x = off;
   off = align_up(off + BH * MP * MP * f);
   p.off_yt = off;
@@ -127,11 +123,9 @@ int run(const lapattn_desc_t* desc, const Args& a, void* workspace, size_t ws_by
 
   char* ws = static_cast<char*>(workspace);
   Buffers b;
-  b.ctr = reinterpret_cast<unsigned*>(ws + p.off_ctr);
   b.L = reinterpret_cast<float*>(ws + p.off_L);
   b.kql = reinterpret_cast<float*>(ws + p.off_kql);
   b.wpart = reinterpret_cast<float*>(ws + p.off_wpart);
-  b.wt = reinterpret_cast<float*>(ws + p.off_wt);
   b.x = reinterpret_cast<float*>(ws + p.off_x);
   b.yt = reinterpret_cast<float*>(ws + p.off_yt);
 
@@ -152,6 +146,8 @@ int run(const lapattn_desc_t* desc, const Args& a, void* workspace, size_t ws_by
     if (!mark(2 * LAPATTN_STAGE_SOLVER + 1, stream) || !mark(2 * LAPATTN_STAGE_MAPS + 1, stream))
       return LAPATTN_ERR_HIP;
   }
+  auto wy = [&] { return launch_wy(p, a, b, stream); };
+  if (!stage(LAPATTN_STAGE_Y, stream, wy)) return LAPATTN_ERR_HIP;
   if (!stage(LAPATTN_STAGE_OUT, stream, out)) return LAPATTN_ERR_HIP;
   return LAPATTN_OK;
 }

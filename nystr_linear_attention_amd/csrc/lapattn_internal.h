@@ -10,9 +10,6 @@ namespace lapattn {
 // Small per-head matrices (A, X, W^T, Y^T) are stored padded to MP columns;
 // padding holds exact zeros.
 constexpr int MP = 64;
-// Counters per head in the workspace: [0] W partials done, [1] join of the
-// solver and the W reduction.
-constexpr int CTR_PER_HEAD = 4;
 
 struct Plan {
   int B, H, gh, gw, D, ph, pw;
@@ -25,17 +22,15 @@ struct Plan {
   int S;        // tiles per key-side workgroup
   int nP;       // key-side workgroups (= W partials) per head
   // workspace byte offsets
-  size_t off_ctr, off_L, off_kql, off_wpart, off_wt, off_x, off_yt;
+  size_t off_L, off_kql, off_wpart, off_x, off_yt;
   size_t total;
 };
 
 struct Buffers {
-  unsigned* ctr;
   float* L;      // [BH][m][D]     landmarks
   float* kql;    // [BH][N][mpad]  k(q_n, l_j), zero for j >= m
   float* wpart;  // [BH][nP][D][MP] partial W^T
-  float* wt;     // [BH][D][MP]    W^T = (K_LK V)^T
-  float* x;      // [BH][MP][MP]   Newton-Schulz result (symmetric)
+  float* x;      // [BH][MP][MP]   Newton-Schulz result
   float* yt;     // [BH][D][MP]    Y^T = (X W)^T
 };
 
@@ -62,6 +57,7 @@ struct Args {
 hipError_t launch_pool(const Plan& p, const Args& a, const Buffers& b, hipStream_t s);
 hipError_t launch_main(const Plan& p, const Args& a, const Buffers& b, bool with_solver,
                        bool with_maps, hipStream_t s);
+hipError_t launch_wy(const Plan& p, const Args& a, const Buffers& b, hipStream_t s);
 hipError_t launch_out(const Plan& p, const Args& a, const Buffers& b, hipStream_t s);
 
 }  // namespace lapattn

@@ -1,6 +1,6 @@
 // HIP kernels for Nystrom kernel attention (forward) on gfx950.
 //
-// Three launches per forward call, all on the caller's stream:
+// Four launches per forward call, back to back on the caller's stream:
 //   pool : landmarks L = window means of K                         (HBM stream)
 //   main : role-split workgroups
 //          - solver WGs (one per head, dispatched first, raised wave priority):
@@ -8,10 +8,11 @@
 //          - map WGs: kernel values of 64 tokens against every landmark on
 //            FP32 VALU (landmark coordinates are wave-uniform scalar operands);
 //            query tiles store K_QL, key tiles contract K_LK V on fp32 MFMA
-//            into per-workgroup partials; the last key workgroup of a head sums
-//            them in fixed order, and whichever of {solver, W reduction} ends
-//            second forms Y = X W.
+//            into per-workgroup partials of W^T
+//   wy   : W^T = sum of the partials in fixed order (deterministic), then
+//          Y^T = W^T X^T
 //   out  : O = K_QL Y on fp32 MFMA, fp32 or bf16 (RNE) store.
+// No workgroup waits on another: every dependency is a launch boundary.
 //
 // Pages behind each step: average-pool landmarks (SOFT review, "method";
 // LaplacianFormer summaries, Nystrom paragraph), Laplacian kernel
@@ -124,22 +125,6 @@ __device__ __forceinline__ float dist_to(const float* x, const float* __restrict
   return d0 + d1;
 }
 
-// Last-arrival join: true in every thread of the workgroup that completes the
-// count.  Prior global stores are released before the increment; the winner
-// acquires before it returns.
-__device__ __forceinline__ bool arrive(unsigned* counter, unsigned target, int* flag_lds) {
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __threadfence();
-    const unsigned old = atomicAdd(counter, 1u);
-    *flag_lds = (old + 1u == target) ? 1 : 0;
-  }
-  __syncthreads();
-  const bool last = *flag_lds != 0;
-  if (last) __threadfence();
-  return last;
-}
-
 struct MainArgs {
   const void* q;
   const void* k;
@@ -147,13 +132,9 @@ struct MainArgs {
   const float* L;     // [BH][m][D]
   float* kql;         // [BH][N][mpad]
   float* wpart;       // [BH][nP][D][MP]
-  float* wt;          // [BH][D][MP]
   float* xw;          // [BH][MP][MP]
-  float* yt;          // [BH][D][MP]
-  unsigned* ctr;
   float* st_a;
   float* st_x;
-  float* st_w;
   float* st_kql;
   float* st_klk;
   int N, m, BH, nT, S, nP, mpad;
@@ -163,49 +144,6 @@ struct MainArgs {
   int kind, bf16, iters;
   float c_exp2, eps;
 };
-
-// ---------------------------------------------------------------------------
-// Y^T = W^T X for one head (X symmetric): 8 waves, output blocks
-// (cb, rb), cb < D/16, rb < MBY; both operands are contiguous row reads.
-// ---------------------------------------------------------------------------
-template <int D, int MBY>
-__device__ void compute_yt(const float* __restrict__ wt, const float* __restrict__ X,
-                           float* __restrict__ yt) {
-  constexpr int KS = 4 * MBY;
-  constexpr int CBN = D / 16;
-  const int lane = threadIdx.x & 63, w = wave_id();
-  const int lr = lane & 15, lg = lane >> 4;
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const int b = w + 8 * s;
-    if (b < CBN * MBY) {
-      const int cb = b % CBN, rb = b / CBN;
-      const float* ar = wt + (16 * cb + lr) * MP + KS * lg;
-      const float* br = X + (16 * rb + lr) * MP + KS * lg;
-      f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int q = 0; q < KS / 4; ++q) {
-        const f4 a4 = ld4(ar + 4 * q), b4 = ld4(br + 4 * q);
-        acc = mfma4(a4[0], b4[0], acc);
-        acc = mfma4(a4[1], b4[1], acc);
-        acc = mfma4(a4[2], b4[2], acc);
-        acc = mfma4(a4[3], b4[3], acc);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) yt[(16 * cb + 4 * lg + i) * MP + 16 * rb + lr] = acc[i];
-    }
-  }
-}
-
-template <int D>
-__device__ void compute_yt_any(const float* wt, const float* X, float* yt, int m) {
-  switch ((m + 15) >> 4) {
-    case 1: compute_yt<D, 1>(wt, X, yt); break;
-    case 2: compute_yt<D, 2>(wt, X, yt); break;
-    case 3: compute_yt<D, 3>(wt, X, yt); break;
-    default: compute_yt<D, 4>(wt, X, yt); break;
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Solver role.  Matrices live in LDS (64 x LS floats, zero padded):
@@ -284,8 +222,8 @@ __device__ __forceinline__ void solver_product(const float* Lm, const float* Rt,
   }
 }
 
-template <int D, int MB>
-__device__ void solver_role(const MainArgs& a, int bh, float* smem, int* flag) {
+template <int D, int MB, int KIND>
+__device__ void solver_role(const MainArgs& a, const float* __restrict__ Lw, int bh, float* smem) {
   using G = SolverGeom<MB>;
   float* A = smem;
   float* XR = smem + MP * LS;
@@ -300,7 +238,7 @@ __device__ void solver_role(const MainArgs& a, int bh, float* smem, int* flag) {
   for (int e = tid; e < 4 * MP * LS; e += WGM) smem[e] = 0.f;
   __syncthreads();
   // landmarks -> TT (scratch), rows of D floats at stride LS
-  const float* Lh = a.L + static_cast<size_t>(bh) * m * D;
+  const float* Lh = Lw + static_cast<size_t>(bh) * m * D;
   for (int e = tid; e < m * (D / 4); e += WGM) {
     const int rr = e / (D / 4), c4 = e % (D / 4);
     st4(TT + rr * LS + 4 * c4, ld4(Lh + rr * D + 4 * c4));
@@ -325,7 +263,7 @@ __device__ void solver_role(const MainArgs& a, int bh, float* smem, int* flag) {
 #pragma unroll
       for (int h = 0; h < 4; h += 2) {
         const float t0 = u[h] - v[h], t1 = u[h + 1] - v[h + 1];
-        if (a.kind == 0) {
+        if constexpr (KIND == 0) {
           d0 += fabsf(t0);
           d1 += fabsf(t1);
         } else {
@@ -348,7 +286,9 @@ __device__ void solver_role(const MainArgs& a, int bh, float* smem, int* flag) {
   if (w < 2) {
     float sum = 0.f;
     if (lane < m) {
-      for (int j = 0; j < m; ++j) sum += fabsf(w == 0 ? A[lane * LS + j] : A[j * LS + lane]);
+      const float* base = w == 0 ? A + lane * LS : A + lane;
+      const int stride = w == 0 ? 1 : LS;
+      for (int j = 0; j < m; ++j) sum += fabsf(base[j * stride]);
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) sum = fmaxf(sum, __shfl_xor(sum, o));
@@ -468,10 +408,6 @@ __device__ void solver_role(const MainArgs& a, int bh, float* smem, int* flag) {
     for (int e = tid; e < m * m; e += WGM)
       a.st_x[static_cast<size_t>(bh) * m * m + e] = XR[(e / m) * LS + (e % m)];
   }
-  if (arrive(&a.ctr[bh * CTR_PER_HEAD + 1], 2u, flag)) {
-    compute_yt_any<D>(a.wt + static_cast<size_t>(bh) * D * MP, Xg,
-                      a.yt + static_cast<size_t>(bh) * D * MP, m);
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -480,8 +416,10 @@ __device__ void solver_role(const MainArgs& a, int bh, float* smem, int* flag) {
 // role: K_QL rows).  Wave g computes landmarks [g m / 8, (g+1) m / 8) for the
 // 64 tokens of the tile (lane = token); the tile's kernel values meet in LDS.
 // ---------------------------------------------------------------------------
-template <int D>
-__device__ void map_role(const MainArgs& a, int b, float* smem, int* flag) {
+template <int D, int KIND, bool BF16>
+__device__ void map_role(const MainArgs& a, const void* __restrict__ q, const void* __restrict__ k,
+                         const void* __restrict__ v, const float* __restrict__ Lw, int b,
+                         float* smem) {
   constexpr int CBN = D / 16;
   float* PJ = smem;                // [64 landmarks][LS]: P[j][token]
   float* PT = smem + MP * LS;      // [64 tokens][LS]:    P[j] of token at [token][j]
@@ -504,7 +442,7 @@ __device__ void map_role(const MainArgs& a, int b, float* smem, int* flag) {
     t_end = t_beg + 1;
   }
   const bool store_kql = !key_role || a.shared_qk;
-  const void* src = key_role ? a.k : a.q;
+  const void* src = key_role ? k : q;
   const int mby = (m + 15) >> 4;
   const int nwb = CBN * mby;  // W output blocks
 
@@ -516,27 +454,33 @@ __device__ void map_role(const MainArgs& a, int b, float* smem, int* flag) {
   __syncthreads();
 
   const int jb = (w * m) / NGRP, je = ((w + 1) * m) / NGRP;
-  const float* Lh = a.L + static_cast<size_t>(bh) * m * D;
+  const float* Lh = Lw + static_cast<size_t>(bh) * m * D;
   f4 wacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 
   for (int t = t_beg; t < t_end; ++t) {
     const int n = t * TILE + lane;
     const bool valid = n < N;
     float x[D];
-    load_row<D>(src, static_cast<size_t>(bh) * N + (valid ? n : N - 1), a.bf16, x);
+    load_row<D>(src, static_cast<size_t>(bh) * N + (valid ? n : N - 1), BF16, x);
     if (key_role) {
-      // V tile -> VT[c][token]; thread (c, token group of 8)
+      // V tile -> VT[c][token]; thread (c, group of TPT tokens); all loads
+      // are issued before the LDS writes (rows past N are clamped, then zeroed)
       const int c = tid % D, tg = tid / D;
-      constexpr int TPT = TILE * D / WGM;  // tokens per thread
+      constexpr int TPT = TILE * D / WGM;
+      float vv[TPT];
+#pragma unroll
+      for (int u = 0; u < TPT; ++u) {
+        const int nv = t * TILE + tg * TPT + u;
+        vv[u] = load1_io(v, (static_cast<size_t>(bh) * N + (nv < N ? nv : N - 1)) * D + c, BF16);
+      }
 #pragma unroll
       for (int u = 0; u < TPT; ++u) {
         const int tok = tg * TPT + u;
-        const int nv = t * TILE + tok;
-        VT[c * LS + tok] = nv < N ? load1_io(a.v, (static_cast<size_t>(bh) * N + nv) * D + c, a.bf16) : 0.f;
+        VT[c * LS + tok] = t * TILE + tok < N ? vv[u] : 0.f;
       }
     }
     for (int j = jb; j < je; ++j) {
-      const float dist = a.kind == 0 ? dist_to<D, 0>(x, Lh + j * D) : dist_to<D, 1>(x, Lh + j * D);
+      const float dist = dist_to<D, KIND>(x, Lh + j * D);
       const float kv = valid ? exp2f(dist * a.c_exp2) : 0.f;
       PJ[j * LS + lane] = kv;
       PT[lane * LS + j] = kv;
@@ -602,65 +546,47 @@ __device__ void map_role(const MainArgs& a, int b, float* smem, int* flag) {
       for (int i = 0; i < 4; ++i) part[(16 * cb + 4 * lg + i) * MP + 16 * jbk + lr] = wacc[s][i];
     }
   }
-  if (!arrive(&a.ctr[bh * CTR_PER_HEAD + 0], static_cast<unsigned>(nK), flag)) return;
-
-  // Last key workgroup of the head: W^T = sum of partials in order 0..nK-1.
-  const float* pb = a.wpart + static_cast<size_t>(bh) * nK * D * MP;
-  float* wt = a.wt + static_cast<size_t>(bh) * D * MP;
-  for (int e4 = tid; e4 < D * MP / 4; e4 += WGM) {
-    const int c = (4 * e4) / MP, j0 = (4 * e4) % MP;
-    f4 s = {0.f, 0.f, 0.f, 0.f};
-    int p = 0;
-    for (; p + 4 <= nK; p += 4) {
-      const f4 v0 = ld4(pb + static_cast<size_t>(p) * D * MP + 4 * e4);
-      const f4 v1 = ld4(pb + static_cast<size_t>(p + 1) * D * MP + 4 * e4);
-      const f4 v2 = ld4(pb + static_cast<size_t>(p + 2) * D * MP + 4 * e4);
-      const f4 v3 = ld4(pb + static_cast<size_t>(p + 3) * D * MP + 4 * e4);
-      s += v0;
-      s += v1;
-      s += v2;
-      s += v3;
-    }
-    for (; p < nK; ++p) s += ld4(pb + static_cast<size_t>(p) * D * MP + 4 * e4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (j0 + i >= m) s[i] = 0.f;
-      else if (a.st_w) a.st_w[(static_cast<size_t>(bh) * m + j0 + i) * D + c] = s[i];
-    }
-    st4(wt + 4 * e4, s);
-  }
-  if (arrive(&a.ctr[bh * CTR_PER_HEAD + 1], 2u, flag)) {
-    compute_yt_any<D>(wt, a.xw + static_cast<size_t>(bh) * MP * MP,
-                      a.yt + static_cast<size_t>(bh) * D * MP, m);
-  }
 }
 
+// Read-only inputs are separate __restrict__ parameters so that wave-uniform
+// reads of them (the landmark coordinates) compile to scalar loads.
 template <int D, int MB>
-__global__ __launch_bounds__(WGM) void main_kernel(MainArgs a) {
+__global__ __launch_bounds__(WGM) void main_kernel(MainArgs a, const void* __restrict__ q,
+                                                    const void* __restrict__ k,
+                                                    const void* __restrict__ v,
+                                                    const float* __restrict__ L) {
   __shared__ __attribute__((aligned(16))) float smem[4 * MP * LS + 4];
-  __shared__ int flag;
   const int b = blockIdx.x;
   if (b < a.ns_blocks) {
-    solver_role<D, MB>(a, b, smem, &flag);
+    if (a.kind == 0)
+      solver_role<D, MB, 0>(a, L, b, smem);
+    else
+      solver_role<D, MB, 1>(a, L, b, smem);
   } else {
-    map_role<D>(a, b - a.ns_blocks, smem, &flag);
+    const int mb = b - a.ns_blocks;
+    if (a.kind == 0) {
+      if (a.bf16) map_role<D, 0, true>(a, q, k, v, L, mb, smem);
+      else map_role<D, 0, false>(a, q, k, v, L, mb, smem);
+    } else {
+      if (a.bf16) map_role<D, 1, true>(a, q, k, v, L, mb, smem);
+      else map_role<D, 1, false>(a, q, k, v, L, mb, smem);
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
 // pool: one workgroup per (landmark, head).  Thread (g, c4) sums a float4
 // column chunk over every G-th token of the window (loads issued 4 at a
-// time); a fixed-order LDS reduction over g finishes the mean.  Workgroup
-// (0, bh) also clears the head's counters.
+// time); a fixed-order LDS reduction over g finishes the mean.
 // ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(WGS) void pool_kernel(const void* __restrict__ K, int bf16,
+template <int D, bool BF16>
+__global__ __launch_bounds__(WGS) void pool_kernel(const void* __restrict__ K,
                                                    float* __restrict__ L,
-                                                   unsigned* __restrict__ ctr,
                                                    float* __restrict__ st_L, int gw, int ph,
                                                    int pw, int m, int N) {
   constexpr int C4 = D / 4;
   constexpr int G = WGS / C4;
+  constexpr int U = 4;  // loads in flight per thread
   __shared__ f4 part[WGS];
   const int j = blockIdx.x, bh = blockIdx.y;
   const int tid = threadIdx.x, c4 = tid % C4, g = tid / C4;
@@ -669,19 +595,18 @@ __global__ __launch_bounds__(WGS) void pool_kernel(const void* __restrict__ K, i
   const int cnt = ph * pw;
   const size_t base = static_cast<size_t>(bh) * N;
   f4 s = {0.f, 0.f, 0.f, 0.f};
-  for (int t0 = g; t0 < cnt; t0 += 4 * G) {
-    f4 v[4];
+  for (int t0 = g; t0 < cnt; t0 += U * G) {
+    f4 v[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int t = t0 + u * G;
-      v[u] = f4{0.f, 0.f, 0.f, 0.f};
-      if (t < cnt) {
-        const int n = (R * ph + t / pw) * gw + C * pw + t % pw;
-        v[u] = load4_io(K, (base + n) * D + 4 * c4, bf16);
-      }
+    for (int u = 0; u < U; ++u) {
+      // tokens past the window are clamped to its first token and dropped below
+      const int t = t0 + u * G < cnt ? t0 + u * G : 0;
+      const int n = (R * ph + t / pw) * gw + C * pw + t % pw;
+      v[u] = load4_io(K, (base + n) * D + 4 * c4, BF16);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) s += v[u];
+    for (int u = 0; u < U; ++u)
+      if (t0 + u * G < cnt) s += v[u];
   }
   part[tid] = s;
   __syncthreads();
@@ -693,7 +618,48 @@ __global__ __launch_bounds__(WGS) void pool_kernel(const void* __restrict__ K, i
     st4(dst, mean);
     if (st_L) st4(st_L + (static_cast<size_t>(bh) * m + j) * D + 4 * tid, mean);
   }
-  if (j == 0 && tid < CTR_PER_HEAD) ctr[bh * CTR_PER_HEAD + tid] = 0u;
+}
+
+// ---------------------------------------------------------------------------
+// wy: workgroup (4 rows of W^T, head).  Thread (row c, column j) sums the nP
+// partials of W^T[c][j] in partial order (8 loads in flight), then forms
+// Y^T[c][r] = sum_k W^T[c][k] X[r][k] for r = j (X rows from the solver).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(WGS) void wy_kernel(const float* __restrict__ wpart,
+                                                 const float* __restrict__ xw,
+                                                 float* __restrict__ yt,
+                                                 float* __restrict__ st_w, int D, int m,
+                                                 int nP) {
+  __shared__ __attribute__((aligned(16))) float wt[4][MP];
+  const int bh = blockIdx.y;
+  const int tid = threadIdx.x, cl = tid / MP, j = tid % MP;
+  const int c = 4 * blockIdx.x + cl;
+  const float* pb = wpart + (static_cast<size_t>(bh) * nP * D + c) * MP + j;
+  const size_t ps = static_cast<size_t>(D) * MP;
+  float sum = 0.f;
+  int p = 0;
+  for (; p + 8 <= nP; p += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = pb[(p + u) * ps];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sum += v[u];
+  }
+  for (; p < nP; ++p) sum += pb[p * ps];
+  if (j >= m) sum = 0.f;
+  wt[cl][j] = sum;
+  if (st_w && j < m) st_w[(static_cast<size_t>(bh) * m + j) * D + c] = sum;
+  __syncthreads();
+  const float* xr = xw + (static_cast<size_t>(bh) * MP + j) * MP;
+  float y0 = 0.f, y1 = 0.f;
+#pragma unroll
+  for (int q = 0; q < MP / 4; q += 2) {
+    const f4 x0 = ld4(xr + 4 * q), x1 = ld4(xr + 4 * q + 4);
+    const f4 w0 = ld4(&wt[cl][4 * q]), w1 = ld4(&wt[cl][4 * q + 4]);
+    y0 = fmaf(w0[0], x0[0], fmaf(w0[1], x0[1], fmaf(w0[2], x0[2], fmaf(w0[3], x0[3], y0))));
+    y1 = fmaf(w1[0], x1[0], fmaf(w1[1], x1[1], fmaf(w1[2], x1[2], fmaf(w1[3], x1[3], y1))));
+  }
+  yt[(static_cast<size_t>(bh) * D + c) * MP + j] = y0 + y1;
 }
 
 // ---------------------------------------------------------------------------
@@ -761,14 +727,18 @@ inline float exp2_scale(float lambda) {
 
 template <int D>
 hipError_t launch_pool_d(const Plan& p, const Args& a, const Buffers& b, hipStream_t s) {
-  hipLaunchKernelGGL((pool_kernel<D>), dim3(p.m, p.BH), dim3(WGS), 0, s, a.k, p.bf16, b.L, b.ctr,
-                     a.st_L, p.gw, p.ph, p.pw, p.m, p.N);
+  if (p.bf16)
+    hipLaunchKernelGGL((pool_kernel<D, true>), dim3(p.m, p.BH), dim3(WGS), 0, s, a.k, b.L,
+                       a.st_L, p.gw, p.ph, p.pw, p.m, p.N);
+  else
+    hipLaunchKernelGGL((pool_kernel<D, false>), dim3(p.m, p.BH), dim3(WGS), 0, s, a.k, b.L,
+                       a.st_L, p.gw, p.ph, p.pw, p.m, p.N);
   return hipGetLastError();
 }
 
 template <int D, int MB>
 hipError_t launch_main_dm(const Plan& p, const MainArgs& ma, unsigned grid, hipStream_t s) {
-  hipLaunchKernelGGL((main_kernel<D, MB>), dim3(grid), dim3(WGM), 0, s, ma);
+  hipLaunchKernelGGL((main_kernel<D, MB>), dim3(grid), dim3(WGM), 0, s, ma, ma.q, ma.k, ma.v, ma.L);
   return hipGetLastError();
 }
 
@@ -824,13 +794,9 @@ hipError_t launch_main(const Plan& p, const Args& a, const Buffers& b, bool with
   ma.L = b.L;
   ma.kql = b.kql;
   ma.wpart = b.wpart;
-  ma.wt = b.wt;
   ma.xw = b.x;
-  ma.yt = b.yt;
-  ma.ctr = b.ctr;
   ma.st_a = a.st_a;
   ma.st_x = a.st_x;
-  ma.st_w = a.st_w;
   ma.st_kql = a.st_kql;
   ma.st_klk = a.st_klk;
   ma.N = p.N;
@@ -857,6 +823,12 @@ hipError_t launch_main(const Plan& p, const Args& a, const Buffers& b, bool with
     case 64: return launch_main_d<64>(p, ma, grid, s);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_wy(const Plan& p, const Args& a, const Buffers& b, hipStream_t s) {
+  hipLaunchKernelGGL(wy_kernel, dim3(p.D / 4, p.BH), dim3(WGS), 0, s, b.wpart, b.x, b.yt, a.st_w,
+                     p.D, p.m, p.nP);
+  return hipGetLastError();
 }
 
 hipError_t launch_out(const Plan& p, const Args& a, const Buffers& b, hipStream_t s) {
