@@ -78,8 +78,10 @@ def stage_work(w):
     return {
         # bytes: read K once, write L
         "pool": {"bytes": BH * (N * d * e + m * d * 4)},
-        # flops: A pairs (3/pair) + 2 m^3 multiply-adds per NS step (4 m^3 flops)
-        "solver": {"flops": BH * (3 * m * m * d + 4 * m ** 3 * w.iters)},
+        # flops: 3 per coordinate pair of the landmark matrix
+        "amat": {"flops": BH * 3 * m * m * d},
+        # flops: 2 m^3 multiply-adds per Newton-Schulz step (4 m^3 flops)
+        "solver": {"flops": BH * 4 * m ** 3 * w.iters},
         # flops: 3 per coordinate pair (sub, |.|, add) or (sub, square, add);
         # bytes: read the token rows of Q and K (once each) and V, write K_QL
         "maps": {"flops": 3 * maps_pairs, "pairs": maps_pairs,

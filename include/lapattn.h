@@ -93,11 +93,12 @@ enum {
 
 /* Stages of one forward call, in launch order (for lapattn_set_stage_events). */
 #define LAPATTN_STAGE_POOL 0     /* landmark average pool                      */
-#define LAPATTN_STAGE_SOLVER 1   /* A = k(L,L) + eps I, alpha, Newton-Schulz  */
-#define LAPATTN_STAGE_MAPS 2     /* K_QL and K_LK maps, partials of K_LK V    */
-#define LAPATTN_STAGE_Y 3        /* W = K_LK V (sum of partials), Y = X W     */
-#define LAPATTN_STAGE_OUT 4      /* O = K_QL Y                                 */
-#define LAPATTN_NUM_STAGES 5
+#define LAPATTN_STAGE_AMAT 1     /* A = k(L,L) + eps I and its row abs-sums   */
+#define LAPATTN_STAGE_SOLVER 2   /* alpha, Newton-Schulz                       */
+#define LAPATTN_STAGE_MAPS 3     /* K_QL and K_LK maps, partials of K_LK V    */
+#define LAPATTN_STAGE_Y 4        /* W = K_LK V (sum of partials), Y = X W     */
+#define LAPATTN_STAGE_OUT 5      /* O = K_QL Y                                 */
+#define LAPATTN_NUM_STAGES 6
 
 typedef struct {
   int32_t B, H;            /* batch and heads; every (b, h) is independent   */

@@ -73,6 +73,10 @@ Plan make_plan(const lapattn_desc_t* d) {
   size_t off = 0;
   p.off_L = off;
   off = align_up(off + BH * p.m * p.D * f);
+  p.off_aw = off;
+  off = align_up(off + BH * MP * MP * f);
+  p.off_rowsum = off;
+  off = align_up(off + BH * MP * f);
   p.off_kql = off;
   off = align_up(off + BH * p.N * p.mpad * f);
   p.off_wpart = off;
@@ -124,6 +128,8 @@ int run(const lapattn_desc_t* desc, const Args& a, void* workspace, size_t ws_by
   char* ws = static_cast<char*>(workspace);
   Buffers b;
   b.L = reinterpret_cast<float*>(ws + p.off_L);
+  b.aw = reinterpret_cast<float*>(ws + p.off_aw);
+  b.rowsum = reinterpret_cast<float*>(ws + p.off_rowsum);
   b.kql = reinterpret_cast<float*>(ws + p.off_kql);
   b.wpart = reinterpret_cast<float*>(ws + p.off_wpart);
   b.x = reinterpret_cast<float*>(ws + p.off_x);
@@ -131,7 +137,9 @@ int run(const lapattn_desc_t* desc, const Args& a, void* workspace, size_t ws_by
 
   auto pool = [&] { return launch_pool(p, a, b, stream); };
   auto out = [&] { return launch_out(p, a, b, stream); };
+  auto amat = [&] { return launch_amat(p, a, b, stream); };
   if (!stage(LAPATTN_STAGE_POOL, stream, pool)) return LAPATTN_ERR_HIP;
+  if (!stage(LAPATTN_STAGE_AMAT, stream, amat)) return LAPATTN_ERR_HIP;
   if (desc->flags & LAPATTN_FLAG_SERIAL) {
     auto solver = [&] { return launch_main(p, a, b, true, false, stream); };
     auto maps = [&] { return launch_main(p, a, b, false, true, stream); };

@@ -22,12 +22,14 @@ struct Plan {
   int S;        // tiles per key-side workgroup
   int nP;       // key-side workgroups (= W partials) per head
   // workspace byte offsets
-  size_t off_L, off_kql, off_wpart, off_x, off_yt;
+  size_t off_L, off_aw, off_rowsum, off_kql, off_wpart, off_x, off_yt;
   size_t total;
 };
 
 struct Buffers {
   float* L;      // [BH][m][D]     landmarks
+  float* aw;     // [BH][MP][MP]   A = k(L, L) + eps I, zero padded
+  float* rowsum; // [BH][MP]       row abs-sums of A
   float* kql;    // [BH][N][mpad]  k(q_n, l_j), zero for j >= m
   float* wpart;  // [BH][nP][D][MP] partial W^T
   float* x;      // [BH][MP][MP]   Newton-Schulz result
@@ -55,6 +57,7 @@ struct Args {
 // the main launch carries: both (one fused launch), or one each in two
 // launches.
 hipError_t launch_pool(const Plan& p, const Args& a, const Buffers& b, hipStream_t s);
+hipError_t launch_amat(const Plan& p, const Args& a, const Buffers& b, hipStream_t s);
 hipError_t launch_main(const Plan& p, const Args& a, const Buffers& b, bool with_solver,
                        bool with_maps, hipStream_t s);
 hipError_t launch_wy(const Plan& p, const Args& a, const Buffers& b, hipStream_t s);

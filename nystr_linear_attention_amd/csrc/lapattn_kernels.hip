@@ -1,10 +1,12 @@
 // HIP kernels for Nystrom kernel attention (forward) on gfx950.
 //
-// Four launches per forward call, back to back on the caller's stream:
+// Five launches per forward call, back to back on the caller's stream:
 //   pool : landmarks L = window means of K                         (HBM stream)
+//   amat : A = k(L, L) + eps I and its row abs-sums (one workgroup per
+//          landmark row, so the m^2 d distance work is spread over the chip)
 //   main : role-split workgroups
 //          - solver WGs (one per head, dispatched first, raised wave priority):
-//            A = k(L, L) + eps I, alpha, Newton-Schulz held in LDS, fp32 MFMA
+//            alpha, then the Newton-Schulz steps held in LDS, fp32 MFMA
 //          - map WGs: kernel values of 64 tokens against every landmark on
 //            FP32 VALU (landmark coordinates are wave-uniform scalar operands);
 //            query tiles store K_QL, key tiles contract K_LK V on fp32 MFMA
@@ -105,6 +107,33 @@ __device__ __forceinline__ void load_row(const void* base, size_t row, int bf16,
   }
 }
 
+// Distances of a register-resident point to two wave-uniform points l0, l1
+// (scalar loads issued together, so their latencies overlap).  Holding more
+// landmark coordinates in flight than this spills scalar registers.
+template <int D, int KIND>
+__device__ __forceinline__ void dist_to2(const float* x, const float* __restrict__ l0,
+                                         const float* __restrict__ l1, float& r0, float& r1) {
+  float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
+#pragma unroll
+  for (int k = 0; k < D; k += 2) {
+    const float s0 = x[k] - l0[k], s1 = x[k + 1] - l0[k + 1];
+    const float t0 = x[k] - l1[k], t1 = x[k + 1] - l1[k + 1];
+    if constexpr (KIND == 0) {
+      a0 += fabsf(s0);
+      a1 += fabsf(s1);
+      b0 += fabsf(t0);
+      b1 += fabsf(t1);
+    } else {
+      a0 = fmaf(s0, s0, a0);
+      a1 = fmaf(s1, s1, a1);
+      b0 = fmaf(t0, t0, b0);
+      b1 = fmaf(t1, t1, b1);
+    }
+  }
+  r0 = a0 + a1;
+  r1 = b0 + b1;
+}
+
 // Distance of a register-resident point to a wave-uniform point `l`
 // (scalar loads): L1 for KIND 0, squared L2 for KIND 1.  Two partial sums.
 template <int D, int KIND>
@@ -133,7 +162,8 @@ struct MainArgs {
   float* kql;         // [BH][N][mpad]
   float* wpart;       // [BH][nP][D][MP]
   float* xw;          // [BH][MP][MP]
-  float* st_a;
+  const float* aw;    // [BH][MP][MP]  A = k(L, L) + eps I, zero padded
+  const float* rowsum;  // [BH][MP]    row abs-sums of A
   float* st_x;
   float* st_kql;
   float* st_klk;
@@ -146,10 +176,12 @@ struct MainArgs {
 };
 
 // ---------------------------------------------------------------------------
-// Solver role.  Matrices live in LDS (64 x LS floats, zero padded):
-//   A  (row-major; exactly symmetric by construction)
-//   XR (X_t row-major), XT (X_t transposed), TT (T transposed)
-//   phase 1: T = A X_t          operands: rows of A, rows of XT
+// Solver role.  Matrices live in LDS (zero padded), rows of SLS floats:
+//   A        (row-major; bitwise symmetric: |a-b| = |b-a| term by term)
+//   XR[2]    (X_t row-major, double buffered)
+//   XT[2]    (X_t transposed, double buffered)
+//   TT       (T transposed)
+//   phase 1: T = A X_t                 operands: rows of A, rows of XT
 //   phase 2: X_{t+1} = 2 X_t - X_t T   operands: rows of XR, rows of TT
 // The recursion is evaluated as printed, with full (unsymmetrised)
 // products: forcing the iterates symmetric turns the quadratic error
@@ -165,8 +197,16 @@ struct SolverGeom {
   static constexpr int NBLK = MB * MB;            // interior 16x16 blocks
   static constexpr int KS = 4 * MB;               // MFMA sub-steps per block
   static constexpr int NBQ = 4 * MB + 1;          // float4 reads per border dot
-  // waves [BW0, 8) share the border entries (fewest interior blocks)
-  static constexpr int BW0 = MB == 0 ? 0 : (MB == 2 ? 4 : 1);
+  // rows and row stride: 16 MB interior + up to 4 border rows / columns.
+  // Strides are 4 (mod 32) or 20 (mod 32) floats, which keeps 16-byte reads
+  // of 8 consecutive rows on distinct LDS banks.
+  static constexpr int ROWS = MB == 4 ? 64 : 16 * MB + 4;
+  static constexpr int SLS = MB == 4 ? 68 : 16 * MB + 4;
+  static constexpr int MAT = ROWS * SLS;          // floats per matrix
+  // Wave w < MB owns interior block-row w (MB blocks); waves MB..7 compute
+  // the border entries concurrently.
+  static constexpr int BW0 = MB;
+  static constexpr int SMEM = 6 * MAT + 4;        // floats of LDS
 };
 
 // Border entry e -> (a, b): Z[a][b] with b a border column (a < m) or a a
@@ -184,123 +224,100 @@ __device__ __forceinline__ void border_ab(int e, int m, int r, int& a, int& b) {
   }
 }
 
-// Interior blocks of Z = Lm R, with Lm given by rows and R by the rows of
-// R^T (Rt), in accumulator layout, for the blocks owned by wave w.
+// Block-row w of Z = Lm R (MB blocks): the A operand is row 16 w + lr of Lm,
+// given as KS/4 float4 in registers (k = KS*lg + s), the B operands are rows
+// of R^T (Rt).  All B rows are read before the MFMA chains start so that the
+// independent chains of the MB blocks overlap in the matrix pipe.  `lb` holds
+// Lm[16 w + 4 lg + i][16 MB .. 16 MB + 3] for the rank-r border update.
 template <int MB>
-__device__ __forceinline__ void solver_product(const float* Lm, const float* Rt, int w, int lane,
-                                               bool has_border, f4 acc[2]) {
+__device__ __forceinline__ void row_product(const f4* areg, const f4* lb, const float* Rt,
+                                            int lane, bool has_border, f4* acc) {
   using G = SolverGeom<MB>;
+  constexpr int KQ = G::KS / 4;
   const int lr = lane & 15, lg = lane >> 4;
+  f4 bv[MB][KQ];
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const int b = w + 8 * s;
-    acc[s] = f4{0.f, 0.f, 0.f, 0.f};
-    if (b < G::NBLK) {
-      const int bi = b / (MB > 0 ? MB : 1), bj = b % (MB > 0 ? MB : 1);
-      const float* ar = Lm + (16 * bi + lr) * LS + G::KS * lg;
-      const float* br = Rt + (16 * bj + lr) * LS + G::KS * lg;
-      f4 c = {0.f, 0.f, 0.f, 0.f};
+  for (int bj = 0; bj < MB; ++bj) {
+    const float* br = Rt + (16 * bj + lr) * G::SLS + G::KS * lg;
 #pragma unroll
-      for (int q = 0; q < G::KS / 4; ++q) {
-        const f4 a4 = ld4(ar + 4 * q), b4 = ld4(br + 4 * q);
-        c = mfma4(a4[0], b4[0], c);
-        c = mfma4(a4[1], b4[1], c);
-        c = mfma4(a4[2], b4[2], c);
-        c = mfma4(a4[3], b4[3], c);
-      }
-      if (MB < 4 && has_border) {
-        // k in [16 MB, 16 MB + 4); padding beyond m is zero
-        const f4 rb = ld4(Rt + (16 * bj + lr) * LS + 16 * MB);
+    for (int q = 0; q < KQ; ++q) bv[bj][q] = ld4(br + 4 * q);
+  }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const f4 la = ld4(Lm + (16 * bi + 4 * lg + i) * LS + 16 * MB);
-          c[i] = fmaf(la[0], rb[0], fmaf(la[1], rb[1], fmaf(la[2], rb[2], fmaf(la[3], rb[3], c[i]))));
-        }
-      }
-      acc[s] = c;
+  for (int bj = 0; bj < MB; ++bj) acc[bj] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < KQ; ++q)
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+#pragma unroll
+      for (int bj = 0; bj < MB; ++bj) acc[bj] = mfma4(areg[q][h], bv[bj][q][h], acc[bj]);
+  if (MB < 4 && has_border) {
+    // k in [16 MB, 16 MB + 4); padding beyond m is zero
+#pragma unroll
+    for (int bj = 0; bj < MB; ++bj) {
+      const f4 rb = ld4(Rt + (16 * bj + lr) * G::SLS + 16 * MB);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[bj][i] = fmaf(lb[i][0], rb[0], fmaf(lb[i][1], rb[1], fmaf(lb[i][2], rb[2], fmaf(lb[i][3], rb[3], acc[bj][i]))));
     }
   }
 }
 
-template <int D, int MB, int KIND>
-__device__ void solver_role(const MainArgs& a, const float* __restrict__ Lw, int bh, float* smem) {
+// Border dot product: row a of Lm against row b of Rt, k < 16 MB + 4.
+template <int MB>
+__device__ __forceinline__ float border_dot(const float* Lm, const float* Rt, int a, int b) {
   using G = SolverGeom<MB>;
+  const float* ra = Lm + a * G::SLS;
+  const float* rb = Rt + b * G::SLS;
+  float d[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < G::NBQ; ++q) {
+    const f4 a4 = ld4(ra + 4 * q), b4 = ld4(rb + 4 * q);
+    d[q & 3] = fmaf(a4[0], b4[0], fmaf(a4[1], b4[1], fmaf(a4[2], b4[2], fmaf(a4[3], b4[3], d[q & 3]))));
+  }
+  return (d[0] + d[1]) + (d[2] + d[3]);
+}
+
+template <int MB>
+__device__ void solver_role(const MainArgs& a, int bh, float* smem) {
+  using G = SolverGeom<MB>;
+  constexpr int S = G::SLS;
   float* A = smem;
-  float* XR = smem + MP * LS;
-  float* XT = smem + 2 * MP * LS;
-  float* TT = smem + 3 * MP * LS;
-  float* red = smem + 4 * MP * LS;  // 4 scalars
+  float* XR0 = smem + G::MAT;
+  float* XR1 = smem + 2 * G::MAT;
+  float* XT0 = smem + 3 * G::MAT;
+  float* XT1 = smem + 4 * G::MAT;
+  float* TT = smem + 5 * G::MAT;
+  float* red = smem + 6 * G::MAT;  // scalars
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int lr = lane & 15, lg = lane >> 4;
   const int m = a.m;
   __builtin_amdgcn_s_setprio(3);
 
-  for (int e = tid; e < 4 * MP * LS; e += WGM) smem[e] = 0.f;
-  __syncthreads();
-  // landmarks -> TT (scratch), rows of D floats at stride LS
-  const float* Lh = Lw + static_cast<size_t>(bh) * m * D;
-  for (int e = tid; e < m * (D / 4); e += WGM) {
-    const int rr = e / (D / 4), c4 = e % (D / 4);
-    st4(TT + rr * LS + 4 * c4, ld4(Lh + rr * D + 4 * c4));
+  // A (built by the A-matrix launch, zero padded to 64 x 64) -> LDS.
+  const float* Ag = a.aw + static_cast<size_t>(bh) * MP * MP;
+  for (int e = tid; e < G::ROWS * (S / 4); e += WGM) {
+    const int row = e / (S / 4), c4 = e % (S / 4);
+    // rows >= m were never written by the A-matrix launch: zero them here
+    st4(A + row * S + 4 * c4,
+        (row < m && 4 * c4 < MP) ? ld4(Ag + row * MP + 4 * c4) : f4{0.f, 0.f, 0.f, 0.f});
   }
-  __syncthreads();
-
-  // A[i][j], i <= j, mirrored (the distance is symmetric term by term).
-  const int npairs = m * (m + 1) / 2;
-  for (int p = tid; p < npairs; p += WGM) {
-    int i = 0, rem = p;
-    while (rem >= m - i) {
-      rem -= m - i;
-      ++i;
-    }
-    const int j = i + rem;
-    const float* li = TT + i * LS;
-    const float* lj = TT + j * LS;
-    float d0 = 0.f, d1 = 0.f;
-#pragma unroll
-    for (int q = 0; q < D / 4; ++q) {
-      const f4 u = ld4(li + 4 * q), v = ld4(lj + 4 * q);
-#pragma unroll
-      for (int h = 0; h < 4; h += 2) {
-        const float t0 = u[h] - v[h], t1 = u[h + 1] - v[h + 1];
-        if constexpr (KIND == 0) {
-          d0 += fabsf(t0);
-          d1 += fabsf(t1);
-        } else {
-          d0 = fmaf(t0, t0, d0);
-          d1 = fmaf(t1, t1, d1);
-        }
-      }
-    }
-    float av = exp2f((d0 + d1) * a.c_exp2);
-    if (i == j) av += a.eps;
-    A[i * LS + j] = av;
-    A[j * LS + i] = av;
-  }
-  __syncthreads();
-  if (a.st_a) {
-    for (int e = tid; e < m * m; e += WGM)
-      a.st_a[static_cast<size_t>(bh) * m * m + e] = A[(e / m) * LS + (e % m)];
-  }
-  // alpha = 1 / (max column abs-sum * max row abs-sum); wave 0 rows, wave 1 columns.
-  if (w < 2) {
-    float sum = 0.f;
-    if (lane < m) {
-      const float* base = w == 0 ? A + lane * LS : A + lane;
-      const int stride = w == 0 ? 1 : LS;
-      for (int j = 0; j < m; ++j) sum += fabsf(base[j * stride]);
-    }
+  // alpha = 1 / (max column abs-sum * max row abs-sum).  A is bitwise
+  // symmetric, so its largest column sum equals its largest row sum.
+  if (w == 0) {
+    float sum = lane < m ? a.rowsum[static_cast<size_t>(bh) * MP + lane] : 0.f;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) sum = fmaxf(sum, __shfl_xor(sum, o));
-    if (lane == 0) red[w] = sum;
+    if (lane == 0) red[0] = sum;
   }
   __syncthreads();
-  const float alpha = 1.0f / (red[0] * red[1]);
-  // X_0 = alpha A in both layouts (A is exactly symmetric); TT back to zero.
-  for (int e = tid; e < MP * LS; e += WGM) {
+  const float alpha = 1.0f / (red[0] * red[0]);
+  // X_0 = alpha A in both layouts; the other buffers zero.
+  for (int e = tid; e < G::MAT; e += WGM) {
     const float x0 = alpha * A[e];
-    XR[e] = x0;
-    XT[e] = x0;
+    XR0[e] = x0;
+    XT0[e] = x0;
+    XR1[e] = 0.f;
+    XT1[e] = 0.f;
     TT[e] = 0.f;
   }
   __syncthreads();
@@ -308,105 +325,109 @@ __device__ void solver_role(const MainArgs& a, const float* __restrict__ Lw, int
   const int r = m > 16 * MB ? m - 16 * MB : 0;  // border width (0 when padded)
   const bool has_border = r > 0;
   const int nbe = r * m + r * 16 * MB;           // border entries
-  const int nl = 64 * (8 - G::BW0);
+  constexpr int NL = 64 * (8 - G::BW0);          // border lanes
+  constexpr int NBE = 2;                         // border entries per lane (max)
+  constexpr int MBR = MB > 0 ? MB : 1;
+  constexpr int KQR = G::KS / 4 > 0 ? G::KS / 4 : 1;
+  const bool row_wave = w < MB;
 
-  // Own entries of X_t in registers (interior accumulator layout, border).
-  f4 xr[2];
-  float xb[2];
-  int ba[2], bb[2];
+  // Row waves: own block-row of X_t (accumulator layout), constant A operand
+  // and A border columns in registers.  Border waves: their border entries.
+  f4 xr[MBR], areg[KQR], alb[4];
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const int b = w + 8 * s;
-    xr[s] = f4{0.f, 0.f, 0.f, 0.f};
-    if (b < G::NBLK) {
-      const int bi = b / (MB > 0 ? MB : 1), bj = b % (MB > 0 ? MB : 1);
+  for (int bj = 0; bj < MBR; ++bj) xr[bj] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xr[s][i] = XR[(16 * bi + 4 * lg + i) * LS + 16 * bj + lr];
+  for (int q = 0; q < KQR; ++q) areg[q] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) alb[i] = f4{0.f, 0.f, 0.f, 0.f};
+  if (row_wave) {
+#pragma unroll
+    for (int bj = 0; bj < MBR; ++bj)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xr[bj][i] = XR0[(16 * w + 4 * lg + i) * S + 16 * bj + lr];
+#pragma unroll
+    for (int q = 0; q < G::KS / 4; ++q) areg[q] = ld4(A + (16 * w + lr) * S + G::KS * lg + 4 * q);
+    if (MB < 4) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) alb[i] = ld4(A + (16 * w + 4 * lg + i) * S + 16 * MB);
     }
+  }
+  float xb[NBE];
+  int ba[NBE], bb[NBE];
+#pragma unroll
+  for (int s = 0; s < NBE; ++s) {
     xb[s] = 0.f;
     ba[s] = -1;
     bb[s] = 0;
     if (has_border && w >= G::BW0) {
-      const int e = tid - 64 * G::BW0 + nl * s;
+      const int e = tid - 64 * G::BW0 + NL * s;
       if (e < nbe) {
         border_ab<MB>(e, m, r, ba[s], bb[s]);
-        xb[s] = XR[ba[s] * LS + bb[s]];
+        xb[s] = XR0[ba[s] * S + bb[s]];
       }
     }
   }
 
   for (int t = 0; t < a.iters; ++t) {
-    f4 acc[2];
+    const float* XRc = (t & 1) ? XR1 : XR0;
+    const float* XTc = (t & 1) ? XT1 : XT0;
+    float* XRn = (t & 1) ? XR0 : XR1;
+    float* XTn = (t & 1) ? XT0 : XT1;
     // phase 1: T = A X_t, stored transposed
-    solver_product<MB>(A, XT, w, lane, has_border, acc);
+    if constexpr (MB > 0) {
+      if (row_wave) {
+        f4 acc[MBR];
+        row_product<MB>(areg, alb, XTc, lane, has_border, acc);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int b = w + 8 * s;
-      if (b < G::NBLK) {
-        const int bi = b / (MB > 0 ? MB : 1), bj = b % (MB > 0 ? MB : 1);
-        st4(TT + (16 * bj + lr) * LS + 16 * bi + 4 * lg, acc[s]);
-      }
-      if (ba[s] >= 0) {
-        const float* ra = A + ba[s] * LS;
-        const float* rb = XT + bb[s] * LS;
-        float d = 0.f;
-#pragma unroll
-        for (int q = 0; q < G::NBQ; ++q) {
-          const f4 a4 = ld4(ra + 4 * q), b4 = ld4(rb + 4 * q);
-          d = fmaf(a4[0], b4[0], fmaf(a4[1], b4[1], fmaf(a4[2], b4[2], fmaf(a4[3], b4[3], d))));
-        }
-        TT[bb[s] * LS + ba[s]] = d;
+        for (int bj = 0; bj < MBR; ++bj) st4(TT + (16 * bj + lr) * S + 16 * w + 4 * lg, acc[bj]);
       }
     }
+#pragma unroll
+    for (int s = 0; s < NBE; ++s)
+      if (ba[s] >= 0) TT[bb[s] * S + ba[s]] = border_dot<MB>(A, XTc, ba[s], bb[s]);
     __syncthreads();
-    // phase 2: X_{t+1} = 2 X_t - X_t T
-    solver_product<MB>(XR, TT, w, lane, has_border, acc);
-    float xbn[2];
+    // phase 2: X_{t+1} = 2 X_t - X_t T, written to the other buffers
+    if constexpr (MB > 0) {
+      if (row_wave) {
+        f4 xa[KQR], xlb[4];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      xbn[s] = xb[s];
-      if (ba[s] >= 0) {
-        const float* ra = XR + ba[s] * LS;
-        const float* rb = TT + bb[s] * LS;
-        float d = 0.f;
+        for (int q = 0; q < G::KS / 4; ++q) xa[q] = ld4(XRc + (16 * w + lr) * S + G::KS * lg + 4 * q);
 #pragma unroll
-        for (int q = 0; q < G::NBQ; ++q) {
-          const f4 a4 = ld4(ra + 4 * q), b4 = ld4(rb + 4 * q);
-          d = fmaf(a4[0], b4[0], fmaf(a4[1], b4[1], fmaf(a4[2], b4[2], fmaf(a4[3], b4[3], d))));
+        for (int i = 0; i < 4; ++i)
+          xlb[i] = MB < 4 ? ld4(XRc + (16 * w + 4 * lg + i) * S + 16 * (MB < 4 ? MB : 0)) : f4{0.f, 0.f, 0.f, 0.f};
+        f4 acc[MBR];
+        row_product<MB>(xa, xlb, TT, lane, has_border, acc);
+#pragma unroll
+        for (int bj = 0; bj < MBR; ++bj) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            xr[bj][i] = 2.0f * xr[bj][i] - acc[bj][i];
+            XRn[(16 * w + 4 * lg + i) * S + 16 * bj + lr] = xr[bj][i];
+          }
+          st4(XTn + (16 * bj + lr) * S + 16 * w + 4 * lg, xr[bj]);
         }
-        xbn[s] = 2.0f * xb[s] - d;
       }
     }
-    __syncthreads();  // every read of XR / TT of this step is done
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int b = w + 8 * s;
-      if (b < G::NBLK) {
-        const int bi = b / (MB > 0 ? MB : 1), bj = b % (MB > 0 ? MB : 1);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          xr[s][i] = 2.0f * xr[s][i] - acc[s][i];
-          XR[(16 * bi + 4 * lg + i) * LS + 16 * bj + lr] = xr[s][i];
-        }
-        st4(XT + (16 * bj + lr) * LS + 16 * bi + 4 * lg, xr[s]);
-      }
+    for (int s = 0; s < NBE; ++s) {
       if (ba[s] >= 0) {
-        xb[s] = xbn[s];
-        XR[ba[s] * LS + bb[s]] = xb[s];
-        XT[bb[s] * LS + ba[s]] = xb[s];
+        xb[s] = 2.0f * xb[s] - border_dot<MB>(XRc, TT, ba[s], bb[s]);
+        XRn[ba[s] * S + bb[s]] = xb[s];
+        XTn[bb[s] * S + ba[s]] = xb[s];
       }
     }
     __syncthreads();
   }
 
+  const float* Xf = (a.iters & 1) ? XR1 : XR0;
   float* Xg = a.xw + static_cast<size_t>(bh) * MP * MP;
-  for (int e = tid; e < MP * (MP / 4); e += WGM) {
-    const int row = e / (MP / 4), c4 = e % (MP / 4);
-    st4(Xg + row * MP + 4 * c4, ld4(XR + row * LS + 4 * c4));
+  for (int e = tid; e < MP * MP; e += WGM) {
+    const int row = e / MP, col = e % MP;
+    Xg[e] = (row < G::ROWS && col < S) ? Xf[row * S + col] : 0.f;
   }
   if (a.st_x) {
     for (int e = tid; e < m * m; e += WGM)
-      a.st_x[static_cast<size_t>(bh) * m * m + e] = XR[(e / m) * LS + (e % m)];
+      a.st_x[static_cast<size_t>(bh) * m * m + e] = Xf[(e / m) * S + (e % m)];
   }
 }
 
@@ -428,6 +449,19 @@ __device__ void map_role(const MainArgs& a, const void* __restrict__ q, const vo
   const int lr = lane & 15, lg = lane >> 4;
   const int m = a.m, N = a.N;
   const int nK = a.nP;
+  // Workgroups are dispatched round-robin over the 8 XCDs.  When the heads
+  // divide evenly, renumber so that XCD x (= b % 8) works through heads
+  // x, x + 8, ... in order: each XCD's L2 and scalar caches then hold the
+  // landmarks of only 1/8 of the heads.
+  if (a.BH % 8 == 0) {
+    const int per_head = nK + a.nQ;
+    const int per_xcd = (a.BH / 8) * per_head;
+    const int x = b % 8, i = b / 8;
+    const int hh = i / per_head, u = i % per_head;  // head slot within the XCD, unit
+    const int head = 8 * hh + x;
+    b = u < nK ? head * nK + u : a.BH * nK + head * a.nQ + (u - nK);
+    (void)per_xcd;
+  }
   const bool key_role = b < a.BH * nK;
   int bh, t_beg, t_end;
   if (key_role) {
@@ -479,11 +513,18 @@ __device__ void map_role(const MainArgs& a, const void* __restrict__ q, const vo
         VT[c * LS + tok] = t * TILE + tok < N ? vv[u] : 0.f;
       }
     }
-    for (int j = jb; j < je; ++j) {
-      const float dist = dist_to<D, KIND>(x, Lh + j * D);
-      const float kv = valid ? exp2f(dist * a.c_exp2) : 0.f;
-      PJ[j * LS + lane] = kv;
-      PT[lane * LS + j] = kv;
+    // landmarks two at a time (their scalar loads overlap); an odd last
+    // landmark is paired with itself and stored once
+    for (int j = jb; j < je; j += 2) {
+      const int j1 = j + 1 < je ? j + 1 : j;
+      float d0, d1;
+      dist_to2<D, KIND>(x, Lh + j * D, Lh + j1 * D, d0, d1);
+      const float k0 = valid ? exp2f(d0 * a.c_exp2) : 0.f;
+      const float k1 = valid ? exp2f(d1 * a.c_exp2) : 0.f;
+      PJ[j * LS + lane] = k0;
+      PT[lane * LS + j] = k0;
+      PJ[j1 * LS + lane] = k1;
+      PT[lane * LS + j1] = k1;
     }
     __syncthreads();
     if (store_kql) {
@@ -555,13 +596,13 @@ __global__ __launch_bounds__(WGM) void main_kernel(MainArgs a, const void* __res
                                                     const void* __restrict__ k,
                                                     const void* __restrict__ v,
                                                     const float* __restrict__ L) {
-  __shared__ __attribute__((aligned(16))) float smem[4 * MP * LS + 4];
+  constexpr int MAP_SMEM = 3 * MP * LS;
+  constexpr int SOLVER_SMEM = SolverGeom<MB>::SMEM;
+  __shared__ __attribute__((aligned(16)))
+  float smem[MAP_SMEM > SOLVER_SMEM ? MAP_SMEM : SOLVER_SMEM];
   const int b = blockIdx.x;
   if (b < a.ns_blocks) {
-    if (a.kind == 0)
-      solver_role<D, MB, 0>(a, L, b, smem);
-    else
-      solver_role<D, MB, 1>(a, L, b, smem);
+    solver_role<MB>(a, b, smem);
   } else {
     const int mb = b - a.ns_blocks;
     if (a.kind == 0) {
@@ -572,6 +613,37 @@ __global__ __launch_bounds__(WGM) void main_kernel(MainArgs a, const void* __res
       else map_role<D, 1, false>(a, q, k, v, L, mb, smem);
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// amat: A = k(L, L) + eps I.  Workgroup (row i, head), one wave: lane j
+// computes A[i][j] with landmark j in registers and landmark i as wave-uniform
+// scalar operands.  A[j][i] comes from workgroup j with the same operations on
+// the same terms (|a - b| = |b - a|), so A is bitwise symmetric.  Rows are
+// written zero padded to 64 columns, with their abs-sums for alpha.
+// ---------------------------------------------------------------------------
+template <int D, int KIND>
+__global__ __launch_bounds__(64) void amat_kernel(const float* __restrict__ L,
+                                                  float* __restrict__ aw,
+                                                  float* __restrict__ rowsum,
+                                                  float* __restrict__ st_a, int m,
+                                                  float c_exp2, float eps) {
+  const int i = blockIdx.x, bh = blockIdx.y, j = threadIdx.x;
+  const float* Lh = L + static_cast<size_t>(bh) * m * D;
+  float x[D];
+  load_row<D>(Lh, j < m ? j : 0, 0, x);
+  const float dist = dist_to<D, KIND>(x, Lh + i * D);
+  float av = 0.f;
+  if (j < m) {
+    av = exp2f(dist * c_exp2);
+    if (i == j) av += eps;
+  }
+  aw[(static_cast<size_t>(bh) * MP + i) * MP + j] = av;
+  if (st_a && j < m) st_a[(static_cast<size_t>(bh) * m + i) * m + j] = av;
+  float sum = fabsf(av);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+  if (j == 0) rowsum[static_cast<size_t>(bh) * MP + i] = sum;
 }
 
 // ---------------------------------------------------------------------------
@@ -736,6 +808,18 @@ hipError_t launch_pool_d(const Plan& p, const Args& a, const Buffers& b, hipStre
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_amat_d(const Plan& p, const Args& a, const Buffers& b, hipStream_t s) {
+  const float c = exp2_scale(a.lambda);
+  if (p.kernel == 0)
+    hipLaunchKernelGGL((amat_kernel<D, 0>), dim3(p.m, p.BH), dim3(64), 0, s, b.L, b.aw, b.rowsum,
+                       a.st_a, p.m, c, a.eps);
+  else
+    hipLaunchKernelGGL((amat_kernel<D, 1>), dim3(p.m, p.BH), dim3(64), 0, s, b.L, b.aw, b.rowsum,
+                       a.st_a, p.m, c, a.eps);
+  return hipGetLastError();
+}
+
 template <int D, int MB>
 hipError_t launch_main_dm(const Plan& p, const MainArgs& ma, unsigned grid, hipStream_t s) {
   hipLaunchKernelGGL((main_kernel<D, MB>), dim3(grid), dim3(WGM), 0, s, ma, ma.q, ma.k, ma.v, ma.L);
@@ -785,6 +869,15 @@ hipError_t launch_pool(const Plan& p, const Args& a, const Buffers& b, hipStream
   return hipErrorInvalidValue;
 }
 
+hipError_t launch_amat(const Plan& p, const Args& a, const Buffers& b, hipStream_t s) {
+  switch (p.D) {
+    case 16: return launch_amat_d<16>(p, a, b, s);
+    case 32: return launch_amat_d<32>(p, a, b, s);
+    case 64: return launch_amat_d<64>(p, a, b, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_main(const Plan& p, const Args& a, const Buffers& b, bool with_solver,
                        bool with_maps, hipStream_t s) {
   MainArgs ma{};
@@ -795,7 +888,8 @@ hipError_t launch_main(const Plan& p, const Args& a, const Buffers& b, bool with
   ma.kql = b.kql;
   ma.wpart = b.wpart;
   ma.xw = b.x;
-  ma.st_a = a.st_a;
+  ma.aw = b.aw;
+  ma.rowsum = b.rowsum;
   ma.st_x = a.st_x;
   ma.st_kql = a.st_kql;
   ma.st_klk = a.st_klk;
