@@ -36,8 +36,9 @@ def log(*a):
 
 
 class HipEvents:
-    """Timing events from the HIP runtime (the library records them on the
-    stream each stage runs on, which torch.cuda.Event cannot follow)."""
+    """Timing events from the HIP runtime.  The library binds a start/stop
+    pair to each kernel launch (hipExtLaunchKernel), so their elapsed time is
+    that kernel's own duration."""
 
     def __init__(self):
         self.rt = ctypes.CDLL("libamdhip64.so")
@@ -69,26 +70,27 @@ class HipEvents:
         self.owned = []
 
 
-def stage_work(w):
-    """Algorithmic work per launch of each stage."""
+def work(w):
+    """Algorithmic work of the launches of one forward call.
+
+    Flops: 3 per coordinate pair of an L1 or squared-L2 distance (difference,
+    |.| or square, accumulate); 2 per multiply-add of a contraction.  Bytes:
+    what the step must read and write at least (inputs once, outputs once)."""
     BH, N, d, m = w.heads, w.N, w.d, w.m
     e = 2 if w.dtype == "bf16" else 4
     sides = 1 if w.shared_qk else 2
-    maps_pairs = BH * sides * N * m * d
+    map_pairs = BH * sides * N * m * d
+    amat_pairs = BH * m * m * d
+    ns = BH * 4 * m ** 3 * w.iters
+    klkv = BH * 2 * m * N * d
     return {
-        # bytes: read K once, write L
+        "map_pairs": map_pairs,
+        "amat_pairs": amat_pairs,
         "pool": {"bytes": BH * (N * d * e + m * d * 4)},
-        # flops: 3 per coordinate pair of the landmark matrix
-        "amat": {"flops": BH * 3 * m * m * d},
-        # flops: 2 m^3 multiply-adds per Newton-Schulz step (4 m^3 flops)
-        "solver": {"flops": BH * 4 * m ** 3 * w.iters},
-        # flops: 3 per coordinate pair (sub, |.|, add) or (sub, square, add);
-        # bytes: read the token rows of Q and K (once each) and V, write K_QL
-        "maps": {"flops": 3 * maps_pairs, "pairs": maps_pairs,
-                 "bytes": BH * (sides * N * d * e + N * d * e + N * m * 4)},
-        # bytes: read the W^T partials and X, write Y^T
-        "y": {},
-        # bytes: read K_QL (fp32), write O
+        "amat": {"flops": 3 * amat_pairs},
+        "solver": {"flops": ns},
+        "maps": {"flops": 3 * map_pairs + klkv},
+        "fused": {"flops": 3 * map_pairs + klkv + ns},
         "out": {"bytes": BH * (m * N * 4 + N * d * e)},
     }
 
@@ -125,15 +127,65 @@ def cpu_baseline(w, inputs, seconds):
     }
 
 
+def source_digest():
+    """sha256 of the kernel sources, to tie stored counter figures to a build."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "nystr_linear_attention_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload, kernel):
+    """HBM bytes per launch from the committed counter summary of `kernel` on
+    `workload`, or None if there is none or the kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("- ") and ":" in line:
+                k, v = line[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("source digest") != source_digest():
+        return None
+    try:
+        return int(fields["bytes per launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(mib):
+    """A plain device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: 5 copies of {mib} MiB ({n * 4} bytes read and written each)")
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=None)
-    ap.add_argument("--serial", action="store_true", help="single-stream launch plan")
+    ap.add_argument("--serial", action="store_true",
+                    help="time the serial launch plan (solver, then maps) instead of the fused one")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-other-plan", action="store_true",
+                    help="skip the pass over the other launch plan (its fields become null)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -141,6 +193,8 @@ def main(argv=None):
               "GPU only (heads are independent, so B*H would shard across GPUs with no "
               "exchange; see DESIGN.md).", file=sys.stderr)
         return 2
+    if args.copy_calibration:
+        return copy_calibration(args.copy_calibration)
 
     import numpy as np
     import torch
@@ -164,82 +218,138 @@ def main(argv=None):
     k = q if w.shared_qk else to_dev(x["k"])
     v = to_dev(x["v"])
     out = torch.empty_like(q)
-    desc = api.make_desc(w.B, w.H, w.grid_h, w.grid_w, w.d, w.pool_h, w.pool_w,
-                         w.kernel, q.dtype, serial=args.serial)
-    ws = api.alloc_workspace(desc, dev)
     lib = _lib.lib()
     api.init()
     stream = torch.cuda.current_stream().cuda_stream
-    call = (ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(), w.lam, w.eps,
-            w.iters, out.data_ptr(), ws.data_ptr(), ws.numel(), stream)
 
-    def step():
-        st = lib.lapattn_forward(*call)
-        if st != 0:
-            raise _lib.LapattnError(st, _lib.strerror(st))
+    def make_step(serial):
+        desc = api.make_desc(w.B, w.H, w.grid_h, w.grid_w, w.d, w.pool_h, w.pool_w,
+                             w.kernel, q.dtype, serial=serial)
+        ws = api.alloc_workspace(desc, dev)
+        call = (ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(), w.lam, w.eps,
+                w.iters, out.data_ptr(), ws.data_ptr(), ws.numel(), stream)
 
+        def step():
+            st = lib.lapattn_forward(*call)
+            if st != 0:
+                raise _lib.LapattnError(st, _lib.strerror(st))
+        step.keep = (desc, ws)
+        return step
+
+    hip = HipEvents()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+
+    def timed(step, steps, kernel_events, unused=()):
+        """Times `steps` calls; with kernel_events, also every kernel's own
+        duration (start/stop events bound to each launch).  Returns
+        (ms per step, {slot: mean kernel ms})."""
+        nev = 2 * len(_lib.STAGES)
+        evsets = [hip.create(nev) for _ in range(steps)] if kernel_events else []
+        torch.cuda.synchronize()
+        t0.record()
+        for i in range(steps):
+            if kernel_events:
+                lib.lapattn_set_stage_events(evsets[i], nev)
+            step()
+        t1.record()
+        lib.lapattn_set_stage_events(None, 0)
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / steps
+        per = {}
+        for s, name in enumerate(_lib.STAGES):
+            if evsets and name not in unused:
+                vals = [hip.elapsed_ms(evs[2 * s], evs[2 * s + 1]) for evs in evsets]
+                per[name] = sum(vals) / len(vals)
+        return ms, per
+
+    fused = make_step(serial=False)
+    serial = make_step(serial=True)
+    main_step = serial if args.serial else fused
     for _ in range(args.warmup):
-        step()
+        main_step()
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} done")
 
-    # Timed region: K steps; the library records per-stage HIP events on the
-    # stream each stage runs on (one event set per step, read afterwards).
-    hip = HipEvents()
-    nev = 2 * len(_lib.STAGES)
-    evsets = [hip.create(nev) for _ in range(args.steps)]
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record()
-    for i in range(args.steps):
-        lib.lapattn_set_stage_events(evsets[i], nev)
-        step()
-    t1.record()
-    lib.lapattn_set_stage_events(None, 0)
-    torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / args.steps
-    stage_ms = {}
-    for s, name in enumerate(_lib.STAGES):
-        vals = [hip.elapsed_ms(evs[2 * s], evs[2 * s + 1]) for evs in evsets]
-        stage_ms[name] = sum(vals) / len(vals)
-    hip.close()
-    log(f"[bench] timed {args.steps} steps: {ms_step * 1e3:.2f} us/step; stages (us): "
-        + ", ".join(f"{n}={t * 1e3:.2f}" for n, t in stage_ms.items()))
-
-    # Second pass without the per-stage events, for reference.
-    torch.cuda.synchronize()
-    t0.record()
-    for _ in range(args.steps):
-        step()
-    t1.record()
-    torch.cuda.synchronize()
-    ms_plain = t0.elapsed_time(t1) / args.steps
-    log(f"[bench] same steps without stage events: {ms_plain * 1e3:.2f} us/step")
+    # Timed region: K steps, plain launches -> value.
+    ms_step, _ = timed(main_step, args.steps, False)
+    log(f"[bench] timed {args.steps} steps: {ms_step * 1e3:.2f} us/step")
+    # Kernel durations: K more steps, each kernel launched with its own
+    # start/stop events (hipExtLaunchKernel).  Binding events to launches
+    # slows the step (each launch then completes with a timestamped signal),
+    # not the kernels; the step time of this pass is reported separately.
+    # The fused plan has no map-only launch: its MAPS slot stays unrecorded.
+    unused = () if args.serial else ("maps",)
+    ms_ev, kern = timed(main_step, args.steps, True, unused)
+    log(f"[bench] kernel-event pass: {ms_ev * 1e3:.2f} us/step; kernels (us): "
+        + ", ".join(f"{n}={t * 1e3:.2f}" for n, t in kern.items()))
+    # The other launch plan, for the L1 stage on its own (serial) or fused.
+    kern_other = {}
+    if not args.no_other_plan:
+        other = fused if args.serial else serial
+        for _ in range(max(2, args.warmup // 4)):
+            other()
+        ms_other, kern_other = timed(other, args.steps, True, ("maps",) if args.serial else ())
+        log(f"[bench] {'fused' if args.serial else 'serial'} plan: {ms_other * 1e3:.2f} us/step; "
+            "kernels (us): " + ", ".join(f"{n}={t * 1e3:.2f}" for n, t in kern_other.items()))
+    kf = kern_other if args.serial else kern      # fused-plan kernels (may be empty)
+    ks = kern if args.serial else kern_other      # serial-plan kernels (may be empty)
 
     tokens = w.B * w.N
     value = tokens / (ms_step * 1e-3)
-    work = stage_work(w)
-    t_maps = stage_ms["maps"] * 1e-3
-    ach = work["maps"]["flops"] / t_maps / 1e12
+    wk = work(w)
+    peak = PEAK_FP32_VALU_TFLOPS
+    # dominant kernel of the timed plan
+    if args.serial:
+        dom, dom_ms, dom_flops = "maps", ks["maps"], wk["maps"]["flops"]
+        dom_desc = "main_kernel, map workgroups only (serial plan)"
+        if ks["main"] > ks["maps"]:
+            dom, dom_ms, dom_flops = "main", ks["main"], wk["solver"]["flops"]
+            dom_desc = "main_kernel, solver workgroups only (serial plan)"
+    else:
+        dom, dom_ms, dom_flops = "main", kf["main"], wk["fused"]["flops"]
+        dom_desc = ("main_kernel (fused: Newton-Schulz workgroups on fp32 MFMA beside the "
+                    "L1 map workgroups on FP32 VALU and their K_LK V partials on fp32 MFMA)")
+    ach = dom_flops / (dom_ms * 1e-3) / 1e12
+    traffic = stored_traffic(w.name, "main_kernel") if not args.serial else None
     roofline = {
-        "kernel": "maps (K_QL and K_LK kernel maps, FP32 VALU)",
+        "kernel": dom_desc,
         "bound": "alu",
         "achieved": round(ach, 3),
-        "peak": PEAK_FP32_VALU_TFLOPS,
+        "peak": peak,
         "unit": "TFLOP/s",
-        "frac": round(ach / PEAK_FP32_VALU_TFLOPS, 4),
-        "traffic": None,
+        "frac": round(ach / peak, 4),
+        "traffic": traffic,
+        "kernel_us": round(dom_ms * 1e3, 3),
+        "flops_per_launch": dom_flops,
     }
-    stages = {}
-    for name, t in stage_ms.items():
+    # L1 stage: the distance maps and A, 3 flops per coordinate pair
+    l1_flops = 3 * (wk["map_pairs"] + wk["amat_pairs"])
+
+    def l1_frac(t_ms):
+        return round(l1_flops / (t_ms * 1e-3) / 1e12 / peak, 4)
+    l1 = {"pairs": wk["map_pairs"] + wk["amat_pairs"],
+          "note": "fused: amat + the whole fused main launch (conservative); maps_only: amat + "
+                  "the map-only launch of the serial plan"}
+    if kf:
+        t = kf["main"] + kf["amat"]
+        l1.update(fused_us=round(t * 1e3, 3), frac_fused=l1_frac(t))
+    if ks:
+        t = ks["maps"] + ks["amat"]
+        l1.update(maps_only_us=round(t * 1e3, 3), frac_maps_only=l1_frac(t))
+    kernels = {}
+    for name, t in kern.items():
         e = {"us": round(t * 1e3, 3)}
-        if "bytes" in work[name] and name != "maps":
-            e["GB/s"] = round(work[name]["bytes"] / (t * 1e-3) / 1e9, 1)
+        if name in ("pool", "out"):
+            e["GB/s"] = round(wk[name]["bytes"] / (t * 1e-3) / 1e9, 1)
             e["hbm_frac"] = round(e["GB/s"] / PEAK_HBM_GBS, 4)
-        if "flops" in work[name]:
-            e["TFLOP/s"] = round(work[name]["flops"] / (t * 1e-3) / 1e12, 3)
-        stages[name] = e
+        kernels[name] = e
+    mfma = None
+    if ks:
+        solver_ms = ks["main"]
+        tf = wk["solver"]["flops"] / (solver_ms * 1e-3) / 1e12
+        mfma = {"solver_only_us": round(solver_ms * 1e3, 3), "TFLOP/s": round(tf, 4),
+                "per_active_cu_frac": round(tf / (peak * w.heads / 256), 4)}
 
     res = {
         "metric": "attention-layer tokens/sec (fwd) at N=3136,d=64,m=49; % FP32 VALU peak of L1 stage",
@@ -253,20 +363,24 @@ def main(argv=None):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32" if w.dtype == wl.F32 else "bf16 I/O, f32 compute",
-        "data": "synthetic (seeded N(0,1)/sqrt(d)*4 inputs, resident in HBM)",
+        "data": "synthetic (seeded, shapes and distributions of the workload; resident in HBM)",
         "config": {
             "workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "m": w.m,
             "pool": f"{w.pool_h}x{w.pool_w}", "lambda": w.lam, "eps": w.eps,
             "iters": w.iters, "kernel": w.kernel,
-            "launch": "serial (solver, then maps)" if args.serial else "fused (solver and map workgroups in one launch)",
+            "launch": "serial (solver, then maps)" if args.serial
+                      else "fused (solver and map workgroups in one launch)",
         },
         "roofline": roofline,
-        "stages": stages,
-        "ms_per_step_without_stage_events": round(ms_plain, 5),
+        "l1_stage": l1,
+        "solver_mfma": mfma,
+        "kernels": kernels,
+        "ms_per_step_kernel_event_pass": round(ms_ev, 5),
     }
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle for ~{args.cpu_seconds:.0f} s")
         res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
+    hip.close()
     print(json.dumps(res), flush=True)
     return 0
 

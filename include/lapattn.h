@@ -91,11 +91,15 @@ enum {
   LAPATTN_ERR_ALIGN = -9         /* q, k, v or out not 16-byte aligned        */
 };
 
-/* Stages of one forward call, in launch order (for lapattn_set_stage_events). */
+/* Launch slots of one forward call, in launch order (for
+ * lapattn_set_stage_events). */
 #define LAPATTN_STAGE_POOL 0     /* landmark average pool                      */
 #define LAPATTN_STAGE_AMAT 1     /* A = k(L,L) + eps I and its row abs-sums   */
-#define LAPATTN_STAGE_SOLVER 2   /* alpha, Newton-Schulz                       */
-#define LAPATTN_STAGE_MAPS 3     /* K_QL and K_LK maps, partials of K_LK V    */
+#define LAPATTN_STAGE_MAIN 2     /* alpha and Newton-Schulz; in the default
+                                    plan also the K_QL / K_LK maps and the
+                                    partials of K_LK V (one fused launch)     */
+#define LAPATTN_STAGE_MAPS 3     /* LAPATTN_FLAG_SERIAL only: the maps and the
+                                    partials of K_LK V as a launch of their own */
 #define LAPATTN_STAGE_Y 4        /* W = K_LK V (sum of partials), Y = X W     */
 #define LAPATTN_STAGE_OUT 5      /* O = K_QL Y                                 */
 #define LAPATTN_NUM_STAGES 6
@@ -162,10 +166,11 @@ int lapattn_forward_stages(const lapattn_desc_t* desc, const void* q,
                            float* a, float* x, float* w);
 
 /* Profiling hook.  For the calling host thread, makes every later forward
- * call record events[2*s] right before and events[2*s+1] right after the
- * launch that carries stage s (LAPATTN_STAGE_*), on the caller's stream.  In
- * the default plan the solver and map stages share one launch, so their two
- * event pairs bracket the same launch.
+ * call launch the kernel of slot s (LAPATTN_STAGE_*) through
+ * hipExtLaunchKernel with events[2*s] and events[2*s+1] as its start and stop
+ * events: hipEventElapsedTime(events[2*s], events[2*s+1]) is then that
+ * kernel's own execution time.  The default plan has no separate map launch
+ * and leaves the LAPATTN_STAGE_MAPS pair unrecorded.
  * `events` holds 2 * LAPATTN_NUM_STAGES hipEvent_t handles (as void*) created
  * by the caller with timing enabled, and must stay valid until the hook is
  * cleared with (NULL, 0).  n must be 0 or 2 * LAPATTN_NUM_STAGES. */

@@ -97,17 +97,10 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 // Per-thread stage events (profiling hook).
 thread_local void* const* t_events = nullptr;
 
-inline bool mark(int slot, hipStream_t s) {
-  if (!t_events) return true;
-  return hipEventRecord(static_cast<hipEvent_t>(t_events[slot]), s) == hipSuccess;
-}
-
-// Launches one stage between its two profiling events.
-template <typename F>
-inline bool stage(int st, hipStream_t s, F&& launch) {
-  if (!mark(2 * st, s)) return false;
-  if (launch() != hipSuccess) return false;
-  return mark(2 * st + 1, s);
+// Events of one launch slot, or none when the hook is not set.
+inline Ev slot(int st) {
+  if (!t_events) return {};
+  return {static_cast<hipEvent_t>(t_events[2 * st]), static_cast<hipEvent_t>(t_events[2 * st + 1])};
 }
 
 bool misaligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 != 0; }
@@ -135,28 +128,19 @@ int run(const lapattn_desc_t* desc, const Args& a, void* workspace, size_t ws_by
   b.x = reinterpret_cast<float*>(ws + p.off_x);
   b.yt = reinterpret_cast<float*>(ws + p.off_yt);
 
-  auto pool = [&] { return launch_pool(p, a, b, stream); };
-  auto out = [&] { return launch_out(p, a, b, stream); };
-  auto amat = [&] { return launch_amat(p, a, b, stream); };
-  if (!stage(LAPATTN_STAGE_POOL, stream, pool)) return LAPATTN_ERR_HIP;
-  if (!stage(LAPATTN_STAGE_AMAT, stream, amat)) return LAPATTN_ERR_HIP;
+  if (launch_pool(p, a, b, stream, slot(LAPATTN_STAGE_POOL)) != hipSuccess) return LAPATTN_ERR_HIP;
+  if (launch_amat(p, a, b, stream, slot(LAPATTN_STAGE_AMAT)) != hipSuccess) return LAPATTN_ERR_HIP;
   if (desc->flags & LAPATTN_FLAG_SERIAL) {
-    auto solver = [&] { return launch_main(p, a, b, true, false, stream); };
-    auto maps = [&] { return launch_main(p, a, b, false, true, stream); };
-    if (!stage(LAPATTN_STAGE_SOLVER, stream, solver)) return LAPATTN_ERR_HIP;
-    if (!stage(LAPATTN_STAGE_MAPS, stream, maps)) return LAPATTN_ERR_HIP;
-  } else {
-    // One launch carries both roles: its event pairs for the solver and the
-    // map stage bracket the same launch.
-    if (!mark(2 * LAPATTN_STAGE_SOLVER, stream) || !mark(2 * LAPATTN_STAGE_MAPS, stream))
+    if (launch_main(p, a, b, true, false, stream, slot(LAPATTN_STAGE_MAIN)) != hipSuccess ||
+        launch_main(p, a, b, false, true, stream, slot(LAPATTN_STAGE_MAPS)) != hipSuccess)
       return LAPATTN_ERR_HIP;
-    if (launch_main(p, a, b, true, true, stream) != hipSuccess) return LAPATTN_ERR_HIP;
-    if (!mark(2 * LAPATTN_STAGE_SOLVER + 1, stream) || !mark(2 * LAPATTN_STAGE_MAPS + 1, stream))
+  } else {
+    // one launch carries both roles; the MAPS slot is left untouched
+    if (launch_main(p, a, b, true, true, stream, slot(LAPATTN_STAGE_MAIN)) != hipSuccess)
       return LAPATTN_ERR_HIP;
   }
-  auto wy = [&] { return launch_wy(p, a, b, stream); };
-  if (!stage(LAPATTN_STAGE_Y, stream, wy)) return LAPATTN_ERR_HIP;
-  if (!stage(LAPATTN_STAGE_OUT, stream, out)) return LAPATTN_ERR_HIP;
+  if (launch_wy(p, a, b, stream, slot(LAPATTN_STAGE_Y)) != hipSuccess) return LAPATTN_ERR_HIP;
+  if (launch_out(p, a, b, stream, slot(LAPATTN_STAGE_OUT)) != hipSuccess) return LAPATTN_ERR_HIP;
   return LAPATTN_OK;
 }
 

@@ -53,14 +53,22 @@ struct Args {
   float* st_w;
 };
 
+// Optional profiling events of one launch.  When set, the launch goes through
+// hipExtLaunchKernel, which records the kernel's own start and end time into
+// them (no extra packets on the stream).
+struct Ev {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
 // Stage launchers.  `with_solver` / `with_maps` select which workgroup roles
 // the main launch carries: both (one fused launch), or one each in two
 // launches.
-hipError_t launch_pool(const Plan& p, const Args& a, const Buffers& b, hipStream_t s);
-hipError_t launch_amat(const Plan& p, const Args& a, const Buffers& b, hipStream_t s);
+hipError_t launch_pool(const Plan& p, const Args& a, const Buffers& b, hipStream_t s, Ev ev);
+hipError_t launch_amat(const Plan& p, const Args& a, const Buffers& b, hipStream_t s, Ev ev);
 hipError_t launch_main(const Plan& p, const Args& a, const Buffers& b, bool with_solver,
-                       bool with_maps, hipStream_t s);
-hipError_t launch_wy(const Plan& p, const Args& a, const Buffers& b, hipStream_t s);
-hipError_t launch_out(const Plan& p, const Args& a, const Buffers& b, hipStream_t s);
+                       bool with_maps, hipStream_t s, Ev ev);
+hipError_t launch_wy(const Plan& p, const Args& a, const Buffers& b, hipStream_t s, Ev ev);
+hipError_t launch_out(const Plan& p, const Args& a, const Buffers& b, hipStream_t s, Ev ev);
 
 }  // namespace lapattn

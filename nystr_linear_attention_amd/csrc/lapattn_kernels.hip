@@ -30,8 +30,12 @@
 // lane reads KS *contiguous* k values of one row of A and one row of B^T.
 // The accumulator holds D[4g + i][r], i = 0..3.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <tuple>
+#include <utility>
 
 #include "lapattn_internal.h"
 
@@ -792,94 +796,109 @@ __global__ __launch_bounds__(WGS) void out_kernel(const float* __restrict__ kql,
   }
 }
 
+// Launches kernel `k` with arguments converted to its parameter types,
+// through hipExtLaunchKernel so that optional events time the kernel itself;
+// returns the launch status.
+template <typename... P, typename... A, size_t... I>
+hipError_t launch_impl(void (*k)(P...), dim3 grid, dim3 block, hipStream_t s, Ev ev,
+                       std::index_sequence<I...>, A&&... a) {
+  std::tuple<P...> t(std::forward<A>(a)...);
+  void* ptrs[sizeof...(P) > 0 ? sizeof...(P) : 1] = {static_cast<void*>(&std::get<I>(t))...};
+  return hipExtLaunchKernel(reinterpret_cast<const void*>(k), grid, block, ptrs, 0, s, ev.start,
+                            ev.stop, 0);
+}
+
+template <typename... P, typename... A>
+hipError_t launch(void (*k)(P...), dim3 grid, dim3 block, hipStream_t s, Ev ev, A&&... a) {
+  static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+  return launch_impl(k, grid, block, s, ev, std::index_sequence_for<P...>{},
+                     std::forward<A>(a)...);
+}
+
 inline float exp2_scale(float lambda) {
   // exp(-d / lambda) = exp2(d * (-log2(e) / lambda))
   return static_cast<float>(-1.4426950408889634 / static_cast<double>(lambda));
 }
 
 template <int D>
-hipError_t launch_pool_d(const Plan& p, const Args& a, const Buffers& b, hipStream_t s) {
+hipError_t launch_pool_d(const Plan& p, const Args& a, const Buffers& b, hipStream_t s, Ev ev) {
+  const dim3 grid(p.m, p.BH);
   if (p.bf16)
-    hipLaunchKernelGGL((pool_kernel<D, true>), dim3(p.m, p.BH), dim3(WGS), 0, s, a.k, b.L,
-                       a.st_L, p.gw, p.ph, p.pw, p.m, p.N);
-  else
-    hipLaunchKernelGGL((pool_kernel<D, false>), dim3(p.m, p.BH), dim3(WGS), 0, s, a.k, b.L,
-                       a.st_L, p.gw, p.ph, p.pw, p.m, p.N);
-  return hipGetLastError();
+    return launch(pool_kernel<D, true>, grid, dim3(WGS), s, ev, a.k, b.L, a.st_L, p.gw, p.ph,
+                  p.pw, p.m, p.N);
+  return launch(pool_kernel<D, false>, grid, dim3(WGS), s, ev, a.k, b.L, a.st_L, p.gw, p.ph, p.pw,
+                p.m, p.N);
 }
 
 template <int D>
-hipError_t launch_amat_d(const Plan& p, const Args& a, const Buffers& b, hipStream_t s) {
+hipError_t launch_amat_d(const Plan& p, const Args& a, const Buffers& b, hipStream_t s, Ev ev) {
   const float c = exp2_scale(a.lambda);
+  const dim3 grid(p.m, p.BH);
   if (p.kernel == 0)
-    hipLaunchKernelGGL((amat_kernel<D, 0>), dim3(p.m, p.BH), dim3(64), 0, s, b.L, b.aw, b.rowsum,
-                       a.st_a, p.m, c, a.eps);
-  else
-    hipLaunchKernelGGL((amat_kernel<D, 1>), dim3(p.m, p.BH), dim3(64), 0, s, b.L, b.aw, b.rowsum,
-                       a.st_a, p.m, c, a.eps);
-  return hipGetLastError();
+    return launch(amat_kernel<D, 0>, grid, dim3(64), s, ev, b.L, b.aw, b.rowsum, a.st_a, p.m, c,
+                  a.eps);
+  return launch(amat_kernel<D, 1>, grid, dim3(64), s, ev, b.L, b.aw, b.rowsum, a.st_a, p.m, c,
+                a.eps);
 }
 
 template <int D, int MB>
-hipError_t launch_main_dm(const Plan& p, const MainArgs& ma, unsigned grid, hipStream_t s) {
-  hipLaunchKernelGGL((main_kernel<D, MB>), dim3(grid), dim3(WGM), 0, s, ma, ma.q, ma.k, ma.v, ma.L);
-  return hipGetLastError();
+hipError_t launch_main_dm(const MainArgs& ma, unsigned grid, hipStream_t s, Ev ev) {
+  return launch(main_kernel<D, MB>, dim3(grid), dim3(WGM), s, ev, ma, ma.q, ma.k, ma.v, ma.L);
 }
 
 template <int D>
-hipError_t launch_main_d(const Plan& p, const MainArgs& ma, unsigned grid, hipStream_t s) {
+hipError_t launch_main_d(const Plan& p, const MainArgs& ma, unsigned grid, hipStream_t s, Ev ev) {
   switch (p.ns_mb) {
-    case 0: return launch_main_dm<D, 0>(p, ma, grid, s);
-    case 1: return launch_main_dm<D, 1>(p, ma, grid, s);
-    case 2: return launch_main_dm<D, 2>(p, ma, grid, s);
-    case 3: return launch_main_dm<D, 3>(p, ma, grid, s);
-    case 4: return launch_main_dm<D, 4>(p, ma, grid, s);
+    case 0: return launch_main_dm<D, 0>(ma, grid, s, ev);
+    case 1: return launch_main_dm<D, 1>(ma, grid, s, ev);
+    case 2: return launch_main_dm<D, 2>(ma, grid, s, ev);
+    case 3: return launch_main_dm<D, 3>(ma, grid, s, ev);
+    case 4: return launch_main_dm<D, 4>(ma, grid, s, ev);
   }
   return hipErrorInvalidValue;
 }
 
 template <int D>
-hipError_t launch_out_d(const Plan& p, const Args& a, const Buffers& b, hipStream_t s) {
+hipError_t launch_out_d(const Plan& p, const Args& a, const Buffers& b, hipStream_t s, Ev ev) {
   const dim3 grid(p.BH * p.nT);
   switch (p.mpad / 16) {
     case 1:
-      hipLaunchKernelGGL((out_kernel<D, 4>), grid, dim3(WGS), 0, s, b.kql, b.yt, a.out, p.bf16, p.N, p.mpad, p.nT);
-      break;
+      return launch(out_kernel<D, 4>, grid, dim3(WGS), s, ev, b.kql, b.yt, a.out, p.bf16, p.N,
+                    p.mpad, p.nT);
     case 2:
-      hipLaunchKernelGGL((out_kernel<D, 8>), grid, dim3(WGS), 0, s, b.kql, b.yt, a.out, p.bf16, p.N, p.mpad, p.nT);
-      break;
+      return launch(out_kernel<D, 8>, grid, dim3(WGS), s, ev, b.kql, b.yt, a.out, p.bf16, p.N,
+                    p.mpad, p.nT);
     case 3:
-      hipLaunchKernelGGL((out_kernel<D, 12>), grid, dim3(WGS), 0, s, b.kql, b.yt, a.out, p.bf16, p.N, p.mpad, p.nT);
-      break;
+      return launch(out_kernel<D, 12>, grid, dim3(WGS), s, ev, b.kql, b.yt, a.out, p.bf16, p.N,
+                    p.mpad, p.nT);
     default:
-      hipLaunchKernelGGL((out_kernel<D, 16>), grid, dim3(WGS), 0, s, b.kql, b.yt, a.out, p.bf16, p.N, p.mpad, p.nT);
-      break;
+      return launch(out_kernel<D, 16>, grid, dim3(WGS), s, ev, b.kql, b.yt, a.out, p.bf16, p.N,
+                    p.mpad, p.nT);
   }
-  return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_pool(const Plan& p, const Args& a, const Buffers& b, hipStream_t s) {
+hipError_t launch_pool(const Plan& p, const Args& a, const Buffers& b, hipStream_t s, Ev ev) {
   switch (p.D) {
-    case 16: return launch_pool_d<16>(p, a, b, s);
-    case 32: return launch_pool_d<32>(p, a, b, s);
-    case 64: return launch_pool_d<64>(p, a, b, s);
+    case 16: return launch_pool_d<16>(p, a, b, s, ev);
+    case 32: return launch_pool_d<32>(p, a, b, s, ev);
+    case 64: return launch_pool_d<64>(p, a, b, s, ev);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_amat(const Plan& p, const Args& a, const Buffers& b, hipStream_t s) {
+hipError_t launch_amat(const Plan& p, const Args& a, const Buffers& b, hipStream_t s, Ev ev) {
   switch (p.D) {
-    case 16: return launch_amat_d<16>(p, a, b, s);
-    case 32: return launch_amat_d<32>(p, a, b, s);
-    case 64: return launch_amat_d<64>(p, a, b, s);
+    case 16: return launch_amat_d<16>(p, a, b, s, ev);
+    case 32: return launch_amat_d<32>(p, a, b, s, ev);
+    case 64: return launch_amat_d<64>(p, a, b, s, ev);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_main(const Plan& p, const Args& a, const Buffers& b, bool with_solver,
-                       bool with_maps, hipStream_t s) {
+                       bool with_maps, hipStream_t s, Ev ev) {
   MainArgs ma{};
   ma.q = a.q;
   ma.k = a.k;
@@ -912,24 +931,23 @@ hipError_t launch_main(const Plan& p, const Args& a, const Buffers& b, bool with
   const unsigned grid = static_cast<unsigned>(ma.ns_blocks + map_wgs);
   if (grid == 0) return hipSuccess;
   switch (p.D) {
-    case 16: return launch_main_d<16>(p, ma, grid, s);
-    case 32: return launch_main_d<32>(p, ma, grid, s);
-    case 64: return launch_main_d<64>(p, ma, grid, s);
+    case 16: return launch_main_d<16>(p, ma, grid, s, ev);
+    case 32: return launch_main_d<32>(p, ma, grid, s, ev);
+    case 64: return launch_main_d<64>(p, ma, grid, s, ev);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_wy(const Plan& p, const Args& a, const Buffers& b, hipStream_t s) {
-  hipLaunchKernelGGL(wy_kernel, dim3(p.D / 4, p.BH), dim3(WGS), 0, s, b.wpart, b.x, b.yt, a.st_w,
-                     p.D, p.m, p.nP);
-  return hipGetLastError();
+hipError_t launch_wy(const Plan& p, const Args& a, const Buffers& b, hipStream_t s, Ev ev) {
+  return launch(wy_kernel, dim3(p.D / 4, p.BH), dim3(WGS), s, ev, b.wpart, b.x, b.yt, a.st_w, p.D,
+                p.m, p.nP);
 }
 
-hipError_t launch_out(const Plan& p, const Args& a, const Buffers& b, hipStream_t s) {
+hipError_t launch_out(const Plan& p, const Args& a, const Buffers& b, hipStream_t s, Ev ev) {
   switch (p.D) {
-    case 16: return launch_out_d<16>(p, a, b, s);
-    case 32: return launch_out_d<32>(p, a, b, s);
-    case 64: return launch_out_d<64>(p, a, b, s);
+    case 16: return launch_out_d<16>(p, a, b, s, ev);
+    case 32: return launch_out_d<32>(p, a, b, s, ev);
+    case 64: return launch_out_d<64>(p, a, b, s, ev);
   }
   return hipErrorInvalidValue;
 }

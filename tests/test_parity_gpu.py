@@ -98,3 +98,43 @@ def test_device_errors_are_reported():
         api.forward(q, q, q, grid_h=14, grid_w=14, pool_h=2, pool_w=2, lam=1.0, eps=0.0,
                     iters=1, out=q)
     assert e.value.status == api._lib.ERR_ALIAS
+
+
+@pytest.mark.parametrize("serial", [False, True], ids=["fused", "serial"])
+def test_kernel_event_hook(serial):
+    """Events bound to each launch time the kernels and change no result."""
+    import ctypes
+
+    from nystr_linear_attention_amd import _lib
+    w = wl.WORKLOADS[0].replace(B=2, H=2)
+    _print_case(w, f"event hook serial={serial}")
+    x = wl.make_inputs(w)
+    plain = run_gpu(w, x, serial=serial)["O"]
+    rt = ctypes.CDLL("libamdhip64.so")
+    rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                       ctypes.c_void_p]
+    rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    n = 2 * len(_lib.STAGES)
+    evs = (ctypes.c_void_p * n)()
+    for i in range(n):
+        e = ctypes.c_void_p()
+        assert rt.hipEventCreate(ctypes.byref(e)) == 0
+        evs[i] = e.value
+    lib = _lib.lib()
+    try:
+        assert lib.lapattn_set_stage_events(evs, n) == _lib.OK
+        timed = run_gpu(w, x, serial=serial)["O"]
+        assert lib.lapattn_set_stage_events(None, 0) == _lib.OK
+        torch.cuda.synchronize()
+        for s, name in enumerate(_lib.STAGES):
+            if name == "maps" and not serial:
+                continue            # the fused plan has no map-only launch
+            ms = ctypes.c_float()
+            assert rt.hipEventElapsedTime(ctypes.byref(ms), evs[2 * s], evs[2 * s + 1]) == 0, name
+            assert 0.0 < ms.value < 1000.0, (name, ms.value)
+    finally:
+        lib.lapattn_set_stage_events(None, 0)
+        for i in range(n):
+            rt.hipEventDestroy(evs[i])
+    assert np.array_equal(plain, timed)
