@@ -58,10 +58,10 @@ Plan make_plan(const lapattn_desc_t* d) {
   p.m = (p.gh / p.ph) * (p.gw / p.pw);
   p.BH = p.B * p.H;
   p.mpad = 16 * ((p.m + 15) / 16);
-  // Solver interior: whole 16x16 blocks; up to 4 border rows/columns go to
-  // VALU, otherwise the interior is padded up to the next block.
-  const int r = p.m % 16;
-  p.ns_mb = (r >= 1 && r <= 4) ? p.m / 16 : (p.m + 15) / 16;
+  // Solver interior: whole 16x16 blocks.  A single extra row/column
+  // (m = 16 MB + 1, e.g. 7x7 landmarks) goes to VALU; otherwise the matrix is
+  // zero padded up to whole blocks.
+  p.ns_mb = (p.m % 16 == 1) ? p.m / 16 : (p.m + 15) / 16;
   p.nT = (p.N + 63) / 64;
   // Key-side workgroups cover S tiles each so that a head has at most 32 W
   // partials.

@@ -180,121 +180,329 @@ struct MainArgs {
 };
 
 // ---------------------------------------------------------------------------
-// Solver role.  Matrices live in LDS (zero padded), rows of SLS floats:
-//   A        (row-major; bitwise symmetric: |a-b| = |b-a| term by term)
-//   XR[2]    (X_t row-major, double buffered)
-//   XT[2]    (X_t transposed, double buffered)
-//   TT       (T transposed)
-//   phase 1: T = A X_t                 operands: rows of A, rows of XT
-//   phase 2: X_{t+1} = 2 X_t - X_t T   operands: rows of XR, rows of TT
-// The recursion is evaluated as printed, with full (unsymmetrised)
-// products: forcing the iterates symmetric turns the quadratic error
-// contraction of the Newton step into a linear map with gain up to
-// (1 + cond(A)) / 2, which diverges near convergence for ill-conditioned A.
-// With m = 16*MB + r, r <= 4, the interior 16MB x 16MB blocks run on MFMA and
-// the r border rows/columns on VALU (rank-r update of the interior blocks
-// plus border dot products); when m % 16 > 4 the interior is padded up to
-// whole blocks and r = 0.
+// Solver role: X_0 = alpha A, X_{t+1} = 2 X_t - X_t (A X_t), exactly `iters`
+// steps, one workgroup per head, everything in LDS and registers.
+//
+// m = 16 MB + r with r <= 1 border row/column (other sizes are zero padded to
+// 16 MB and r = 0; the border code is written for any r <= 4).  Both products are full and unsymmetrised:
+// forcing the iterates symmetric turns the quadratic error contraction of the
+// Newton step into a linear map with gain up to (1 + cond(A)) / 2, which
+// diverges near convergence for ill-conditioned A.
+//
+// Interior wave c < MB owns column block c (16 columns) of X_t, of
+// T = A X_t and of X_{t+1}:
+//   T[:, c]       = A X_t[:, c]              (needs only its own X columns)
+//   X_{t+1}[:, c] = 2 X_t[:, c] - X_t T[:, c] (needs the rows of X_t)
+// With the contraction index of MFMA sub-step s = 4 i + j taken as
+// k = 16 i + 4 g + j for lane (g, lr), the accumulator layout of a 16 x 16
+// block (lane (g, lr) holds rows 4 g + j of column lr) is exactly the B
+// operand layout, so X_t[:, c] and T[:, c] never leave registers; the A
+// operands (rows of A, rows of X_t) are 16-byte LDS reads.  Only the rows of
+// X_t are exchanged, once per step: one barrier per step.
+// The border: interior waves compute T and X_{t+1} on the border rows of
+// their own columns (VALU dot products and a 4-lane reduction); border wave
+// b < r computes border column 16 MB + b of T and X_{t+1} (one row per lane).
+// Border terms of the interior blocks (k >= 16 MB) initialise the
+// accumulators.  A is bitwise symmetric (|a - b| = |b - a| term by term), so
+// its border columns are read as rows.
+//
+// LDS (floats, row stride SLS): A, X[2] (row-major, double buffered),
+// XTB[2][4][64] (border columns of X_t, transposed), TX[4][64] (border columns
+// of T, private to each border wave), scalars.
 // ---------------------------------------------------------------------------
 template <int MB>
-struct SolverGeom {
-  static constexpr int NBLK = MB * MB;            // interior 16x16 blocks
-  static constexpr int KS = 4 * MB;               // MFMA sub-steps per block
-  static constexpr int NBQ = 4 * MB + 1;          // float4 reads per border dot
-  // rows and row stride: 16 MB interior + up to 4 border rows / columns.
-  // Strides are 4 (mod 32) or 20 (mod 32) floats, which keeps 16-byte reads
-  // of 8 consecutive rows on distinct LDS banks.
-  static constexpr int ROWS = MB == 4 ? 64 : 16 * MB + 4;
-  static constexpr int SLS = MB == 4 ? 68 : 16 * MB + 4;
-  static constexpr int MAT = ROWS * SLS;          // floats per matrix
-  // Wave w < MB owns interior block-row w (MB blocks); waves MB..7 compute
-  // the border entries concurrently.
-  static constexpr int BW0 = MB;
-  static constexpr int SMEM = 6 * MAT + 4;        // floats of LDS
+struct NsGeom {
+  static constexpr int N16 = 16 * MB;               // interior size
+  // rows and row stride: the interior plus up to 4 border rows / columns.
+  // Strides are 4 or 20 (mod 32) floats, so 16-byte reads of 8 consecutive
+  // rows fall on distinct LDS banks.
+  static constexpr int ROWS = MB == 4 ? 64 : N16 + 4;
+  static constexpr int SLS = MB == 4 ? 68 : N16 + 4;
+  static constexpr int MAT = ROWS * SLS;
+  static constexpr int NQ = ROWS / 4;               // float4 per border dot
+  static constexpr int OFF_XTB = 3 * MAT;
+  static constexpr int OFF_TX = OFF_XTB + 2 * 4 * 64;
+  static constexpr int OFF_RED = OFF_TX + 4 * 64;
+  static constexpr int SMEM = OFF_RED + 4;
 };
 
-// Border entry e -> (a, b): Z[a][b] with b a border column (a < m) or a a
-// border row (b < 16 MB).
-template <int MB>
-__device__ __forceinline__ void border_ab(int e, int m, int r, int& a, int& b) {
-  a = e % m;
-  b = 16 * MB + e / m;
-  if constexpr (MB > 0) {
-    if (e >= r * m) {
-      const int e2 = e - r * m;
-      a = 16 * MB + e2 / (16 * MB);
-      b = e2 % (16 * MB);
-    }
-  }
+// Sum over the 4 lanes (g = 0..3) that share lr, on VALU: a lane-half swap
+// with itself leaves v[l] + v[l ^ 32] as the sum of the two results (and
+// likewise for 16-lane rows).
+__device__ __forceinline__ float sum_over_g(float v) {
+  const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
-// Block-row w of Z = Lm R (MB blocks): the A operand is row 16 w + lr of Lm,
-// given as KS/4 float4 in registers (k = KS*lg + s), the B operands are rows
-// of R^T (Rt).  All B rows are read before the MFMA chains start so that the
-// independent chains of the MB blocks overlap in the matrix pipe.  `lb` holds
-// Lm[16 w + 4 lg + i][16 MB .. 16 MB + 3] for the rank-r border update.
-template <int MB>
-__device__ __forceinline__ void row_product(const f4* areg, const f4* lb, const float* Rt,
-                                            int lane, bool has_border, f4* acc) {
-  using G = SolverGeom<MB>;
-  constexpr int KQ = G::KS / 4;
+template <int MB, int R>
+__device__ void ns_interior_wave(const MainArgs& a, float* smem, int c, int lane) {
+  constexpr int r = R;  // border width
+  using G = NsGeom<MB>;
+  constexpr int S = G::SLS, N16 = G::N16;
+  // Buffers are addressed by offsets from the shared base (never through a
+  // table of pointers) so that every access stays an LDS instruction.
+  const float* A = smem;
+  const float* X0 = smem + G::MAT;
   const int lr = lane & 15, lg = lane >> 4;
-  f4 bv[MB][KQ];
+  const int col = 16 * c + lr;
+
+  // own columns of X_0 (accumulator layout) and of its border rows
+  f4 xc[MB];
+  float xbr[4];
 #pragma unroll
-  for (int bj = 0; bj < MB; ++bj) {
-    const float* br = Rt + (16 * bj + lr) * G::SLS + G::KS * lg;
+  for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int q = 0; q < KQ; ++q) bv[bj][q] = ld4(br + 4 * q);
-  }
+    for (int j = 0; j < 4; ++j) xc[i][j] = X0[(16 * i + 4 * lg + j) * S + col];
 #pragma unroll
-  for (int bj = 0; bj < MB; ++bj) acc[bj] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < 4; ++b) xbr[b] = b < r ? X0[(N16 + b) * S + col] : 0.f;
+  // constant operands: the border rows of A at the own k (for T's border
+  // rows), A's border corner
+  f4 abr[4][MB];
+  float acor[4][4];
 #pragma unroll
-  for (int q = 0; q < KQ; ++q)
+  for (int b = 0; b < 4; ++b)
 #pragma unroll
-    for (int h = 0; h < 4; ++h)
+    for (int i = 0; i < MB; ++i)
+      abr[b][i] = b < r ? ld4(A + (N16 + b) * S + 16 * i + 4 * lg) : f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int bj = 0; bj < MB; ++bj) acc[bj] = mfma4(areg[q][h], bv[bj][q][h], acc[bj]);
-  if (MB < 4 && has_border) {
-    // k in [16 MB, 16 MB + 4); padding beyond m is zero
+  for (int b = 0; b < 4; ++b)
 #pragma unroll
-    for (int bj = 0; bj < MB; ++bj) {
-      const f4 rb = ld4(Rt + (16 * bj + lr) * G::SLS + 16 * MB);
+    for (int bb = 0; bb < 4; ++bb) acor[b][bb] = (b < r && bb < r) ? A[(N16 + b) * S + N16 + bb] : 0.f;
+
+  // Output blocks are computed one after another (a single accumulation
+  // chain runs at the full MFMA rate), so that each block's epilogue and the
+  // next block's operand reads overlap the running MFMAs.  The A operand of
+  // the first block of phase 1 is constant and is read before the barrier.
+  f4 aop[MB];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        acc[bj][i] = fmaf(lb[i][0], rb[0], fmaf(lb[i][1], rb[1], fmaf(lb[i][2], rb[2], fmaf(lb[i][3], rb[3], acc[bj][i]))));
+  for (int i = 0; i < MB; ++i) aop[i] = ld4(A + lr * S + 16 * i + 4 * lg);
+
+  for (int t = 0; t < a.iters; ++t) {
+    const int cb = t & 1;
+    const float* cur = smem + G::MAT * (1 + cb);
+    float* nxt = smem + G::MAT * (2 - cb);
+    const float* xtb = smem + G::OFF_XTB + 256 * cb;
+
+    // reads that only need X_t: the phase-2 operand of block 0, the border
+    // columns of X_t at the own rows, the border rows of X_t at the own k
+    f4 xop[MB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) xop[i] = ld4(cur + lr * S + 16 * i + 4 * lg);
+    f4 xbc[4][MB], xbrow[4][MB];
+    float xcor[4][4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        xbc[b][i] = b < r ? ld4(xtb + 64 * b + 16 * i + 4 * lg) : f4{0.f, 0.f, 0.f, 0.f};
+        xbrow[b][i] = b < r ? ld4(cur + (N16 + b) * S + 16 * i + 4 * lg) : f4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) xcor[b][bb] = (b < r && bb < r) ? cur[(N16 + b) * S + N16 + bb] : 0.f;
+
+    // phase 1: T[:, c] = A X_t[:, c], block by block; the border terms
+    // (k >= 16 MB) initialise each block: A[rows][N16+b] = A[N16+b][rows].
+    // The scheduling fences keep every operand read ahead of the MFMAs of
+    // the block before the one that needs it, and put VALU work between
+    // MFMAs, so the matrix pipe never waits on LDS.
+    f4 tc[MB];
+    float tbr[4];
+#pragma unroll
+    for (int ip = 0; ip < MB; ++ip) {
+      f4 anx[MB];
+      if (ip + 1 < MB) {
+#pragma unroll
+        for (int i = 0; i < MB; ++i) anx[i] = ld4(A + (16 * (ip + 1) + lr) * S + 16 * i + 4 * lg);
+      }
+      f4 t4 = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        if (b < r) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) t4[j] = fmaf(abr[b][ip][j], xbr[b], t4[j]);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+      t4 = mfma4(aop[0][0], xc[0][0], t4);
+      t4 = mfma4(aop[0][1], xc[0][1], t4);
+      __builtin_amdgcn_sched_barrier(0);
+      if (ip == 0) {
+        // T on the border rows of the own columns:
+        // T[N16+b][col] = sum_k A[N16+b][k] X_t[k][col]
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          tbr[b] = 0.f;
+          if (b < r) {
+            float p = 0.f;
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) p = fmaf(abr[b][i][j], xc[i][j], p);
+            p = sum_over_g(p);
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb)
+              if (bb < r) p = fmaf(acor[b][bb], xbr[bb], p);
+            tbr[b] = p;
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s4 = 2; s4 < 4 * MB; ++s4) t4 = mfma4(aop[s4 / 4][s4 % 4], xc[s4 / 4][s4 % 4], t4);
+      __builtin_amdgcn_sched_barrier(0);
+      tc[ip] = t4;
+      if (ip + 1 < MB) {
+#pragma unroll
+        for (int i = 0; i < MB; ++i) aop[i] = anx[i];
+      }
     }
+
+    // phase 2: X_{t+1}[:, c] = 2 X_t[:, c] - X_t T[:, c], block by block;
+    // border terms X_t[rows][N16+b] T[N16+b][col] initialise each block.
+    // The epilogue of block ip - 1 (2 X - acc, row-major LDS store) runs
+    // between the MFMAs of block ip.
+    float xbn[4];
+    f4 prev = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ip = 0; ip < MB; ++ip) {
+      f4 xnx[MB];
+      if (ip + 1 < MB) {
+#pragma unroll
+        for (int i = 0; i < MB; ++i) xnx[i] = ld4(cur + (16 * (ip + 1) + lr) * S + 16 * i + 4 * lg);
+      } else {
+        // the constant phase-1 operand of the next step (block 0)
+#pragma unroll
+        for (int i = 0; i < MB; ++i) xnx[i] = ld4(A + lr * S + 16 * i + 4 * lg);
+      }
+      f4 t4 = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        if (b < r) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) t4[j] = fmaf(xbc[b][ip][j], tbr[b], t4[j]);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+      t4 = mfma4(xop[0][0], tc[0][0], t4);
+      t4 = mfma4(xop[0][1], tc[0][1], t4);
+      __builtin_amdgcn_sched_barrier(0);
+      if (ip > 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          xc[ip - 1][j] = 2.0f * xc[ip - 1][j] - prev[j];
+          nxt[(16 * (ip - 1) + 4 * lg + j) * S + col] = xc[ip - 1][j];
+        }
+      } else {
+        // X_{t+1} on the border rows of the own columns:
+        // 2 X_t[N16+b][col] - sum_k X_t[N16+b][k] T[k][col]
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          xbn[b] = 0.f;
+          if (b < r) {
+            float p = 0.f;
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) p = fmaf(xbrow[b][i][j], tc[i][j], p);
+            p = sum_over_g(p);
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb)
+              if (bb < r) p = fmaf(xcor[b][bb], tbr[bb], p);
+            xbn[b] = 2.0f * xbr[b] - p;
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s4 = 2; s4 < 4 * MB; ++s4) t4 = mfma4(xop[s4 / 4][s4 % 4], tc[s4 / 4][s4 % 4], t4);
+      __builtin_amdgcn_sched_barrier(0);
+      prev = t4;
+      if (ip + 1 < MB) {
+#pragma unroll
+        for (int i = 0; i < MB; ++i) xop[i] = xnx[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < MB; ++i) aop[i] = xnx[i];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      xc[MB - 1][j] = 2.0f * xc[MB - 1][j] - prev[j];
+      nxt[(16 * (MB - 1) + 4 * lg + j) * S + col] = xc[MB - 1][j];
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      if (b < r) {
+        xbr[b] = xbn[b];
+        if (lg == 0) nxt[(N16 + b) * S + col] = xbr[b];
+      }
+    __syncthreads();
   }
 }
 
-// Border dot product: row a of Lm against row b of Rt, k < 16 MB + 4.
+// Border wave b: column N16 + b of T and X_{t+1}, lane k = row k (k < m).
 template <int MB>
-__device__ __forceinline__ float border_dot(const float* Lm, const float* Rt, int a, int b) {
-  using G = SolverGeom<MB>;
-  const float* ra = Lm + a * G::SLS;
-  const float* rb = Rt + b * G::SLS;
-  float d[4] = {0.f, 0.f, 0.f, 0.f};
+__device__ void ns_border_wave(const MainArgs& a, float* smem, int b, int lane) {
+  using G = NsGeom<MB>;
+  constexpr int S = G::SLS, N16 = G::N16;
+  const float* A = smem;
+  float* TX = smem + G::OFF_TX + 64 * b;
+  const int k = lane;
+  const bool row = k < a.m;           // m <= ROWS
+  float xk = row ? smem[G::MAT + k * S + N16 + b] : 0.f;
+
+  for (int t = 0; t < a.iters; ++t) {
+    const int cb = t & 1;
+    const float* cur = smem + G::MAT * (1 + cb);
+    float* nxt = smem + G::MAT * (2 - cb);
+    const float* xtb = smem + G::OFF_XTB + 256 * cb + 64 * b;
+    float* xtn = smem + G::OFF_XTB + 256 * (1 - cb) + 64 * b;
+    // T[k][N16+b] = sum_k' A[k][k'] X_t[k'][N16+b]
+    float tk = 0.f;
+    if (row) {
+      float d[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int q = 0; q < G::NBQ; ++q) {
-    const f4 a4 = ld4(ra + 4 * q), b4 = ld4(rb + 4 * q);
-    d[q & 3] = fmaf(a4[0], b4[0], fmaf(a4[1], b4[1], fmaf(a4[2], b4[2], fmaf(a4[3], b4[3], d[q & 3]))));
+      for (int q = 0; q < G::NQ; ++q) {
+        const f4 ar = ld4(A + k * S + 4 * q), xv = ld4(xtb + 4 * q);
+        d[q & 3] = fmaf(ar[3], xv[3], fmaf(ar[2], xv[2], fmaf(ar[1], xv[1], fmaf(ar[0], xv[0], d[q & 3]))));
+      }
+      tk = (d[0] + d[1]) + (d[2] + d[3]);
+    }
+    TX[k] = tk;  // rows >= m are zero
+    // make the whole column visible to every lane of this wave
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // X_{t+1}[k][N16+b] = 2 X_t[k][N16+b] - sum_k' X_t[k][k'] T[k'][N16+b]
+    if (row) {
+      float d[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < G::NQ; ++q) {
+        const f4 xr = ld4(cur + k * S + 4 * q), tv = ld4(TX + 4 * q);
+        d[q & 3] = fmaf(xr[3], tv[3], fmaf(xr[2], tv[2], fmaf(xr[1], tv[1], fmaf(xr[0], tv[0], d[q & 3]))));
+      }
+      xk = 2.0f * xk - ((d[0] + d[1]) + (d[2] + d[3]));
+      nxt[k * S + N16 + b] = xk;
+      xtn[k] = xk;
+    }
+    __syncthreads();
   }
-  return (d[0] + d[1]) + (d[2] + d[3]);
 }
 
 template <int MB>
 __device__ void solver_role(const MainArgs& a, int bh, float* smem) {
-  using G = SolverGeom<MB>;
-  constexpr int S = G::SLS;
+  using G = NsGeom<MB>;
+  constexpr int S = G::SLS, N16 = G::N16;
   float* A = smem;
-  float* XR0 = smem + G::MAT;
-  float* XR1 = smem + 2 * G::MAT;
-  float* XT0 = smem + 3 * G::MAT;
-  float* XT1 = smem + 4 * G::MAT;
-  float* TT = smem + 5 * G::MAT;
-  float* red = smem + 6 * G::MAT;  // scalars
+  float* X0 = smem + G::MAT;
+  float* X1 = smem + 2 * G::MAT;
+  float* XTB = smem + G::OFF_XTB;
+  float* red = smem + G::OFF_RED;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
-  const int lr = lane & 15, lg = lane >> 4;
   const int m = a.m;
+  const int r = m > N16 ? m - N16 : 0;  // border width (0 when padded)
   __builtin_amdgcn_s_setprio(3);
 
   // A (built by the A-matrix launch, zero padded to 64 x 64) -> LDS.
@@ -315,115 +523,31 @@ __device__ void solver_role(const MainArgs& a, int bh, float* smem) {
   }
   __syncthreads();
   const float alpha = 1.0f / (red[0] * red[0]);
-  // X_0 = alpha A in both layouts; the other buffers zero.
+  // X_0 = alpha A; the second buffer zero (its padding stays zero)
   for (int e = tid; e < G::MAT; e += WGM) {
-    const float x0 = alpha * A[e];
-    XR0[e] = x0;
-    XT0[e] = x0;
-    XR1[e] = 0.f;
-    XT1[e] = 0.f;
-    TT[e] = 0.f;
+    X0[e] = alpha * A[e];
+    X1[e] = 0.f;
+  }
+  for (int e = tid; e < 2 * 4 * 64; e += WGM) {
+    const int buf = e / 256, bb = (e / 64) % 4, kk = e % 64;
+    XTB[e] = (buf == 0 && bb < r && kk < m) ? alpha * A[kk * S + N16 + bb] : 0.f;
   }
   __syncthreads();
 
-  const int r = m > 16 * MB ? m - 16 * MB : 0;  // border width (0 when padded)
-  const bool has_border = r > 0;
-  const int nbe = r * m + r * 16 * MB;           // border entries
-  constexpr int NL = 64 * (8 - G::BW0);          // border lanes
-  constexpr int NBE = 2;                         // border entries per lane (max)
-  constexpr int MBR = MB > 0 ? MB : 1;
-  constexpr int KQR = G::KS / 4 > 0 ? G::KS / 4 : 1;
-  const bool row_wave = w < MB;
-
-  // Row waves: own block-row of X_t (accumulator layout), constant A operand
-  // and A border columns in registers.  Border waves: their border entries.
-  f4 xr[MBR], areg[KQR], alb[4];
-#pragma unroll
-  for (int bj = 0; bj < MBR; ++bj) xr[bj] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int q = 0; q < KQR; ++q) areg[q] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) alb[i] = f4{0.f, 0.f, 0.f, 0.f};
-  if (row_wave) {
-#pragma unroll
-    for (int bj = 0; bj < MBR; ++bj)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) xr[bj][i] = XR0[(16 * w + 4 * lg + i) * S + 16 * bj + lr];
-#pragma unroll
-    for (int q = 0; q < G::KS / 4; ++q) areg[q] = ld4(A + (16 * w + lr) * S + G::KS * lg + 4 * q);
-    if (MB < 4) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) alb[i] = ld4(A + (16 * w + 4 * lg + i) * S + 16 * MB);
-    }
-  }
-  float xb[NBE];
-  int ba[NBE], bb[NBE];
-#pragma unroll
-  for (int s = 0; s < NBE; ++s) {
-    xb[s] = 0.f;
-    ba[s] = -1;
-    bb[s] = 0;
-    if (has_border && w >= G::BW0) {
-      const int e = tid - 64 * G::BW0 + NL * s;
-      if (e < nbe) {
-        border_ab<MB>(e, m, r, ba[s], bb[s]);
-        xb[s] = XR0[ba[s] * S + bb[s]];
-      }
-    }
-  }
-
-  for (int t = 0; t < a.iters; ++t) {
-    const float* XRc = (t & 1) ? XR1 : XR0;
-    const float* XTc = (t & 1) ? XT1 : XT0;
-    float* XRn = (t & 1) ? XR0 : XR1;
-    float* XTn = (t & 1) ? XT0 : XT1;
-    // phase 1: T = A X_t, stored transposed
+  if (w < MB) {
     if constexpr (MB > 0) {
-      if (row_wave) {
-        f4 acc[MBR];
-        row_product<MB>(areg, alb, XTc, lane, has_border, acc);
-#pragma unroll
-        for (int bj = 0; bj < MBR; ++bj) st4(TT + (16 * bj + lr) * S + 16 * w + 4 * lg, acc[bj]);
-      }
+      // the border width is a template argument so that the border code is
+      // straight-line
+      if (MB < 4 && r == 1) ns_interior_wave<MB, (MB < 4 ? 1 : 0)>(a, smem, w, lane);
+      else ns_interior_wave<MB, 0>(a, smem, w, lane);
     }
-#pragma unroll
-    for (int s = 0; s < NBE; ++s)
-      if (ba[s] >= 0) TT[bb[s] * S + ba[s]] = border_dot<MB>(A, XTc, ba[s], bb[s]);
-    __syncthreads();
-    // phase 2: X_{t+1} = 2 X_t - X_t T, written to the other buffers
-    if constexpr (MB > 0) {
-      if (row_wave) {
-        f4 xa[KQR], xlb[4];
-#pragma unroll
-        for (int q = 0; q < G::KS / 4; ++q) xa[q] = ld4(XRc + (16 * w + lr) * S + G::KS * lg + 4 * q);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          xlb[i] = MB < 4 ? ld4(XRc + (16 * w + 4 * lg + i) * S + 16 * (MB < 4 ? MB : 0)) : f4{0.f, 0.f, 0.f, 0.f};
-        f4 acc[MBR];
-        row_product<MB>(xa, xlb, TT, lane, has_border, acc);
-#pragma unroll
-        for (int bj = 0; bj < MBR; ++bj) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            xr[bj][i] = 2.0f * xr[bj][i] - acc[bj][i];
-            XRn[(16 * w + 4 * lg + i) * S + 16 * bj + lr] = xr[bj][i];
-          }
-          st4(XTn + (16 * bj + lr) * S + 16 * w + 4 * lg, xr[bj]);
-        }
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < NBE; ++s) {
-      if (ba[s] >= 0) {
-        xb[s] = 2.0f * xb[s] - border_dot<MB>(XRc, TT, ba[s], bb[s]);
-        XRn[ba[s] * S + bb[s]] = xb[s];
-        XTn[bb[s] * S + ba[s]] = xb[s];
-      }
-    }
-    __syncthreads();
+  } else if (w - MB < r) {
+    ns_border_wave<MB>(a, smem, w - MB, lane);
+  } else {
+    for (int t = 0; t < a.iters; ++t) __syncthreads();
   }
 
-  const float* Xf = (a.iters & 1) ? XR1 : XR0;
+  const float* Xf = (a.iters & 1) ? X1 : X0;
   float* Xg = a.xw + static_cast<size_t>(bh) * MP * MP;
   for (int e = tid; e < MP * MP; e += WGM) {
     const int row = e / MP, col = e % MP;
@@ -601,7 +725,7 @@ __global__ __launch_bounds__(WGM) void main_kernel(MainArgs a, const void* __res
                                                     const void* __restrict__ v,
                                                     const float* __restrict__ L) {
   constexpr int MAP_SMEM = 3 * MP * LS;
-  constexpr int SOLVER_SMEM = SolverGeom<MB>::SMEM;
+  constexpr int SOLVER_SMEM = NsGeom<MB>::SMEM;
   __shared__ __attribute__((aligned(16)))
   float smem[MAP_SMEM > SOLVER_SMEM ? MAP_SMEM : SOLVER_SMEM];
   const int b = blockIdx.x;
