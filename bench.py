@@ -279,7 +279,7 @@ def main(argv=None):
     # slows the step (each launch then completes with a timestamped signal),
     # not the kernels; the step time of this pass is reported separately.
     # The fused plan has no map-only launch: its MAPS slot stays unrecorded.
-    unused = () if args.serial else ("maps",)
+    unused = (() if args.serial else ("maps",)) + (() if w.shared_qk else ("out",))
     ms_ev, kern = timed(main_step, args.steps, True, unused)
     log(f"[bench] kernel-event pass: {ms_ev * 1e3:.2f} us/step; kernels (us): "
         + ", ".join(f"{n}={t * 1e3:.2f}" for n, t in kern.items()))
@@ -289,7 +289,8 @@ def main(argv=None):
         other = fused if args.serial else serial
         for _ in range(max(2, args.warmup // 4)):
             other()
-        ms_other, kern_other = timed(other, args.steps, True, ("maps",) if args.serial else ())
+        ms_other, kern_other = timed(other, args.steps, True,
+                                     (("maps",) if args.serial else ()) + (() if w.shared_qk else ("out",)))
         log(f"[bench] {'fused' if args.serial else 'serial'} plan: {ms_other * 1e3:.2f} us/step; "
             "kernels (us): " + ", ".join(f"{n}={t * 1e3:.2f}" for n, t in kern_other.items()))
     kf = kern_other if args.serial else kern      # fused-plan kernels (may be empty)

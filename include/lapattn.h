@@ -96,13 +96,12 @@ enum {
 #define LAPATTN_STAGE_POOL 0     /* landmark average pool                      */
 #define LAPATTN_STAGE_AMAT 1     /* A = k(L,L) + eps I and its row abs-sums   */
 #define LAPATTN_STAGE_MAIN 2     /* alpha and Newton-Schulz; in the default
-                                    plan also the K_QL / K_LK maps and the
-                                    partials of K_LK V (one fused launch)     */
-#define LAPATTN_STAGE_MAPS 3     /* LAPATTN_FLAG_SERIAL only: the maps and the
-                                    partials of K_LK V as a launch of their own */
-#define LAPATTN_STAGE_Y 4        /* W = K_LK V (sum of partials), Y = X W     */
-#define LAPATTN_STAGE_OUT 5      /* O = K_QL Y                                 */
-#define LAPATTN_NUM_STAGES 6
+                                    plan also the K_QL / K_LK maps, W = K_LK V,
+                                    Y = X W and (Q != K) the output rows      */
+#define LAPATTN_STAGE_MAPS 3     /* LAPATTN_FLAG_SERIAL only: the map roles as
+                                    a launch of their own                      */
+#define LAPATTN_STAGE_OUT 4      /* Q == K only: O = K_QL Y as its own launch  */
+#define LAPATTN_NUM_STAGES 5
 
 typedef struct {
   int32_t B, H;            /* batch and heads; every (b, h) is independent   */
@@ -144,7 +143,9 @@ int lapattn_init(void);
  *             aligned; its contents on entry are ignored
  *   stream    hipStream_t (as void*) the work is ordered on
  * Concurrent calls that share a workspace race; calls on different streams
- * with different workspaces are independent. */
+ * with different workspaces are independent.  Within a call, workgroups of
+ * one launch hand per-head results to each other through the workspace
+ * (device-scope release / acquire); every such wait is bounded in time. */
 int lapattn_forward(const lapattn_desc_t* desc, const void* q, const void* k,
                     const void* v, float lambda, float eps, int32_t iters,
                     void* out, void* workspace, size_t workspace_bytes,
@@ -169,8 +170,9 @@ int lapattn_forward_stages(const lapattn_desc_t* desc, const void* q,
  * call launch the kernel of slot s (LAPATTN_STAGE_*) through
  * hipExtLaunchKernel with events[2*s] and events[2*s+1] as its start and stop
  * events: hipEventElapsedTime(events[2*s], events[2*s+1]) is then that
- * kernel's own execution time.  The default plan has no separate map launch
- * and leaves the LAPATTN_STAGE_MAPS pair unrecorded.
+ * kernel's own execution time.  Slots without a launch in the call are left
+ * unrecorded: LAPATTN_STAGE_MAPS outside LAPATTN_FLAG_SERIAL, and
+ * LAPATTN_STAGE_OUT unless K is the same pointer as Q.
  * `events` holds 2 * LAPATTN_NUM_STAGES hipEvent_t handles (as void*) created
  * by the caller with timing enabled, and must stay valid until the hook is
  * cleared with (NULL, 0).  n must be 0 or 2 * LAPATTN_NUM_STAGES. */

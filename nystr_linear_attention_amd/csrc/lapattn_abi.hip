@@ -83,8 +83,12 @@ Plan make_plan(const lapattn_desc_t* d) {
   off = align_up(off + BH * p.nP * p.D * MP * f);
   p.off_x = off;
   off = align_up(off + BH * MP * MP * f);
+  p.off_wt = off;
+  off = align_up(off + BH * p.D * MP * f);
   p.off_yt = off;
   off = align_up(off + BH * p.D * MP * f);
+  p.off_sync = off;
+  off = align_up(off + (4 + 3 * BH) * sizeof(unsigned));
   p.total = off;
   return p;
 }
@@ -126,7 +130,9 @@ int run(const lapattn_desc_t* desc, const Args& a, void* workspace, size_t ws_by
   b.kql = reinterpret_cast<float*>(ws + p.off_kql);
   b.wpart = reinterpret_cast<float*>(ws + p.off_wpart);
   b.x = reinterpret_cast<float*>(ws + p.off_x);
+  b.wt = reinterpret_cast<float*>(ws + p.off_wt);
   b.yt = reinterpret_cast<float*>(ws + p.off_yt);
+  b.sync = reinterpret_cast<unsigned*>(ws + p.off_sync);
 
   if (launch_pool(p, a, b, stream, slot(LAPATTN_STAGE_POOL)) != hipSuccess) return LAPATTN_ERR_HIP;
   if (launch_amat(p, a, b, stream, slot(LAPATTN_STAGE_AMAT)) != hipSuccess) return LAPATTN_ERR_HIP;
@@ -139,8 +145,11 @@ int run(const lapattn_desc_t* desc, const Args& a, void* workspace, size_t ws_by
     if (launch_main(p, a, b, true, true, stream, slot(LAPATTN_STAGE_MAIN)) != hipSuccess)
       return LAPATTN_ERR_HIP;
   }
-  if (launch_wy(p, a, b, stream, slot(LAPATTN_STAGE_Y)) != hipSuccess) return LAPATTN_ERR_HIP;
-  if (launch_out(p, a, b, stream, slot(LAPATTN_STAGE_OUT)) != hipSuccess) return LAPATTN_ERR_HIP;
+  // W = K_LK V, Y = X W and (when Q != K) the output rows are formed inside the
+  // main launch; with Q == K there are no query workgroups and the output
+  // product runs as its own launch.
+  if (a.shared_qk && launch_out(p, a, b, stream, slot(LAPATTN_STAGE_OUT)) != hipSuccess)
+    return LAPATTN_ERR_HIP;
   return LAPATTN_OK;
 }
 

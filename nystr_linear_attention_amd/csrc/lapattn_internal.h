@@ -22,7 +22,7 @@ struct Plan {
   int S;        // tiles per key-side workgroup
   int nP;       // key-side workgroups (= W partials) per head
   // workspace byte offsets
-  size_t off_L, off_aw, off_rowsum, off_kql, off_wpart, off_x, off_yt;
+  size_t off_L, off_aw, off_rowsum, off_kql, off_wpart, off_x, off_wt, off_yt, off_sync;
   size_t total;
 };
 
@@ -33,7 +33,9 @@ struct Buffers {
   float* kql;    // [BH][N][mpad]  k(q_n, l_j), zero for j >= m
   float* wpart;  // [BH][nP][D][MP] partial W^T
   float* x;      // [BH][MP][MP]   Newton-Schulz result
+  float* wt;     // [BH][D][MP]    W^T = (K_LK V)^T, zero for columns >= m
   float* yt;     // [BH][D][MP]    Y^T = (X W)^T
+  unsigned* sync;  // [4 + 3 BH]   hand-off counters (see the main kernel)
 };
 
 struct Args {
@@ -63,12 +65,12 @@ struct Ev {
 
 // Stage launchers.  `with_solver` / `with_maps` select which workgroup roles
 // the main launch carries: both (one fused launch), or one each in two
-// launches.
+// launches.  launch_out is needed only when Q and K are the same tensor (no
+// query workgroups to form the output).
 hipError_t launch_pool(const Plan& p, const Args& a, const Buffers& b, hipStream_t s, Ev ev);
 hipError_t launch_amat(const Plan& p, const Args& a, const Buffers& b, hipStream_t s, Ev ev);
 hipError_t launch_main(const Plan& p, const Args& a, const Buffers& b, bool with_solver,
                        bool with_maps, hipStream_t s, Ev ev);
-hipError_t launch_wy(const Plan& p, const Args& a, const Buffers& b, hipStream_t s, Ev ev);
 hipError_t launch_out(const Plan& p, const Args& a, const Buffers& b, hipStream_t s, Ev ev);
 
 }  // namespace lapattn

@@ -168,9 +168,17 @@ struct MainArgs {
   float* xw;          // [BH][MP][MP]
   const float* aw;    // [BH][MP][MP]  A = k(L, L) + eps I, zero padded
   const float* rowsum;  // [BH][MP]    row abs-sums of A
+  float* wt;          // [BH][D][MP]  W^T (reduced partials)
+  float* yt;          // [BH][D][MP]  Y^T = (X W)^T
+  void* out;          // [BH][N][D]   O (query workgroups write it)
+  unsigned* sync;     // hand-off words, zeroed by the pool launch:
+                      //   [0] count of bounded waits that timed out,
+                      //   [4 + bh] key-workgroup arrivals, [4 + BH + bh]
+                      //   arrivals of W and X, [4 + 2 BH + bh] Y-ready flag
   float* st_x;
   float* st_kql;
   float* st_klk;
+  float* st_w;
   int N, m, BH, nT, S, nP, mpad;
   int ns_blocks;      // workgroups [0, ns_blocks) are solver workgroups
   int nQ;             // query-tile workgroups per head (0 when Q == K)
@@ -178,6 +186,125 @@ struct MainArgs {
   int kind, bf16, iters;
   float c_exp2, eps;
 };
+
+// ---------------------------------------------------------------------------
+// Hand-offs inside the main launch.  Per head: the key workgroups publish W^T
+// partials and count their arrivals; the last one reduces them (fixed order,
+// so the result does not depend on which one is last) and publishes W^T.  W^T
+// and X (from the solver workgroup) each count one arrival; whichever is
+// second forms Y^T = W^T X^T and raises the head's Y-ready flag, on which the
+// query workgroups wait before forming their output rows.
+//
+// Coherence across XCDs without cache-wide fences: everything handed over
+// inside the launch (partials, W^T, X, Y^T) is stored with device-scope
+// relaxed atomic stores, which write through the per-XCD L2 to memory; a
+// publisher drains its stores (vmcnt(0)) and meets its workgroup at a
+// barrier before one thread counts the arrival or raises the flag (device-
+// scope atomics).  Consumers read the handed-over data with plain loads
+// after seeing the count or flag: no XCD touches those addresses earlier in
+// the launch, and every launch starts with invalidated caches, so the loads
+// miss to memory.  (A device-scope release / acquire fence would instead
+// write back / invalidate the whole L2 of the XCD, which costs microseconds
+// and evicts what the map workgroups stream; device-scope loads of the data
+// itself are several times slower than plain misses.)
+//
+// Forward progress: solver workgroups come first in the grid and each head's
+// key workgroups precede its query workgroups, so with in-order dispatch
+// every producer has started before a consumer can wait on it.  The wait is
+// bounded in time regardless (it then counts a timeout in sync[0] and goes
+// on), so no wave can spin forever.
+// ---------------------------------------------------------------------------
+constexpr long long kWaitTicks = 2000000;  // 20 ms of the 100 MHz device clock
+
+__device__ __forceinline__ unsigned* cnt_w(const MainArgs& a, int bh) { return a.sync + 4 + bh; }
+__device__ __forceinline__ unsigned* cnt_y(const MainArgs& a, int bh) {
+  return a.sync + 4 + a.BH + bh;
+}
+__device__ __forceinline__ unsigned* flag_y(const MainArgs& a, int bh) {
+  return a.sync + 4 + 2 * a.BH + bh;
+}
+
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Waits until this thread's global stores have completed.
+__device__ __forceinline__ void drain_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Completes this workgroup's device-scope stores, then counts one arrival at
+// *ctr; returns the previous count in every thread.
+__device__ __forceinline__ unsigned publish_arrive(unsigned* ctr) {
+  __shared__ unsigned old_s;
+  drain_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) old_s = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  return old_s;
+}
+
+__device__ __forceinline__ void raise_flag(unsigned* flag) {
+  drain_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_store(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void wait_flag(unsigned* flag, unsigned* timeouts) {
+  if (threadIdx.x == 0) {
+    const long long t0 = wall_clock64();
+    while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+      if (wall_clock64() - t0 > kWaitTicks) {
+        __hip_atomic_fetch_add(timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  __syncthreads();
+}
+
+// Y^T = W^T X^T for one head on fp32 MFMA, D x 64 outputs (columns >= m are
+// zero because X is zero padded), operands straight from global memory.
+template <int D>
+__device__ void compute_y(const MainArgs& a, int bh) {
+  constexpr int CBN = D / 16;
+  constexpr int NBLK = 4 * CBN;  // 16x16 output blocks
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int lr = lane & 15, lg = lane >> 4;
+  const float* wg = a.wt + static_cast<size_t>(bh) * D * MP;
+  const float* xg = a.xw + static_cast<size_t>(bh) * MP * MP;
+  float* yg = a.yt + static_cast<size_t>(bh) * D * MP;
+#pragma unroll
+  for (int s = 0; s < (NBLK + 7) / 8; ++s) {
+    const int blk = w + 8 * s;
+    if (blk < NBLK) {
+      const int cb = blk / 4, jb = blk % 4;
+      // lane (g, r) supplies W^T[16 cb + r][16 g + u] and X[16 jb + r][16 g + u]
+      const float* ar = wg + (16 * cb + lr) * MP + 16 * lg;
+      const float* br = xg + (16 * jb + lr) * MP + 16 * lg;
+      f4 av[4], bv[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        av[q] = ld4(ar + 4 * q);
+        bv[q] = ld4(br + 4 * q);
+      }
+      f4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int h = 0; h < 4; ++h) c = mfma4(av[q][h], bv[q][h], c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st_dev(yg + (16 * cb + 4 * lg + i) * MP + 16 * jb + lr, c[i]);
+    }
+  }
+}
+
+// Second arrival of (W^T, X) for head bh forms Y^T and raises the flag.
+template <int D>
+__device__ void arrive_y(const MainArgs& a, int bh) {
+  if (publish_arrive(cnt_y(a, bh)) == 1u) {
+    compute_y<D>(a, bh);
+    raise_flag(flag_y(a, bh));
+  }
+}
 
 // ---------------------------------------------------------------------------
 // Solver role: X_0 = alpha A, X_{t+1} = 2 X_t - X_t (A X_t), exactly `iters`
@@ -551,7 +678,7 @@ __device__ void solver_role(const MainArgs& a, int bh, float* smem) {
   float* Xg = a.xw + static_cast<size_t>(bh) * MP * MP;
   for (int e = tid; e < MP * MP; e += WGM) {
     const int row = e / MP, col = e % MP;
-    Xg[e] = (row < G::ROWS && col < S) ? Xf[row * S + col] : 0.f;
+    st_dev(Xg + e, (row < G::ROWS && col < S) ? Xf[row * S + col] : 0.f);
   }
   if (a.st_x) {
     for (int e = tid; e < m * m; e += WGM)
@@ -565,6 +692,81 @@ __device__ void solver_role(const MainArgs& a, int bh, float* smem) {
 // role: K_QL rows).  Wave g computes landmarks [g m / 8, (g+1) m / 8) for the
 // 64 tokens of the tile (lane = token); the tile's kernel values meet in LDS.
 // ---------------------------------------------------------------------------
+// W^T[c][j] = sum of the nP partials in partial order, zero for j >= m; run
+// by the last key workgroup of the head.  Thread: 8 elements (stride WGM),
+// 8 partials of each in flight.
+template <int D>
+__device__ void reduce_w(const MainArgs& a, int bh) {
+  constexpr int EPT = D * MP / WGM;  // elements per thread
+  const int nP = a.nP, m = a.m;
+  const size_t ps = static_cast<size_t>(D) * MP;
+  const float* pb = a.wpart + static_cast<size_t>(bh) * nP * ps;
+  float* wg = a.wt + static_cast<size_t>(bh) * ps;
+  const int tid = threadIdx.x;
+  float sum[EPT];
+#pragma unroll
+  for (int u = 0; u < EPT; ++u) sum[u] = 0.f;
+  int p = 0;
+  for (; p + 8 <= nP; p += 8) {
+    float v[EPT][8];
+#pragma unroll
+    for (int u = 0; u < EPT; ++u)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[u][q] = pb[(p + q) * ps + tid + u * WGM];
+#pragma unroll
+    for (int u = 0; u < EPT; ++u)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) sum[u] += v[u][q];
+  }
+  for (; p < nP; ++p) {
+#pragma unroll
+    for (int u = 0; u < EPT; ++u) sum[u] += pb[p * ps + tid + u * WGM];
+  }
+#pragma unroll
+  for (int u = 0; u < EPT; ++u) {
+    const int e = tid + u * WGM, c = e / MP, j = e % MP;
+    const float w = j < m ? sum[u] : 0.f;
+    st_dev(wg + e, w);
+    if (a.st_w && j < m) a.st_w[(static_cast<size_t>(bh) * m + j) * D + c] = w;
+  }
+}
+
+// O rows of one 64-token tile: K_QL tile (PT, LDS, zero beyond m) times Y
+// (rows of Y^T from global memory) on fp32 MFMA.  Wave w: tokens
+// 16 (w % 4) .. +15, column blocks w / 4, w / 4 + 2, ...
+template <int D>
+__device__ void out_tile(const MainArgs& a, int bh, int t, const float* PT) {
+  constexpr int CBN = D / 16;
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int lr = lane & 15, lg = lane >> 4;
+  const int tb = w & 3, ch = w >> 2;
+  const float* yg = a.yt + static_cast<size_t>(bh) * D * MP;
+  f4 av[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) av[q] = ld4(PT + (16 * tb + lr) * LS + 16 * lg + 4 * q);
+#pragma unroll
+  for (int cb = ch; cb < CBN; cb += 2) {
+    const float* br = yg + (16 * cb + lr) * MP + 16 * lg;
+    f4 bv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) bv[q] = ld4(br + 4 * q);
+    f4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int h = 0; h < 4; ++h) c = mfma4(av[q][h], bv[q][h], c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int n = t * TILE + 16 * tb + 4 * lg + i;
+      if (n < a.N) {
+        const size_t o = (static_cast<size_t>(bh) * a.N + n) * D + 16 * cb + lr;
+        if (a.bf16) static_cast<uint16_t*>(a.out)[o] = f32_to_bf16_rne(c[i]);
+        else static_cast<float*>(a.out)[o] = c[i];
+      }
+    }
+  }
+}
+
 template <int D, int KIND, bool BF16>
 __device__ void map_role(const MainArgs& a, const void* __restrict__ q, const void* __restrict__ k,
                          const void* __restrict__ v, const float* __restrict__ Lw, int b,
@@ -603,7 +805,10 @@ __device__ void map_role(const MainArgs& a, const void* __restrict__ q, const vo
     t_beg = bq % a.nQ;
     t_end = t_beg + 1;
   }
-  const bool store_kql = !key_role || a.shared_qk;
+  // K_QL goes to global memory only when Q == K (the output launch reads
+  // it); query tiles keep theirs in LDS and form their output rows here.
+  const bool store_kql = key_role && a.shared_qk;
+  const bool stage_kql = a.st_kql && (!key_role || a.shared_qk);
   const void* src = key_role ? k : q;
   const int mby = (m + 15) >> 4;
   const int nwb = CBN * mby;  // W output blocks
@@ -663,12 +868,12 @@ __device__ void map_role(const MainArgs& a, const void* __restrict__ q, const vo
         const int tok = e / q4, c4 = e % q4;
         if (t * TILE + tok < N) st4(dst + tok * a.mpad + 4 * c4, ld4(PT + tok * LS + 4 * c4));
       }
-      if (a.st_kql) {
-        for (int e = tid; e < TILE * m; e += WGM) {
-          const int tok = e / m, j = e % m;
-          if (t * TILE + tok < N)
-            a.st_kql[(static_cast<size_t>(bh) * N + t * TILE + tok) * m + j] = PT[tok * LS + j];
-        }
+    }
+    if (stage_kql) {
+      for (int e = tid; e < TILE * m; e += WGM) {
+        const int tok = e / m, j = e % m;
+        if (t * TILE + tok < N)
+          a.st_kql[(static_cast<size_t>(bh) * N + t * TILE + tok) * m + j] = PT[tok * LS + j];
       }
     }
     if (key_role) {
@@ -702,7 +907,12 @@ __device__ void map_role(const MainArgs& a, const void* __restrict__ q, const vo
     }
     __syncthreads();
   }
-  if (!key_role) return;
+  if (!key_role) {
+    // the tile's K_QL rows are still in PT: wait for Y of the head
+    wait_flag(flag_y(a, bh), a.sync);
+    out_tile<D>(a, bh, t_beg, PT);
+    return;
+  }
 
   const int kw = b % nK;
   float* part = a.wpart + (static_cast<size_t>(bh) * nK + kw) * D * MP;
@@ -712,8 +922,13 @@ __device__ void map_role(const MainArgs& a, const void* __restrict__ q, const vo
     if (blk < nwb) {
       const int cb = blk % CBN, jbk = blk / CBN;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) part[(16 * cb + 4 * lg + i) * MP + 16 * jbk + lr] = wacc[s][i];
+      for (int i = 0; i < 4; ++i) st_dev(part + (16 * cb + 4 * lg + i) * MP + 16 * jbk + lr, wacc[s][i]);
     }
+  }
+  // the last key workgroup of the head reduces the partials
+  if (publish_arrive(cnt_w(a, bh)) == static_cast<unsigned>(nK - 1)) {
+    reduce_w<D>(a, bh);
+    arrive_y<D>(a, bh);
   }
 }
 
@@ -731,6 +946,7 @@ __global__ __launch_bounds__(WGM) void main_kernel(MainArgs a, const void* __res
   const int b = blockIdx.x;
   if (b < a.ns_blocks) {
     solver_role<MB>(a, b, smem);
+    arrive_y<D>(a, b);
   } else {
     const int mb = b - a.ns_blocks;
     if (a.kind == 0) {
@@ -782,7 +998,8 @@ __global__ __launch_bounds__(64) void amat_kernel(const float* __restrict__ L,
 template <int D, bool BF16>
 __global__ __launch_bounds__(WGS) void pool_kernel(const void* __restrict__ K,
                                                    float* __restrict__ L,
-                                                   float* __restrict__ st_L, int gw, int ph,
+                                                   float* __restrict__ st_L,
+                                                   unsigned* __restrict__ sync, int gw, int ph,
                                                    int pw, int m, int N) {
   constexpr int C4 = D / 4;
   constexpr int G = WGS / C4;
@@ -790,6 +1007,14 @@ __global__ __launch_bounds__(WGS) void pool_kernel(const void* __restrict__ K,
   __shared__ f4 part[WGS];
   const int j = blockIdx.x, bh = blockIdx.y;
   const int tid = threadIdx.x, c4 = tid % C4, g = tid / C4;
+  // hand-off words of the main launch start at zero every call
+  if (j == 0 && tid == 0) {
+    const int BH = gridDim.y;
+    sync[4 + bh] = 0u;
+    sync[4 + BH + bh] = 0u;
+    sync[4 + 2 * BH + bh] = 0u;
+    if (bh == 0) sync[0] = 0u;
+  }
   const int mw = gw / pw;
   const int R = j / mw, C = j % mw;
   const int cnt = ph * pw;
@@ -818,48 +1043,6 @@ __global__ __launch_bounds__(WGS) void pool_kernel(const void* __restrict__ K,
     st4(dst, mean);
     if (st_L) st4(st_L + (static_cast<size_t>(bh) * m + j) * D + 4 * tid, mean);
   }
-}
-
-// ---------------------------------------------------------------------------
-// wy: workgroup (4 rows of W^T, head).  Thread (row c, column j) sums the nP
-// partials of W^T[c][j] in partial order (8 loads in flight), then forms
-// Y^T[c][r] = sum_k W^T[c][k] X[r][k] for r = j (X rows from the solver).
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(WGS) void wy_kernel(const float* __restrict__ wpart,
-                                                 const float* __restrict__ xw,
-                                                 float* __restrict__ yt,
-                                                 float* __restrict__ st_w, int D, int m,
-                                                 int nP) {
-  __shared__ __attribute__((aligned(16))) float wt[4][MP];
-  const int bh = blockIdx.y;
-  const int tid = threadIdx.x, cl = tid / MP, j = tid % MP;
-  const int c = 4 * blockIdx.x + cl;
-  const float* pb = wpart + (static_cast<size_t>(bh) * nP * D + c) * MP + j;
-  const size_t ps = static_cast<size_t>(D) * MP;
-  float sum = 0.f;
-  int p = 0;
-  for (; p + 8 <= nP; p += 8) {
-    float v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = pb[(p + u) * ps];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) sum += v[u];
-  }
-  for (; p < nP; ++p) sum += pb[p * ps];
-  if (j >= m) sum = 0.f;
-  wt[cl][j] = sum;
-  if (st_w && j < m) st_w[(static_cast<size_t>(bh) * m + j) * D + c] = sum;
-  __syncthreads();
-  const float* xr = xw + (static_cast<size_t>(bh) * MP + j) * MP;
-  float y0 = 0.f, y1 = 0.f;
-#pragma unroll
-  for (int q = 0; q < MP / 4; q += 2) {
-    const f4 x0 = ld4(xr + 4 * q), x1 = ld4(xr + 4 * q + 4);
-    const f4 w0 = ld4(&wt[cl][4 * q]), w1 = ld4(&wt[cl][4 * q + 4]);
-    y0 = fmaf(w0[0], x0[0], fmaf(w0[1], x0[1], fmaf(w0[2], x0[2], fmaf(w0[3], x0[3], y0))));
-    y1 = fmaf(w1[0], x1[0], fmaf(w1[1], x1[1], fmaf(w1[2], x1[2], fmaf(w1[3], x1[3], y1))));
-  }
-  yt[(static_cast<size_t>(bh) * D + c) * MP + j] = y0 + y1;
 }
 
 // ---------------------------------------------------------------------------
@@ -948,10 +1131,10 @@ template <int D>
 hipError_t launch_pool_d(const Plan& p, const Args& a, const Buffers& b, hipStream_t s, Ev ev) {
   const dim3 grid(p.m, p.BH);
   if (p.bf16)
-    return launch(pool_kernel<D, true>, grid, dim3(WGS), s, ev, a.k, b.L, a.st_L, p.gw, p.ph,
-                  p.pw, p.m, p.N);
-  return launch(pool_kernel<D, false>, grid, dim3(WGS), s, ev, a.k, b.L, a.st_L, p.gw, p.ph, p.pw,
-                p.m, p.N);
+    return launch(pool_kernel<D, true>, grid, dim3(WGS), s, ev, a.k, b.L, a.st_L, b.sync, p.gw,
+                  p.ph, p.pw, p.m, p.N);
+  return launch(pool_kernel<D, false>, grid, dim3(WGS), s, ev, a.k, b.L, a.st_L, b.sync, p.gw,
+                p.ph, p.pw, p.m, p.N);
 }
 
 template <int D>
@@ -1033,9 +1216,14 @@ hipError_t launch_main(const Plan& p, const Args& a, const Buffers& b, bool with
   ma.xw = b.x;
   ma.aw = b.aw;
   ma.rowsum = b.rowsum;
+  ma.wt = b.wt;
+  ma.yt = b.yt;
+  ma.out = a.out;
+  ma.sync = b.sync;
   ma.st_x = a.st_x;
   ma.st_kql = a.st_kql;
   ma.st_klk = a.st_klk;
+  ma.st_w = a.st_w;
   ma.N = p.N;
   ma.m = p.m;
   ma.BH = p.BH;
@@ -1060,11 +1248,6 @@ hipError_t launch_main(const Plan& p, const Args& a, const Buffers& b, bool with
     case 64: return launch_main_d<64>(p, ma, grid, s, ev);
   }
   return hipErrorInvalidValue;
-}
-
-hipError_t launch_wy(const Plan& p, const Args& a, const Buffers& b, hipStream_t s, Ev ev) {
-  return launch(wy_kernel, dim3(p.D / 4, p.BH), dim3(WGS), s, ev, b.wpart, b.x, b.yt, a.st_w, p.D,
-                p.m, p.nP);
 }
 
 hipError_t launch_out(const Plan& p, const Args& a, const Buffers& b, hipStream_t s, Ev ev) {

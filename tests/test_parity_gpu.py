@@ -128,8 +128,8 @@ def test_kernel_event_hook(serial):
         assert lib.lapattn_set_stage_events(None, 0) == _lib.OK
         torch.cuda.synchronize()
         for s, name in enumerate(_lib.STAGES):
-            if name == "maps" and not serial:
-                continue            # the fused plan has no map-only launch
+            if (name == "maps" and not serial) or (name == "out" and not w.shared_qk):
+                continue            # slots without a launch in this call
             ms = ctypes.c_float()
             assert rt.hipEventElapsedTime(ctypes.byref(ms), evs[2 * s], evs[2 * s + 1]) == 0, name
             assert 0.0 < ms.value < 1000.0, (name, ms.value)
