@@ -94,14 +94,14 @@ enum {
 /* Launch slots of one forward call, in launch order (for
  * lapattn_set_stage_events). */
 #define LAPATTN_STAGE_POOL 0     /* landmark average pool                      */
-#define LAPATTN_STAGE_AMAT 1     /* A = k(L,L) + eps I and its row abs-sums   */
-#define LAPATTN_STAGE_MAIN 2     /* alpha and Newton-Schulz; in the default
-                                    plan also the K_QL / K_LK maps, W = K_LK V,
-                                    Y = X W and (Q != K) the output rows      */
-#define LAPATTN_STAGE_MAPS 3     /* LAPATTN_FLAG_SERIAL only: the map roles as
+#define LAPATTN_STAGE_MAIN 1     /* A = k(L,L) + eps I, alpha and Newton-Schulz;
+                                    in the default plan also the K_QL / K_LK
+                                    maps, W = K_LK V, Y = X W and (Q != K) the
+                                    output rows                                */
+#define LAPATTN_STAGE_MAPS 2     /* LAPATTN_FLAG_SERIAL only: the map roles as
                                     a launch of their own                      */
-#define LAPATTN_STAGE_OUT 4      /* Q == K only: O = K_QL Y as its own launch  */
-#define LAPATTN_NUM_STAGES 5
+#define LAPATTN_STAGE_OUT 3      /* Q == K only: O = K_QL Y as its own launch  */
+#define LAPATTN_NUM_STAGES 4
 
 typedef struct {
   int32_t B, H;            /* batch and heads; every (b, h) is independent   */

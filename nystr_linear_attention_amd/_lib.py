@@ -33,7 +33,7 @@ EXPORTS = ("lapattn_version", "lapattn_strerror", "lapattn_check",
            "lapattn_workspace_bytes", "lapattn_init", "lapattn_forward",
            "lapattn_forward_stages", "lapattn_set_stage_events")
 
-STAGES = ("pool", "amat", "main", "maps", "out")
+STAGES = ("pool", "main", "maps", "out")
 
 
 class Desc(ctypes.Structure):

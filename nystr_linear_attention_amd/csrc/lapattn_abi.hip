@@ -73,10 +73,6 @@ Plan make_plan(const lapattn_desc_t* d) {
   size_t off = 0;
   p.off_L = off;
   off = align_up(off + BH * p.m * p.D * f);
-  p.off_aw = off;
-  off = align_up(off + BH * MP * MP * f);
-  p.off_rowsum = off;
-  off = align_up(off + BH * MP * f);
   p.off_kql = off;
   off = align_up(off + BH * p.N * p.mpad * f);
   p.off_wpart = off;
@@ -125,8 +121,6 @@ int run(const lapattn_desc_t* desc, const Args& a, void* workspace, size_t ws_by
   char* ws = static_cast<char*>(workspace);
   Buffers b;
   b.L = reinterpret_cast<float*>(ws + p.off_L);
-  b.aw = reinterpret_cast<float*>(ws + p.off_aw);
-  b.rowsum = reinterpret_cast<float*>(ws + p.off_rowsum);
   b.kql = reinterpret_cast<float*>(ws + p.off_kql);
   b.wpart = reinterpret_cast<float*>(ws + p.off_wpart);
   b.x = reinterpret_cast<float*>(ws + p.off_x);
@@ -135,7 +129,6 @@ int run(const lapattn_desc_t* desc, const Args& a, void* workspace, size_t ws_by
   b.sync = reinterpret_cast<unsigned*>(ws + p.off_sync);
 
   if (launch_pool(p, a, b, stream, slot(LAPATTN_STAGE_POOL)) != hipSuccess) return LAPATTN_ERR_HIP;
-  if (launch_amat(p, a, b, stream, slot(LAPATTN_STAGE_AMAT)) != hipSuccess) return LAPATTN_ERR_HIP;
   if (desc->flags & LAPATTN_FLAG_SERIAL) {
     if (launch_main(p, a, b, true, false, stream, slot(LAPATTN_STAGE_MAIN)) != hipSuccess ||
         launch_main(p, a, b, false, true, stream, slot(LAPATTN_STAGE_MAPS)) != hipSuccess)

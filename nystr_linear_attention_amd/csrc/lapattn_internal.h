@@ -22,14 +22,12 @@ struct Plan {
   int S;        // tiles per key-side workgroup
   int nP;       // key-side workgroups (= W partials) per head
   // workspace byte offsets
-  size_t off_L, off_aw, off_rowsum, off_kql, off_wpart, off_x, off_wt, off_yt, off_sync;
+  size_t off_L, off_kql, off_wpart, off_x, off_wt, off_yt, off_sync;
   size_t total;
 };
 
 struct Buffers {
   float* L;      // [BH][m][D]     landmarks
-  float* aw;     // [BH][MP][MP]   A = k(L, L) + eps I, zero padded
-  float* rowsum; // [BH][MP]       row abs-sums of A
   float* kql;    // [BH][N][mpad]  k(q_n, l_j), zero for j >= m
   float* wpart;  // [BH][nP][D][MP] partial W^T
   float* x;      // [BH][MP][MP]   Newton-Schulz result
@@ -68,7 +66,6 @@ struct Ev {
 // launches.  launch_out is needed only when Q and K are the same tensor (no
 // query workgroups to form the output).
 hipError_t launch_pool(const Plan& p, const Args& a, const Buffers& b, hipStream_t s, Ev ev);
-hipError_t launch_amat(const Plan& p, const Args& a, const Buffers& b, hipStream_t s, Ev ev);
 hipError_t launch_main(const Plan& p, const Args& a, const Buffers& b, bool with_solver,
                        bool with_maps, hipStream_t s, Ev ev);
 hipError_t launch_out(const Plan& p, const Args& a, const Buffers& b, hipStream_t s, Ev ev);

@@ -1,20 +1,22 @@
 // HIP kernels for Nystrom kernel attention (forward) on gfx950.
 //
-// Five launches per forward call, back to back on the caller's stream:
+// Two launches per forward call (three when Q and K are the same tensor),
+// back to back on the caller's stream:
 //   pool : landmarks L = window means of K                         (HBM stream)
-//   amat : A = k(L, L) + eps I and its row abs-sums (one workgroup per
-//          landmark row, so the m^2 d distance work is spread over the chip)
 //   main : role-split workgroups
-//          - solver WGs (one per head, dispatched first, raised wave priority):
-//            alpha, then the Newton-Schulz steps held in LDS, fp32 MFMA
+//          - solver WGs (one per head, first in the grid, raised wave
+//            priority): A = k(L, L) + eps I, alpha, then the Newton-Schulz
+//            steps held in LDS on fp32 MFMA
 //          - map WGs: kernel values of 64 tokens against every landmark on
 //            FP32 VALU (landmark coordinates are wave-uniform scalar operands);
-//            query tiles store K_QL, key tiles contract K_LK V on fp32 MFMA
-//            into per-workgroup partials of W^T
-//   wy   : W^T = sum of the partials in fixed order (deterministic), then
-//          Y^T = W^T X^T
-//   out  : O = K_QL Y on fp32 MFMA, fp32 or bf16 (RNE) store.
-// No workgroup waits on another: every dependency is a launch boundary.
+//            key tiles contract K_LK V on fp32 MFMA into per-workgroup
+//            partials of W^T; query tiles keep their K_QL rows in LDS
+//          - hand-offs: the last key WG of a head reduces the partials (fixed
+//            order, deterministic) into W^T; the second of (W^T, X) forms
+//            Y^T = W^T X^T; query WGs wait for it and write O = K_QL Y
+//   out  : (Q == K only) O = K_QL Y on fp32 MFMA from K_QL stored by the key
+//          tiles.
+// Outputs are fp32 or bf16 (RNE).
 //
 // Pages behind each step: average-pool landmarks (SOFT review, "method";
 // LaplacianFormer summaries, Nystrom paragraph), Laplacian kernel
@@ -49,6 +51,7 @@ constexpr int WGM = 512;      // main kernel: 8 wave64
 constexpr int WGS = 256;      // pool / out kernels: 4 wave64
 constexpr int TILE = 64;      // tokens per map tile (one per lane)
 constexpr int NGRP = 8;       // landmark groups per map tile (one per wave)
+constexpr int QT = 2;         // 64-token tiles per query workgroup
 
 __device__ __forceinline__ f4 mfma4(float a, float b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -166,8 +169,6 @@ struct MainArgs {
   float* kql;         // [BH][N][mpad]
   float* wpart;       // [BH][nP][D][MP]
   float* xw;          // [BH][MP][MP]
-  const float* aw;    // [BH][MP][MP]  A = k(L, L) + eps I, zero padded
-  const float* rowsum;  // [BH][MP]    row abs-sums of A
   float* wt;          // [BH][D][MP]  W^T (reduced partials)
   float* yt;          // [BH][D][MP]  Y^T = (X W)^T
   void* out;          // [BH][N][D]   O (query workgroups write it)
@@ -175,13 +176,14 @@ struct MainArgs {
                       //   [0] count of bounded waits that timed out,
                       //   [4 + bh] key-workgroup arrivals, [4 + BH + bh]
                       //   arrivals of W and X, [4 + 2 BH + bh] Y-ready flag
+  float* st_a;
   float* st_x;
   float* st_kql;
   float* st_klk;
   float* st_w;
   int N, m, BH, nT, S, nP, mpad;
   int ns_blocks;      // workgroups [0, ns_blocks) are solver workgroups
-  int nQ;             // query-tile workgroups per head (0 when Q == K)
+  int nQ;             // query workgroups per head, QT tiles each (0 when Q == K)
   int shared_qk;      // Q and K are the same tensor
   int kind, bf16, iters;
   float c_exp2, eps;
@@ -262,29 +264,31 @@ __device__ __forceinline__ void wait_flag(unsigned* flag, unsigned* timeouts) {
 }
 
 // Y^T = W^T X^T for one head on fp32 MFMA, D x 64 outputs (columns >= m are
-// zero because X is zero padded), operands straight from global memory.
+// zero because X is zero padded).  W^T rows have stride wts; X has xrows
+// rows of stride xs (columns >= xs and rows >= xrows read as zero), so the
+// operands may come from global memory or from the solver's LDS: the same
+// values in the same MFMA order give the same Y^T either way.
 template <int D>
-__device__ void compute_y(const MainArgs& a, int bh) {
+__device__ void compute_y(const float* wt, int wts, const float* x, int xs, int xrows,
+                          float* yg) {
   constexpr int CBN = D / 16;
   constexpr int NBLK = 4 * CBN;  // 16x16 output blocks
   const int lane = threadIdx.x & 63, w = wave_id();
   const int lr = lane & 15, lg = lane >> 4;
-  const float* wg = a.wt + static_cast<size_t>(bh) * D * MP;
-  const float* xg = a.xw + static_cast<size_t>(bh) * MP * MP;
-  float* yg = a.yt + static_cast<size_t>(bh) * D * MP;
 #pragma unroll
   for (int s = 0; s < (NBLK + 7) / 8; ++s) {
     const int blk = w + 8 * s;
     if (blk < NBLK) {
       const int cb = blk / 4, jb = blk % 4;
       // lane (g, r) supplies W^T[16 cb + r][16 g + u] and X[16 jb + r][16 g + u]
-      const float* ar = wg + (16 * cb + lr) * MP + 16 * lg;
-      const float* br = xg + (16 * jb + lr) * MP + 16 * lg;
+      const float* ar = wt + (16 * cb + lr) * wts + 16 * lg;
+      const int xr = 16 * jb + lr;
       f4 av[4], bv[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         av[q] = ld4(ar + 4 * q);
-        bv[q] = ld4(br + 4 * q);
+        const int c0 = 16 * lg + 4 * q;
+        bv[q] = (xr < xrows && c0 < xs) ? ld4(x + xr * xs + c0) : f4{0.f, 0.f, 0.f, 0.f};
       }
       f4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -297,11 +301,18 @@ __device__ void compute_y(const MainArgs& a, int bh) {
   }
 }
 
+template <int D>
+__device__ __forceinline__ void compute_y_global(const MainArgs& a, int bh) {
+  compute_y<D>(a.wt + static_cast<size_t>(bh) * D * MP, MP,
+               a.xw + static_cast<size_t>(bh) * MP * MP, MP, MP,
+               a.yt + static_cast<size_t>(bh) * D * MP);
+}
+
 // Second arrival of (W^T, X) for head bh forms Y^T and raises the flag.
 template <int D>
 __device__ void arrive_y(const MainArgs& a, int bh) {
   if (publish_arrive(cnt_y(a, bh)) == 1u) {
-    compute_y<D>(a, bh);
+    compute_y_global<D>(a, bh);
     raise_flag(flag_y(a, bh));
   }
 }
@@ -618,7 +629,62 @@ __device__ void ns_border_wave(const MainArgs& a, float* smem, int b, int lane) 
   }
 }
 
-template <int MB>
+// The 2 x 2 blocks of the upper triangle of A = k(L, L) + eps I (see
+// solver_role): landmarks staged in Ls (rows of LDL floats), A in LDS with
+// row stride S.
+template <int D, int KIND>
+__device__ void build_a(const MainArgs& a, int bh, const float* Ls, float* A, int S) {
+  constexpr int LDL = D + 4;
+  const int m = a.m, nb = (m + 1) / 2;
+  float* sa = a.st_a ? a.st_a + static_cast<size_t>(bh) * m * m : nullptr;
+  for (int blk = threadIdx.x; blk < nb * (nb + 1) / 2; blk += WGM) {
+    // blk = bj (bj + 1) / 2 + bi with bi <= bj
+    int bj = static_cast<int>((sqrtf(8.0f * blk + 1.0f) - 1.0f) * 0.5f);
+    while (bj * (bj + 1) / 2 > blk) --bj;
+    while ((bj + 1) * (bj + 2) / 2 <= blk) ++bj;
+    const int bi = blk - bj * (bj + 1) / 2;
+    const float* r0 = Ls + (2 * bi) * LDL;
+    const float* r1 = r0 + LDL;
+    const float* c0 = Ls + (2 * bj) * LDL;
+    const float* c1 = c0 + LDL;
+    // d[u][h]: pair u = (row, col) in {00, 01, 10, 11}, two partial sums
+    float d[4][2] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
+    // partial unroll: full unrolling hoists every row read and spills
+#pragma unroll 4
+    for (int q = 0; q < D / 4; ++q) {
+      const f4 x0 = ld4(r0 + 4 * q), x1 = ld4(r1 + 4 * q);
+      const f4 y0 = ld4(c0 + 4 * q), y1 = ld4(c1 + 4 * q);
+      const f4 t[4] = {x0 - y0, x0 - y1, x1 - y0, x1 - y1};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if constexpr (KIND == 0) {
+          d[u][0] += fabsf(t[u][0]) + fabsf(t[u][2]);
+          d[u][1] += fabsf(t[u][1]) + fabsf(t[u][3]);
+        } else {
+          d[u][0] = fmaf(t[u][0], t[u][0], fmaf(t[u][2], t[u][2], d[u][0]));
+          d[u][1] = fmaf(t[u][1], t[u][1], fmaf(t[u][3], t[u][3], d[u][1]));
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = 2 * bi + (u >> 1), j = 2 * bj + (u & 1);
+      // in the diagonal block, (2bi+1, 2bi) repeats (2bi, 2bi+1)
+      if (i < m && j < m && i <= j) {
+        float v = exp2f((d[u][0] + d[u][1]) * a.c_exp2);
+        if (i == j) v += a.eps;
+        A[i * S + j] = v;
+        A[j * S + i] = v;
+        if (sa) {
+          sa[i * m + j] = v;
+          sa[j * m + i] = v;
+        }
+      }
+    }
+  }
+}
+
+template <int D, int MB>
 __device__ void solver_role(const MainArgs& a, int bh, float* smem) {
   using G = NsGeom<MB>;
   constexpr int S = G::SLS, N16 = G::N16;
@@ -627,26 +693,50 @@ __device__ void solver_role(const MainArgs& a, int bh, float* smem) {
   float* X1 = smem + 2 * G::MAT;
   float* XTB = smem + G::OFF_XTB;
   float* red = smem + G::OFF_RED;
+  constexpr int WLS = MP + 4;              // row stride of the W^T copy
+  float* WTL = smem + G::SMEM;             // [D][WLS] W^T copy (see below)
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int m = a.m;
   const int r = m > N16 ? m - N16 : 0;  // border width (0 when padded)
   __builtin_amdgcn_s_setprio(3);
 
-  // A (built by the A-matrix launch, zero padded to 64 x 64) -> LDS.
-  const float* Ag = a.aw + static_cast<size_t>(bh) * MP * MP;
-  for (int e = tid; e < G::ROWS * (S / 4); e += WGM) {
-    const int row = e / (S / 4), c4 = e % (S / 4);
-    // rows >= m were never written by the A-matrix launch: zero them here
-    st4(A + row * S + 4 * c4,
-        (row < m && 4 * c4 < MP) ? ld4(Ag + row * MP + 4 * c4) : f4{0.f, 0.f, 0.f, 0.f});
+  // A = k(L, L) + eps I, built here in LDS.  The landmarks are staged in LDS
+  // (over the iterate buffers, which are initialised afterwards; rows up to
+  // an even count, padding zero).  Each thread computes a 2 x 2 block (rows 2 bi, 2 bi + 1; columns 2 bj, 2 bj + 1), bi <= bj, of
+  // the upper triangle, streaming the four landmark rows; every unordered
+  // pair is computed once and written to A[i][j] and A[j][i], so A is exactly
+  // symmetric (the border code relies on it).
+  constexpr int LDL = D + 4;
+  float* Ls = smem + G::MAT;
+  const int nb = (m + 1) / 2;
+  {
+    const float* Lg = a.L + static_cast<size_t>(bh) * m * D;
+    for (int e = tid; e < 2 * nb * (D / 4); e += WGM) {
+      const int row = e / (D / 4), c4 = e % (D / 4);
+      st4(Ls + row * LDL + 4 * c4, row < m ? ld4(Lg + row * D + 4 * c4) : f4{0.f, 0.f, 0.f, 0.f});
+    }
+    for (int e = tid; e < G::ROWS * S; e += WGM) A[e] = 0.f;
   }
-  // alpha = 1 / (max column abs-sum * max row abs-sum).  A is bitwise
-  // symmetric, so its largest column sum equals its largest row sum.
+  __syncthreads();
+  if (a.kind == 0) build_a<D, 0>(a, bh, Ls, A, S);
+  else build_a<D, 1>(a, bh, Ls, A, S);
+  __syncthreads();
+  // alpha = 1 / (max column abs-sum * max row abs-sum); A is symmetric, so
+  // its largest column sum equals its largest row sum.
   if (w == 0) {
-    float sum = lane < m ? a.rowsum[static_cast<size_t>(bh) * MP + lane] : 0.f;
+    float sum = 0.f;
+    if (lane < m) {
+      for (int q = 0; q < (m + 3) / 4; ++q) {
+        const f4 v = ld4(A + lane * S + 4 * q);  // zero beyond m
+        sum += fabsf(v[0]) + fabsf(v[1]) + fabsf(v[2]) + fabsf(v[3]);
+      }
+    }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) sum = fmaxf(sum, __shfl_xor(sum, o));
-    if (lane == 0) red[0] = sum;
+    if (lane == 0) {
+      red[0] = sum;
+      red[1] = 0.f;  // set once W^T is in LDS
+    }
   }
   __syncthreads();
   const float alpha = 1.0f / (red[0] * red[0]);
@@ -671,19 +761,75 @@ __device__ void solver_role(const MainArgs& a, int bh, float* smem) {
   } else if (w - MB < r) {
     ns_border_wave<MB>(a, smem, w - MB, lane);
   } else {
-    for (int t = 0; t < a.iters; ++t) __syncthreads();
+    // idle waves; the first one watches for the head's W^T (published by the
+    // last key workgroup) during the second half of the steps and copies it
+    // to LDS, so that Y can be formed right after the last step.  Each global
+    // read is issued before a barrier and consumed after it (a barrier does
+    // not wait for global loads), so the watcher never delays the steps.
+    const bool watcher = w == MB + r;
+    constexpr int NW = D * (MP / 4) / 64;  // float4 of W^T per lane
+    const float* wg = a.wt + static_cast<size_t>(bh) * D * MP;
+    int state = 0;  // 0 polling, 1 W^T reads in flight, 2 copied
+    bool polled = false;
+    unsigned cnt = 0u;
+    f4 wv[NW];
+    for (int t = 0; t < a.iters; ++t) {
+      if (watcher) {
+        if (state == 1) {
+#pragma unroll
+          for (int u = 0; u < NW; ++u) {
+            const int e = lane + 64 * u, row = e / (MP / 4), c4 = e % (MP / 4);
+            st4(WTL + row * WLS + 4 * c4, wv[u]);
+          }
+          if (lane == 0) red[1] = 1.0f;
+          state = 2;
+        }
+        if (state == 0 && polled && __builtin_amdgcn_readfirstlane(cnt) >= 1u) {
+#pragma unroll
+          for (int u = 0; u < NW; ++u) {
+            const int e = lane + 64 * u, row = e / (MP / 4), c4 = e % (MP / 4);
+            wv[u] = ld4(wg + row * MP + 4 * c4);
+          }
+          state = 1;
+        }
+        if (state == 0 && 2 * t >= a.iters) {
+          if (lane == 0) cnt = __hip_atomic_load(cnt_y(a, bh), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          polled = true;
+        }
+      }
+      __syncthreads();
+      asm volatile("" : "+v"(cnt));
+    }
+    if (watcher && state == 1) {
+#pragma unroll
+      for (int u = 0; u < NW; ++u) {
+        const int e = lane + 64 * u, row = e / (MP / 4), c4 = e % (MP / 4);
+        st4(WTL + row * WLS + 4 * c4, wv[u]);
+      }
+      if (lane == 0) red[1] = 1.0f;
+    }
   }
+  __syncthreads();  // the W^T copy and its flag are complete
 
   const float* Xf = (a.iters & 1) ? X1 : X0;
+  if (a.st_x) {
+    for (int e = tid; e < m * m; e += WGM)
+      a.st_x[static_cast<size_t>(bh) * m * m + e] = Xf[(e / m) * S + (e % m)];
+  }
+  if (red[1] != 0.f) {
+    // W^T is already published (its arrival counted) and copied to LDS: this
+    // workgroup is the second of (W, X) and forms Y^T from LDS directly
+    compute_y<D>(WTL, WLS, Xf, S, G::ROWS, a.yt + static_cast<size_t>(bh) * D * MP);
+    raise_flag(flag_y(a, bh));
+    return;
+  }
+  // otherwise publish X and count its arrival
   float* Xg = a.xw + static_cast<size_t>(bh) * MP * MP;
   for (int e = tid; e < MP * MP; e += WGM) {
     const int row = e / MP, col = e % MP;
     st_dev(Xg + e, (row < G::ROWS && col < S) ? Xf[row * S + col] : 0.f);
   }
-  if (a.st_x) {
-    for (int e = tid; e < m * m; e += WGM)
-      a.st_x[static_cast<size_t>(bh) * m * m + e] = Xf[(e / m) * S + (e % m)];
-  }
+  arrive_y<D>(a, bh);
 }
 
 // ---------------------------------------------------------------------------
@@ -800,10 +946,12 @@ __device__ void map_role(const MainArgs& a, const void* __restrict__ q, const vo
     t_beg = kw * a.S;
     t_end = min(t_beg + a.S, a.nT);
   } else {
+    // QT tiles per query workgroup (their K_QL rows stay in LDS until Y is
+    // ready, in PT and in the V^T area, which query tiles do not use)
     const int bq = b - a.BH * nK;
     bh = bq / a.nQ;
-    t_beg = bq % a.nQ;
-    t_end = t_beg + 1;
+    t_beg = QT * (bq % a.nQ);
+    t_end = min(t_beg + QT, a.nT);
   }
   // K_QL goes to global memory only when Q == K (the output launch reads
   // it); query tiles keep theirs in LDS and form their output rows here.
@@ -817,6 +965,7 @@ __device__ void map_role(const MainArgs& a, const void* __restrict__ q, const vo
   for (int e = tid; e < MP * LS; e += WGM) {
     PJ[e] = 0.f;
     PT[e] = 0.f;
+    if (!key_role) VT[e] = 0.f;
   }
   __syncthreads();
 
@@ -825,6 +974,7 @@ __device__ void map_role(const MainArgs& a, const void* __restrict__ q, const vo
   f4 wacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 
   for (int t = t_beg; t < t_end; ++t) {
+    float* PTt = (key_role || t == t_beg) ? PT : VT;  // this tile's K_QL rows
     const int n = t * TILE + lane;
     const bool valid = n < N;
     float x[D];
@@ -854,10 +1004,12 @@ __device__ void map_role(const MainArgs& a, const void* __restrict__ q, const vo
       dist_to2<D, KIND>(x, Lh + j * D, Lh + j1 * D, d0, d1);
       const float k0 = valid ? exp2f(d0 * a.c_exp2) : 0.f;
       const float k1 = valid ? exp2f(d1 * a.c_exp2) : 0.f;
-      PJ[j * LS + lane] = k0;
-      PT[lane * LS + j] = k0;
-      PJ[j1 * LS + lane] = k1;
-      PT[lane * LS + j1] = k1;
+      if (key_role) {
+        PJ[j * LS + lane] = k0;
+        PJ[j1 * LS + lane] = k1;
+      }
+      PTt[lane * LS + j] = k0;
+      PTt[lane * LS + j1] = k1;
     }
     __syncthreads();
     if (store_kql) {
@@ -866,14 +1018,14 @@ __device__ void map_role(const MainArgs& a, const void* __restrict__ q, const vo
       float* dst = a.kql + (static_cast<size_t>(bh) * N + t * TILE) * a.mpad;
       for (int e = tid; e < TILE * q4; e += WGM) {
         const int tok = e / q4, c4 = e % q4;
-        if (t * TILE + tok < N) st4(dst + tok * a.mpad + 4 * c4, ld4(PT + tok * LS + 4 * c4));
+        if (t * TILE + tok < N) st4(dst + tok * a.mpad + 4 * c4, ld4(PTt + tok * LS + 4 * c4));
       }
     }
     if (stage_kql) {
       for (int e = tid; e < TILE * m; e += WGM) {
         const int tok = e / m, j = e % m;
         if (t * TILE + tok < N)
-          a.st_kql[(static_cast<size_t>(bh) * N + t * TILE + tok) * m + j] = PT[tok * LS + j];
+          a.st_kql[(static_cast<size_t>(bh) * N + t * TILE + tok) * m + j] = PTt[tok * LS + j];
       }
     }
     if (key_role) {
@@ -908,9 +1060,10 @@ __device__ void map_role(const MainArgs& a, const void* __restrict__ q, const vo
     __syncthreads();
   }
   if (!key_role) {
-    // the tile's K_QL rows are still in PT: wait for Y of the head
+    // the tiles' K_QL rows are still in LDS: wait for Y of the head
     wait_flag(flag_y(a, bh), a.sync);
     out_tile<D>(a, bh, t_beg, PT);
+    if (t_beg + 1 < t_end) out_tile<D>(a, bh, t_beg + 1, VT);
     return;
   }
 
@@ -940,13 +1093,16 @@ __global__ __launch_bounds__(WGM) void main_kernel(MainArgs a, const void* __res
                                                     const void* __restrict__ v,
                                                     const float* __restrict__ L) {
   constexpr int MAP_SMEM = 3 * MP * LS;
-  constexpr int SOLVER_SMEM = NsGeom<MB>::SMEM;
+  // solver: the Newton-Schulz layout plus a W^T copy; landmark staging
+  // while A is built
+  constexpr int SOLVER_A = NsGeom<MB>::SMEM + D * (MP + 4);
+  constexpr int SOLVER_B = NsGeom<MB>::MAT + MP * (D + 4);
+  constexpr int SOLVER_SMEM = SOLVER_A > SOLVER_B ? SOLVER_A : SOLVER_B;
   __shared__ __attribute__((aligned(16)))
   float smem[MAP_SMEM > SOLVER_SMEM ? MAP_SMEM : SOLVER_SMEM];
   const int b = blockIdx.x;
   if (b < a.ns_blocks) {
-    solver_role<MB>(a, b, smem);
-    arrive_y<D>(a, b);
+    solver_role<D, MB>(a, b, smem);
   } else {
     const int mb = b - a.ns_blocks;
     if (a.kind == 0) {
@@ -957,37 +1113,6 @@ __global__ __launch_bounds__(WGM) void main_kernel(MainArgs a, const void* __res
       else map_role<D, 1, false>(a, q, k, v, L, mb, smem);
     }
   }
-}
-
-// ---------------------------------------------------------------------------
-// amat: A = k(L, L) + eps I.  Workgroup (row i, head), one wave: lane j
-// computes A[i][j] with landmark j in registers and landmark i as wave-uniform
-// scalar operands.  A[j][i] comes from workgroup j with the same operations on
-// the same terms (|a - b| = |b - a|), so A is bitwise symmetric.  Rows are
-// written zero padded to 64 columns, with their abs-sums for alpha.
-// ---------------------------------------------------------------------------
-template <int D, int KIND>
-__global__ __launch_bounds__(64) void amat_kernel(const float* __restrict__ L,
-                                                  float* __restrict__ aw,
-                                                  float* __restrict__ rowsum,
-                                                  float* __restrict__ st_a, int m,
-                                                  float c_exp2, float eps) {
-  const int i = blockIdx.x, bh = blockIdx.y, j = threadIdx.x;
-  const float* Lh = L + static_cast<size_t>(bh) * m * D;
-  float x[D];
-  load_row<D>(Lh, j < m ? j : 0, 0, x);
-  const float dist = dist_to<D, KIND>(x, Lh + i * D);
-  float av = 0.f;
-  if (j < m) {
-    av = exp2f(dist * c_exp2);
-    if (i == j) av += eps;
-  }
-  aw[(static_cast<size_t>(bh) * MP + i) * MP + j] = av;
-  if (st_a && j < m) st_a[(static_cast<size_t>(bh) * m + i) * m + j] = av;
-  float sum = fabsf(av);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
-  if (j == 0) rowsum[static_cast<size_t>(bh) * MP + i] = sum;
 }
 
 // ---------------------------------------------------------------------------
@@ -1137,17 +1262,6 @@ hipError_t launch_pool_d(const Plan& p, const Args& a, const Buffers& b, hipStre
                 p.ph, p.pw, p.m, p.N);
 }
 
-template <int D>
-hipError_t launch_amat_d(const Plan& p, const Args& a, const Buffers& b, hipStream_t s, Ev ev) {
-  const float c = exp2_scale(a.lambda);
-  const dim3 grid(p.m, p.BH);
-  if (p.kernel == 0)
-    return launch(amat_kernel<D, 0>, grid, dim3(64), s, ev, b.L, b.aw, b.rowsum, a.st_a, p.m, c,
-                  a.eps);
-  return launch(amat_kernel<D, 1>, grid, dim3(64), s, ev, b.L, b.aw, b.rowsum, a.st_a, p.m, c,
-                a.eps);
-}
-
 template <int D, int MB>
 hipError_t launch_main_dm(const MainArgs& ma, unsigned grid, hipStream_t s, Ev ev) {
   return launch(main_kernel<D, MB>, dim3(grid), dim3(WGM), s, ev, ma, ma.q, ma.k, ma.v, ma.L);
@@ -1195,15 +1309,6 @@ hipError_t launch_pool(const Plan& p, const Args& a, const Buffers& b, hipStream
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_amat(const Plan& p, const Args& a, const Buffers& b, hipStream_t s, Ev ev) {
-  switch (p.D) {
-    case 16: return launch_amat_d<16>(p, a, b, s, ev);
-    case 32: return launch_amat_d<32>(p, a, b, s, ev);
-    case 64: return launch_amat_d<64>(p, a, b, s, ev);
-  }
-  return hipErrorInvalidValue;
-}
-
 hipError_t launch_main(const Plan& p, const Args& a, const Buffers& b, bool with_solver,
                        bool with_maps, hipStream_t s, Ev ev) {
   MainArgs ma{};
@@ -1214,12 +1319,11 @@ hipError_t launch_main(const Plan& p, const Args& a, const Buffers& b, bool with
   ma.kql = b.kql;
   ma.wpart = b.wpart;
   ma.xw = b.x;
-  ma.aw = b.aw;
-  ma.rowsum = b.rowsum;
   ma.wt = b.wt;
   ma.yt = b.yt;
   ma.out = a.out;
   ma.sync = b.sync;
+  ma.st_a = a.st_a;
   ma.st_x = a.st_x;
   ma.st_kql = a.st_kql;
   ma.st_klk = a.st_klk;
@@ -1232,7 +1336,7 @@ hipError_t launch_main(const Plan& p, const Args& a, const Buffers& b, bool with
   ma.nP = p.nP;
   ma.mpad = p.mpad;
   ma.shared_qk = a.shared_qk;
-  ma.nQ = a.shared_qk ? 0 : p.nT;
+  ma.nQ = a.shared_qk ? 0 : (p.nT + QT - 1) / QT;
   ma.kind = p.kernel;
   ma.bf16 = p.bf16;
   ma.iters = a.iters;
