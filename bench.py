@@ -282,7 +282,12 @@ def main(argv=None):
     # slows the step (each launch then completes with a timestamped signal),
     # not the kernels; the step time of this pass is reported separately.
     # The fused plan has no map-only launch: its MAPS slot stays unrecorded.
-    unused = (() if args.serial else ("maps",)) + (() if w.shared_qk else ("out",))
+    def unused_slots(serial_plan):
+        desc = api.make_desc(w.B, w.H, w.grid_h, w.grid_w, w.d, w.pool_h, w.pool_w, w.kernel,
+                             q.dtype, serial=serial_plan)
+        used = api.launches(desc, w.shared_qk)
+        return tuple(n for n in _lib.STAGES if n not in used)
+    unused = unused_slots(args.serial)
     ms_ev, kern = timed(main_step, args.steps, True, unused)
     log(f"[bench] kernel-event pass: {ms_ev * 1e3:.2f} us/step; kernels (us): "
         + ", ".join(f"{n}={t * 1e3:.2f}" for n, t in kern.items()))
@@ -292,8 +297,7 @@ def main(argv=None):
         other = fused if args.serial else serial
         for _ in range(max(2, args.warmup // 4)):
             other()
-        ms_other, kern_other = timed(other, args.steps, True,
-                                     (("maps",) if args.serial else ()) + (() if w.shared_qk else ("out",)))
+        ms_other, kern_other = timed(other, args.steps, True, unused_slots(not args.serial))
         log(f"[bench] {'fused' if args.serial else 'serial'} plan: {ms_other * 1e3:.2f} us/step; "
             "kernels (us): " + ", ".join(f"{n}={t * 1e3:.2f}" for n, t in kern_other.items()))
     kf = kern_other if args.serial else kern      # fused-plan kernels (may be empty)

@@ -166,6 +166,11 @@ int lapattn_forward_stages(const lapattn_desc_t* desc, const void* q,
                            void* stream, float* L, float* kql, float* klk,
                            float* a, float* x, float* w);
 
+/* Launch slots (bit s for LAPATTN_STAGE_s) that a forward call with this
+ * descriptor enqueues; q_is_k says whether k will be the same pointer as q.
+ * Host-only, no GPU work.  Returns a negative error code for a bad desc. */
+int lapattn_launches(const lapattn_desc_t* desc, int q_is_k);
+
 /* Profiling hook.  For the calling host thread, makes every later forward
  * call launch the kernel of slot s (LAPATTN_STAGE_*) through
  * hipExtLaunchKernel with events[2*s] and events[2*s+1] as its start and stop

@@ -31,7 +31,7 @@ FLAG_SERIAL = 1
 # Names of every entry point declared in include/lapattn.h.
 EXPORTS = ("lapattn_version", "lapattn_strerror", "lapattn_check",
            "lapattn_workspace_bytes", "lapattn_init", "lapattn_forward",
-           "lapattn_forward_stages", "lapattn_set_stage_events")
+           "lapattn_forward_stages", "lapattn_set_stage_events", "lapattn_launches")
 
 STAGES = ("pool", "main", "maps", "out")
 
@@ -82,6 +82,8 @@ def _declare(lib):
     lib.lapattn_forward_stages.restype = ctypes.c_int
     lib.lapattn_set_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
     lib.lapattn_set_stage_events.restype = ctypes.c_int
+    lib.lapattn_launches.argtypes = [dp, ctypes.c_int]
+    lib.lapattn_launches.restype = ctypes.c_int
     return lib
 
 

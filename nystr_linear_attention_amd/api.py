@@ -123,3 +123,11 @@ def forward_stages(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, grid_h:
         res["A"].data_ptr(), res["X"].data_ptr(), res["W"].data_ptr())
     _lib.check(st)
     return res
+
+
+def launches(desc: Desc, q_is_k: bool) -> tuple:
+    """Names of the launch slots a forward call with this descriptor uses."""
+    mask = _lib.lib().lapattn_launches(ctypes.byref(desc), 1 if q_is_k else 0)
+    if mask < 0:
+        raise _lib.LapattnError(mask, _lib.strerror(mask))
+    return tuple(name for s, name in enumerate(_lib.STAGES) if mask >> s & 1)

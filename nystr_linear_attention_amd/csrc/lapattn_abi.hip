@@ -105,9 +105,11 @@ inline Ev slot(int st) {
 
 bool misaligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 != 0; }
 
-int run(const lapattn_desc_t* desc, const Args& a, void* workspace, size_t ws_bytes,
+int run(const lapattn_desc_t* desc, const Args& args, void* workspace, size_t ws_bytes,
         hipStream_t stream) {
   const Plan p = make_plan(desc);
+  Args a = args;
+  a.out_in_main = out_in_main_launch(p, a.shared_qk) ? 1 : 0;
   if (misaligned16(a.q) || misaligned16(a.k) || misaligned16(a.v) || misaligned16(a.out))
     return LAPATTN_ERR_ALIGN;
   if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return LAPATTN_ERR_WORKSPACE;
@@ -141,7 +143,7 @@ int run(const lapattn_desc_t* desc, const Args& a, void* workspace, size_t ws_by
   // W = K_LK V, Y = X W and (when Q != K) the output rows are formed inside the
   // main launch; with Q == K there are no query workgroups and the output
   // product runs as its own launch.
-  if (a.shared_qk && launch_out(p, a, b, stream, slot(LAPATTN_STAGE_OUT)) != hipSuccess)
+  if (!a.out_in_main && launch_out(p, a, b, stream, slot(LAPATTN_STAGE_OUT)) != hipSuccess)
     return LAPATTN_ERR_HIP;
   return LAPATTN_OK;
 }
@@ -206,6 +208,16 @@ int lapattn_check(const lapattn_desc_t* desc, float lambda, float eps, int32_t i
 size_t lapattn_workspace_bytes(const lapattn_desc_t* desc) {
   if (lapattn::check_desc(desc) != LAPATTN_OK) return 0;
   return lapattn::make_plan(desc).total;
+}
+
+int lapattn_launches(const lapattn_desc_t* desc, int q_is_k) {
+  const int st = lapattn::check_desc(desc);
+  if (st != LAPATTN_OK) return st;
+  const lapattn::Plan p = lapattn::make_plan(desc);
+  int mask = (1 << LAPATTN_STAGE_POOL) | (1 << LAPATTN_STAGE_MAIN);
+  if (desc->flags & LAPATTN_FLAG_SERIAL) mask |= 1 << LAPATTN_STAGE_MAPS;
+  if (!lapattn::out_in_main_launch(p, q_is_k ? 1 : 0)) mask |= 1 << LAPATTN_STAGE_OUT;
+  return mask;
 }
 
 int lapattn_set_stage_events(void* const* events, int n) {

@@ -44,6 +44,7 @@ struct Args {
   float lambda, eps;
   int iters;
   int shared_qk;
+  int out_in_main;  // query workgroups form O inside the main launch
   // optional fp32 stage copies (may be null)
   float* st_L;
   float* st_kql;
@@ -63,11 +64,18 @@ struct Ev {
 
 // Stage launchers.  `with_solver` / `with_maps` select which workgroup roles
 // the main launch carries: both (one fused launch), or one each in two
-// launches.  launch_out is needed only when Q and K are the same tensor (no
-// query workgroups to form the output).
+// launches.  launch_out forms O when the main launch does not (Q and K the
+// same tensor, or a grid too large to be resident at once; see
+// out_in_main_launch).
 hipError_t launch_pool(const Plan& p, const Args& a, const Buffers& b, hipStream_t s, Ev ev);
 hipError_t launch_main(const Plan& p, const Args& a, const Buffers& b, bool with_solver,
                        bool with_maps, hipStream_t s, Ev ev);
 hipError_t launch_out(const Plan& p, const Args& a, const Buffers& b, hipStream_t s, Ev ev);
+
+// Whether query workgroups form O inside the main launch: only when there are
+// query workgroups (Q != K) and every workgroup of the launch can be resident
+// at once, so that the ones waiting for Y never keep key workgroups of the
+// same head from starting.
+bool out_in_main_launch(const Plan& p, int shared_qk);
 
 }  // namespace lapattn

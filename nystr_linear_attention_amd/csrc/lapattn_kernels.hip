@@ -185,6 +185,8 @@ struct MainArgs {
   int ns_blocks;      // workgroups [0, ns_blocks) are solver workgroups
   int nQ;             // query workgroups per head, QT tiles each (0 when Q == K)
   int shared_qk;      // Q and K are the same tensor
+  int out_in_main;    // query workgroups wait for Y and write O (else they
+                      // store K_QL and the output launch forms O)
   int kind, bf16, iters;
   float c_exp2, eps;
 };
@@ -913,6 +915,74 @@ __device__ void out_tile(const MainArgs& a, int bh, int t, const float* PT) {
   }
 }
 
+// Squared-L2 kernel values of one 64-token tile against every landmark, with
+// the distance recast as |x|^2 + |l|^2 - 2 x.l and x.l on fp32 MFMA (clamped
+// at zero: the expanded form can round slightly below it).  Wave w computes
+// the 16x16 blocks (tokens 16 (w % 4) .., landmarks 16 jb ..) for
+// jb = w / 4, w / 4 + 2; lane (g, r) supplies coordinates
+// (D/4) g .. (D/4) g + D/4 - 1 of token / landmark r of its blocks, read
+// straight from global memory.  Writes PTt[token][j] and, for key tiles,
+// PJ[j][token]; landmarks j in [m, 16 ceil(m/16)) get exact zeros.
+template <int D, bool BF16>
+__device__ void gauss_tile(const MainArgs& a, const void* src, const float* Lh, int bh, int t,
+                           float* PTt, float* PJ, float* xx, bool key_role) {
+  constexpr int KS = D / 4;  // MFMA sub-steps; floats per lane per operand
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int lr = lane & 15, lg = lane >> 4;
+  const int tb = w & 3;
+  const int m = a.m, N = a.N;
+  const int mby = (m + 15) >> 4;
+  // token operand: KS coordinates of token 16 tb + lr
+  const int n = t * TILE + 16 * tb + lr;
+  const size_t row = static_cast<size_t>(bh) * N + (n < N ? n : N - 1);
+  float av[KS];
+#pragma unroll
+  for (int q = 0; q < KS / 4; ++q) {
+    const f4 u = load4_io(src, row * D + KS * lg + 4 * q, BF16);
+    av[4 * q] = u[0];
+    av[4 * q + 1] = u[1];
+    av[4 * q + 2] = u[2];
+    av[4 * q + 3] = u[3];
+  }
+  float px = 0.f;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) px = fmaf(av[s], av[s], px);
+  px = sum_over_g(px);
+  if (w < 4 && lg == 0) xx[16 * tb + lr] = px;
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int jb = (w >> 2) + 2 * h;
+    if (jb < mby) {
+      const int j = 16 * jb + lr;
+      float bv[KS];
+#pragma unroll
+      for (int q = 0; q < KS / 4; ++q) {
+        const f4 u = j < m ? ld4(Lh + j * D + KS * lg + 4 * q) : f4{0.f, 0.f, 0.f, 0.f};
+        bv[4 * q] = u[0];
+        bv[4 * q + 1] = u[1];
+        bv[4 * q + 2] = u[2];
+        bv[4 * q + 3] = u[3];
+      }
+      float pl = 0.f;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) pl = fmaf(bv[s], bv[s], pl);
+      pl = sum_over_g(pl);
+      f4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) c = mfma4(av[s], bv[s], c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tt = 16 * tb + 4 * lg + i;
+        const float d = fmaxf(fmaf(-2.0f, c[i], xx[tt] + pl), 0.0f);
+        const float kv = (j < m && t * TILE + tt < N) ? exp2f(d * a.c_exp2) : 0.f;
+        PTt[tt * LS + j] = kv;
+        if (key_role) PJ[j * LS + tt] = kv;
+      }
+    }
+  }
+}
+
 template <int D, int KIND, bool BF16>
 __device__ void map_role(const MainArgs& a, const void* __restrict__ q, const void* __restrict__ k,
                          const void* __restrict__ v, const float* __restrict__ Lw, int b,
@@ -921,6 +991,7 @@ __device__ void map_role(const MainArgs& a, const void* __restrict__ q, const vo
   float* PJ = smem;                // [64 landmarks][LS]: P[j][token]
   float* PT = smem + MP * LS;      // [64 tokens][LS]:    P[j] of token at [token][j]
   float* VT = smem + 2 * MP * LS;  // [D][LS]:            V[token][c] at [c][token]
+  float* xx = smem + 3 * MP * LS;  // [64]: squared norms of a tile's tokens (Gaussian)
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int lr = lane & 15, lg = lane >> 4;
   const int m = a.m, N = a.N;
@@ -955,7 +1026,7 @@ __device__ void map_role(const MainArgs& a, const void* __restrict__ q, const vo
   }
   // K_QL goes to global memory only when Q == K (the output launch reads
   // it); query tiles keep theirs in LDS and form their output rows here.
-  const bool store_kql = key_role && a.shared_qk;
+  const bool store_kql = key_role ? a.shared_qk != 0 : a.out_in_main == 0;
   const bool stage_kql = a.st_kql && (!key_role || a.shared_qk);
   const void* src = key_role ? k : q;
   const int mby = (m + 15) >> 4;
@@ -977,8 +1048,8 @@ __device__ void map_role(const MainArgs& a, const void* __restrict__ q, const vo
     float* PTt = (key_role || t == t_beg) ? PT : VT;  // this tile's K_QL rows
     const int n = t * TILE + lane;
     const bool valid = n < N;
-    float x[D];
-    load_row<D>(src, static_cast<size_t>(bh) * N + (valid ? n : N - 1), BF16, x);
+    float x[KIND == 0 ? D : 1];
+    if constexpr (KIND == 0) load_row<D>(src, static_cast<size_t>(bh) * N + (valid ? n : N - 1), BF16, x);
     if (key_role) {
       // V tile -> VT[c][token]; thread (c, group of TPT tokens); all loads
       // are issued before the LDS writes (rows past N are clamped, then zeroed)
@@ -996,20 +1067,24 @@ __device__ void map_role(const MainArgs& a, const void* __restrict__ q, const vo
         VT[c * LS + tok] = t * TILE + tok < N ? vv[u] : 0.f;
       }
     }
-    // landmarks two at a time (their scalar loads overlap); an odd last
-    // landmark is paired with itself and stored once
-    for (int j = jb; j < je; j += 2) {
-      const int j1 = j + 1 < je ? j + 1 : j;
-      float d0, d1;
-      dist_to2<D, KIND>(x, Lh + j * D, Lh + j1 * D, d0, d1);
-      const float k0 = valid ? exp2f(d0 * a.c_exp2) : 0.f;
-      const float k1 = valid ? exp2f(d1 * a.c_exp2) : 0.f;
-      if (key_role) {
-        PJ[j * LS + lane] = k0;
-        PJ[j1 * LS + lane] = k1;
+    if constexpr (KIND == 0) {
+      // L1 distances on VALU: landmarks two at a time (their scalar loads
+      // overlap); an odd last landmark is paired with itself and stored once
+      for (int j = jb; j < je; j += 2) {
+        const int j1 = j + 1 < je ? j + 1 : j;
+        float d0, d1;
+        dist_to2<D, KIND>(x, Lh + j * D, Lh + j1 * D, d0, d1);
+        const float k0 = valid ? exp2f(d0 * a.c_exp2) : 0.f;
+        const float k1 = valid ? exp2f(d1 * a.c_exp2) : 0.f;
+        if (key_role) {
+          PJ[j * LS + lane] = k0;
+          PJ[j1 * LS + lane] = k1;
+        }
+        PTt[lane * LS + j] = k0;
+        PTt[lane * LS + j1] = k1;
       }
-      PTt[lane * LS + j] = k0;
-      PTt[lane * LS + j1] = k1;
+    } else {
+      gauss_tile<D, BF16>(a, src, Lh, bh, t, PTt, PJ, xx, key_role);
     }
     __syncthreads();
     if (store_kql) {
@@ -1060,6 +1135,7 @@ __device__ void map_role(const MainArgs& a, const void* __restrict__ q, const vo
     __syncthreads();
   }
   if (!key_role) {
+    if (!a.out_in_main) return;  // K_QL stored; the output launch forms O
     // the tiles' K_QL rows are still in LDS: wait for Y of the head
     wait_flag(flag_y(a, bh), a.sync);
     out_tile<D>(a, bh, t_beg, PT);
@@ -1092,7 +1168,7 @@ __global__ __launch_bounds__(WGM) void main_kernel(MainArgs a, const void* __res
                                                     const void* __restrict__ k,
                                                     const void* __restrict__ v,
                                                     const float* __restrict__ L) {
-  constexpr int MAP_SMEM = 3 * MP * LS;
+  constexpr int MAP_SMEM = 3 * MP * LS + TILE;
   // solver: the Newton-Schulz layout plus a W^T copy; landmark staging
   // while A is built
   constexpr int SOLVER_A = NsGeom<MB>::SMEM + D * (MP + 4);
@@ -1300,6 +1376,15 @@ hipError_t launch_out_d(const Plan& p, const Args& a, const Buffers& b, hipStrea
 
 }  // namespace
 
+bool out_in_main_launch(const Plan& p, int shared_qk) {
+  // 256 CUs x 2 main-kernel workgroups (LDS and registers allow two), with
+  // some margin
+  constexpr long kResident = 448;
+  if (shared_qk) return false;
+  const long nQ = (p.nT + QT - 1) / QT;
+  return static_cast<long>(p.BH) * (1 + p.nP + nQ) <= kResident;
+}
+
 hipError_t launch_pool(const Plan& p, const Args& a, const Buffers& b, hipStream_t s, Ev ev) {
   switch (p.D) {
     case 16: return launch_pool_d<16>(p, a, b, s, ev);
@@ -1336,6 +1421,7 @@ hipError_t launch_main(const Plan& p, const Args& a, const Buffers& b, bool with
   ma.nP = p.nP;
   ma.mpad = p.mpad;
   ma.shared_qk = a.shared_qk;
+  ma.out_in_main = a.out_in_main;
   ma.nQ = a.shared_qk ? 0 : (p.nT + QT - 1) / QT;
   ma.kind = p.kernel;
   ma.bf16 = p.bf16;

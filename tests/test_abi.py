@@ -135,3 +135,22 @@ def test_forward_rejects_before_launch():
                                            FAKE, FAKE, 1 << 30, None, None, None, None, None,
                                            None, None)
     assert st == _lib.ERR_NULL
+
+
+def test_launch_slots():
+    """Launch plan per descriptor: pool and main always; the map launch only
+    in the serial plan; the output launch when Q == K or when the main grid
+    cannot be resident at once."""
+    import torch
+
+    from nystr_linear_attention_amd import api
+    small = api.make_desc(8, 1, 56, 56, 64, 8, 8, "laplacian", torch.float32)
+    assert api.launches(small, False) == ("pool", "main")
+    assert api.launches(small, True) == ("pool", "main", "out")
+    serial = api.make_desc(8, 1, 56, 56, 64, 8, 8, "laplacian", torch.float32, serial=True)
+    assert api.launches(serial, False) == ("pool", "main", "maps")
+    many = api.make_desc(32, 5, 28, 28, 64, 4, 4, "laplacian", torch.float32)
+    assert api.launches(many, False) == ("pool", "main", "out")
+    bad = api.make_desc(8, 1, 56, 55, 64, 8, 8, "laplacian", torch.float32)
+    with pytest.raises(_lib.LapattnError):
+        api.launches(bad, False)

@@ -127,8 +127,11 @@ def test_kernel_event_hook(serial):
         timed = run_gpu(w, x, serial=serial)["O"]
         assert lib.lapattn_set_stage_events(None, 0) == _lib.OK
         torch.cuda.synchronize()
+        desc = api.make_desc(w.B, w.H, w.grid_h, w.grid_w, w.d, w.pool_h, w.pool_w, w.kernel,
+                             torch.float32, serial=serial)
+        used = api.launches(desc, w.shared_qk)
         for s, name in enumerate(_lib.STAGES):
-            if (name == "maps" and not serial) or (name == "out" and not w.shared_qk):
+            if name not in used:
                 continue            # slots without a launch in this call
             ms = ctypes.c_float()
             assert rt.hipEventElapsedTime(ctypes.byref(ms), evs[2 * s], evs[2 * s + 1]) == 0, name
