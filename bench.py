@@ -71,7 +71,7 @@ class HipEvents:
 
 
 def work(w):
-    """Algorithmic work of the launches of one forward call (see DESIGN.md).
+    """Algorithmic work of the launches of one forward call.
 
     Flops: 3 per coordinate pair of an L1 or squared-L2 distance (difference,
     |.| or square, accumulate); 2 per multiply-add of a contraction.  Bytes:
@@ -192,9 +192,9 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported: this build runs on one "
+        print(f"bench.py: --gpus {args.gpus} is not supported: the library runs on one "
               "GPU only (heads are independent, so B*H would shard across GPUs with no "
-              "exchange; see DESIGN.md).", file=sys.stderr)
+              "exchange).", file=sys.stderr)
         return 2
     if args.copy_calibration:
         return copy_calibration(args.copy_calibration)

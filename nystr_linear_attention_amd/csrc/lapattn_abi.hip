@@ -58,10 +58,8 @@ Plan make_plan(const lapattn_desc_t* d) {
   p.m = (p.gh / p.ph) * (p.gw / p.pw);
   p.BH = p.B * p.H;
   p.mpad = 16 * ((p.m + 15) / 16);
-  // Solver interior: whole 16x16 blocks.  A single extra row/column
-  // (m = 16 MB + 1, e.g. 7x7 landmarks) goes to VALU; otherwise the matrix is
-  // zero padded up to whole blocks.
-  p.ns_mb = (p.m % 16 == 1) ? p.m / 16 : (p.m + 15) / 16;
+  // Solver: the matrix zero padded up to whole 16x16 blocks.
+  p.ns_mb = (p.m + 15) / 16;
   p.nT = (p.N + 63) / 64;
   // Key-side workgroups cover S tiles each so that a head has at most 32 W
   // partials.
@@ -84,7 +82,7 @@ Plan make_plan(const lapattn_desc_t* d) {
   p.off_yt = off;
   off = align_up(off + BH * p.D * MP * f);
   p.off_sync = off;
-  off = align_up(off + (4 + 3 * BH) * sizeof(unsigned));
+  off = align_up(off + kSyncHead * (BH + 1) * sizeof(unsigned));
   p.total = off;
   return p;
 }

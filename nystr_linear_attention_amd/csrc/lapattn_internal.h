@@ -10,6 +10,8 @@ namespace lapattn {
 // Small per-head matrices (A, X, W^T, Y^T) are stored padded to MP columns;
 // padding holds exact zeros.
 constexpr int MP = 64;
+// Hand-off words per head (and once more for the words of the whole call).
+constexpr int kSyncHead = 128;
 
 struct Plan {
   int B, H, gh, gw, D, ph, pw;
@@ -33,7 +35,7 @@ struct Buffers {
   float* x;      // [BH][MP][MP]   Newton-Schulz result
   float* wt;     // [BH][D][MP]    W^T = (K_LK V)^T, zero for columns >= m
   float* yt;     // [BH][D][MP]    Y^T = (X W)^T
-  unsigned* sync;  // [4 + 3 BH]   hand-off counters (see the main kernel)
+  unsigned* sync;  // [kSyncHead (BH + 1)] hand-off words (see the main kernel)
 };
 
 struct Args {

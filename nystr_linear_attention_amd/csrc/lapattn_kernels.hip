@@ -37,6 +37,7 @@
 #include <stdint.h>
 
 #include <tuple>
+#include <type_traits>
 #include <utility>
 
 #include "lapattn_internal.h"
@@ -172,10 +173,9 @@ struct MainArgs {
   float* wt;          // [BH][D][MP]  W^T (reduced partials)
   float* yt;          // [BH][D][MP]  Y^T = (X W)^T
   void* out;          // [BH][N][D]   O (query workgroups write it)
-  unsigned* sync;     // hand-off words, zeroed by the pool launch:
-                      //   [0] count of bounded waits that timed out,
-                      //   [4 + bh] key-workgroup arrivals, [4 + BH + bh]
-                      //   arrivals of W and X, [4 + 2 BH + bh] Y-ready flag
+  unsigned* sync;     // hand-off words, zeroed by the pool launch: [0] counts
+                      // bounded waits that timed out; head bh owns the
+                      // kSyncHead words from kSyncHead (bh + 1) (see below)
   float* st_a;
   float* st_x;
   float* st_kql;
@@ -192,12 +192,22 @@ struct MainArgs {
 };
 
 // ---------------------------------------------------------------------------
-// Hand-offs inside the main launch.  Per head: the key workgroups publish W^T
-// partials and count their arrivals; the last one reduces them (fixed order,
-// so the result does not depend on which one is last) and publishes W^T.  W^T
-// and X (from the solver workgroup) each count one arrival; whichever is
-// second forms Y^T = W^T X^T and raises the head's Y-ready flag, on which the
-// query workgroups wait before forming their output rows.
+// Hand-offs inside the main launch.  Per head, the key workgroups publish
+// W^T partials and the solver workgroup publishes X.  Then either
+//  - (query workgroups form the output rows here) each key workgroup raises
+//    its own ready flag; query workgroup u < R reduces lines [u LPS, ..) of
+//    W^T (fixed partial order, so the result does not depend on timing) and
+//    raises its slice flag; every query workgroup waits for all slices and
+//    X, forms Y^T = W^T X^T in its LDS and writes its output rows; or
+//  - (the output launch forms O) the key workgroups count their arrivals;
+//    the last one reduces the partials (same order) and publishes W^T.  W^T
+//    and X each count one arrival; whichever is second forms Y^T for the
+//    output launch.
+// Words of head bh (kSyncHead from kSyncHead (bh + 1), each group on its own
+// cache lines): [0, 32) key ready flags, [32, 64) W^T slice flags, [64] X
+// ready, [96] key arrivals, [97] arrivals of W and X, [98] Y ready.
+// Flags are plain device-scope stores (no read-modify-write on a shared word,
+// which serialises at memory when many workgroups arrive at once).
 //
 // Coherence across XCDs without cache-wide fences: everything handed over
 // inside the launch (partials, W^T, X, Y^T) is stored with device-scope
@@ -220,13 +230,15 @@ struct MainArgs {
 // ---------------------------------------------------------------------------
 constexpr long long kWaitTicks = 2000000;  // 20 ms of the 100 MHz device clock
 
-__device__ __forceinline__ unsigned* cnt_w(const MainArgs& a, int bh) { return a.sync + 4 + bh; }
-__device__ __forceinline__ unsigned* cnt_y(const MainArgs& a, int bh) {
-  return a.sync + 4 + a.BH + bh;
+__device__ __forceinline__ unsigned* head_sync(const MainArgs& a, int bh) {
+  return a.sync + kSyncHead * (bh + 1);
 }
-__device__ __forceinline__ unsigned* flag_y(const MainArgs& a, int bh) {
-  return a.sync + 4 + 2 * a.BH + bh;
-}
+__device__ __forceinline__ unsigned* key_flags(const MainArgs& a, int bh) { return head_sync(a, bh); }
+__device__ __forceinline__ unsigned* slice_flags(const MainArgs& a, int bh) { return head_sync(a, bh) + 32; }
+__device__ __forceinline__ unsigned* flag_x(const MainArgs& a, int bh) { return head_sync(a, bh) + 64; }
+__device__ __forceinline__ unsigned* cnt_w(const MainArgs& a, int bh) { return head_sync(a, bh) + 96; }
+__device__ __forceinline__ unsigned* cnt_y(const MainArgs& a, int bh) { return head_sync(a, bh) + 97; }
+__device__ __forceinline__ unsigned* flag_y(const MainArgs& a, int bh) { return head_sync(a, bh) + 98; }
 
 __device__ __forceinline__ void st_dev(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -245,6 +257,7 @@ __device__ __forceinline__ unsigned publish_arrive(unsigned* ctr) {
   return old_s;
 }
 
+// Completes this workgroup's device-scope stores, then sets *flag.
 __device__ __forceinline__ void raise_flag(unsigned* flag) {
   drain_stores();
   __syncthreads();
@@ -265,13 +278,37 @@ __device__ __forceinline__ void wait_flag(unsigned* flag, unsigned* timeouts) {
   __syncthreads();
 }
 
+// Waits until flags[0 .. n) (n <= 32) and, when given, *extra are all set:
+// lane l of wave 0 polls one word; bounded in time like wait_flag.
+__device__ __forceinline__ void wait_flags(const unsigned* flags, int n, const unsigned* extra,
+                                           unsigned* timeouts) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const unsigned* p = lane < n ? flags + lane : (lane == 63 ? extra : nullptr);
+    bool done = p == nullptr;
+    const long long t0 = wall_clock64();
+    while (true) {
+      if (!done) done = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+      if (__all(done)) break;
+      if (wall_clock64() - t0 > kWaitTicks) {
+        if (lane == 0) __hip_atomic_fetch_add(timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  __syncthreads();
+}
+
 // Y^T = W^T X^T for one head on fp32 MFMA, D x 64 outputs (columns >= m are
 // zero because X is zero padded).  W^T rows have stride wts; X has xrows
-// rows of stride xs (columns >= xs and rows >= xrows read as zero), so the
+// rows of stride xs (columns >= xcols and rows >= xrows read as zero), so the
 // operands may come from global memory or from the solver's LDS: the same
-// values in the same MFMA order give the same Y^T either way.
-template <int D>
-__device__ void compute_y(const float* wt, int wts, const float* x, int xs, int xrows,
+// values in the same MFMA order give the same Y^T either way.  The result
+// goes to global memory (device-scope stores, row stride MP) or, with
+// TO_LDS, to LDS (row stride LS).
+template <int D, bool TO_LDS = false>
+__device__ void compute_y(const float* wt, int wts, const float* x, int xs, int xrows, int xcols,
                           float* yg) {
   constexpr int CBN = D / 16;
   constexpr int NBLK = 4 * CBN;  // 16x16 output blocks
@@ -290,7 +327,7 @@ __device__ void compute_y(const float* wt, int wts, const float* x, int xs, int 
       for (int q = 0; q < 4; ++q) {
         av[q] = ld4(ar + 4 * q);
         const int c0 = 16 * lg + 4 * q;
-        bv[q] = (xr < xrows && c0 < xs) ? ld4(x + xr * xs + c0) : f4{0.f, 0.f, 0.f, 0.f};
+        bv[q] = (xr < xrows && c0 < xcols) ? ld4(x + xr * xs + c0) : f4{0.f, 0.f, 0.f, 0.f};
       }
       f4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -298,7 +335,10 @@ __device__ void compute_y(const float* wt, int wts, const float* x, int xs, int 
 #pragma unroll
         for (int h = 0; h < 4; ++h) c = mfma4(av[q][h], bv[q][h], c);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) st_dev(yg + (16 * cb + 4 * lg + i) * MP + 16 * jb + lr, c[i]);
+      for (int i = 0; i < 4; ++i) {
+        if (TO_LDS) yg[(16 * cb + 4 * lg + i) * LS + 16 * jb + lr] = c[i];
+        else st_dev(yg + (16 * cb + 4 * lg + i) * MP + 16 * jb + lr, c[i]);
+      }
     }
   }
 }
@@ -306,7 +346,7 @@ __device__ void compute_y(const float* wt, int wts, const float* x, int xs, int 
 template <int D>
 __device__ __forceinline__ void compute_y_global(const MainArgs& a, int bh) {
   compute_y<D>(a.wt + static_cast<size_t>(bh) * D * MP, MP,
-               a.xw + static_cast<size_t>(bh) * MP * MP, MP, MP,
+               a.xw + static_cast<size_t>(bh) * MP * MP, MP, MP, MP,
                a.yt + static_cast<size_t>(bh) * D * MP);
 }
 
@@ -323,48 +363,64 @@ __device__ void arrive_y(const MainArgs& a, int bh) {
 // Solver role: X_0 = alpha A, X_{t+1} = 2 X_t - X_t (A X_t), exactly `iters`
 // steps, one workgroup per head, everything in LDS and registers.
 //
-// m = 16 MB + r with r <= 1 border row/column (other sizes are zero padded to
-// 16 MB and r = 0; the border code is written for any r <= 4).  Both products are full and unsymmetrised:
-// forcing the iterates symmetric turns the quadratic error contraction of the
-// Newton step into a linear map with gain up to (1 + cond(A)) / 2, which
-// diverges near convergence for ill-conditioned A.
+// Both products are full and unsymmetrised: forcing the iterates symmetric
+// turns the quadratic error contraction of the Newton step into a linear map
+// with gain up to (1 + cond(A)) / 2, which diverges near convergence for
+// ill-conditioned A.
 //
-// Interior wave c < MB owns column block c (16 columns) of X_t, of
-// T = A X_t and of X_{t+1}:
+// The m x m problem is zero padded to n = 16 MB, MB = ceil(m / 16).  The
+// padding rows and columns of A, and so of X_0 = alpha A and of every later
+// iterate, are zero, and the leading m x m block evolves exactly as the
+// unpadded iteration.
+//
+// Products run on fp16 MFMA (16x16x32, fp32 accumulation) with each operand
+// split in two: x = hi + lo, hi = fp16(x), lo = fp16(x - hi), both rounded
+// to nearest, after scaling by a power of two that keeps every entry inside
+// fp16 range.  A product is formed as hi hi + lo hi + hi lo: about 22
+// significant bits per operand (fp32 has 24) at a quarter of the matrix-core
+// cycles of fp32 MFMA.  The scales are exact powers of two, removed from the
+// fp32 accumulators:
+//   A   : 2^eA with max|A| 2^eA < 2^14;
+//   T   : 2^14.  T = A X_t is a polynomial in A with eigenvalues in (0, 1]
+//         (mu -> 2 mu - mu^2 from mu = alpha lambda^2 <= 1), so |T_ij| <= 1;
+//   X_t : 2^e_t, shared by the workgroup, with max|X_{t-2}| 2^e_t < 2^7 (the
+//         column-block maxima are published in LDS).  X_t is positive
+//         semi-definite with spectral norm at most twice that of X_{t-1}, and
+//         max|X| >= ||X||_2 / n, so max|X_t| 2^e_t < 4 n 2^7 <= 2^15 for
+//         n <= 64: no overflow.
+//
+// Wave c < MB owns column block c (16 columns) of X_t, of T = A X_t and of
+// X_{t+1}:
 //   T[:, c]       = A X_t[:, c]              (needs only its own X columns)
 //   X_{t+1}[:, c] = 2 X_t[:, c] - X_t T[:, c] (needs the rows of X_t)
-// With the contraction index of MFMA sub-step s = 4 i + j taken as
-// k = 16 i + 4 g + j for lane (g, lr), the accumulator layout of a 16 x 16
-// block (lane (g, lr) holds rows 4 g + j of column lr) is exactly the B
-// operand layout, so X_t[:, c] and T[:, c] never leave registers; the A
-// operands (rows of A, rows of X_t) are 16-byte LDS reads.  Only the rows of
-// X_t are exchanged, once per step: one barrier per step.
-// The border: interior waves compute T and X_{t+1} on the border rows of
-// their own columns (VALU dot products and a 4-lane reduction); border wave
-// b < r computes border column 16 MB + b of T and X_{t+1} (one row per lane).
-// Border terms of the interior blocks (k >= 16 MB) initialise the
-// accumulators.  A is bitwise symmetric (|a - b| = |b - a| term by term), so
-// its border columns are read as rows.
-//
-// LDS (floats, row stride SLS): A, X[2] (row-major, double buffered),
-// XTB[2][4][64] (border columns of X_t, transposed), TX[4][64] (border columns
-// of T, private to each border wave), scalars.
+// Chunk p of the contraction covers 16-row blocks 2p and 2p + 1: slot s of
+// lane (g, lr) takes k = 16 (2p + s / 4) + 4 g + s % 4.  The accumulators of
+// blocks 2p and 2p + 1 (lane (g, lr) holds rows 4 g + j of column lr) are then
+// exactly the B operand, so X_t[:, c] and T[:, c] stay in registers, in fp32
+// and split.  The A operands (rows of A, rows of X_t) come from half-precision
+// arrays in LDS whose columns are permuted (hpos) so that a lane's 8 values
+// are one 16-byte read.  Only X_t is exchanged, once per step: one barrier
+// per step.
 // ---------------------------------------------------------------------------
-template <int MB>
-struct NsGeom {
-  static constexpr int N16 = 16 * MB;               // interior size
-  // rows and row stride: the interior plus up to 4 border rows / columns.
-  // Strides are 4 or 20 (mod 32) floats, so 16-byte reads of 8 consecutive
-  // rows fall on distinct LDS banks.
-  static constexpr int ROWS = MB == 4 ? 64 : N16 + 4;
-  static constexpr int SLS = MB == 4 ? 68 : N16 + 4;
-  static constexpr int MAT = ROWS * SLS;
-  static constexpr int NQ = ROWS / 4;               // float4 per border dot
-  static constexpr int OFF_XTB = 3 * MAT;
-  static constexpr int OFF_TX = OFF_XTB + 2 * 4 * 64;
-  static constexpr int OFF_RED = OFF_TX + 4 * 64;
-  static constexpr int SMEM = OFF_RED + 4;
-};
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f4 mfma_h(u32x4 a, u32x4 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a), __builtin_bit_cast(h8, b),
+                                                 c, 0, 0, 0);
+}
+
+// Two values into packed fp16 high parts and packed fp16 remainders.
+__device__ __forceinline__ void split2(float x0, float x1, unsigned& hi, unsigned& lo) {
+  const h2 h = __builtin_convertvector(f2{x0, x1}, h2);
+  const float r0 = x0 - static_cast<float>(h[0]);
+  const float r1 = x1 - static_cast<float>(h[1]);
+  hi = __builtin_bit_cast(unsigned, h);
+  lo = __builtin_bit_cast(unsigned, __builtin_convertvector(f2{r0, r1}, h2));
+}
 
 // Sum over the 4 lanes (g = 0..3) that share lr, on VALU: a lane-half swap
 // with itself leaves v[l] + v[l ^ 32] as the sum of the two results (and
@@ -376,259 +432,231 @@ __device__ __forceinline__ float sum_over_g(float v) {
   return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
-template <int MB, int R>
-__device__ void ns_interior_wave(const MainArgs& a, float* smem, int c, int lane) {
-  constexpr int r = R;  // border width
-  using G = NsGeom<MB>;
-  constexpr int S = G::SLS, N16 = G::N16;
-  // Buffers are addressed by offsets from the shared base (never through a
-  // table of pointers) so that every access stays an LDS instruction.
-  const float* A = smem;
-  const float* X0 = smem + G::MAT;
-  const int lr = lane & 15, lg = lane >> 4;
-  const int col = 16 * c + lr;
+// Maximum over the 64 lanes of a wave, in every lane.
+__device__ __forceinline__ unsigned wave_max_u(unsigned v) {
+  const auto h = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  v = max(h[0], h[1]);
+  const auto q = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max(q[0], q[1]);
+  v = max(v, static_cast<unsigned>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0xB1, 0xF, 0xF, false)));
+  v = max(v, static_cast<unsigned>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x4E, 0xF, 0xF, false)));
+  v = max(v, static_cast<unsigned>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x141, 0xF, 0xF, false)));
+  v = max(v, static_cast<unsigned>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x140, 0xF, 0xF, false)));
+  return v;
+}
 
-  // own columns of X_0 (accumulator layout) and of its border rows
-  f4 xc[MB];
-  float xbr[4];
-#pragma unroll
-  for (int i = 0; i < MB; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) xc[i][j] = X0[(16 * i + 4 * lg + j) * S + col];
-#pragma unroll
-  for (int b = 0; b < 4; ++b) xbr[b] = b < r ? X0[(N16 + b) * S + col] : 0.f;
-  // constant operands: the border rows of A at the own k (for T's border
-  // rows), A's border corner
-  f4 abr[4][MB];
-  float acor[4][4];
-#pragma unroll
-  for (int b = 0; b < 4; ++b)
-#pragma unroll
-    for (int i = 0; i < MB; ++i)
-      abr[b][i] = b < r ? ld4(A + (N16 + b) * S + 16 * i + 4 * lg) : f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int b = 0; b < 4; ++b)
-#pragma unroll
-    for (int bb = 0; bb < 4; ++bb) acor[b][bb] = (b < r && bb < r) ? A[(N16 + b) * S + N16 + bb] : 0.f;
+template <int MB, int D>
+struct NsGeom {
+  static constexpr int N16 = 16 * MB;          // padded size
+  static constexpr int NC = (MB + 1) / 2;      // 32-wide contraction chunks
+  static constexpr bool ODD = (MB & 1) != 0;   // the last chunk holds one block
+  // Half-precision arrays: N16 rows of RSW 32-bit words.  RSW / 4 is odd, so
+  // the 16-byte reads of 16 consecutive rows fall on distinct bank groups.
+  static constexpr int RSW = 8 * MB + 4;
+  static constexpr int RSH = 2 * RSW;          // row stride in halves
+  static constexpr int ARR = N16 * RSW;        // words per array
+  static constexpr int SX = N16 + 4;           // fp32 row stride (A while set up, final X)
+  static constexpr int OFF_AH = 0;             // A hi, A lo
+  static constexpr int OFF_AL = ARR;
+  static constexpr int OFF_X = 2 * ARR;        // [parity][hi, lo] X_t halves
+  static constexpr int OFF_SLOT = 6 * ARR;     // [parity][4][64] column-block maxima
+                                               // of X, one copy per lane
+  static constexpr int OFF_RED = OFF_SLOT + 512; // row-sum maximum, W^T flag, max|A|
+  static constexpr int OFF_WT = OFF_RED + 4;   // W^T copy; landmarks while A is built
+  static constexpr int WLS = MP + 4;           // row stride of the W^T copy
+  static constexpr int TAIL = D * WLS > MP * (D + 4) ? D * WLS : MP * (D + 4);
+  static constexpr int SMEM = OFF_WT + TAIL;
+  static_assert(N16 * SX <= 2 * ARR, "fp32 matrix fits one parity of the X halves");
+};
 
-  // Output blocks are computed one after another (a single accumulation
-  // chain runs at the full MFMA rate), so that each block's epilogue and the
-  // next block's operand reads overlap the running MFMAs.  The A operand of
-  // the first block of phase 1 is constant and is read before the barrier.
-  f4 aop[MB];
-#pragma unroll
-  for (int i = 0; i < MB; ++i) aop[i] = ld4(A + lr * S + 16 * i + 4 * lg);
+// Position (in halves) of column k in a row of a half-precision array.  The
+// 16-column blocks go in pairs (2p, 2p + 1); within pair p, lane group q's
+// four columns of block 2p and four of block 2p + 1 are 8 consecutive
+// halves.  An odd last block stands alone, 4 halves per lane group.
+template <int MB>
+__device__ __forceinline__ int hpos(int k) {
+  const int c = k >> 4, q = (k >> 2) & 3, j = k & 3;
+  if ((MB & 1) && c == MB - 1) return 16 * c + 4 * q + j;
+  return 32 * (c >> 1) + 8 * q + 4 * (c & 1) + j;
+}
 
-  for (int t = 0; t < a.iters; ++t) {
-    const int cb = t & 1;
-    const float* cur = smem + G::MAT * (1 + cb);
-    float* nxt = smem + G::MAT * (2 - cb);
-    const float* xtb = smem + G::OFF_XTB + 256 * cb;
-
-    // reads that only need X_t: the phase-2 operand of block 0, the border
-    // columns of X_t at the own rows, the border rows of X_t at the own k
-    f4 xop[MB];
+// A operand of one 16-row block: row `row` of the arrays at word offsets
+// offh (hi) and offl (lo), chunks 0..NC-1 (the lone block of an odd last
+// chunk fills slots 0..3, slots 4..7 are zero).
+template <int MB, int D>
+__device__ __forceinline__ void load_op(const float* smem, int offh, int offl, int row, int lg,
+                                        u32x4* h, u32x4* l) {
+  using G = NsGeom<MB, D>;
+  const int base = row * G::RSW;
 #pragma unroll
-    for (int i = 0; i < MB; ++i) xop[i] = ld4(cur + lr * S + 16 * i + 4 * lg);
-    f4 xbc[4][MB], xbrow[4][MB];
-    float xcor[4][4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int i = 0; i < MB; ++i) {
-        xbc[b][i] = b < r ? ld4(xtb + 64 * b + 16 * i + 4 * lg) : f4{0.f, 0.f, 0.f, 0.f};
-        xbrow[b][i] = b < r ? ld4(cur + (N16 + b) * S + 16 * i + 4 * lg) : f4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int bb = 0; bb < 4; ++bb) xcor[b][bb] = (b < r && bb < r) ? cur[(N16 + b) * S + N16 + bb] : 0.f;
-
-    // phase 1: T[:, c] = A X_t[:, c], block by block; the border terms
-    // (k >= 16 MB) initialise each block: A[rows][N16+b] = A[N16+b][rows].
-    // The scheduling fences keep every operand read ahead of the MFMAs of
-    // the block before the one that needs it, and put VALU work between
-    // MFMAs, so the matrix pipe never waits on LDS.
-    f4 tc[MB];
-    float tbr[4];
-#pragma unroll
-    for (int ip = 0; ip < MB; ++ip) {
-      f4 anx[MB];
-      if (ip + 1 < MB) {
-#pragma unroll
-        for (int i = 0; i < MB; ++i) anx[i] = ld4(A + (16 * (ip + 1) + lr) * S + 16 * i + 4 * lg);
-      }
-      f4 t4 = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-        if (b < r) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) t4[j] = fmaf(abr[b][ip][j], xbr[b], t4[j]);
-        }
-      __builtin_amdgcn_sched_barrier(0);
-      t4 = mfma4(aop[0][0], xc[0][0], t4);
-      t4 = mfma4(aop[0][1], xc[0][1], t4);
-      __builtin_amdgcn_sched_barrier(0);
-      if (ip == 0) {
-        // T on the border rows of the own columns:
-        // T[N16+b][col] = sum_k A[N16+b][k] X_t[k][col]
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          tbr[b] = 0.f;
-          if (b < r) {
-            float p = 0.f;
-#pragma unroll
-            for (int i = 0; i < MB; ++i)
-#pragma unroll
-              for (int j = 0; j < 4; ++j) p = fmaf(abr[b][i][j], xc[i][j], p);
-            p = sum_over_g(p);
-#pragma unroll
-            for (int bb = 0; bb < 4; ++bb)
-              if (bb < r) p = fmaf(acor[b][bb], xbr[bb], p);
-            tbr[b] = p;
-          }
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int s4 = 2; s4 < 4 * MB; ++s4) t4 = mfma4(aop[s4 / 4][s4 % 4], xc[s4 / 4][s4 % 4], t4);
-      __builtin_amdgcn_sched_barrier(0);
-      tc[ip] = t4;
-      if (ip + 1 < MB) {
-#pragma unroll
-        for (int i = 0; i < MB; ++i) aop[i] = anx[i];
-      }
+  for (int p = 0; p < G::NC; ++p) {
+    if (G::ODD && p == G::NC - 1) {
+      const u32x2 vh = *reinterpret_cast<const u32x2*>(smem + offh + base + 16 * p + 2 * lg);
+      const u32x2 vl = *reinterpret_cast<const u32x2*>(smem + offl + base + 16 * p + 2 * lg);
+      h[p] = u32x4{vh[0], vh[1], 0u, 0u};
+      l[p] = u32x4{vl[0], vl[1], 0u, 0u};
+    } else {
+      h[p] = *reinterpret_cast<const u32x4*>(smem + offh + base + 16 * p + 4 * lg);
+      l[p] = *reinterpret_cast<const u32x4*>(smem + offl + base + 16 * p + 4 * lg);
     }
-
-    // phase 2: X_{t+1}[:, c] = 2 X_t[:, c] - X_t T[:, c], block by block;
-    // border terms X_t[rows][N16+b] T[N16+b][col] initialise each block.
-    // The epilogue of block ip - 1 (2 X - acc, row-major LDS store) runs
-    // between the MFMAs of block ip.
-    float xbn[4];
-    f4 prev = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ip = 0; ip < MB; ++ip) {
-      f4 xnx[MB];
-      if (ip + 1 < MB) {
-#pragma unroll
-        for (int i = 0; i < MB; ++i) xnx[i] = ld4(cur + (16 * (ip + 1) + lr) * S + 16 * i + 4 * lg);
-      } else {
-        // the constant phase-1 operand of the next step (block 0)
-#pragma unroll
-        for (int i = 0; i < MB; ++i) xnx[i] = ld4(A + lr * S + 16 * i + 4 * lg);
-      }
-      f4 t4 = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-        if (b < r) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) t4[j] = fmaf(xbc[b][ip][j], tbr[b], t4[j]);
-        }
-      __builtin_amdgcn_sched_barrier(0);
-      t4 = mfma4(xop[0][0], tc[0][0], t4);
-      t4 = mfma4(xop[0][1], tc[0][1], t4);
-      __builtin_amdgcn_sched_barrier(0);
-      if (ip > 0) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          xc[ip - 1][j] = 2.0f * xc[ip - 1][j] - prev[j];
-          nxt[(16 * (ip - 1) + 4 * lg + j) * S + col] = xc[ip - 1][j];
-        }
-      } else {
-        // X_{t+1} on the border rows of the own columns:
-        // 2 X_t[N16+b][col] - sum_k X_t[N16+b][k] T[k][col]
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          xbn[b] = 0.f;
-          if (b < r) {
-            float p = 0.f;
-#pragma unroll
-            for (int i = 0; i < MB; ++i)
-#pragma unroll
-              for (int j = 0; j < 4; ++j) p = fmaf(xbrow[b][i][j], tc[i][j], p);
-            p = sum_over_g(p);
-#pragma unroll
-            for (int bb = 0; bb < 4; ++bb)
-              if (bb < r) p = fmaf(xcor[b][bb], tbr[bb], p);
-            xbn[b] = 2.0f * xbr[b] - p;
-          }
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int s4 = 2; s4 < 4 * MB; ++s4) t4 = mfma4(xop[s4 / 4][s4 % 4], tc[s4 / 4][s4 % 4], t4);
-      __builtin_amdgcn_sched_barrier(0);
-      prev = t4;
-      if (ip + 1 < MB) {
-#pragma unroll
-        for (int i = 0; i < MB; ++i) xop[i] = xnx[i];
-      } else {
-#pragma unroll
-        for (int i = 0; i < MB; ++i) aop[i] = xnx[i];
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      xc[MB - 1][j] = 2.0f * xc[MB - 1][j] - prev[j];
-      nxt[(16 * (MB - 1) + 4 * lg + j) * S + col] = xc[MB - 1][j];
-    }
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-      if (b < r) {
-        xbr[b] = xbn[b];
-        if (lg == 0) nxt[(N16 + b) * S + col] = xbr[b];
-      }
-    __syncthreads();
   }
 }
 
-// Border wave b: column N16 + b of T and X_{t+1}, lane k = row k (k < m).
-template <int MB>
-__device__ void ns_border_wave(const MainArgs& a, float* smem, int b, int lane) {
-  using G = NsGeom<MB>;
-  constexpr int S = G::SLS, N16 = G::N16;
-  const float* A = smem;
-  float* TX = smem + G::OFF_TX + 64 * b;
-  const int k = lane;
-  const bool row = k < a.m;           // m <= ROWS
-  float xk = row ? smem[G::MAT + k * S + N16 + b] : 0.f;
+// Splits accumulator block i into the B operand registers of its chunk.
+__device__ __forceinline__ void split_block(f4 x, int i, u32x4* h, u32x4* l) {
+  unsigned h0, l0, h1, l1;
+  split2(x[0], x[1], h0, l0);
+  split2(x[2], x[3], h1, l1);
+  h[i >> 1][2 * (i & 1)] = h0;
+  h[i >> 1][2 * (i & 1) + 1] = h1;
+  l[i >> 1][2 * (i & 1)] = l0;
+  l[i >> 1][2 * (i & 1) + 1] = l1;
+}
 
-  for (int t = 0; t < a.iters; ++t) {
-    const int cb = t & 1;
-    const float* cur = smem + G::MAT * (1 + cb);
-    float* nxt = smem + G::MAT * (2 - cb);
-    const float* xtb = smem + G::OFF_XTB + 256 * cb + 64 * b;
-    float* xtn = smem + G::OFF_XTB + 256 * (1 - cb) + 64 * b;
-    // T[k][N16+b] = sum_k' A[k][k'] X_t[k'][N16+b]
-    float tk = 0.f;
-    if (row) {
-      float d[4] = {0.f, 0.f, 0.f, 0.f};
+// Interior wave c: the Newton-Schulz steps on column block c.
+template <int MB, int D>
+__device__ void ns_wave(const MainArgs& a, float* smem, int c, int lane, float alpha, int eA,
+                        int e0) {
+  using G = NsGeom<MB, D>;
+  constexpr int NC = G::NC, RSH = G::RSH, SX = G::SX, ARR = G::ARR;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int col = 16 * c + lr;
+  const int iters = a.iters;
+  float* slot = smem + G::OFF_SLOT;
+
+  // X-hat_0 = 2^e0 alpha A on the own columns, fp32 and split (the same
+  // arithmetic as the shared copy, so the two agree bit for bit)
+  f4 xs[MB];
+  u32x4 xh[NC], xl[NC];
+  {
+    const float* Af = smem + G::OFF_X + 2 * ARR;
 #pragma unroll
-      for (int q = 0; q < G::NQ; ++q) {
-        const f4 ar = ld4(A + k * S + 4 * q), xv = ld4(xtb + 4 * q);
-        d[q & 3] = fmaf(ar[3], xv[3], fmaf(ar[2], xv[2], fmaf(ar[1], xv[1], fmaf(ar[0], xv[0], d[q & 3]))));
-      }
-      tk = (d[0] + d[1]) + (d[2] + d[3]);
-    }
-    TX[k] = tk;  // rows >= m are zero
-    // make the whole column visible to every lane of this wave
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // X_{t+1}[k][N16+b] = 2 X_t[k][N16+b] - sum_k' X_t[k][k'] T[k'][N16+b]
-    if (row) {
-      float d[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
-      for (int q = 0; q < G::NQ; ++q) {
-        const f4 xr = ld4(cur + k * S + 4 * q), tv = ld4(TX + 4 * q);
-        d[q & 3] = fmaf(xr[3], tv[3], fmaf(xr[2], tv[2], fmaf(xr[1], tv[1], fmaf(xr[0], tv[0], d[q & 3]))));
-      }
-      xk = 2.0f * xk - ((d[0] + d[1]) + (d[2] + d[3]));
-      nxt[k * S + N16 + b] = xk;
-      xtn[k] = xk;
-    }
-    __syncthreads();
+      for (int j = 0; j < 4; ++j) xs[i][j] = ldexpf(alpha * Af[(16 * i + 4 * lg + j) * SX + col], e0);
   }
+#pragma unroll
+  for (int p = 0; p < NC; ++p) xh[p] = xl[p] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < MB; ++i) split_block(xs[i], i, xh, xl);
+  __syncthreads();  // the fp32 A (in the parity-1 X halves) is dead from here
+
+  const int hp = hpos<MB>(col);
+  int ep = e0, ec = e0;  // scale exponents of X_{t-1} and X_t
+  // the operand of the first block of phase 1 (rows 0..15 of A) is constant
+  u32x4 oh[NC], ol[NC];
+  load_op<MB, D>(smem, G::OFF_AH, G::OFF_AL, lr, lg, oh, ol);
+
+  // One step; the last one writes X_{t+1} in fp32 instead of split.
+  auto step = [&](int t, auto last_c) {
+    constexpr bool LAST = decltype(last_c)::value;
+    const int cb = t & 1;
+    const int xoh = G::OFF_X + 2 * ARR * cb, xol = xoh + ARR;        // X_t
+    const int noh = G::OFF_X + 2 * ARR * (1 - cb), nol = noh + ARR;  // X_{t+1}
+    // column-block maxima of X-hat_{t-1} (units 2^ep): the scale of X_{t+1}
+    float sv[MB];
+    if (!LAST) {
+#pragma unroll
+      for (int i = 0; i < MB; ++i) sv[i] = slot[256 * (1 - cb) + 64 * i + lane];
+    }
+
+    // phase 1: T-hat[:, c] = 2^(14 - eA - ec) A-hat X-hat_t[:, c]
+    const int sT = 14 - eA - ec;
+    u32x4 th[NC], tl[NC];
+#pragma unroll
+    for (int p = 0; p < NC; ++p) th[p] = tl[p] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int ip = 0; ip < MB; ++ip) {
+      u32x4 nh[NC], nl[NC];
+      if (ip + 1 < MB) load_op<MB, D>(smem, G::OFF_AH, G::OFF_AL, 16 * (ip + 1) + lr, lg, nh, nl);
+      else load_op<MB, D>(smem, xoh, xol, lr, lg, nh, nl);  // phase 2, block 0
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int p = 0; p < NC; ++p) {
+        acc = mfma_h(oh[p], xh[p], acc);
+        acc = mfma_h(ol[p], xh[p], acc);
+        acc = mfma_h(oh[p], xl[p], acc);
+      }
+      if (!LAST && ip == 0) {
+        // publish max|X-hat_t| of the own columns (units 2^ec), one copy per
+        // lane; magnitudes compare as unsigned bit patterns
+        unsigned mx = 0u;
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) mx = max(mx, __float_as_uint(xs[i][j]) & 0x7fffffffu);
+        slot[256 * cb + 64 * c + lane] = __uint_as_float(wave_max_u(mx));
+      }
+      f4 tv;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) tv[j] = ldexpf(acc[j], sT);
+      split_block(tv, ip, th, tl);
+#pragma unroll
+      for (int p = 0; p < NC; ++p) {
+        oh[p] = nh[p];
+        ol[p] = nl[p];
+      }
+    }
+
+    // scale of X_{t+1}: max|X_{t-1}| 2^eN < 2^7 (the last X stays at 2^ec)
+    int eN = ec;
+    if (!LAST) {
+      float mp = sv[0];
+#pragma unroll
+      for (int i = 1; i < MB; ++i) mp = fmaxf(mp, sv[i]);
+      if (mp > 0.f) eN = ep + 7 - __builtin_amdgcn_frexp_expf(mp);
+    }
+    // X-hat_{t+1} = 2^(eN - ec + 1) X-hat_t - 2^(eN - ec - 14) (X-hat_t T-hat)
+    const float c1 = ldexpf(1.0f, eN - ec + 1), c2 = -ldexpf(1.0f, eN - ec - 14);
+    uint16_t* H = reinterpret_cast<uint16_t*>(smem + noh);
+    uint16_t* L = reinterpret_cast<uint16_t*>(smem + nol);
+    float* XF = smem + noh;
+
+    // phase 2: X_{t+1}[:, c] = 2 X_t[:, c] - X_t T[:, c]
+#pragma unroll
+    for (int ip = 0; ip < MB; ++ip) {
+      u32x4 nh[NC], nl[NC];
+      if (ip + 1 < MB) load_op<MB, D>(smem, xoh, xol, 16 * (ip + 1) + lr, lg, nh, nl);
+      else if (!LAST) load_op<MB, D>(smem, G::OFF_AH, G::OFF_AL, lr, lg, nh, nl);  // next step
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int p = 0; p < NC; ++p) {
+        acc = mfma_h(oh[p], th[p], acc);
+        acc = mfma_h(ol[p], th[p], acc);
+        acc = mfma_h(oh[p], tl[p], acc);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xs[ip][j] = fmaf(acc[j], c2, c1 * xs[ip][j]);
+      if (!LAST) {
+        split_block(xs[ip], ip, xh, xl);
+        const unsigned hv[2] = {xh[ip >> 1][2 * (ip & 1)], xh[ip >> 1][2 * (ip & 1) + 1]};
+        const unsigned lv[2] = {xl[ip >> 1][2 * (ip & 1)], xl[ip >> 1][2 * (ip & 1) + 1]};
+        const int r0 = (16 * ip + 4 * lg) * RSH + hp;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          H[r0 + j * RSH] = static_cast<uint16_t>(hv[j >> 1] >> (16 * (j & 1)));
+          L[r0 + j * RSH] = static_cast<uint16_t>(lv[j >> 1] >> (16 * (j & 1)));
+        }
+      } else {
+        // the final iterate in fp32, over the X_{t+1} halves
+#pragma unroll
+        for (int j = 0; j < 4; ++j) XF[(16 * ip + 4 * lg + j) * SX + col] = ldexpf(xs[ip][j], -eN);
+      }
+      if (ip + 1 < MB || !LAST) {
+#pragma unroll
+        for (int p = 0; p < NC; ++p) {
+          oh[p] = nh[p];
+          ol[p] = nl[p];
+        }
+      }
+    }
+    ep = ec;
+    ec = eN;
+    __syncthreads();
+  };
+
+  for (int t = 0; t + 1 < iters; ++t) step(t, std::false_type{});
+  if (iters > 0) step(iters - 1, std::true_type{});
 }
 
 // The 2 x 2 blocks of the upper triangle of A = k(L, L) + eps I (see
@@ -687,29 +715,25 @@ __device__ void build_a(const MainArgs& a, int bh, const float* Ls, float* A, in
 }
 
 template <int D, int MB>
-__device__ void solver_role(const MainArgs& a, int bh, float* smem) {
-  using G = NsGeom<MB>;
-  constexpr int S = G::SLS, N16 = G::N16;
-  float* A = smem;
-  float* X0 = smem + G::MAT;
-  float* X1 = smem + 2 * G::MAT;
-  float* XTB = smem + G::OFF_XTB;
+__device__ __forceinline__ void solver_role(const MainArgs& a, int bh, float* smem) {
+  using G = NsGeom<MB, D>;
+  constexpr int SX = G::SX, N16 = G::N16, RSH = G::RSH, WLS = G::WLS;
+  float* Af = smem + G::OFF_X + 2 * G::ARR;  // A in fp32 while set up
   float* red = smem + G::OFF_RED;
-  constexpr int WLS = MP + 4;              // row stride of the W^T copy
-  float* WTL = smem + G::SMEM;             // [D][WLS] W^T copy (see below)
+  float* slot = smem + G::OFF_SLOT;
+  float* WTL = smem + G::OFF_WT;             // [D][WLS] W^T copy (see below)
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int m = a.m;
-  const int r = m > N16 ? m - N16 : 0;  // border width (0 when padded)
   __builtin_amdgcn_s_setprio(3);
 
   // A = k(L, L) + eps I, built here in LDS.  The landmarks are staged in LDS
-  // (over the iterate buffers, which are initialised afterwards; rows up to
-  // an even count, padding zero).  Each thread computes a 2 x 2 block (rows 2 bi, 2 bi + 1; columns 2 bj, 2 bj + 1), bi <= bj, of
-  // the upper triangle, streaming the four landmark rows; every unordered
-  // pair is computed once and written to A[i][j] and A[j][i], so A is exactly
-  // symmetric (the border code relies on it).
+  // (rows up to an even count, padding zero).  Each thread computes a 2 x 2
+  // block (rows 2 bi, 2 bi + 1; columns 2 bj, 2 bj + 1), bi <= bj, of the
+  // upper triangle, streaming the four landmark rows; every unordered pair is
+  // computed once and written to A[i][j] and A[j][i], so A is exactly
+  // symmetric.
   constexpr int LDL = D + 4;
-  float* Ls = smem + G::MAT;
+  float* Ls = smem + G::OFF_WT;
   const int nb = (m + 1) / 2;
   {
     const float* Lg = a.L + static_cast<size_t>(bh) * m * D;
@@ -717,58 +741,82 @@ __device__ void solver_role(const MainArgs& a, int bh, float* smem) {
       const int row = e / (D / 4), c4 = e % (D / 4);
       st4(Ls + row * LDL + 4 * c4, row < m ? ld4(Lg + row * D + 4 * c4) : f4{0.f, 0.f, 0.f, 0.f});
     }
-    for (int e = tid; e < G::ROWS * S; e += WGM) A[e] = 0.f;
+    for (int e = tid; e < N16 * SX; e += WGM) Af[e] = 0.f;
   }
   __syncthreads();
-  if (a.kind == 0) build_a<D, 0>(a, bh, Ls, A, S);
-  else build_a<D, 1>(a, bh, Ls, A, S);
+  if (a.kind == 0) build_a<D, 0>(a, bh, Ls, Af, SX);
+  else build_a<D, 1>(a, bh, Ls, Af, SX);
   __syncthreads();
   // alpha = 1 / (max column abs-sum * max row abs-sum); A is symmetric, so
-  // its largest column sum equals its largest row sum.
+  // its largest column sum equals its largest row sum.  Also max|A|.
   if (w == 0) {
-    float sum = 0.f;
+    float sum = 0.f, amx = 0.f;
     if (lane < m) {
       for (int q = 0; q < (m + 3) / 4; ++q) {
-        const f4 v = ld4(A + lane * S + 4 * q);  // zero beyond m
+        const f4 v = ld4(Af + lane * SX + 4 * q);  // zero beyond m
         sum += fabsf(v[0]) + fabsf(v[1]) + fabsf(v[2]) + fabsf(v[3]);
+        amx = fmaxf(amx, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
       }
     }
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) sum = fmaxf(sum, __shfl_xor(sum, o));
+    for (int o = 32; o > 0; o >>= 1) {
+      sum = fmaxf(sum, __shfl_xor(sum, o));
+      amx = fmaxf(amx, __shfl_xor(amx, o));
+    }
     if (lane == 0) {
       red[0] = sum;
       red[1] = 0.f;  // set once W^T is in LDS
+      red[2] = amx;
     }
   }
   __syncthreads();
   const float alpha = 1.0f / (red[0] * red[0]);
-  // X_0 = alpha A; the second buffer zero (its padding stays zero)
-  for (int e = tid; e < G::MAT; e += WGM) {
-    X0[e] = alpha * A[e];
-    X1[e] = 0.f;
-  }
-  for (int e = tid; e < 2 * 4 * 64; e += WGM) {
-    const int buf = e / 256, bb = (e / 64) % 4, kk = e % 64;
-    XTB[e] = (buf == 0 && bb < r && kk < m) ? alpha * A[kk * S + N16 + bb] : 0.f;
+  const int eA = 14 - __builtin_amdgcn_frexp_expf(red[2]);
+  const float m0 = alpha * red[2];  // max|X_0|
+  const int e0 = 7 - __builtin_amdgcn_frexp_expf(m0);
+  // A and X_0 = alpha A, scaled and split, into the half-precision arrays
+  // (four consecutive columns per thread: 8-byte stores); with no steps to
+  // run, X_0 in fp32 instead
+  {
+    constexpr int Q4 = N16 / 4;
+    uint16_t* AH = reinterpret_cast<uint16_t*>(smem + G::OFF_AH);
+    uint16_t* AL = reinterpret_cast<uint16_t*>(smem + G::OFF_AL);
+    uint16_t* XH = reinterpret_cast<uint16_t*>(smem + G::OFF_X);
+    uint16_t* XL = reinterpret_cast<uint16_t*>(smem + G::OFF_X + G::ARR);
+    for (int e = tid; e < N16 * Q4; e += WGM) {
+      const int i = e / Q4, q = e % Q4;
+      const f4 av = ld4(Af + i * SX + 4 * q);
+      const int h0 = i * RSH + hpos<MB>(4 * q);  // a multiple of 4
+      unsigned h0w, l0w, h1w, l1w;
+      split2(ldexpf(av[0], eA), ldexpf(av[1], eA), h0w, l0w);
+      split2(ldexpf(av[2], eA), ldexpf(av[3], eA), h1w, l1w);
+      *reinterpret_cast<u32x2*>(AH + h0) = u32x2{h0w, h1w};
+      *reinterpret_cast<u32x2*>(AL + h0) = u32x2{l0w, l1w};
+      const f4 xv = {alpha * av[0], alpha * av[1], alpha * av[2], alpha * av[3]};
+      if (a.iters > 0) {
+        split2(ldexpf(xv[0], e0), ldexpf(xv[1], e0), h0w, l0w);
+        split2(ldexpf(xv[2], e0), ldexpf(xv[3], e0), h1w, l1w);
+        *reinterpret_cast<u32x2*>(XH + h0) = u32x2{h0w, h1w};
+        *reinterpret_cast<u32x2*>(XL + h0) = u32x2{l0w, l1w};
+      } else {
+        st4(smem + G::OFF_X + i * SX + 4 * q, xv);
+      }
+    }
+    // the first step reads these as the maxima of the step before
+    slot[tid] = ldexpf(m0, e0);
   }
   __syncthreads();
 
   if (w < MB) {
-    if constexpr (MB > 0) {
-      // the border width is a template argument so that the border code is
-      // straight-line
-      if (MB < 4 && r == 1) ns_interior_wave<MB, (MB < 4 ? 1 : 0)>(a, smem, w, lane);
-      else ns_interior_wave<MB, 0>(a, smem, w, lane);
-    }
-  } else if (w - MB < r) {
-    ns_border_wave<MB>(a, smem, w - MB, lane);
+    ns_wave<MB, D>(a, smem, w, lane, alpha, eA, e0);
   } else {
     // idle waves; the first one watches for the head's W^T (published by the
     // last key workgroup) during the second half of the steps and copies it
     // to LDS, so that Y can be formed right after the last step.  Each global
     // read is issued before a barrier and consumed after it (a barrier does
     // not wait for global loads), so the watcher never delays the steps.
-    const bool watcher = w == MB + r;
+    __syncthreads();  // matches the set-up barrier of the solving waves
+    const bool watcher = w == MB && !a.out_in_main;
     constexpr int NW = D * (MP / 4) / 64;  // float4 of W^T per lane
     const float* wg = a.wt + static_cast<size_t>(bh) * D * MP;
     int state = 0;  // 0 polling, 1 W^T reads in flight, 2 copied
@@ -813,15 +861,26 @@ __device__ void solver_role(const MainArgs& a, int bh, float* smem) {
   }
   __syncthreads();  // the W^T copy and its flag are complete
 
-  const float* Xf = (a.iters & 1) ? X1 : X0;
+  // the final iterate, fp32, row stride SX (zero in the padding)
+  const float* Xf = smem + G::OFF_X + 2 * G::ARR * (a.iters & 1);
   if (a.st_x) {
     for (int e = tid; e < m * m; e += WGM)
-      a.st_x[static_cast<size_t>(bh) * m * m + e] = Xf[(e / m) * S + (e % m)];
+      a.st_x[static_cast<size_t>(bh) * m * m + e] = Xf[(e / m) * SX + (e % m)];
+  }
+  if (a.out_in_main) {
+    // the query workgroups form Y themselves: publish X and raise its flag
+    float* Xg = a.xw + static_cast<size_t>(bh) * MP * MP;
+    for (int e = tid; e < MP * MP; e += WGM) {
+      const int row = e / MP, col = e % MP;
+      st_dev(Xg + e, (row < N16 && col < N16) ? Xf[row * SX + col] : 0.f);
+    }
+    raise_flag(flag_x(a, bh));
+    return;
   }
   if (red[1] != 0.f) {
     // W^T is already published (its arrival counted) and copied to LDS: this
     // workgroup is the second of (W, X) and forms Y^T from LDS directly
-    compute_y<D>(WTL, WLS, Xf, S, G::ROWS, a.yt + static_cast<size_t>(bh) * D * MP);
+    compute_y<D>(WTL, WLS, Xf, SX, N16, N16, a.yt + static_cast<size_t>(bh) * D * MP);
     raise_flag(flag_y(a, bh));
     return;
   }
@@ -829,7 +888,7 @@ __device__ void solver_role(const MainArgs& a, int bh, float* smem) {
   float* Xg = a.xw + static_cast<size_t>(bh) * MP * MP;
   for (int e = tid; e < MP * MP; e += WGM) {
     const int row = e / MP, col = e % MP;
-    st_dev(Xg + e, (row < G::ROWS && col < S) ? Xf[row * S + col] : 0.f);
+    st_dev(Xg + e, (row < N16 && col < N16) ? Xf[row * SX + col] : 0.f);
   }
   arrive_y<D>(a, bh);
 }
@@ -879,22 +938,51 @@ __device__ void reduce_w(const MainArgs& a, int bh) {
   }
 }
 
-// O rows of one 64-token tile: K_QL tile (PT, LDS, zero beyond m) times Y
-// (rows of Y^T from global memory) on fp32 MFMA.  Wave w: tokens
-// 16 (w % 4) .. +15, column blocks w / 4, w / 4 + 2, ...
+// Lines [l0, l1) (32 floats each) of W^T: the same sums as reduce_w, one
+// element per thread, every partial's load in flight at once (nP <= 32).
+// Slices are whole cache lines, so no line of W^T is written by two
+// workgroups.
 template <int D>
-__device__ void out_tile(const MainArgs& a, int bh, int t, const float* PT) {
+__device__ void reduce_w_lines(const MainArgs& a, int bh, int l0, int l1) {
+  const int nP = a.nP, m = a.m;
+  const size_t ps = static_cast<size_t>(D) * MP;
+  const float* pb = a.wpart + static_cast<size_t>(bh) * nP * ps;
+  float* wg = a.wt + static_cast<size_t>(bh) * ps;
+  for (int e = 32 * l0 + static_cast<int>(threadIdx.x); e < 32 * l1; e += WGM) {
+    float v[32];
+#pragma unroll
+    for (int p = 0; p < 32; ++p) v[p] = p < nP ? pb[p * ps + e] : 0.f;
+    float sum = 0.f;
+    int p = 0;
+    // eight at a time, like reduce_w
+    for (; p + 8 <= nP; p += 8) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) sum += v[p + q];
+    }
+    for (; p < nP; ++p) sum += v[p];
+    const int c = e / MP, j = e % MP;
+    const float w = j < m ? sum : 0.f;
+    st_dev(wg + e, w);
+    if (a.st_w && j < m) a.st_w[(static_cast<size_t>(bh) * m + j) * D + c] = w;
+  }
+}
+
+// O rows of one 64-token tile: K_QL tile (PT, LDS, zero beyond m) times Y
+// (rows of Y^T at yb, row stride ys: global memory or LDS) on fp32 MFMA.
+// Wave w: tokens 16 (w % 4) .. +15, column blocks w / 4, w / 4 + 2, ...
+template <int D>
+__device__ void out_tile(const MainArgs& a, int bh, int t, const float* PT, const float* yg,
+                         int ys) {
   constexpr int CBN = D / 16;
   const int lane = threadIdx.x & 63, w = wave_id();
   const int lr = lane & 15, lg = lane >> 4;
   const int tb = w & 3, ch = w >> 2;
-  const float* yg = a.yt + static_cast<size_t>(bh) * D * MP;
   f4 av[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) av[q] = ld4(PT + (16 * tb + lr) * LS + 16 * lg + 4 * q);
 #pragma unroll
   for (int cb = ch; cb < CBN; cb += 2) {
-    const float* br = yg + (16 * cb + lr) * MP + 16 * lg;
+    const float* br = yg + (16 * cb + lr) * ys + 16 * lg;
     f4 bv[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) bv[q] = ld4(br + 4 * q);
@@ -984,7 +1072,7 @@ __device__ void gauss_tile(const MainArgs& a, const void* src, const float* Lh, 
 }
 
 template <int D, int KIND, bool BF16>
-__device__ void map_role(const MainArgs& a, const void* __restrict__ q, const void* __restrict__ k,
+__device__ __forceinline__ void map_role(const MainArgs& a, const void* __restrict__ q, const void* __restrict__ k,
                          const void* __restrict__ v, const float* __restrict__ Lw, int b,
                          float* smem) {
   constexpr int CBN = D / 16;
@@ -1136,10 +1224,26 @@ __device__ void map_role(const MainArgs& a, const void* __restrict__ q, const vo
   }
   if (!key_role) {
     if (!a.out_in_main) return;  // K_QL stored; the output launch forms O
-    // the tiles' K_QL rows are still in LDS: wait for Y of the head
-    wait_flag(flag_y(a, bh), a.sync);
-    out_tile<D>(a, bh, t_beg, PT);
-    if (t_beg + 1 < t_end) out_tile<D>(a, bh, t_beg + 1, VT);
+    // Query workgroup u < R reduces its slice of W^T once every key
+    // workgroup of the head has published its partial.
+    const int u = t_beg / QT;
+    constexpr int LINES = D * MP / 32;  // cache lines of W^T
+    const int R = a.nQ < 32 ? a.nQ : 32;
+    const int lps = (LINES + R - 1) / R;
+    const int nslice = (LINES + lps - 1) / lps;
+    if (u < nslice) {
+      wait_flags(key_flags(a, bh), nK, nullptr, a.sync);
+      reduce_w_lines<D>(a, bh, u * lps, min((u + 1) * lps, LINES));
+      raise_flag(slice_flags(a, bh) + u);
+    }
+    // every slice and X published: Y^T = W^T X^T into LDS (PJ is unused by
+    // query tiles), then the output rows of the tiles (K_QL rows in LDS)
+    wait_flags(slice_flags(a, bh), nslice, flag_x(a, bh), a.sync);
+    compute_y<D, true>(a.wt + static_cast<size_t>(bh) * D * MP, MP,
+                       a.xw + static_cast<size_t>(bh) * MP * MP, MP, MP, MP, PJ);
+    __syncthreads();
+    out_tile<D>(a, bh, t_beg, PT, PJ, LS);
+    if (t_beg + 1 < t_end) out_tile<D>(a, bh, t_beg + 1, VT, PJ, LS);
     return;
   }
 
@@ -1154,6 +1258,11 @@ __device__ void map_role(const MainArgs& a, const void* __restrict__ q, const vo
       for (int i = 0; i < 4; ++i) st_dev(part + (16 * cb + 4 * lg + i) * MP + 16 * jbk + lr, wacc[s][i]);
     }
   }
+  if (a.out_in_main) {
+    // the query workgroups reduce the partials
+    raise_flag(key_flags(a, bh) + kw);
+    return;
+  }
   // the last key workgroup of the head reduces the partials
   if (publish_arrive(cnt_w(a, bh)) == static_cast<unsigned>(nK - 1)) {
     reduce_w<D>(a, bh);
@@ -1164,16 +1273,14 @@ __device__ void map_role(const MainArgs& a, const void* __restrict__ q, const vo
 // Read-only inputs are separate __restrict__ parameters so that wave-uniform
 // reads of them (the landmark coordinates) compile to scalar loads.
 template <int D, int MB>
-__global__ __launch_bounds__(WGM) void main_kernel(MainArgs a, const void* __restrict__ q,
+__global__ __launch_bounds__(WGM, 2) void main_kernel(MainArgs a, const void* __restrict__ q,
                                                     const void* __restrict__ k,
                                                     const void* __restrict__ v,
                                                     const float* __restrict__ L) {
   constexpr int MAP_SMEM = 3 * MP * LS + TILE;
-  // solver: the Newton-Schulz layout plus a W^T copy; landmark staging
-  // while A is built
-  constexpr int SOLVER_A = NsGeom<MB>::SMEM + D * (MP + 4);
-  constexpr int SOLVER_B = NsGeom<MB>::MAT + MP * (D + 4);
-  constexpr int SOLVER_SMEM = SOLVER_A > SOLVER_B ? SOLVER_A : SOLVER_B;
+  // solver: the Newton-Schulz arrays plus a W^T copy (landmarks while A is
+  // built)
+  constexpr int SOLVER_SMEM = NsGeom<MB, D>::SMEM;
   __shared__ __attribute__((aligned(16)))
   float smem[MAP_SMEM > SOLVER_SMEM ? MAP_SMEM : SOLVER_SMEM];
   const int b = blockIdx.x;
@@ -1209,12 +1316,9 @@ __global__ __launch_bounds__(WGS) void pool_kernel(const void* __restrict__ K,
   const int j = blockIdx.x, bh = blockIdx.y;
   const int tid = threadIdx.x, c4 = tid % C4, g = tid / C4;
   // hand-off words of the main launch start at zero every call
-  if (j == 0 && tid == 0) {
-    const int BH = gridDim.y;
-    sync[4 + bh] = 0u;
-    sync[4 + BH + bh] = 0u;
-    sync[4 + 2 * BH + bh] = 0u;
-    if (bh == 0) sync[0] = 0u;
+  if (j == 0) {
+    for (int e = tid; e < kSyncHead; e += WGS) sync[kSyncHead * (bh + 1) + e] = 0u;
+    if (bh == 0 && tid == 0) sync[0] = 0u;
   }
   const int mw = gw / pw;
   const int R = j / mw, C = j % mw;
@@ -1346,7 +1450,6 @@ hipError_t launch_main_dm(const MainArgs& ma, unsigned grid, hipStream_t s, Ev e
 template <int D>
 hipError_t launch_main_d(const Plan& p, const MainArgs& ma, unsigned grid, hipStream_t s, Ev ev) {
   switch (p.ns_mb) {
-    case 0: return launch_main_dm<D, 0>(ma, grid, s, ev);
     case 1: return launch_main_dm<D, 1>(ma, grid, s, ev);
     case 2: return launch_main_dm<D, 2>(ma, grid, s, ev);
     case 3: return launch_main_dm<D, 3>(ma, grid, s, ev);
