@@ -305,9 +305,8 @@ __device__ __forceinline__ void wait_flags(const unsigned* flags, int n, const u
 // rows of stride xs (columns >= xcols and rows >= xrows read as zero), so the
 // operands may come from global memory or from the solver's LDS: the same
 // values in the same MFMA order give the same Y^T either way.  The result
-// goes to global memory (device-scope stores, row stride MP) or, with
-// TO_LDS, to LDS (row stride LS).
-template <int D, bool TO_LDS = false>
+// goes to global memory (device-scope stores, row stride MP).
+template <int D>
 __device__ void compute_y(const float* wt, int wts, const float* x, int xs, int xrows, int xcols,
                           float* yg) {
   constexpr int CBN = D / 16;
@@ -335,10 +334,7 @@ __device__ void compute_y(const float* wt, int wts, const float* x, int xs, int 
 #pragma unroll
         for (int h = 0; h < 4; ++h) c = mfma4(av[q][h], bv[q][h], c);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (TO_LDS) yg[(16 * cb + 4 * lg + i) * LS + 16 * jb + lr] = c[i];
-        else st_dev(yg + (16 * cb + 4 * lg + i) * MP + 16 * jb + lr, c[i]);
-      }
+      for (int i = 0; i < 4; ++i) st_dev(yg + (16 * cb + 4 * lg + i) * MP + 16 * jb + lr, c[i]);
     }
   }
 }
@@ -938,6 +934,54 @@ __device__ void reduce_w(const MainArgs& a, int bh) {
   }
 }
 
+// Y^T = W^T X^T in place: W^T in LDS (rows of LS floats) is replaced by Y^T;
+// X (MP x MP, zero padded) is read from global memory, every operand load
+// issued before the first MFMA.  Same blocks and MFMA order as compute_y.
+template <int D>
+__device__ void y_in_lds(float* WL, const float* xg) {
+  constexpr int CBN = D / 16;
+  constexpr int NBLK = 4 * CBN;          // 16x16 output blocks
+  constexpr int NSB = (NBLK + 7) / 8;    // blocks per wave
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int lr = lane & 15, lg = lane >> 4;
+  f4 bv[NSB][4], acc[NSB];
+#pragma unroll
+  for (int s = 0; s < NSB; ++s) {
+    const int blk = w + 8 * s;
+    if (blk < NBLK) {
+      const int jb = blk % 4;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) bv[s][q] = ld4(xg + (16 * jb + lr) * MP + 16 * lg + 4 * q);
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < NSB; ++s) {
+    const int blk = w + 8 * s;
+    acc[s] = f4{0.f, 0.f, 0.f, 0.f};
+    if (blk < NBLK) {
+      const int cb = blk / 4;
+      const float* ar = WL + (16 * cb + lr) * LS + 16 * lg;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f4 av = ld4(ar + 4 * q);
+#pragma unroll
+        for (int h = 0; h < 4; ++h) acc[s] = mfma4(av[h], bv[s][q][h], acc[s]);
+      }
+    }
+  }
+  __syncthreads();  // every wave has read its W^T rows
+#pragma unroll
+  for (int s = 0; s < NSB; ++s) {
+    const int blk = w + 8 * s;
+    if (blk < NBLK) {
+      const int cb = blk / 4, jb = blk % 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) WL[(16 * cb + 4 * lg + i) * LS + 16 * jb + lr] = acc[s][i];
+    }
+  }
+  __syncthreads();
+}
+
 // Lines [l0, l1) (32 floats each) of W^T: the same sums as reduce_w, one
 // element per thread, every partial's load in flight at once (nP <= 32).
 // Slices are whole cache lines, so no line of W^T is written by two
@@ -1236,12 +1280,19 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
       reduce_w_lines<D>(a, bh, u * lps, min((u + 1) * lps, LINES));
       raise_flag(slice_flags(a, bh) + u);
     }
-    // every slice and X published: Y^T = W^T X^T into LDS (PJ is unused by
-    // query tiles), then the output rows of the tiles (K_QL rows in LDS)
-    wait_flags(slice_flags(a, bh), nslice, flag_x(a, bh), a.sync);
-    compute_y<D, true>(a.wt + static_cast<size_t>(bh) * D * MP, MP,
-                       a.xw + static_cast<size_t>(bh) * MP * MP, MP, MP, MP, PJ);
-    __syncthreads();
+    // W^T complete: copy it to LDS (PJ is unused by query tiles) while the
+    // solver may still be running; then Y^T = W^T X^T in place, then the
+    // output rows of the tiles (K_QL rows in LDS)
+    wait_flags(slice_flags(a, bh), nslice, nullptr, a.sync);
+    {
+      const float* wg = a.wt + static_cast<size_t>(bh) * D * MP;
+      for (int e = tid; e < D * (MP / 4); e += WGM) {
+        const int row = e / (MP / 4), c4 = e % (MP / 4);
+        st4(PJ + row * LS + 4 * c4, ld4(wg + row * MP + 4 * c4));
+      }
+    }
+    wait_flag(flag_x(a, bh), a.sync);
+    y_in_lds<D>(PJ, a.xw + static_cast<size_t>(bh) * MP * MP);
     out_tile<D>(a, bh, t_beg, PT, PJ, LS);
     if (t_beg + 1 < t_end) out_tile<D>(a, bh, t_beg + 1, VT, PJ, LS);
     return;
