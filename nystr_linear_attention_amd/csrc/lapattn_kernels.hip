@@ -428,6 +428,39 @@ __device__ __forceinline__ float sum_over_g(float v) {
   return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
+// Single (not iterated) products run on bf16 MFMA (16x16x32) with both
+// operands split into bf16 parts, x = hi + lo + O(2^-18 |x|), formed as
+// hi hi + lo hi + hi lo with fp32 accumulation: about 17 significant bits,
+// at a fifth of the matrix-core cycles of fp32 MFMA.
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f4 mfma_b(u32x4 a, u32x4 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, a), __builtin_bit_cast(bf8, b),
+                                                  c, 0, 0, 0);
+}
+
+// Two values into packed bf16 high parts and packed bf16 remainders (both
+// rounded to nearest).
+__device__ __forceinline__ void split2b(float x0, float x1, unsigned& hi, unsigned& lo) {
+  const unsigned h = __builtin_bit_cast(unsigned, __builtin_convertvector(f2{x0, x1}, bf2));
+  const float r0 = x0 - __uint_as_float(h << 16);
+  const float r1 = x1 - __uint_as_float(h & 0xffff0000u);
+  hi = h;
+  lo = __builtin_bit_cast(unsigned, __builtin_convertvector(f2{r0, r1}, bf2));
+}
+
+// Eight consecutive values (two float4) into one bf16 operand pair.
+__device__ __forceinline__ void split8b(f4 a, f4 b, u32x4& hi, u32x4& lo) {
+  unsigned h[4], l[4];
+  split2b(a[0], a[1], h[0], l[0]);
+  split2b(a[2], a[3], h[1], l[1]);
+  split2b(b[0], b[1], h[2], l[2]);
+  split2b(b[2], b[3], h[3], l[3]);
+  hi = u32x4{h[0], h[1], h[2], h[3]};
+  lo = u32x4{l[0], l[1], l[2], l[3]};
+}
+
 // Maximum over the 64 lanes of a wave, in every lane.
 __device__ __forceinline__ unsigned wave_max_u(unsigned v) {
   const auto h = __builtin_amdgcn_permlane32_swap(v, v, false, false);
@@ -446,23 +479,31 @@ struct NsGeom {
   static constexpr int N16 = 16 * MB;          // padded size
   static constexpr int NC = (MB + 1) / 2;      // 32-wide contraction chunks
   static constexpr bool ODD = (MB & 1) != 0;   // the last chunk holds one block
-  // Half-precision arrays: N16 rows of RSW 32-bit words.  RSW / 4 is odd, so
-  // the 16-byte reads of 16 consecutive rows fall on distinct bank groups.
+  // A in half precision, row major: N16 rows of RSW 32-bit words, columns
+  // permuted (hpos).  RSW / 4 is odd, so the 16-byte reads of 16
+  // consecutive rows fall on distinct bank groups.
   static constexpr int RSW = 8 * MB + 4;
   static constexpr int RSH = 2 * RSW;          // row stride in halves
   static constexpr int ARR = N16 * RSW;        // words per array
+  // X_t in half precision, column major: line k holds X_t[0..N16)[k], lines
+  // of XSW words (8 mod 32, so the 8-byte reads of 16 lines x 4 chunks and
+  // the 8-byte writes of 16 lines x 4 row groups spread over the banks).
+  static constexpr int XSW = 40;
+  static constexpr int XSH = 2 * XSW;          // line stride in halves
+  static constexpr int XARR = N16 * XSW;       // words per array
   static constexpr int SX = N16 + 4;           // fp32 row stride (A while set up, final X)
   static constexpr int OFF_AH = 0;             // A hi, A lo
   static constexpr int OFF_AL = ARR;
   static constexpr int OFF_X = 2 * ARR;        // [parity][hi, lo] X_t halves
-  static constexpr int OFF_SLOT = 6 * ARR;     // [parity][4][64] column-block maxima
-                                               // of X, one copy per lane
+  static constexpr int OFF_SLOT = 2 * ARR + 4 * XARR;  // [parity][4][64] column-block
+                                               // maxima of X, one copy per lane
   static constexpr int OFF_RED = OFF_SLOT + 512; // row-sum maximum, W^T flag, max|A|
   static constexpr int OFF_WT = OFF_RED + 4;   // W^T copy; landmarks while A is built
   static constexpr int WLS = MP + 4;           // row stride of the W^T copy
   static constexpr int TAIL = D * WLS > MP * (D + 4) ? D * WLS : MP * (D + 4);
   static constexpr int SMEM = OFF_WT + TAIL;
-  static_assert(N16 * SX <= 2 * ARR, "fp32 matrix fits one parity of the X halves");
+  static_assert(N16 * SX <= 2 * XARR, "fp32 matrix fits one parity of the X halves");
+  static_assert(N16 / 2 <= XSW, "X line fits");
 };
 
 // Position (in halves) of column k in a row of a half-precision array.  The
@@ -498,6 +539,44 @@ __device__ __forceinline__ void load_op(const float* smem, int offh, int offl, i
   }
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// A operand of one 16-row block of X_t (rows r0 .. r0 + 15) from the column-
+// major arrays at word offsets offh / offl, with transposing LDS reads: in
+// each 16-lane group, lane i receives half i % 4 of the 8 bytes read by lane
+// 4 j + i / 4 as its element j.  So lane L = 4 j + q of group g reads rows
+// r0 + 4q .. + 3 of line k = 16 (2p + h) + 4 g + j, and lane (g, lr) ends up
+// with X_t[r0 + lr][k] for j = 0..3: slots 4 h .. 4 h + 3 of chunk p.
+template <int MB, int D>
+__device__ __forceinline__ void load_xop(float* smem, int offh, int offl, int r0, int lane,
+                                         u32x4* h, u32x4* l) {
+  using G = NsGeom<MB, D>;
+  const int lg = lane >> 4, j = (lane >> 2) & 3, q = lane & 3;
+  // halves offset of (line 4 g + j, row r0 + 4 q)
+  const int base = (4 * lg + j) * G::XSH + r0 + 4 * q;
+  uint16_t* H = reinterpret_cast<uint16_t*>(smem + offh);
+  uint16_t* L = reinterpret_cast<uint16_t*>(smem + offl);
+#pragma unroll
+  for (int p = 0; p < G::NC; ++p) {
+    u32x2 v[2][2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      if (G::ODD && p == G::NC - 1 && hh == 1) {
+        v[0][hh] = v[1][hh] = u32x2{0u, 0u};
+      } else {
+        const int o = base + 16 * (2 * p + hh) * G::XSH;
+        v[0][hh] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                 (lds_s16x4*)(H + o)));
+        v[1][hh] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                 (lds_s16x4*)(L + o)));
+      }
+    }
+    h[p] = u32x4{v[0][0][0], v[0][0][1], v[0][1][0], v[0][1][1]};
+    l[p] = u32x4{v[1][0][0], v[1][0][1], v[1][1][0], v[1][1][1]};
+  }
+}
+
 // Splits accumulator block i into the B operand registers of its chunk.
 __device__ __forceinline__ void split_block(f4 x, int i, u32x4* h, u32x4* l) {
   unsigned h0, l0, h1, l1;
@@ -514,7 +593,7 @@ template <int MB, int D>
 __device__ void ns_wave(const MainArgs& a, float* smem, int c, int lane, float alpha, int eA,
                         int e0) {
   using G = NsGeom<MB, D>;
-  constexpr int NC = G::NC, RSH = G::RSH, SX = G::SX, ARR = G::ARR;
+  constexpr int NC = G::NC, XSH = G::XSH, SX = G::SX, XARR = G::XARR;
   const int lr = lane & 15, lg = lane >> 4;
   const int col = 16 * c + lr;
   const int iters = a.iters;
@@ -525,7 +604,7 @@ __device__ void ns_wave(const MainArgs& a, float* smem, int c, int lane, float a
   f4 xs[MB];
   u32x4 xh[NC], xl[NC];
   {
-    const float* Af = smem + G::OFF_X + 2 * ARR;
+    const float* Af = smem + G::OFF_X + 2 * G::XARR;
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -537,7 +616,6 @@ __device__ void ns_wave(const MainArgs& a, float* smem, int c, int lane, float a
   for (int i = 0; i < MB; ++i) split_block(xs[i], i, xh, xl);
   __syncthreads();  // the fp32 A (in the parity-1 X halves) is dead from here
 
-  const int hp = hpos<MB>(col);
   int ep = e0, ec = e0;  // scale exponents of X_{t-1} and X_t
   // the operand of the first block of phase 1 (rows 0..15 of A) is constant
   u32x4 oh[NC], ol[NC];
@@ -547,8 +625,8 @@ __device__ void ns_wave(const MainArgs& a, float* smem, int c, int lane, float a
   auto step = [&](int t, auto last_c) {
     constexpr bool LAST = decltype(last_c)::value;
     const int cb = t & 1;
-    const int xoh = G::OFF_X + 2 * ARR * cb, xol = xoh + ARR;        // X_t
-    const int noh = G::OFF_X + 2 * ARR * (1 - cb), nol = noh + ARR;  // X_{t+1}
+    const int xoh = G::OFF_X + 2 * XARR * cb, xol = xoh + XARR;        // X_t
+    const int noh = G::OFF_X + 2 * XARR * (1 - cb), nol = noh + XARR;  // X_{t+1}
     // column-block maxima of X-hat_{t-1} (units 2^ep): the scale of X_{t+1}
     float sv[MB];
     if (!LAST) {
@@ -565,7 +643,7 @@ __device__ void ns_wave(const MainArgs& a, float* smem, int c, int lane, float a
     for (int ip = 0; ip < MB; ++ip) {
       u32x4 nh[NC], nl[NC];
       if (ip + 1 < MB) load_op<MB, D>(smem, G::OFF_AH, G::OFF_AL, 16 * (ip + 1) + lr, lg, nh, nl);
-      else load_op<MB, D>(smem, xoh, xol, lr, lg, nh, nl);  // phase 2, block 0
+      else load_xop<MB, D>(smem, xoh, xol, 0, lane, nh, nl);  // phase 2, block 0
       f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int p = 0; p < NC; ++p) {
@@ -612,8 +690,7 @@ __device__ void ns_wave(const MainArgs& a, float* smem, int c, int lane, float a
 #pragma unroll
     for (int ip = 0; ip < MB; ++ip) {
       u32x4 nh[NC], nl[NC];
-      if (ip + 1 < MB) load_op<MB, D>(smem, xoh, xol, 16 * (ip + 1) + lr, lg, nh, nl);
-      else if (!LAST) load_op<MB, D>(smem, G::OFF_AH, G::OFF_AL, lr, lg, nh, nl);  // next step
+      if (ip + 1 < MB) load_xop<MB, D>(smem, xoh, xol, 16 * (ip + 1), lane, nh, nl);
       f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int p = 0; p < NC; ++p) {
@@ -625,20 +702,18 @@ __device__ void ns_wave(const MainArgs& a, float* smem, int c, int lane, float a
       for (int j = 0; j < 4; ++j) xs[ip][j] = fmaf(acc[j], c2, c1 * xs[ip][j]);
       if (!LAST) {
         split_block(xs[ip], ip, xh, xl);
-        const unsigned hv[2] = {xh[ip >> 1][2 * (ip & 1)], xh[ip >> 1][2 * (ip & 1) + 1]};
-        const unsigned lv[2] = {xl[ip >> 1][2 * (ip & 1)], xl[ip >> 1][2 * (ip & 1) + 1]};
-        const int r0 = (16 * ip + 4 * lg) * RSH + hp;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          H[r0 + j * RSH] = static_cast<uint16_t>(hv[j >> 1] >> (16 * (j & 1)));
-          L[r0 + j * RSH] = static_cast<uint16_t>(lv[j >> 1] >> (16 * (j & 1)));
-        }
+        // rows 16 ip + 4 g .. + 3 of line col: one 8-byte store per part
+        const int o = col * XSH + 16 * ip + 4 * lg;
+        *reinterpret_cast<u32x2*>(H + o) =
+            u32x2{xh[ip >> 1][2 * (ip & 1)], xh[ip >> 1][2 * (ip & 1) + 1]};
+        *reinterpret_cast<u32x2*>(L + o) =
+            u32x2{xl[ip >> 1][2 * (ip & 1)], xl[ip >> 1][2 * (ip & 1) + 1]};
       } else {
         // the final iterate in fp32, over the X_{t+1} halves
 #pragma unroll
         for (int j = 0; j < 4; ++j) XF[(16 * ip + 4 * lg + j) * SX + col] = ldexpf(xs[ip][j], -eN);
       }
-      if (ip + 1 < MB || !LAST) {
+      if (ip + 1 < MB) {
 #pragma unroll
         for (int p = 0; p < NC; ++p) {
           oh[p] = nh[p];
@@ -648,7 +723,24 @@ __device__ void ns_wave(const MainArgs& a, float* smem, int c, int lane, float a
     }
     ep = ec;
     ec = eN;
-    __syncthreads();
+    if (!LAST) {
+      // The operand of the next step's first block (rows 0..15 of A, which
+      // never changes) is read after this step's stores and may still be in
+      // flight at the barrier: wait only until the stores (issued before the
+      // 2 NC reads) have completed.  LDS operations of a wave complete in
+      // order.
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      load_op<MB, D>(smem, G::OFF_AH, G::OFF_AL, lr, lg, oh, ol);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (NC == 2) asm volatile("s_waitcnt lgkmcnt(4)" ::: "memory");
+      else asm volatile("s_waitcnt lgkmcnt(2)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" ::: "memory");
+    } else {
+      __syncthreads();
+    }
   };
 
   for (int t = 0; t + 1 < iters; ++t) step(t, std::false_type{});
@@ -714,7 +806,7 @@ template <int D, int MB>
 __device__ __forceinline__ void solver_role(const MainArgs& a, int bh, float* smem) {
   using G = NsGeom<MB, D>;
   constexpr int SX = G::SX, N16 = G::N16, RSH = G::RSH, WLS = G::WLS;
-  float* Af = smem + G::OFF_X + 2 * G::ARR;  // A in fp32 while set up
+  float* Af = smem + G::OFF_X + 2 * G::XARR;  // A in fp32 while set up
   float* red = smem + G::OFF_RED;
   float* slot = smem + G::OFF_SLOT;
   float* WTL = smem + G::OFF_WT;             // [D][WLS] W^T copy (see below)
@@ -778,7 +870,7 @@ __device__ __forceinline__ void solver_role(const MainArgs& a, int bh, float* sm
     uint16_t* AH = reinterpret_cast<uint16_t*>(smem + G::OFF_AH);
     uint16_t* AL = reinterpret_cast<uint16_t*>(smem + G::OFF_AL);
     uint16_t* XH = reinterpret_cast<uint16_t*>(smem + G::OFF_X);
-    uint16_t* XL = reinterpret_cast<uint16_t*>(smem + G::OFF_X + G::ARR);
+    uint16_t* XL = reinterpret_cast<uint16_t*>(smem + G::OFF_X + G::XARR);
     for (int e = tid; e < N16 * Q4; e += WGM) {
       const int i = e / Q4, q = e % Q4;
       const f4 av = ld4(Af + i * SX + 4 * q);
@@ -790,10 +882,11 @@ __device__ __forceinline__ void solver_role(const MainArgs& a, int bh, float* sm
       *reinterpret_cast<u32x2*>(AL + h0) = u32x2{l0w, l1w};
       const f4 xv = {alpha * av[0], alpha * av[1], alpha * av[2], alpha * av[3]};
       if (a.iters > 0) {
+        // X_0 is exactly symmetric: its line i (column i) is its row i
         split2(ldexpf(xv[0], e0), ldexpf(xv[1], e0), h0w, l0w);
         split2(ldexpf(xv[2], e0), ldexpf(xv[3], e0), h1w, l1w);
-        *reinterpret_cast<u32x2*>(XH + h0) = u32x2{h0w, h1w};
-        *reinterpret_cast<u32x2*>(XL + h0) = u32x2{l0w, l1w};
+        *reinterpret_cast<u32x2*>(XH + i * G::XSH + 4 * q) = u32x2{h0w, h1w};
+        *reinterpret_cast<u32x2*>(XL + i * G::XSH + 4 * q) = u32x2{l0w, l1w};
       } else {
         st4(smem + G::OFF_X + i * SX + 4 * q, xv);
       }
@@ -858,17 +951,24 @@ __device__ __forceinline__ void solver_role(const MainArgs& a, int bh, float* sm
   __syncthreads();  // the W^T copy and its flag are complete
 
   // the final iterate, fp32, row stride SX (zero in the padding)
-  const float* Xf = smem + G::OFF_X + 2 * G::ARR * (a.iters & 1);
+  const float* Xf = smem + G::OFF_X + 2 * G::XARR * (a.iters & 1);
   if (a.st_x) {
     for (int e = tid; e < m * m; e += WGM)
       a.st_x[static_cast<size_t>(bh) * m * m + e] = Xf[(e / m) * SX + (e % m)];
   }
   if (a.out_in_main) {
-    // the query workgroups form Y themselves: publish X and raise its flag
-    float* Xg = a.xw + static_cast<size_t>(bh) * MP * MP;
-    for (int e = tid; e < MP * MP; e += WGM) {
-      const int row = e / MP, col = e % MP;
-      st_dev(Xg + e, (row < N16 && col < N16) ? Xf[row * SX + col] : 0.f);
+    // the query workgroups form Y themselves: publish X, split into bf16
+    // parts (hi [MP][MP], then lo [MP][MP], two per 32-bit word), and raise
+    // its flag
+    unsigned* Xh = reinterpret_cast<unsigned*>(a.xw + static_cast<size_t>(bh) * MP * MP);
+    unsigned* Xl = Xh + MP * MP / 2;
+    for (int e = tid; e < MP * MP / 2; e += WGM) {
+      const int row = e / (MP / 2), col = 2 * (e % (MP / 2));
+      const bool in = row < N16 && col < N16;  // N16 is even
+      unsigned hw, lw;
+      split2b(in ? Xf[row * SX + col] : 0.f, in ? Xf[row * SX + col + 1] : 0.f, hw, lw);
+      __hip_atomic_store(Xh + e, hw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(Xl + e, lw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     raise_flag(flag_x(a, bh));
     return;
@@ -934,24 +1034,40 @@ __device__ void reduce_w(const MainArgs& a, int bh) {
   }
 }
 
-// Y^T = W^T X^T in place: W^T in LDS (rows of LS floats) is replaced by Y^T;
-// X (MP x MP, zero padded) is read from global memory, every operand load
-// issued before the first MFMA.  Same blocks and MFMA order as compute_y.
+// Y^T = W^T X^T in place on split-bf16 MFMA: W^T in LDS as bf16 parts
+// (rows of WLD halves: hi at WH, lo at WL) is replaced by Y^T in the same
+// form; X comes split from global memory (hi then lo, rows of MP halves),
+// every operand load issued before the first MFMA.  Lane (g, r), slot s of
+// chunk p: contraction index 32 p + 8 g + s.
+constexpr int WLD = MP + 8;  // row stride (halves) of the split W^T / Y^T copies
+
+// Floats of the map role's first LDS area: P[j][token], or the two split
+// copies of W^T / Y^T.
 template <int D>
-__device__ void y_in_lds(float* WL, const float* xg) {
+constexpr int map_pj_size() {
+  return MP * LS > D * WLD ? MP * LS : D * WLD;
+}
+
+template <int D>
+__device__ void y_in_lds(uint16_t* WH, uint16_t* WL, const uint16_t* xh, const uint16_t* xl) {
   constexpr int CBN = D / 16;
   constexpr int NBLK = 4 * CBN;          // 16x16 output blocks
   constexpr int NSB = (NBLK + 7) / 8;    // blocks per wave
   const int lane = threadIdx.x & 63, w = wave_id();
   const int lr = lane & 15, lg = lane >> 4;
-  f4 bv[NSB][4], acc[NSB];
+  u32x4 bh[NSB][2], bl[NSB][2];
+  f4 acc[NSB];
 #pragma unroll
   for (int s = 0; s < NSB; ++s) {
     const int blk = w + 8 * s;
     if (blk < NBLK) {
       const int jb = blk % 4;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) bv[s][q] = ld4(xg + (16 * jb + lr) * MP + 16 * lg + 4 * q);
+      for (int p = 0; p < 2; ++p) {
+        const int o = (16 * jb + lr) * MP + 32 * p + 8 * lg;
+        bh[s][p] = *reinterpret_cast<const u32x4*>(xh + o);
+        bl[s][p] = *reinterpret_cast<const u32x4*>(xl + o);
+      }
     }
   }
 #pragma unroll
@@ -960,12 +1076,14 @@ __device__ void y_in_lds(float* WL, const float* xg) {
     acc[s] = f4{0.f, 0.f, 0.f, 0.f};
     if (blk < NBLK) {
       const int cb = blk / 4;
-      const float* ar = WL + (16 * cb + lr) * LS + 16 * lg;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f4 av = ld4(ar + 4 * q);
-#pragma unroll
-        for (int h = 0; h < 4; ++h) acc[s] = mfma4(av[h], bv[s][q][h], acc[s]);
+      for (int p = 0; p < 2; ++p) {
+        const int o = (16 * cb + lr) * WLD + 32 * p + 8 * lg;
+        const u32x4 ah = *reinterpret_cast<const u32x4*>(WH + o);
+        const u32x4 al = *reinterpret_cast<const u32x4*>(WL + o);
+        acc[s] = mfma_b(ah, bh[s][p], acc[s]);
+        acc[s] = mfma_b(al, bh[s][p], acc[s]);
+        acc[s] = mfma_b(ah, bl[s][p], acc[s]);
       }
     }
   }
@@ -975,8 +1093,15 @@ __device__ void y_in_lds(float* WL, const float* xg) {
     const int blk = w + 8 * s;
     if (blk < NBLK) {
       const int cb = blk / 4, jb = blk % 4;
+      unsigned h[2], l[2];
+      split2b(acc[s][0], acc[s][1], h[0], l[0]);
+      split2b(acc[s][2], acc[s][3], h[1], l[1]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) WL[(16 * cb + 4 * lg + i) * LS + 16 * jb + lr] = acc[s][i];
+      for (int i = 0; i < 4; ++i) {
+        const int o = (16 * cb + 4 * lg + i) * WLD + 16 * jb + lr;
+        WH[o] = static_cast<uint16_t>(h[i >> 1] >> (16 * (i & 1)));
+        WL[o] = static_cast<uint16_t>(l[i >> 1] >> (16 * (i & 1)));
+      }
     }
   }
   __syncthreads();
@@ -1011,39 +1136,52 @@ __device__ void reduce_w_lines(const MainArgs& a, int bh, int l0, int l1) {
   }
 }
 
-// O rows of one 64-token tile: K_QL tile (PT, LDS, zero beyond m) times Y
-// (rows of Y^T at yb, row stride ys: global memory or LDS) on fp32 MFMA.
-// Wave w: tokens 16 (w % 4) .. +15, column blocks w / 4, w / 4 + 2, ...
+// Stores output block (tokens 16 tb + 4 g + i, columns 16 cb + lr) of tile t
+// from accumulator c (lane (g, lr)), fp32 or bf16 (round to nearest even).
 template <int D>
-__device__ void out_tile(const MainArgs& a, int bh, int t, const float* PT, const float* yg,
-                         int ys) {
+__device__ __forceinline__ void store_o_block(const MainArgs& a, int bh, int t, int tb, int cb, f4 c) {
+  const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int n = t * TILE + 16 * tb + 4 * lg + i;
+    if (n < a.N) {
+      const size_t o = (static_cast<size_t>(bh) * a.N + n) * D + 16 * cb + lr;
+      if (a.bf16) static_cast<uint16_t*>(a.out)[o] = f32_to_bf16_rne(c[i]);
+      else static_cast<float*>(a.out)[o] = c[i];
+    }
+  }
+}
+
+// O rows of one 64-token tile: K_QL tile (PT, LDS, zero beyond m) times Y on
+// split-bf16 MFMA, with Y^T as bf16 parts in LDS (rows of WLD halves); the
+// tile's K_QL rows are split here, once per tile.  Wave w: tokens
+// 16 (w % 4) .. +15, column blocks w / 4, w / 4 + 2, ...
+template <int D>
+__device__ void out_tile(const MainArgs& a, int bh, int t, const float* PT, const uint16_t* YH,
+                           const uint16_t* YL) {
   constexpr int CBN = D / 16;
   const int lane = threadIdx.x & 63, w = wave_id();
   const int lr = lane & 15, lg = lane >> 4;
   const int tb = w & 3, ch = w >> 2;
-  f4 av[4];
+  u32x4 kh[2], kl[2];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) av[q] = ld4(PT + (16 * tb + lr) * LS + 16 * lg + 4 * q);
+  for (int p = 0; p < 2; ++p) {
+    const float* ar = PT + (16 * tb + lr) * LS + 32 * p + 8 * lg;
+    split8b(ld4(ar), ld4(ar + 4), kh[p], kl[p]);
+  }
 #pragma unroll
   for (int cb = ch; cb < CBN; cb += 2) {
-    const float* br = yg + (16 * cb + lr) * ys + 16 * lg;
-    f4 bv[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) bv[q] = ld4(br + 4 * q);
     f4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int h = 0; h < 4; ++h) c = mfma4(av[q][h], bv[q][h], c);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int n = t * TILE + 16 * tb + 4 * lg + i;
-      if (n < a.N) {
-        const size_t o = (static_cast<size_t>(bh) * a.N + n) * D + 16 * cb + lr;
-        if (a.bf16) static_cast<uint16_t*>(a.out)[o] = f32_to_bf16_rne(c[i]);
-        else static_cast<float*>(a.out)[o] = c[i];
-      }
+    for (int p = 0; p < 2; ++p) {
+      const int o = (16 * cb + lr) * WLD + 32 * p + 8 * lg;
+      const u32x4 yh = *reinterpret_cast<const u32x4*>(YH + o);
+      const u32x4 yl = *reinterpret_cast<const u32x4*>(YL + o);
+      c = mfma_b(kh[p], yh, c);
+      c = mfma_b(kl[p], yh, c);
+      c = mfma_b(kh[p], yl, c);
     }
+    store_o_block<D>(a, bh, t, tb, cb, c);
   }
 }
 
@@ -1120,10 +1258,12 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
                          const void* __restrict__ v, const float* __restrict__ Lw, int b,
                          float* smem) {
   constexpr int CBN = D / 16;
-  float* PJ = smem;                // [64 landmarks][LS]: P[j][token]
-  float* PT = smem + MP * LS;      // [64 tokens][LS]:    P[j] of token at [token][j]
-  float* VT = smem + 2 * MP * LS;  // [D][LS]:            V[token][c] at [c][token]
-  float* xx = smem + 3 * MP * LS;  // [64]: squared norms of a tile's tokens (Gaussian)
+  // PJ also holds the split W^T / Y^T copies of query workgroups
+  constexpr int PJS = map_pj_size<D>();
+  float* PJ = smem;                      // [64 landmarks][LS]: P[j][token]
+  float* PT = smem + PJS;                // [64 tokens][LS]:    P[j] of token at [token][j]
+  float* VT = smem + PJS + MP * LS;      // [D][LS]:            V[token][c] at [c][token]
+  float* xx = smem + PJS + 2 * MP * LS;  // [64]: squared norms of a tile's tokens (Gaussian)
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int lr = lane & 15, lg = lane >> 4;
   const int m = a.m, N = a.N;
@@ -1284,17 +1424,25 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
     // solver may still be running; then Y^T = W^T X^T in place, then the
     // output rows of the tiles (K_QL rows in LDS)
     wait_flags(slice_flags(a, bh), nslice, nullptr, a.sync);
+    uint16_t* WH = reinterpret_cast<uint16_t*>(PJ);
+    uint16_t* WL = WH + D * WLD;
     {
       const float* wg = a.wt + static_cast<size_t>(bh) * D * MP;
-      for (int e = tid; e < D * (MP / 4); e += WGM) {
-        const int row = e / (MP / 4), c4 = e % (MP / 4);
-        st4(PJ + row * LS + 4 * c4, ld4(wg + row * MP + 4 * c4));
+      for (int e = tid; e < D * (MP / 8); e += WGM) {
+        const int row = e / (MP / 8), k8 = 8 * (e % (MP / 8));
+        u32x4 hv, lv;
+        split8b(ld4(wg + row * MP + k8), ld4(wg + row * MP + k8 + 4), hv, lv);
+        *reinterpret_cast<u32x4*>(WH + row * WLD + k8) = hv;
+        *reinterpret_cast<u32x4*>(WL + row * WLD + k8) = lv;
       }
     }
     wait_flag(flag_x(a, bh), a.sync);
-    y_in_lds<D>(PJ, a.xw + static_cast<size_t>(bh) * MP * MP);
-    out_tile<D>(a, bh, t_beg, PT, PJ, LS);
-    if (t_beg + 1 < t_end) out_tile<D>(a, bh, t_beg + 1, VT, PJ, LS);
+    {
+      const uint16_t* xh = reinterpret_cast<const uint16_t*>(a.xw + static_cast<size_t>(bh) * MP * MP);
+      y_in_lds<D>(WH, WL, xh, xh + MP * MP);
+    }
+    out_tile<D>(a, bh, t_beg, PT, WH, WL);
+    if (t_beg + 1 < t_end) out_tile<D>(a, bh, t_beg + 1, VT, WH, WL);
     return;
   }
 
@@ -1328,7 +1476,7 @@ __global__ __launch_bounds__(WGM, 2) void main_kernel(MainArgs a, const void* __
                                                     const void* __restrict__ k,
                                                     const void* __restrict__ v,
                                                     const float* __restrict__ L) {
-  constexpr int MAP_SMEM = 3 * MP * LS + TILE;
+  constexpr int MAP_SMEM = map_pj_size<D>() + 2 * MP * LS + TILE;
   // solver: the Newton-Schulz arrays plus a W^T copy (landmarks while A is
   // built)
   constexpr int SOLVER_SMEM = NsGeom<MB, D>::SMEM;
