@@ -29,6 +29,7 @@ if ROOT not in sys.path:
 PEAK_HBM_GBS = 8000.0
 PEAK_FP32_VALU_TFLOPS = 157.3
 PEAK_FP32_MFMA_TFLOPS = 157.3
+PEAK_FP16_MFMA_TFLOPS = 2500.0   # dense fp16 / bf16 MFMA
 
 
 def log(*a):
@@ -316,8 +317,9 @@ def main(argv=None):
             dom_desc = "main_kernel, solver workgroups only (serial plan)"
     else:
         dom, dom_ms, dom_flops = "main", kf["main"], wk["fused"]["flops"]
-        dom_desc = ("main_kernel (fused: Newton-Schulz workgroups on fp32 MFMA beside the "
-                    "L1 map workgroups on FP32 VALU and their K_LK V partials on fp32 MFMA)")
+        dom_desc = ("main_kernel (fused: Newton-Schulz workgroups on split-fp16 MFMA beside "
+                    "the L1 map workgroups on FP32 VALU, their K_LK V partials on fp32 MFMA "
+                    "and Y, O on split-bf16 MFMA)")
     ach = dom_flops / (dom_ms * 1e-3) / 1e12
     traffic = stored_traffic(w.name, "main_kernel") if not args.serial else None
     roofline = {
@@ -354,10 +356,21 @@ def main(argv=None):
         kernels[name] = e
     mfma = None
     if ks:
+        # The solver launch of the serial plan: one workgroup (one CU) per
+        # head.  Its Newton-Schulz steps issue 3 fp16 products (hi*hi, lo*hi,
+        # hi*lo) for each of the 2 matrix products per step, on the matrix
+        # zero padded to n = 16 ceil(m / 16).
         solver_ms = ks["main"]
-        tf = wk["solver"]["flops"] / (solver_ms * 1e-3) / 1e12
-        mfma = {"solver_only_us": round(solver_ms * 1e3, 3), "TFLOP/s": round(tf, 4),
-                "per_active_cu_frac": round(tf / (peak * w.heads / 256), 4)}
+        n16 = 16 * ((w.m + 15) // 16)
+        f16 = w.heads * w.iters * 2 * 3 * 2 * n16 ** 3
+        tf = f16 / (solver_ms * 1e-3) / 1e12
+        per_cu_peak = PEAK_FP16_MFMA_TFLOPS / 256
+        mfma = {"solver_only_us": round(solver_ms * 1e3, 3),
+                "fp16_mfma_flops_issued": f16,
+                "TFLOP/s": round(tf, 3),
+                "per_active_cu_frac_of_fp16_peak": round(tf / (per_cu_peak * w.heads), 4),
+                "note": "whole solver launch (A, alpha, set-up and the steps) per active CU "
+                        "against 1/256 of the dense fp16 MFMA peak"}
 
     res = {
         "metric": "attention-layer tokens/sec (fwd) at N=3136,d=64,m=49; % FP32 VALU peak of L1 stage",
@@ -371,6 +384,10 @@ def main(argv=None):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32" if w.dtype == wl.F32 else "bf16 I/O, f32 compute",
+        "arithmetic": "L1 / squared-L2 maps on FP32 VALU; Newton-Schulz products as fp16 "
+                      "hi+lo splits on fp16 MFMA (about 22 significant bits); Y and O as "
+                      "bf16 hi+lo splits on bf16 MFMA (about 17 bits); K_LK V on fp32 MFMA; "
+                      "fp32 accumulation throughout",
         "data": "synthetic (seeded, shapes and distributions of the workload; resident in HBM)",
         "config": {
             "workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "m": w.m,
