@@ -205,7 +205,8 @@ struct MainArgs {
 //    output launch.
 // Words of head bh (kSyncHead from kSyncHead (bh + 1), each group on its own
 // cache lines): [0, 32) key ready flags, [32, 64) W^T slice flags, [64] X
-// ready, [96] key arrivals, [97] arrivals of W and X, [98] Y ready.
+// ready, [65] scale exponent of the published X, [96] key arrivals, [97]
+// arrivals of W and X, [98] Y ready.
 // Flags are plain device-scope stores (no read-modify-write on a shared word,
 // which serialises at memory when many workgroups arrive at once).
 //
@@ -236,6 +237,7 @@ __device__ __forceinline__ unsigned* head_sync(const MainArgs& a, int bh) {
 __device__ __forceinline__ unsigned* key_flags(const MainArgs& a, int bh) { return head_sync(a, bh); }
 __device__ __forceinline__ unsigned* slice_flags(const MainArgs& a, int bh) { return head_sync(a, bh) + 32; }
 __device__ __forceinline__ unsigned* flag_x(const MainArgs& a, int bh) { return head_sync(a, bh) + 64; }
+__device__ __forceinline__ unsigned* x_exp(const MainArgs& a, int bh) { return head_sync(a, bh) + 65; }
 __device__ __forceinline__ unsigned* cnt_w(const MainArgs& a, int bh) { return head_sync(a, bh) + 96; }
 __device__ __forceinline__ unsigned* cnt_y(const MainArgs& a, int bh) { return head_sync(a, bh) + 97; }
 __device__ __forceinline__ unsigned* flag_y(const MainArgs& a, int bh) { return head_sync(a, bh) + 98; }
@@ -428,37 +430,29 @@ __device__ __forceinline__ float sum_over_g(float v) {
   return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
-// Single (not iterated) products run on bf16 MFMA (16x16x32) with both
-// operands split into bf16 parts, x = hi + lo + O(2^-18 |x|), formed as
-// hi hi + lo hi + hi lo with fp32 accumulation: about 17 significant bits,
-// at a fifth of the matrix-core cycles of fp32 MFMA.
-typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
-
-__device__ __forceinline__ f4 mfma_b(u32x4 a, u32x4 b, f4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, a), __builtin_bit_cast(bf8, b),
-                                                  c, 0, 0, 0);
-}
-
-// Two values into packed bf16 high parts and packed bf16 remainders (both
-// rounded to nearest).
-__device__ __forceinline__ void split2b(float x0, float x1, unsigned& hi, unsigned& lo) {
-  const unsigned h = __builtin_bit_cast(unsigned, __builtin_convertvector(f2{x0, x1}, bf2));
-  const float r0 = x0 - __uint_as_float(h << 16);
-  const float r1 = x1 - __uint_as_float(h & 0xffff0000u);
-  hi = h;
-  lo = __builtin_bit_cast(unsigned, __builtin_convertvector(f2{r0, r1}, bf2));
-}
-
-// Eight consecutive values (two float4) into one bf16 operand pair.
-__device__ __forceinline__ void split8b(f4 a, f4 b, u32x4& hi, u32x4& lo) {
+// Eight consecutive values (two float4), scaled by 2^e, into one fp16
+// operand pair (hi, lo).
+__device__ __forceinline__ void split8h(f4 a, f4 b, int e, u32x4& hi, u32x4& lo) {
   unsigned h[4], l[4];
-  split2b(a[0], a[1], h[0], l[0]);
-  split2b(a[2], a[3], h[1], l[1]);
-  split2b(b[0], b[1], h[2], l[2]);
-  split2b(b[2], b[3], h[3], l[3]);
+  split2(ldexpf(a[0], e), ldexpf(a[1], e), h[0], l[0]);
+  split2(ldexpf(a[2], e), ldexpf(a[3], e), h[1], l[1]);
+  split2(ldexpf(b[0], e), ldexpf(b[1], e), h[2], l[2]);
+  split2(ldexpf(b[2], e), ldexpf(b[3], e), h[3], l[3]);
   hi = u32x4{h[0], h[1], h[2], h[3]};
   lo = u32x4{l[0], l[1], l[2], l[3]};
+}
+
+// Maximum of non-negative v over the 8 lanes of an aligned 8-lane group, in
+// every lane of the group; magnitudes compare as unsigned bit patterns.
+__device__ __forceinline__ unsigned max8_u(unsigned v) {
+  v = max(v, static_cast<unsigned>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0xB1, 0xF, 0xF, false)));
+  v = max(v, static_cast<unsigned>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x4E, 0xF, 0xF, false)));
+  return max(v, static_cast<unsigned>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x141, 0xF, 0xF, false)));
+}
+
+// Exponent e with max 2^e < 2^15 (0 for max = 0).
+__device__ __forceinline__ int fp16_scale(float mx) {
+  return mx > 0.f ? 15 - __builtin_amdgcn_frexp_expf(mx) : 0;
 }
 
 // Maximum over the 64 lanes of a wave, in every lane.
@@ -497,7 +491,8 @@ struct NsGeom {
   static constexpr int OFF_X = 2 * ARR;        // [parity][hi, lo] X_t halves
   static constexpr int OFF_SLOT = 2 * ARR + 4 * XARR;  // [parity][4][64] column-block
                                                // maxima of X, one copy per lane
-  static constexpr int OFF_RED = OFF_SLOT + 512; // row-sum maximum, W^T flag, max|A|
+  static constexpr int OFF_RED = OFF_SLOT + 512; // row-sum maximum, W^T flag, max|A|,
+                                                 // scale exponent of the final X
   static constexpr int OFF_WT = OFF_RED + 4;   // W^T copy; landmarks while A is built
   static constexpr int WLS = MP + 4;           // row stride of the W^T copy
   static constexpr int TAIL = D * WLS > MP * (D + 4) ? D * WLS : MP * (D + 4);
@@ -745,6 +740,8 @@ __device__ void ns_wave(const MainArgs& a, float* smem, int c, int lane, float a
 
   for (int t = 0; t + 1 < iters; ++t) step(t, std::false_type{});
   if (iters > 0) step(iters - 1, std::true_type{});
+  // the final iterate's scale: max|X| 2^ec < 2^15
+  if (c == 0 && lane == 0) smem[G::OFF_RED + 3] = __int_as_float(ec);
 }
 
 // The 2 x 2 blocks of the upper triangle of A = k(L, L) + eps I (see
@@ -957,19 +954,22 @@ __device__ __forceinline__ void solver_role(const MainArgs& a, int bh, float* sm
       a.st_x[static_cast<size_t>(bh) * m * m + e] = Xf[(e / m) * SX + (e % m)];
   }
   if (a.out_in_main) {
-    // the query workgroups form Y themselves: publish X, split into bf16
-    // parts (hi [MP][MP], then lo [MP][MP], two per 32-bit word), and raise
-    // its flag
+    // the query workgroups form Y themselves: publish 2^ex X (max < 2^15,
+    // ex from the Newton-Schulz scales) split into fp16 parts (hi [MP][MP],
+    // then lo [MP][MP], two per 32-bit word) and ex, then raise the flag
+    const int ex = __float_as_int(red[3]);
     unsigned* Xh = reinterpret_cast<unsigned*>(a.xw + static_cast<size_t>(bh) * MP * MP);
     unsigned* Xl = Xh + MP * MP / 2;
     for (int e = tid; e < MP * MP / 2; e += WGM) {
       const int row = e / (MP / 2), col = 2 * (e % (MP / 2));
       const bool in = row < N16 && col < N16;  // N16 is even
       unsigned hw, lw;
-      split2b(in ? Xf[row * SX + col] : 0.f, in ? Xf[row * SX + col + 1] : 0.f, hw, lw);
+      split2(in ? ldexpf(Xf[row * SX + col], ex) : 0.f, in ? ldexpf(Xf[row * SX + col + 1], ex) : 0.f,
+             hw, lw);
       __hip_atomic_store(Xh + e, hw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(Xl + e, lw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    if (tid == 0) __hip_atomic_store(x_exp(a, bh), static_cast<unsigned>(ex), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     raise_flag(flag_x(a, bh));
     return;
   }
@@ -1034,25 +1034,47 @@ __device__ void reduce_w(const MainArgs& a, int bh) {
   }
 }
 
-// Y^T = W^T X^T in place on split-bf16 MFMA: W^T in LDS as bf16 parts
-// (rows of WLD halves: hi at WH, lo at WL) is replaced by Y^T in the same
-// form; X comes split from global memory (hi then lo, rows of MP halves),
-// every operand load issued before the first MFMA.  Lane (g, r), slot s of
-// chunk p: contraction index 32 p + 8 g + s.
+// Single (not iterated) products also run on fp16 MFMA with two-part
+// operands (hi hi + lo hi + hi lo), each operand scaled by a power of two
+// into fp16 range first: per row for W^T and Y^T, one exponent for X (from
+// the Newton-Schulz scales), 2^14 for K_QL (values in (0, 1]).  Sums with
+// cancellation (Y and O mix signs) keep about 22 significant bits of each
+// term.
 constexpr int WLD = MP + 8;  // row stride (halves) of the split W^T / Y^T copies
 
-// Floats of the map role's first LDS area: P[j][token], or the two split
-// copies of W^T / Y^T.
+// Layout of the query workgroups' first LDS area: the split W^T / Y^T copies
+// (hi, lo: D rows of WLD halves each) and the per-row exponents EW.
+template <int D>
+struct QGeom {
+  static constexpr int OFF_WL = D * WLD / 2;   // floats
+  static constexpr int OFF_EW = D * WLD;
+  static constexpr int SIZE = OFF_EW + D;
+};
+
+// Floats of the map role's first LDS area: P[j][token], or the query
+// workgroups' split copies of W^T / Y^T.
 template <int D>
 constexpr int map_pj_size() {
-  return MP * LS > D * WLD ? MP * LS : D * WLD;
+  return MP * LS > QGeom<D>::SIZE ? MP * LS : QGeom<D>::SIZE;
 }
 
+// Y^T = W^T X^T in place: the split, row-scaled W^T in LDS (row c scaled by
+// 2^EW[c]) is replaced by the split Y^T with the same row scales times
+// 2^(ex - 22); X comes split from global memory (hi then lo, rows of MP
+// halves, scaled by 2^ex), every operand load issued before the first MFMA.
+// Lane (g, r), slot s of chunk p: contraction index 32 p + 8 g + s.
+// Each term of a row's sums is below 2^15 2^15 and n <= 64 terms, so the
+// accumulator is below 2^36 and 2^-22 of it is in fp16 range; values that
+// fall below fp16's normal range carry less than the fp32 accumulation's own
+// error.
 template <int D>
-__device__ void y_in_lds(uint16_t* WH, uint16_t* WL, const uint16_t* xh, const uint16_t* xl) {
+__device__ void y_in_lds(float* Q, const uint16_t* xh, const uint16_t* xl) {
+  using QG = QGeom<D>;
   constexpr int CBN = D / 16;
   constexpr int NBLK = 4 * CBN;          // 16x16 output blocks
   constexpr int NSB = (NBLK + 7) / 8;    // blocks per wave
+  uint16_t* WH = reinterpret_cast<uint16_t*>(Q);
+  uint16_t* WL = reinterpret_cast<uint16_t*>(Q + QG::OFF_WL);
   const int lane = threadIdx.x & 63, w = wave_id();
   const int lr = lane & 15, lg = lane >> 4;
   u32x4 bh[NSB][2], bl[NSB][2];
@@ -1081,9 +1103,9 @@ __device__ void y_in_lds(uint16_t* WH, uint16_t* WL, const uint16_t* xh, const u
         const int o = (16 * cb + lr) * WLD + 32 * p + 8 * lg;
         const u32x4 ah = *reinterpret_cast<const u32x4*>(WH + o);
         const u32x4 al = *reinterpret_cast<const u32x4*>(WL + o);
-        acc[s] = mfma_b(ah, bh[s][p], acc[s]);
-        acc[s] = mfma_b(al, bh[s][p], acc[s]);
-        acc[s] = mfma_b(ah, bl[s][p], acc[s]);
+        acc[s] = mfma_h(ah, bh[s][p], acc[s]);
+        acc[s] = mfma_h(al, bh[s][p], acc[s]);
+        acc[s] = mfma_h(ah, bl[s][p], acc[s]);
       }
     }
   }
@@ -1094,8 +1116,8 @@ __device__ void y_in_lds(uint16_t* WH, uint16_t* WL, const uint16_t* xh, const u
     if (blk < NBLK) {
       const int cb = blk / 4, jb = blk % 4;
       unsigned h[2], l[2];
-      split2b(acc[s][0], acc[s][1], h[0], l[0]);
-      split2b(acc[s][2], acc[s][3], h[1], l[1]);
+      split2(ldexpf(acc[s][0], -22), ldexpf(acc[s][1], -22), h[0], l[0]);
+      split2(ldexpf(acc[s][2], -22), ldexpf(acc[s][3], -22), h[1], l[1]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int o = (16 * cb + 4 * lg + i) * WLD + 16 * jb + lr;
@@ -1153,13 +1175,16 @@ __device__ __forceinline__ void store_o_block(const MainArgs& a, int bh, int t, 
 }
 
 // O rows of one 64-token tile: K_QL tile (PT, LDS, zero beyond m) times Y on
-// split-bf16 MFMA, with Y^T as bf16 parts in LDS (rows of WLD halves); the
-// tile's K_QL rows are split here, once per tile.  Wave w: tokens
-// 16 (w % 4) .. +15, column blocks w / 4, w / 4 + 2, ...
+// fp16 MFMA, with Y^T split in LDS (row c scaled by 2^(EW[c] + ex - 22),
+// y_in_lds) and the tile's K_QL rows scaled by 2^14 and split here, once per
+// tile.  Wave w: tokens 16 (w % 4) .. +15, column blocks w / 4, w / 4 + 2, ...
 template <int D>
-__device__ void out_tile(const MainArgs& a, int bh, int t, const float* PT, const uint16_t* YH,
-                           const uint16_t* YL) {
+__device__ void out_tile(const MainArgs& a, int bh, int t, const float* PT, const float* Q, int ex) {
+  using QG = QGeom<D>;
   constexpr int CBN = D / 16;
+  const uint16_t* YH = reinterpret_cast<const uint16_t*>(Q);
+  const uint16_t* YL = reinterpret_cast<const uint16_t*>(Q + QG::OFF_WL);
+  const int* EW = reinterpret_cast<const int*>(Q + QG::OFF_EW);
   const int lane = threadIdx.x & 63, w = wave_id();
   const int lr = lane & 15, lg = lane >> 4;
   const int tb = w & 3, ch = w >> 2;
@@ -1167,7 +1192,7 @@ __device__ void out_tile(const MainArgs& a, int bh, int t, const float* PT, cons
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     const float* ar = PT + (16 * tb + lr) * LS + 32 * p + 8 * lg;
-    split8b(ld4(ar), ld4(ar + 4), kh[p], kl[p]);
+    split8h(ld4(ar), ld4(ar + 4), 14, kh[p], kl[p]);
   }
 #pragma unroll
   for (int cb = ch; cb < CBN; cb += 2) {
@@ -1177,10 +1202,13 @@ __device__ void out_tile(const MainArgs& a, int bh, int t, const float* PT, cons
       const int o = (16 * cb + lr) * WLD + 32 * p + 8 * lg;
       const u32x4 yh = *reinterpret_cast<const u32x4*>(YH + o);
       const u32x4 yl = *reinterpret_cast<const u32x4*>(YL + o);
-      c = mfma_b(kh[p], yh, c);
-      c = mfma_b(kl[p], yh, c);
-      c = mfma_b(kh[p], yl, c);
+      c = mfma_h(kh[p], yh, c);
+      c = mfma_h(kl[p], yh, c);
+      c = mfma_h(kh[p], yl, c);
     }
+    const int sc = 8 - ex - EW[16 * cb + lr];  // 22 - 14 - (EW + ex)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[i] = ldexpf(c[i], sc);
     store_o_block<D>(a, bh, t, tb, cb, c);
   }
 }
@@ -1424,25 +1452,38 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
     // solver may still be running; then Y^T = W^T X^T in place, then the
     // output rows of the tiles (K_QL rows in LDS)
     wait_flags(slice_flags(a, bh), nslice, nullptr, a.sync);
-    uint16_t* WH = reinterpret_cast<uint16_t*>(PJ);
-    uint16_t* WL = WH + D * WLD;
     {
+      // row c of W^T (8 threads, consecutive lanes) scaled by 2^EW[c] into
+      // fp16 range, split
+      using QG = QGeom<D>;
+      static_assert(D * (MP / 8) <= WGM, "one W^T chunk per thread");
+      uint16_t* WH = reinterpret_cast<uint16_t*>(PJ);
+      uint16_t* WL = reinterpret_cast<uint16_t*>(PJ + QG::OFF_WL);
+      int* EW = reinterpret_cast<int*>(PJ + QG::OFF_EW);
       const float* wg = a.wt + static_cast<size_t>(bh) * D * MP;
-      for (int e = tid; e < D * (MP / 8); e += WGM) {
-        const int row = e / (MP / 8), k8 = 8 * (e % (MP / 8));
+      if (tid < D * (MP / 8)) {
+        const int row = tid / (MP / 8), k8 = 8 * (tid % (MP / 8));
+        const f4 v0 = ld4(wg + row * MP + k8), v1 = ld4(wg + row * MP + k8 + 4);
+        unsigned m = 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          m = max(m, max(__float_as_uint(v0[i]) & 0x7fffffffu, __float_as_uint(v1[i]) & 0x7fffffffu));
+        const int ew = fp16_scale(__uint_as_float(max8_u(m)));
         u32x4 hv, lv;
-        split8b(ld4(wg + row * MP + k8), ld4(wg + row * MP + k8 + 4), hv, lv);
+        split8h(v0, v1, ew, hv, lv);
         *reinterpret_cast<u32x4*>(WH + row * WLD + k8) = hv;
         *reinterpret_cast<u32x4*>(WL + row * WLD + k8) = lv;
+        if (k8 == 0) EW[row] = ew;
       }
     }
     wait_flag(flag_x(a, bh), a.sync);
+    const int ex = static_cast<int>(__hip_atomic_load(x_exp(a, bh), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     {
       const uint16_t* xh = reinterpret_cast<const uint16_t*>(a.xw + static_cast<size_t>(bh) * MP * MP);
-      y_in_lds<D>(WH, WL, xh, xh + MP * MP);
+      y_in_lds<D>(PJ, xh, xh + MP * MP);
     }
-    out_tile<D>(a, bh, t_beg, PT, WH, WL);
-    if (t_beg + 1 < t_end) out_tile<D>(a, bh, t_beg + 1, VT, WH, WL);
+    out_tile<D>(a, bh, t_beg, PT, PJ, ex);
+    if (t_beg + 1 < t_end) out_tile<D>(a, bh, t_beg + 1, VT, PJ, ex);
     return;
   }
 
