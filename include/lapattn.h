@@ -28,8 +28,11 @@
  *
  * Data layout.  Q, K, V and O are device pointers to [B, H, N, d] C-contiguous
  * tensors, 16-byte aligned, N = grid_h * grid_w, token n = row * grid_w + col.  The element
- * type is fp32 (LAPATTN_F32) or bf16 (LAPATTN_BF16) for all four; arithmetic
- * is fp32 throughout and bf16 outputs are rounded to nearest even.
+ * type is fp32 (LAPATTN_F32) or bf16 (LAPATTN_BF16) for all four.  Accuracy
+ * is that of fp32: kernel values in fp32; the Newton-Schulz products, X W
+ * and K_QL Y as fp32 sums of fp16 two-part operands scaled by powers of two
+ * (about 22 significant bits per operand); K_LK V in fp32.  bf16 outputs
+ * are rounded to nearest even.
  *
  * Ownership.  The caller allocates and frees Q, K, V, O and the workspace.
  * Compute entry points never allocate or free memory and never synchronise
@@ -145,7 +148,8 @@ int lapattn_init(void);
  * Concurrent calls that share a workspace race; calls on different streams
  * with different workspaces are independent.  Within a call, workgroups of
  * one launch hand per-head results to each other through the workspace
- * (device-scope release / acquire); every such wait is bounded in time. */
+ * (device-scope stores, then a per-workgroup flag); every such wait is
+ * bounded in time. */
 int lapattn_forward(const lapattn_desc_t* desc, const void* q, const void* k,
                     const void* v, float lambda, float eps, int32_t iters,
                     void* out, void* workspace, size_t workspace_bytes,

@@ -1,21 +1,23 @@
 // HIP kernels for Nystrom kernel attention (forward) on gfx950.
 //
-// Two launches per forward call (three when Q and K are the same tensor),
-// back to back on the caller's stream:
+// Two launches per forward call (three when Q and K are the same tensor, or
+// when the main grid cannot be resident at once), back to back on the
+// caller's stream:
 //   pool : landmarks L = window means of K                         (HBM stream)
 //   main : role-split workgroups
 //          - solver WGs (one per head, first in the grid, raised wave
 //            priority): A = k(L, L) + eps I, alpha, then the Newton-Schulz
-//            steps held in LDS on fp32 MFMA
+//            steps held in LDS on fp16 MFMA with scaled two-part operands
 //          - map WGs: kernel values of 64 tokens against every landmark on
 //            FP32 VALU (landmark coordinates are wave-uniform scalar operands);
 //            key tiles contract K_LK V on fp32 MFMA into per-workgroup
 //            partials of W^T; query tiles keep their K_QL rows in LDS
-//          - hand-offs: the last key WG of a head reduces the partials (fixed
-//            order, deterministic) into W^T; the second of (W^T, X) forms
-//            Y^T = W^T X^T; query WGs wait for it and write O = K_QL Y
-//   out  : (Q == K only) O = K_QL Y on fp32 MFMA from K_QL stored by the key
-//          tiles.
+//          - hand-offs: query WGs reduce the partials in fixed-order slices,
+//            copy W^T, wait for X from the solver, form Y = X W in LDS and
+//            write O = K_QL Y (fp16 MFMA, scaled two-part operands); on the
+//            output-launch plan the last key WG reduces and the second of
+//            (W^T, X) forms Y^T for the output launch
+//   out  : O = K_QL Y on fp32 MFMA from K_QL stored by the map WGs.
 // Outputs are fp32 or bf16 (RNE).
 //
 // Pages behind each step: average-pool landmarks (SOFT review, "method";
@@ -26,11 +28,12 @@
 // (LaplacianFormer summaries; SOFT review, "method"), S_hat = P^T A^+ P
 // (SOFT review, "method").
 //
-// MFMA operand convention used throughout (v_mfma_f32_16x16x4f32): for an
-// output block D[16][16] += sum_k A[i][k] B[k][j], lane l = 16*g + r supplies
-// A[r][k] and B[k][r] at sub-step s with k = KS*g + s (KS sub-steps), so each
-// lane reads KS *contiguous* k values of one row of A and one row of B^T.
-// The accumulator holds D[4g + i][r], i = 0..3.
+// MFMA operand convention: for an output block D[16][16] += sum_k A[i][k]
+// B[k][j], lane l = 16*g + r supplies A[r][k] and B[k][r] for the k values of
+// lane group g (v_mfma_f32_16x16x4f32: k = KS*g + s at sub-step s, so each
+// lane reads KS contiguous k values of one row of A and one row of B^T;
+// 16x16x32 fp16: 8 k values per instruction, assigned per use below).  The
+// accumulator holds D[4g + i][r], i = 0..3.
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
