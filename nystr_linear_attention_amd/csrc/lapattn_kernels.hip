@@ -208,8 +208,8 @@ struct MainArgs {
 //    output launch.
 // Words of head bh (kSyncHead from kSyncHead (bh + 1), each group on its own
 // cache lines): [0, 32) key ready flags, [32, 64) W^T slice flags, [64] X
-// ready, [65] scale exponent of the published X, [96] key arrivals, [97]
-// arrivals of W and X, [98] Y ready.
+// ready (its value carries the scale exponent of the published X), [96] key
+// arrivals, [97] arrivals of W and X, [98] Y ready.
 // Flags are plain device-scope stores (no read-modify-write on a shared word,
 // which serialises at memory when many workgroups arrive at once).
 //
@@ -240,7 +240,6 @@ __device__ __forceinline__ unsigned* head_sync(const MainArgs& a, int bh) {
 __device__ __forceinline__ unsigned* key_flags(const MainArgs& a, int bh) { return head_sync(a, bh); }
 __device__ __forceinline__ unsigned* slice_flags(const MainArgs& a, int bh) { return head_sync(a, bh) + 32; }
 __device__ __forceinline__ unsigned* flag_x(const MainArgs& a, int bh) { return head_sync(a, bh) + 64; }
-__device__ __forceinline__ unsigned* x_exp(const MainArgs& a, int bh) { return head_sync(a, bh) + 65; }
 __device__ __forceinline__ unsigned* cnt_w(const MainArgs& a, int bh) { return head_sync(a, bh) + 96; }
 __device__ __forceinline__ unsigned* cnt_y(const MainArgs& a, int bh) { return head_sync(a, bh) + 97; }
 __device__ __forceinline__ unsigned* flag_y(const MainArgs& a, int bh) { return head_sync(a, bh) + 98; }
@@ -262,25 +261,31 @@ __device__ __forceinline__ unsigned publish_arrive(unsigned* ctr) {
   return old_s;
 }
 
-// Completes this workgroup's device-scope stores, then sets *flag.
-__device__ __forceinline__ void raise_flag(unsigned* flag) {
+// Completes this workgroup's device-scope stores, then sets *flag to v.
+__device__ __forceinline__ void raise_flag(unsigned* flag, unsigned v = 1u) {
   drain_stores();
   __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_store(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) __hip_atomic_store(flag, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ void wait_flag(unsigned* flag, unsigned* timeouts) {
+// Waits until *flag is nonzero (bounded in time: then counts a timeout and
+// goes on); returns the value seen, in every thread.
+__device__ __forceinline__ unsigned wait_flag(unsigned* flag, unsigned* timeouts) {
+  __shared__ unsigned seen;
   if (threadIdx.x == 0) {
     const long long t0 = wall_clock64();
-    while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+    unsigned v;
+    while ((v = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0u) {
       if (wall_clock64() - t0 > kWaitTicks) {
         __hip_atomic_fetch_add(timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
       __builtin_amdgcn_s_sleep(2);
     }
+    seen = v;
   }
   __syncthreads();
+  return seen;
 }
 
 // Waits until flags[0 .. n) (n <= 32) and, when given, *extra are all set:
@@ -972,8 +977,8 @@ __device__ __forceinline__ void solver_role(const MainArgs& a, int bh, float* sm
       __hip_atomic_store(Xh + e, hw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(Xl + e, lw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (tid == 0) __hip_atomic_store(x_exp(a, bh), static_cast<unsigned>(ex), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    raise_flag(flag_x(a, bh));
+    // the flag's value carries ex (nonzero for any ex)
+    raise_flag(flag_x(a, bh), 0x10000u | (static_cast<unsigned>(ex) & 0xffffu));
     return;
   }
   if (red[1] != 0.f) {
@@ -1479,8 +1484,7 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
         if (k8 == 0) EW[row] = ew;
       }
     }
-    wait_flag(flag_x(a, bh), a.sync);
-    const int ex = static_cast<int>(__hip_atomic_load(x_exp(a, bh), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    const int ex = static_cast<int16_t>(wait_flag(flag_x(a, bh), a.sync) & 0xffffu);
     {
       const uint16_t* xh = reinterpret_cast<const uint16_t*>(a.xw + static_cast<size_t>(bh) * MP * MP);
       y_in_lds<D>(PJ, xh, xh + MP * MP);
