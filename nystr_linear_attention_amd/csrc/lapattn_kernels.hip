@@ -620,9 +620,19 @@ __device__ void ns_wave(const MainArgs& a, float* smem, int c, int lane, float a
   __syncthreads();  // the fp32 A (in the parity-1 X halves) is dead from here
 
   int ep = e0, ec = e0;  // scale exponents of X_{t-1} and X_t
-  // the operand of the first block of phase 1 (rows 0..15 of A) is constant
-  u32x4 oh[NC], ol[NC];
-  load_op<MB, D>(smem, G::OFF_AH, G::OFF_AL, lr, lg, oh, ol);
+  // A step is 2 MB blocks: q < MB is phase-1 block q (operand: rows 16 q ..
+  // of A), q >= MB is phase-2 block q - MB (operand: rows of X_t).  Operands
+  // go through a ring of 3 register slots, read 2 blocks ahead; the reads of
+  // the first two blocks, rows of A, which never changes, are issued at the
+  // end of the step before and stay in flight across its barrier.
+  u32x4 bh[3][NC], bl[3][NC];
+  auto load_block = [&](int q, int xoh, int xol, u32x4* h, u32x4* l) {
+    if (q < MB) load_op<MB, D>(smem, G::OFF_AH, G::OFF_AL, 16 * q + lr, lg, h, l);
+    else load_xop<MB, D>(smem, xoh, xol, 16 * (q - MB), lane, h, l);
+  };
+  constexpr int NPRE = MB >= 2 ? 2 : 1;  // leading blocks that are rows of A
+#pragma unroll
+  for (int q = 0; q < NPRE; ++q) load_block(q, 0, 0, bh[q], bl[q]);
 
   // One step; the last one writes X_{t+1} in fp32 instead of split.
   auto step = [&](int t, auto last_c) {
@@ -636,107 +646,127 @@ __device__ void ns_wave(const MainArgs& a, float* smem, int c, int lane, float a
 #pragma unroll
       for (int i = 0; i < MB; ++i) sv[i] = slot[256 * (1 - cb) + 64 * i + lane];
     }
+    // leading blocks that are rows of X_t (only when MB == 1)
+#pragma unroll
+    for (int q = NPRE; q < 2; ++q) load_block(q, xoh, xol, bh[q], bl[q]);
 
-    // phase 1: T-hat[:, c] = 2^(14 - eA - ec) A-hat X-hat_t[:, c]
-    const int sT = 14 - eA - ec;
+    const int sT = 14 - eA - ec;  // T-hat = 2^sT (A-hat X-hat_t)
     u32x4 th[NC], tl[NC];
 #pragma unroll
     for (int p = 0; p < NC; ++p) th[p] = tl[p] = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int ip = 0; ip < MB; ++ip) {
-      u32x4 nh[NC], nl[NC];
-      if (ip + 1 < MB) load_op<MB, D>(smem, G::OFF_AH, G::OFF_AL, 16 * (ip + 1) + lr, lg, nh, nl);
-      else load_xop<MB, D>(smem, xoh, xol, 0, lane, nh, nl);  // phase 2, block 0
-      f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int p = 0; p < NC; ++p) {
-        acc = mfma_h(oh[p], xh[p], acc);
-        acc = mfma_h(ol[p], xh[p], acc);
-        acc = mfma_h(oh[p], xl[p], acc);
-      }
-      if (!LAST && ip == 0) {
-        // publish max|X-hat_t| of the own columns (units 2^ec), one copy per
-        // lane; magnitudes compare as unsigned bit patterns
-        unsigned mx = 0u;
-#pragma unroll
-        for (int i = 0; i < MB; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) mx = max(mx, __float_as_uint(xs[i][j]) & 0x7fffffffu);
-        slot[256 * cb + 64 * c + lane] = __uint_as_float(wave_max_u(mx));
-      }
-      f4 tv;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) tv[j] = ldexpf(acc[j], sT);
-      split_block(tv, ip, th, tl);
-#pragma unroll
-      for (int p = 0; p < NC; ++p) {
-        oh[p] = nh[p];
-        ol[p] = nl[p];
-      }
-    }
-
-    // scale of X_{t+1}: max|X_{t-1}| 2^eN < 2^7 (the last X stays at 2^ec)
     int eN = ec;
-    if (!LAST) {
-      float mp = sv[0];
-#pragma unroll
-      for (int i = 1; i < MB; ++i) mp = fmaxf(mp, sv[i]);
-      if (mp > 0.f) eN = ep + 7 - __builtin_amdgcn_frexp_expf(mp);
-    }
-    // X-hat_{t+1} = 2^(eN - ec + 1) X-hat_t - 2^(eN - ec - 14) (X-hat_t T-hat)
-    const float c1 = ldexpf(1.0f, eN - ec + 1), c2 = -ldexpf(1.0f, eN - ec - 14);
+    float c1 = 0.f, c2 = 0.f;
     uint16_t* H = reinterpret_cast<uint16_t*>(smem + noh);
     uint16_t* L = reinterpret_cast<uint16_t*>(smem + nol);
     float* XF = smem + noh;
 
-    // phase 2: X_{t+1}[:, c] = 2 X_t[:, c] - X_t T[:, c]
-#pragma unroll
-    for (int ip = 0; ip < MB; ++ip) {
-      u32x4 nh[NC], nl[NC];
-      if (ip + 1 < MB) load_xop<MB, D>(smem, xoh, xol, 16 * (ip + 1), lane, nh, nl);
-      f4 acc = {0.f, 0.f, 0.f, 0.f};
+    // MFMAs of chunks [p0, p1) of block q into acc.
+    auto mfmas = [&](int q, int p0, int p1, f4 acc) -> f4 {
+      const u32x4* oh = bh[q % 3];
+      const u32x4* ol = bl[q % 3];
 #pragma unroll
       for (int p = 0; p < NC; ++p) {
-        acc = mfma_h(oh[p], th[p], acc);
-        acc = mfma_h(ol[p], th[p], acc);
-        acc = mfma_h(oh[p], tl[p], acc);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) xs[ip][j] = fmaf(acc[j], c2, c1 * xs[ip][j]);
-      if (!LAST) {
-        split_block(xs[ip], ip, xh, xl);
-        // rows 16 ip + 4 g .. + 3 of line col: one 8-byte store per part
-        const int o = col * XSH + 16 * ip + 4 * lg;
-        *reinterpret_cast<u32x2*>(H + o) =
-            u32x2{xh[ip >> 1][2 * (ip & 1)], xh[ip >> 1][2 * (ip & 1) + 1]};
-        *reinterpret_cast<u32x2*>(L + o) =
-            u32x2{xl[ip >> 1][2 * (ip & 1)], xl[ip >> 1][2 * (ip & 1) + 1]};
-      } else {
-        // the final iterate in fp32, over the X_{t+1} halves
-#pragma unroll
-        for (int j = 0; j < 4; ++j) XF[(16 * ip + 4 * lg + j) * SX + col] = ldexpf(xs[ip][j], -eN);
-      }
-      if (ip + 1 < MB) {
-#pragma unroll
-        for (int p = 0; p < NC; ++p) {
-          oh[p] = nh[p];
-          ol[p] = nl[p];
+        if (p < p0 || p >= p1) continue;
+        if (q < MB) {
+          // phase 1: T-hat[:, c] = 2^(14 - eA - ec) A-hat X-hat_t[:, c]
+          acc = mfma_h(oh[p], xh[p], acc);
+          acc = mfma_h(ol[p], xh[p], acc);
+          acc = mfma_h(oh[p], xl[p], acc);
+        } else {
+          // phase 2: X_{t+1}[:, c] = 2 X_t[:, c] - X_t T[:, c]
+          acc = mfma_h(oh[p], th[p], acc);
+          acc = mfma_h(ol[p], th[p], acc);
+          acc = mfma_h(oh[p], tl[p], acc);
         }
       }
+      return acc;
+    };
+    // What block q's result feeds: T-hat parts (phase 1) or X_{t+1} (phase 2).
+    auto epilogue = [&](int q, f4 acc) {
+      if (q < MB) {
+        const int ip = q;
+        if (!LAST && ip == 0) {
+          // publish max|X-hat_t| of the own columns (units 2^ec), one copy per
+          // lane; magnitudes compare as unsigned bit patterns
+          unsigned mx = 0u;
+#pragma unroll
+          for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) mx = max(mx, __float_as_uint(xs[i][j]) & 0x7fffffffu);
+          slot[256 * cb + 64 * c + lane] = __uint_as_float(wave_max_u(mx));
+        }
+        f4 tv;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) tv[j] = ldexpf(acc[j], sT);
+        split_block(tv, ip, th, tl);
+        if (ip == MB - 1) {
+          // scale of X_{t+1}: max|X_{t-1}| 2^eN < 2^7 (the last X stays at
+          // 2^ec); X-hat_{t+1} = 2^(eN - ec + 1) X-hat_t
+          //                      - 2^(eN - ec - 14) (X-hat_t T-hat)
+          if (!LAST) {
+            float mp = sv[0];
+#pragma unroll
+            for (int i = 1; i < MB; ++i) mp = fmaxf(mp, sv[i]);
+            if (mp > 0.f) eN = ep + 7 - __builtin_amdgcn_frexp_expf(mp);
+          }
+          c1 = ldexpf(1.0f, eN - ec + 1);
+          c2 = -ldexpf(1.0f, eN - ec - 14);
+        }
+      } else {
+        const int ip = q - MB;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xs[ip][j] = fmaf(acc[j], c2, c1 * xs[ip][j]);
+        if (!LAST) {
+          split_block(xs[ip], ip, xh, xl);
+          // rows 16 ip + 4 g .. + 3 of line col: one 8-byte store per part
+          const int o = col * XSH + 16 * ip + 4 * lg;
+          *reinterpret_cast<u32x2*>(H + o) =
+              u32x2{xh[ip >> 1][2 * (ip & 1)], xh[ip >> 1][2 * (ip & 1) + 1]};
+          *reinterpret_cast<u32x2*>(L + o) =
+              u32x2{xl[ip >> 1][2 * (ip & 1)], xl[ip >> 1][2 * (ip & 1) + 1]};
+        } else {
+          // the final iterate in fp32, over the X_{t+1} halves
+#pragma unroll
+          for (int j = 0; j < 4; ++j) XF[(16 * ip + 4 * lg + j) * SX + col] = ldexpf(xs[ip][j], -eN);
+        }
+      }
+    };
+
+    // Software pipeline: block q's operand reads go out 2 blocks ahead, and
+    // block q - 1's epilogue runs between block q's first-chunk MFMAs and the
+    // rest (scheduling fences keep that order).  The last phase-1 block feeds
+    // the phase-2 operand's chunk (MB - 1) / 2: deferring its epilogue into
+    // the first phase-2 block works only when that is not chunk 0.
+    constexpr bool DEFER_LAST_T = (MB - 1) / 2 > 0;
+    f4 prev = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < 2 * MB; ++q) {
+      if (q + 2 < 2 * MB) load_block(q + 2, xoh, xol, bh[(q + 2) % 3], bl[(q + 2) % 3]);
+      __builtin_amdgcn_sched_barrier(0);
+      f4 acc = mfmas(q, 0, 1, f4{0.f, 0.f, 0.f, 0.f});
+      __builtin_amdgcn_sched_barrier(0);
+      if (q > 0 && !(q == MB && !DEFER_LAST_T)) epilogue(q - 1, prev);
+      __builtin_amdgcn_sched_barrier(0);
+      acc = mfmas(q, 1, NC, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      prev = acc;
+      if (q == MB - 1 && !DEFER_LAST_T) epilogue(q, prev);
     }
+    epilogue(2 * MB - 1, prev);
     ep = ec;
     ec = eN;
     if (!LAST) {
-      // The operand of the next step's first block (rows 0..15 of A, which
-      // never changes) is read after this step's stores and may still be in
-      // flight at the barrier: wait only until the stores (issued before the
-      // 2 NC reads) have completed.  LDS operations of a wave complete in
-      // order.
+      // The next step's leading operands (rows of A, which never changes)
+      // are read after this step's stores and may still be in flight at the
+      // barrier: wait only until the stores (issued before those 2 NC NPRE
+      // reads) have completed.  LDS operations of a wave complete in order.
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
-      load_op<MB, D>(smem, G::OFF_AH, G::OFF_AL, lr, lg, oh, ol);
+#pragma unroll
+      for (int q = 0; q < NPRE; ++q) load_block(q, 0, 0, bh[q], bl[q]);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (NC == 2) asm volatile("s_waitcnt lgkmcnt(4)" ::: "memory");
+      if constexpr (2 * NC * NPRE == 8) asm volatile("s_waitcnt lgkmcnt(8)" ::: "memory");
+      else if constexpr (2 * NC * NPRE == 4) asm volatile("s_waitcnt lgkmcnt(4)" ::: "memory");
       else asm volatile("s_waitcnt lgkmcnt(2)" ::: "memory");
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
