@@ -1548,9 +1548,11 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
 }
 
 // Read-only inputs are separate __restrict__ parameters so that wave-uniform
-// reads of them (the landmark coordinates) compile to scalar loads.
+// reads of them (the landmark coordinates) compile to scalar loads.  At least
+// 4 waves per SIMD (at most 128 VGPRs): two workgroups per CU, which the
+// in-launch hand-offs count on (every workgroup of the grid resident).
 template <int D, int MB>
-__global__ __launch_bounds__(WGM, 2) void main_kernel(MainArgs a, const void* __restrict__ q,
+__global__ __launch_bounds__(WGM, 4) void main_kernel(MainArgs a, const void* __restrict__ q,
                                                     const void* __restrict__ k,
                                                     const void* __restrict__ v,
                                                     const float* __restrict__ L) {
