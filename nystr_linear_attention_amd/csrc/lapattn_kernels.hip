@@ -1115,21 +1115,19 @@ __device__ void y_in_lds(float* Q, const uint16_t* xh, const uint16_t* xl) {
   uint16_t* WL = reinterpret_cast<uint16_t*>(Q + QG::OFF_WL);
   const int lane = threadIdx.x & 63, w = wave_id();
   const int lr = lane & 15, lg = lane >> 4;
-  u32x4 bh[NSB][2], bl[NSB][2];
-  f4 acc[NSB];
+  // a wave's blocks w, w + 8 share column block jb = w % 4, so X rows
+  // 16 jb .. + 15 are read once per wave
+  const int jb = w % 4;
+  u32x4 bh[2], bl[2];
+  if (w < NBLK) {
 #pragma unroll
-  for (int s = 0; s < NSB; ++s) {
-    const int blk = w + 8 * s;
-    if (blk < NBLK) {
-      const int jb = blk % 4;
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const int o = (16 * jb + lr) * MP + 32 * p + 8 * lg;
-        bh[s][p] = *reinterpret_cast<const u32x4*>(xh + o);
-        bl[s][p] = *reinterpret_cast<const u32x4*>(xl + o);
-      }
+    for (int p = 0; p < 2; ++p) {
+      const int o = (16 * jb + lr) * MP + 32 * p + 8 * lg;
+      bh[p] = *reinterpret_cast<const u32x4*>(xh + o);
+      bl[p] = *reinterpret_cast<const u32x4*>(xl + o);
     }
   }
+  f4 acc[NSB];
 #pragma unroll
   for (int s = 0; s < NSB; ++s) {
     const int blk = w + 8 * s;
@@ -1141,9 +1139,9 @@ __device__ void y_in_lds(float* Q, const uint16_t* xh, const uint16_t* xl) {
         const int o = (16 * cb + lr) * WLD + 32 * p + 8 * lg;
         const u32x4 ah = *reinterpret_cast<const u32x4*>(WH + o);
         const u32x4 al = *reinterpret_cast<const u32x4*>(WL + o);
-        acc[s] = mfma_h(ah, bh[s][p], acc[s]);
-        acc[s] = mfma_h(al, bh[s][p], acc[s]);
-        acc[s] = mfma_h(ah, bl[s][p], acc[s]);
+        acc[s] = mfma_h(ah, bh[p], acc[s]);
+        acc[s] = mfma_h(al, bh[p], acc[s]);
+        acc[s] = mfma_h(ah, bl[p], acc[s]);
       }
     }
   }
@@ -1152,7 +1150,7 @@ __device__ void y_in_lds(float* Q, const uint16_t* xh, const uint16_t* xl) {
   for (int s = 0; s < NSB; ++s) {
     const int blk = w + 8 * s;
     if (blk < NBLK) {
-      const int cb = blk / 4, jb = blk % 4;
+      const int cb = blk / 4;
       unsigned h[2], l[2];
       split2(ldexpf(acc[s][0], -22), ldexpf(acc[s][1], -22), h[0], l[0]);
       split2(ldexpf(acc[s][2], -22), ldexpf(acc[s][3], -22), h[1], l[1]);
