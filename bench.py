@@ -319,7 +319,7 @@ def main(argv=None):
         dom, dom_ms, dom_flops = "main", kf["main"], wk["fused"]["flops"]
         dom_desc = ("main_kernel (fused: Newton-Schulz workgroups on split-fp16 MFMA beside "
                     "the L1 map workgroups on FP32 VALU, their K_LK V partials on fp32 MFMA "
-                    "and Y, O on split-bf16 MFMA)")
+                    "and Y, O on scaled split-fp16 MFMA)")
     ach = dom_flops / (dom_ms * 1e-3) / 1e12
     traffic = stored_traffic(w.name, "main_kernel") if not args.serial else None
     roofline = {
@@ -386,7 +386,7 @@ def main(argv=None):
         "dtype": "f32" if w.dtype == wl.F32 else "bf16 I/O, f32 compute",
         "arithmetic": "L1 / squared-L2 maps on FP32 VALU; Newton-Schulz products as fp16 "
                       "hi+lo splits on fp16 MFMA (about 22 significant bits); Y and O as "
-                      "bf16 hi+lo splits on bf16 MFMA (about 17 bits); K_LK V on fp32 MFMA; "
+                      "power-of-two scaled fp16 hi+lo splits on fp16 MFMA; K_LK V on fp32 MFMA; "
                       "fp32 accumulation throughout",
         "data": "synthetic (seeded, shapes and distributions of the workload; resident in HBM)",
         "config": {
