@@ -61,9 +61,24 @@ Plan make_plan(const lapattn_desc_t* d) {
   // Solver: the matrix zero padded up to whole 16x16 blocks.
   p.ns_mb = (p.m + 15) / 16;
   p.nT = (p.N + 63) / 64;
-  // Key-side workgroups cover S tiles each so that a head has at most 32 W
-  // partials.
+  // Key-side workgroups cover S tiles each.  At most 32 W partials per head
+  // when the last key workgroup reduces them alone (output-launch plan).
+  // When the whole grid can be resident at once (the query workgroups then
+  // reduce the partials in slices), the fewest tiles per key workgroup that
+  // keep it resident, up to 128 partials per head; the plan assumes separate
+  // Q and K (query workgroups present), which only sizes the workspace
+  // larger when they are the same tensor.
   p.S = (p.nT + 31) / 32;
+  {
+    const long nQ = (p.nT + kQueryTiles - 1) / kQueryTiles;
+    for (int S = 1; S < p.S; ++S) {
+      const long nP = (p.nT + S - 1) / S;
+      if (nP <= kMaxPartials && static_cast<long>(p.BH) * (1 + nP + nQ) <= kResidentWGs) {
+        p.S = S;
+        break;
+      }
+    }
+  }
   p.nP = (p.nT + p.S - 1) / p.S;
 
   const size_t BH = static_cast<size_t>(p.BH);

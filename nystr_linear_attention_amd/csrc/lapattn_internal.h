@@ -11,7 +11,14 @@ namespace lapattn {
 // padding holds exact zeros.
 constexpr int MP = 64;
 // Hand-off words per head (and once more for the words of the whole call).
-constexpr int kSyncHead = 128;
+constexpr int kSyncHead = 256;
+// 64-token tiles per query workgroup.
+constexpr int kQueryTiles = 2;
+// W partials per head at most (key ready flags per head).
+constexpr int kMaxPartials = 128;
+// Main-kernel workgroups that can be resident at once: 256 CUs x 2 (LDS and
+// registers allow two), with some margin.
+constexpr long kResidentWGs = 448;
 
 struct Plan {
   int B, H, gh, gw, D, ph, pw;

@@ -55,7 +55,7 @@ constexpr int WGM = 512;      // main kernel: 8 wave64
 constexpr int WGS = 256;      // pool / out kernels: 4 wave64
 constexpr int TILE = 64;      // tokens per map tile (one per lane)
 constexpr int NGRP = 8;       // landmark groups per map tile (one per wave)
-constexpr int QT = 2;         // 64-token tiles per query workgroup
+constexpr int QT = kQueryTiles;  // 64-token tiles per query workgroup
 
 __device__ __forceinline__ f4 mfma4(float a, float b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -207,9 +207,9 @@ struct MainArgs {
 //    and X each count one arrival; whichever is second forms Y^T for the
 //    output launch.
 // Words of head bh (kSyncHead from kSyncHead (bh + 1), each group on its own
-// cache lines): [0, 32) key ready flags, [32, 64) W^T slice flags, [64] X
-// ready (its value carries the scale exponent of the published X), [96] key
-// arrivals, [97] arrivals of W and X, [98] Y ready.
+// cache lines): [0, 128) key ready flags, [128, 160) W^T slice flags, [192]
+// X ready (its value carries the scale exponent of the published X), [224]
+// key arrivals, [225] arrivals of W and X, [226] Y ready.
 // Flags are plain device-scope stores (no read-modify-write on a shared word,
 // which serialises at memory when many workgroups arrive at once).
 //
@@ -238,11 +238,11 @@ __device__ __forceinline__ unsigned* head_sync(const MainArgs& a, int bh) {
   return a.sync + kSyncHead * (bh + 1);
 }
 __device__ __forceinline__ unsigned* key_flags(const MainArgs& a, int bh) { return head_sync(a, bh); }
-__device__ __forceinline__ unsigned* slice_flags(const MainArgs& a, int bh) { return head_sync(a, bh) + 32; }
-__device__ __forceinline__ unsigned* flag_x(const MainArgs& a, int bh) { return head_sync(a, bh) + 64; }
-__device__ __forceinline__ unsigned* cnt_w(const MainArgs& a, int bh) { return head_sync(a, bh) + 96; }
-__device__ __forceinline__ unsigned* cnt_y(const MainArgs& a, int bh) { return head_sync(a, bh) + 97; }
-__device__ __forceinline__ unsigned* flag_y(const MainArgs& a, int bh) { return head_sync(a, bh) + 98; }
+__device__ __forceinline__ unsigned* slice_flags(const MainArgs& a, int bh) { return head_sync(a, bh) + 128; }
+__device__ __forceinline__ unsigned* flag_x(const MainArgs& a, int bh) { return head_sync(a, bh) + 192; }
+__device__ __forceinline__ unsigned* cnt_w(const MainArgs& a, int bh) { return head_sync(a, bh) + 224; }
+__device__ __forceinline__ unsigned* cnt_y(const MainArgs& a, int bh) { return head_sync(a, bh) + 225; }
+__device__ __forceinline__ unsigned* flag_y(const MainArgs& a, int bh) { return head_sync(a, bh) + 226; }
 
 __device__ __forceinline__ void st_dev(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -288,18 +288,17 @@ __device__ __forceinline__ unsigned wait_flag(unsigned* flag, unsigned* timeouts
   return seen;
 }
 
-// Waits until flags[0 .. n) (n <= 32) and, when given, *extra are all set:
-// lane l of wave 0 polls one word; bounded in time like wait_flag.
-__device__ __forceinline__ void wait_flags(const unsigned* flags, int n, const unsigned* extra,
-                                           unsigned* timeouts) {
+// Waits until flags[0 .. n) (n <= 128) are all set: lane l of wave 0 polls
+// words l and l + 64; bounded in time like wait_flag.
+__device__ __forceinline__ void wait_flags(const unsigned* flags, int n, unsigned* timeouts) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
-    const unsigned* p = lane < n ? flags + lane : (lane == 63 ? extra : nullptr);
-    bool done = p == nullptr;
+    bool d0 = lane >= n, d1 = lane + 64 >= n;
     const long long t0 = wall_clock64();
     while (true) {
-      if (!done) done = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
-      if (__all(done)) break;
+      if (!d0) d0 = __hip_atomic_load(flags + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+      if (!d1) d1 = __hip_atomic_load(flags + lane + 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+      if (__all(d0 && d1)) break;
       if (wall_clock64() - t0 > kWaitTicks) {
         if (lane == 0) __hip_atomic_fetch_add(timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
@@ -881,11 +880,9 @@ __device__ __forceinline__ void solver_role(const MainArgs& a, int bh, float* sm
         amx = fmaxf(amx, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
       }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      sum = fmaxf(sum, __shfl_xor(sum, o));
-      amx = fmaxf(amx, __shfl_xor(amx, o));
-    }
+    // both are non-negative, so they compare as unsigned bit patterns
+    sum = __uint_as_float(wave_max_u(__float_as_uint(sum)));
+    amx = __uint_as_float(wave_max_u(__float_as_uint(amx)));
     if (lane == 0) {
       red[0] = sum;
       red[1] = 0.f;  // set once W^T is in LDS
@@ -1166,9 +1163,9 @@ __device__ void y_in_lds(float* Q, const uint16_t* xh, const uint16_t* xl) {
 }
 
 // Lines [l0, l1) (32 floats each) of W^T: the same sums as reduce_w, one
-// element per thread, every partial's load in flight at once (nP <= 32).
-// Slices are whole cache lines, so no line of W^T is written by two
-// workgroups.
+// element per thread, the loads of up to 32 partials in flight at once
+// (nP <= 128).  Slices are whole cache lines, so no line of W^T is written by
+// two workgroups.
 template <int D>
 __device__ void reduce_w_lines(const MainArgs& a, int bh, int l0, int l1) {
   const int nP = a.nP, m = a.m;
@@ -1176,17 +1173,17 @@ __device__ void reduce_w_lines(const MainArgs& a, int bh, int l0, int l1) {
   const float* pb = a.wpart + static_cast<size_t>(bh) * nP * ps;
   float* wg = a.wt + static_cast<size_t>(bh) * ps;
   for (int e = 32 * l0 + static_cast<int>(threadIdx.x); e < 32 * l1; e += WGM) {
-    float v[32];
-#pragma unroll
-    for (int p = 0; p < 32; ++p) v[p] = p < nP ? pb[p * ps + e] : 0.f;
     float sum = 0.f;
-    int p = 0;
-    // eight at a time, like reduce_w
-    for (; p + 8 <= nP; p += 8) {
+    for (int p0 = 0; p0 < nP; p0 += 32) {
+      const int np = nP - p0 < 32 ? nP - p0 : 32;
+      float v[32];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) sum += v[p + q];
+      for (int q = 0; q < 32; ++q) v[q] = q < np ? pb[(p0 + q) * ps + e] : 0.f;
+      // in partial order, like reduce_w
+#pragma unroll
+      for (int q = 0; q < 32; ++q)
+        if (q < np) sum += v[q];
     }
-    for (; p < nP; ++p) sum += v[p];
     const int c = e / MP, j = e % MP;
     const float w = j < m ? sum : 0.f;
     st_dev(wg + e, w);
@@ -1405,19 +1402,24 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
     }
     if constexpr (KIND == 0) {
       // L1 distances on VALU: landmarks two at a time (their scalar loads
-      // overlap); an odd last landmark is paired with itself and stored once
-      for (int j = jb; j < je; j += 2) {
-        const int j1 = j + 1 < je ? j + 1 : j;
+      // overlap); an odd last landmark on its own
+      int j = jb;
+      for (; j + 1 < je; j += 2) {
         float d0, d1;
-        dist_to2<D, KIND>(x, Lh + j * D, Lh + j1 * D, d0, d1);
+        dist_to2<D, KIND>(x, Lh + j * D, Lh + (j + 1) * D, d0, d1);
         const float k0 = valid ? exp2f(d0 * a.c_exp2) : 0.f;
         const float k1 = valid ? exp2f(d1 * a.c_exp2) : 0.f;
         if (key_role) {
           PJ[j * LS + lane] = k0;
-          PJ[j1 * LS + lane] = k1;
+          PJ[(j + 1) * LS + lane] = k1;
         }
         PTt[lane * LS + j] = k0;
-        PTt[lane * LS + j1] = k1;
+        PTt[lane * LS + j + 1] = k1;
+      }
+      if (j < je) {
+        const float k0 = valid ? exp2f(dist_to<D, KIND>(x, Lh + j * D) * a.c_exp2) : 0.f;
+        if (key_role) PJ[j * LS + lane] = k0;
+        PTt[lane * LS + j] = k0;
       }
     } else {
       gauss_tile<D, BF16>(a, src, Lh, bh, t, PTt, PJ, xx, key_role);
@@ -1480,14 +1482,14 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
     const int lps = (LINES + R - 1) / R;
     const int nslice = (LINES + lps - 1) / lps;
     if (u < nslice) {
-      wait_flags(key_flags(a, bh), nK, nullptr, a.sync);
+      wait_flags(key_flags(a, bh), nK, a.sync);
       reduce_w_lines<D>(a, bh, u * lps, min((u + 1) * lps, LINES));
       raise_flag(slice_flags(a, bh) + u);
     }
     // W^T complete: copy it to LDS (PJ is unused by query tiles) while the
     // solver may still be running; then Y^T = W^T X^T in place, then the
     // output rows of the tiles (K_QL rows in LDS)
-    wait_flags(slice_flags(a, bh), nslice, nullptr, a.sync);
+    wait_flags(slice_flags(a, bh), nslice, a.sync);
     {
       // row c of W^T (8 threads, consecutive lanes) scaled by 2^EW[c] into
       // fp16 range, split
@@ -1757,12 +1759,9 @@ hipError_t launch_out_d(const Plan& p, const Args& a, const Buffers& b, hipStrea
 }  // namespace
 
 bool out_in_main_launch(const Plan& p, int shared_qk) {
-  // 256 CUs x 2 main-kernel workgroups (LDS and registers allow two), with
-  // some margin
-  constexpr long kResident = 448;
   if (shared_qk) return false;
   const long nQ = (p.nT + QT - 1) / QT;
-  return static_cast<long>(p.BH) * (1 + p.nP + nQ) <= kResident;
+  return static_cast<long>(p.BH) * (1 + p.nP + nQ) <= kResidentWGs;
 }
 
 hipError_t launch_pool(const Plan& p, const Args& a, const Buffers& b, hipStream_t s, Ev ev) {

@@ -100,11 +100,17 @@ def test_null_desc():
 def test_workspace_bytes_linear_in_tokens():
     lib = _lib.lib()
     assert lib.lapattn_workspace_bytes(ctypes.byref(good_desc(d=48))) == 0
-    a = lib.lapattn_workspace_bytes(ctypes.byref(good_desc(B=1, H=1, grid_h=56, grid_w=56, d=64, pool_h=8, pool_w=8)))
-    b = lib.lapattn_workspace_bytes(ctypes.byref(good_desc(B=8, H=1, grid_h=56, grid_w=56, d=64, pool_h=8, pool_w=8)))
-    assert a > 0 and 7.5 * a <= b <= 8.5 * a
+    # 8 and 16 heads of 3136 tokens share the per-head plan (2 tiles per key
+    # workgroup), so the workspace doubles with the heads
+    a = lib.lapattn_workspace_bytes(ctypes.byref(good_desc(B=8, H=1, grid_h=56, grid_w=56, d=64, pool_h=8, pool_w=8)))
+    b = lib.lapattn_workspace_bytes(ctypes.byref(good_desc(B=16, H=1, grid_h=56, grid_w=56, d=64, pool_h=8, pool_w=8)))
+    assert a > 0 and 1.9 * a <= b <= 2.1 * a
+    # a single head takes one tile per key workgroup (more W partials), so
+    # its share is at least that of one of the 8 heads
+    c = lib.lapattn_workspace_bytes(ctypes.byref(good_desc(B=1, H=1, grid_h=56, grid_w=56, d=64, pool_h=8, pool_w=8)))
+    assert a / 8 <= c <= a / 4
     # at least the two [m, N] kernel maps in fp32
-    assert a >= 2 * 49 * 3136 * 4
+    assert c >= 2 * 49 * 3136 * 4
 
 
 def _fwd(desc, q=FAKE, k=FAKE + 0x1000000, v=FAKE + 0x2000000, out=FAKE + 0x3000000,
