@@ -592,7 +592,7 @@ __device__ __forceinline__ void split_block(f4 x, int i, u32x4* h, u32x4* l) {
 
 // Interior wave c: the Newton-Schulz steps on column block c.
 template <int MB, int D>
-__device__ void ns_wave(const MainArgs& a, float* smem, int c, int lane, float alpha, int eA,
+__device__ __forceinline__ void ns_wave(const MainArgs& a, float* smem, int c, int lane, float alpha, int eA,
                         int e0) {
   using G = NsGeom<MB, D>;
   constexpr int NC = G::NC, XSH = G::XSH, SX = G::SX, XARR = G::XARR;
@@ -836,7 +836,7 @@ __device__ void build_a(const MainArgs& a, int bh, const float* Ls, float* A, in
   }
 }
 
-template <int D, int MB>
+template <int D, int MB, int KIND>
 __device__ __forceinline__ void solver_role(const MainArgs& a, int bh, float* smem) {
   using G = NsGeom<MB, D>;
   constexpr int SX = G::SX, N16 = G::N16, RSH = G::RSH, WLS = G::WLS;
@@ -866,8 +866,7 @@ __device__ __forceinline__ void solver_role(const MainArgs& a, int bh, float* sm
     for (int e = tid; e < N16 * SX; e += WGM) Af[e] = 0.f;
   }
   __syncthreads();
-  if (a.kind == 0) build_a<D, 0>(a, bh, Ls, Af, SX);
-  else build_a<D, 1>(a, bh, Ls, Af, SX);
+  build_a<D, KIND>(a, bh, Ls, Af, SX);
   __syncthreads();
   // alpha = 1 / (max column abs-sum * max row abs-sum); A is symmetric, so
   // its largest column sum equals its largest row sum.  Also max|A|.
@@ -1162,32 +1161,50 @@ __device__ void y_in_lds(float* Q, const uint16_t* xh, const uint16_t* xl) {
   __syncthreads();
 }
 
-// Lines [l0, l1) (32 floats each) of W^T: the same sums as reduce_w, one
-// element per thread, the loads of up to 32 partials in flight at once
-// (nP <= 128).  Slices are whole cache lines, so no line of W^T is written by
-// two workgroups.
+// Lines [l0, l1) (32 floats each) of W^T, nP <= 128 partials, in chunks of
+// at most 512 elements: G threads per element (G = 512 / elements, at most
+// 8, a power of two), thread g sums partials [g P, (g + 1) P) in order with
+// the loads of up to 16 in flight, and the G sums are added in order of g
+// through LDS (red, up to 512 floats).  Slices are whole cache lines, so no
+// line of W^T is written by two workgroups.
 template <int D>
-__device__ void reduce_w_lines(const MainArgs& a, int bh, int l0, int l1) {
+__device__ void reduce_w_lines(const MainArgs& a, int bh, int l0, int l1, float* red) {
   const int nP = a.nP, m = a.m;
   const size_t ps = static_cast<size_t>(D) * MP;
   const float* pb = a.wpart + static_cast<size_t>(bh) * nP * ps;
   float* wg = a.wt + static_cast<size_t>(bh) * ps;
-  for (int e = 32 * l0 + static_cast<int>(threadIdx.x); e < 32 * l1; e += WGM) {
-    float sum = 0.f;
-    for (int p0 = 0; p0 < nP; p0 += 32) {
-      const int np = nP - p0 < 32 ? nP - p0 : 32;
-      float v[32];
+  const int tid = threadIdx.x;
+  for (int e0 = 32 * l0; e0 < 32 * l1; e0 += WGM) {
+    const int E = min(WGM, 32 * l1 - e0);
+    int G = 1;
+    while (G < 8 && 2 * G * E <= WGM) G *= 2;
+    const int P = (nP + G - 1) / G;
+    const int el = tid % E, g = tid / E;
+    if (g < G) {
+      const int pe = min(nP, (g + 1) * P);
+      float sum = 0.f;
+      for (int p0 = g * P; p0 < pe; p0 += 16) {
+        const int np = min(pe - p0, 16);
+        float v[16];
 #pragma unroll
-      for (int q = 0; q < 32; ++q) v[q] = q < np ? pb[(p0 + q) * ps + e] : 0.f;
-      // in partial order, like reduce_w
+        for (int q = 0; q < 16; ++q) v[q] = q < np ? pb[(p0 + q) * ps + e0 + el] : 0.f;
 #pragma unroll
-      for (int q = 0; q < 32; ++q)
-        if (q < np) sum += v[q];
+        for (int q = 0; q < 16; ++q)
+          if (q < np) sum += v[q];
+      }
+      red[g * E + el] = sum;
     }
-    const int c = e / MP, j = e % MP;
-    const float w = j < m ? sum : 0.f;
-    st_dev(wg + e, w);
-    if (a.st_w && j < m) a.st_w[(static_cast<size_t>(bh) * m + j) * D + c] = w;
+    __syncthreads();
+    if (tid < E) {
+      float sum = red[tid];
+      for (int h = 1; h < G; ++h) sum += red[h * E + tid];
+      const int e = e0 + tid;
+      const int c = e / MP, j = e % MP;
+      const float w = j < m ? sum : 0.f;
+      st_dev(wg + e, w);
+      if (a.st_w && j < m) a.st_w[(static_cast<size_t>(bh) * m + j) * D + c] = w;
+    }
+    __syncthreads();  // red is reused by the next chunk
   }
 }
 
@@ -1483,7 +1500,7 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
     const int nslice = (LINES + lps - 1) / lps;
     if (u < nslice) {
       wait_flags(key_flags(a, bh), nK, a.sync);
-      reduce_w_lines<D>(a, bh, u * lps, min((u + 1) * lps, LINES));
+      reduce_w_lines<D>(a, bh, u * lps, min((u + 1) * lps, LINES), PJ);
       raise_flag(slice_flags(a, bh) + u);
     }
     // W^T complete: copy it to LDS (PJ is unused by query tiles) while the
@@ -1550,8 +1567,10 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
 // Read-only inputs are separate __restrict__ parameters so that wave-uniform
 // reads of them (the landmark coordinates) compile to scalar loads.  At least
 // 4 waves per SIMD (at most 128 VGPRs): two workgroups per CU, which the
-// in-launch hand-offs count on (every workgroup of the grid resident).
-template <int D, int MB>
+// in-launch hand-offs count on (every workgroup of the grid resident).  One
+// kernel per kernel kind and I/O type, so that a launch carries the code of
+// its own map role only (the code of all four exceeds the instruction cache).
+template <int D, int MB, int KIND, bool BF16>
 __global__ __launch_bounds__(WGM, 4) void main_kernel(MainArgs a, const void* __restrict__ q,
                                                     const void* __restrict__ k,
                                                     const void* __restrict__ v,
@@ -1564,25 +1583,21 @@ __global__ __launch_bounds__(WGM, 4) void main_kernel(MainArgs a, const void* __
   float smem[MAP_SMEM > SOLVER_SMEM ? MAP_SMEM : SOLVER_SMEM];
   const int b = blockIdx.x;
   if (b < a.ns_blocks) {
-    solver_role<D, MB>(a, b, smem);
+    solver_role<D, MB, KIND>(a, b, smem);
   } else {
-    const int mb = b - a.ns_blocks;
-    if (a.kind == 0) {
-      if (a.bf16) map_role<D, 0, true>(a, q, k, v, L, mb, smem);
-      else map_role<D, 0, false>(a, q, k, v, L, mb, smem);
-    } else {
-      if (a.bf16) map_role<D, 1, true>(a, q, k, v, L, mb, smem);
-      else map_role<D, 1, false>(a, q, k, v, L, mb, smem);
-    }
+    map_role<D, KIND, BF16>(a, q, k, v, L, b - a.ns_blocks, smem);
   }
 }
 
 // ---------------------------------------------------------------------------
-// pool: one workgroup per (landmark, head).  Thread (g, c4) sums a float4
-// column chunk over every G-th token of the window (loads issued 4 at a
-// time); a fixed-order LDS reduction over g finishes the mean.
+// pool: one workgroup per (LPW consecutive landmarks, head).  Thread
+// (g, c4) sums a float4 column chunk over every G-th token of each window,
+// the loads of all LPW windows (4 tokens each per pass) issued together; a
+// fixed-order LDS reduction over g finishes each mean.  LPW > 1 when the
+// grid of one landmark per workgroup would not be resident at once: fewer,
+// longer workgroups with more loads in flight.
 // ---------------------------------------------------------------------------
-template <int D, bool BF16>
+template <int D, bool BF16, int LPW>
 __global__ __launch_bounds__(WGS) void pool_kernel(const void* __restrict__ K,
                                                    float* __restrict__ L,
                                                    float* __restrict__ st_L,
@@ -1590,97 +1605,147 @@ __global__ __launch_bounds__(WGS) void pool_kernel(const void* __restrict__ K,
                                                    int pw, int m, int N) {
   constexpr int C4 = D / 4;
   constexpr int G = WGS / C4;
-  constexpr int U = 4;  // loads in flight per thread
-  __shared__ f4 part[WGS];
-  const int j = blockIdx.x, bh = blockIdx.y;
+  constexpr int U = 4;  // loads in flight per thread and window
+  __shared__ f4 part[LPW][WGS];
+  const int j0 = blockIdx.x * LPW, bh = blockIdx.y;
   const int tid = threadIdx.x, c4 = tid % C4, g = tid / C4;
   // hand-off words of the main launch start at zero every call
-  if (j == 0) {
+  if (blockIdx.x == 0) {
     for (int e = tid; e < kSyncHead; e += WGS) sync[kSyncHead * (bh + 1) + e] = 0u;
     if (bh == 0 && tid == 0) sync[0] = 0u;
   }
   const int mw = gw / pw;
-  const int R = j / mw, C = j % mw;
   const int cnt = ph * pw;
   const size_t base = static_cast<size_t>(bh) * N;
-  f4 s = {0.f, 0.f, 0.f, 0.f};
-  for (int t0 = g; t0 < cnt; t0 += U * G) {
-    f4 v[U];
+  f4 s[LPW];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      // tokens past the window are clamped to its first token and dropped below
-      const int t = t0 + u * G < cnt ? t0 + u * G : 0;
-      const int n = (R * ph + t / pw) * gw + C * pw + t % pw;
-      v[u] = load4_io(K, (base + n) * D + 4 * c4, BF16);
+  for (int l = 0; l < LPW; ++l) s[l] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int t0 = g; t0 < cnt; t0 += U * G) {
+    f4 v[LPW][U];
+#pragma unroll
+    for (int l = 0; l < LPW; ++l) {
+      // landmarks past m read window 0 and are dropped below
+      const int j = j0 + l < m ? j0 + l : 0;
+      const int R = j / mw, C = j % mw;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        // tokens past the window are clamped to its first token and dropped below
+        const int t = t0 + u * G < cnt ? t0 + u * G : 0;
+        const int n = (R * ph + t / pw) * gw + C * pw + t % pw;
+        v[l][u] = load4_io(K, (base + n) * D + 4 * c4, BF16);
+      }
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (t0 + u * G < cnt) s += v[u];
+    for (int l = 0; l < LPW; ++l)
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (t0 + u * G < cnt) s[l] += v[l][u];
   }
-  part[tid] = s;
+#pragma unroll
+  for (int l = 0; l < LPW; ++l) part[l][tid] = s[l];
   __syncthreads();
-  if (tid < C4) {
-    f4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int i = 0; i < G; ++i) acc += part[i * C4 + tid];
-    const f4 mean = acc / static_cast<float>(cnt);
-    float* dst = L + (static_cast<size_t>(bh) * m + j) * D + 4 * tid;
-    st4(dst, mean);
-    if (st_L) st4(st_L + (static_cast<size_t>(bh) * m + j) * D + 4 * tid, mean);
+  if (tid < LPW * C4) {
+    const int l = tid / C4, c = tid % C4, j = j0 + l;
+    if (j < m) {
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < G; ++i) acc += part[l][i * C4 + c];
+      const f4 mean = acc / static_cast<float>(cnt);
+      st4(L + (static_cast<size_t>(bh) * m + j) * D + 4 * c, mean);
+      if (st_L) st4(st_L + (static_cast<size_t>(bh) * m + j) * D + 4 * c, mean);
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// out: O = K_QL Y.  Workgroup = (head, 64 tokens); wave w computes tokens
-// 16w..16w+15 of the tile against all D columns, contraction over KS*4 =
-// 16 ceil(m/16) landmarks (zero padded).
+// out: O = K_QL Y for the output-launch plan.  Workgroup = (head, 4 tiles of
+// 64 tokens); Y^T (from compute_y, columns >= m zero) is scaled per row into
+// fp16 range and split in LDS once per workgroup; wave w forms the output
+// rows of tile w on fp16 MFMA with two-part operands, K_QL scaled by 2^14 and
+// split in registers (the arithmetic of out_tile in the main launch).
+// Contraction chunks of 32 landmarks past mpad read as zero.
 // ---------------------------------------------------------------------------
-template <int D, int KS>
+constexpr int OUT_TILES = WGS / 64;  // tiles per output workgroup (one per wave)
+
+template <int D>
 __global__ __launch_bounds__(WGS) void out_kernel(const float* __restrict__ kql,
                                                   const float* __restrict__ yt,
                                                   void* __restrict__ O, int bf16, int N,
-                                                  int mpad, int nT) {
+                                                  int mpad, int nWo) {
   constexpr int CBN = D / 16;
-  const int bh = blockIdx.x / nT, t = blockIdx.x % nT;
-  const int lane = threadIdx.x & 63, w = wave_id();
+  __shared__ __attribute__((aligned(16))) uint16_t YH[D * WLD];
+  __shared__ __attribute__((aligned(16))) uint16_t YL[D * WLD];
+  __shared__ int EW[D];
+  const int bh = blockIdx.x / nWo, wo = blockIdx.x % nWo;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int lr = lane & 15, lg = lane >> 4;
-  const int tok = t * TILE + 16 * w + lr;
-  const int tokc = tok < N ? tok : N - 1;
-  const float* ar = kql + (static_cast<size_t>(bh) * N + tokc) * mpad + KS * lg;
-  float av[KS];
+  const int t = wo * OUT_TILES + w;  // this wave's tile
+  const bool active = t * TILE < N;
+  // K_QL operands of the tile's 4 token blocks, loads issued before the Y^T
+  // split so that the two memory latencies overlap
+  const float* kb = kql + static_cast<size_t>(bh) * N * mpad;
+  f4 av[4][2][2];
 #pragma unroll
-  for (int q = 0; q < KS / 4; ++q) {
-    const f4 u = ld4(ar + 4 * q);
-    av[4 * q] = u[0];
-    av[4 * q + 1] = u[1];
-    av[4 * q + 2] = u[2];
-    av[4 * q + 3] = u[3];
-  }
-  f4 acc[CBN];
+  for (int tb = 0; tb < 4; ++tb) {
+    const int n = t * TILE + 16 * tb + lr;
+    const float* ar = kb + static_cast<size_t>(n < N ? n : N - 1) * mpad;
 #pragma unroll
-  for (int cb = 0; cb < CBN; ++cb) {
-    const float* br = yt + (static_cast<size_t>(bh) * D + 16 * cb + lr) * MP + KS * lg;
-    f4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int q = 0; q < KS / 4; ++q) {
-      const f4 b4 = ld4(br + 4 * q);
-      c = mfma4(av[4 * q], b4[0], c);
-      c = mfma4(av[4 * q + 1], b4[1], c);
-      c = mfma4(av[4 * q + 2], b4[2], c);
-      c = mfma4(av[4 * q + 3], b4[3], c);
+    for (int p = 0; p < 2; ++p) {
+      const int k = 32 * p + 8 * lg;
+      if (active && k < mpad) {
+        av[tb][p][0] = ld4(ar + k);
+        av[tb][p][1] = ld4(ar + k + 4);
+      } else {
+        av[tb][p][0] = av[tb][p][1] = f4{0.f, 0.f, 0.f, 0.f};
+      }
     }
-    acc[cb] = c;
   }
+  // row c of Y^T by 8 consecutive lanes (8 values each), scaled by 2^EW[c]
+  // into fp16 range and split
+  {
+    const float* yg = yt + static_cast<size_t>(bh) * D * MP;
+    for (int e = tid; e < D * (MP / 8); e += WGS) {
+      const int row = e / (MP / 8), k8 = 8 * (e % (MP / 8));
+      const f4 v0 = ld4(yg + row * MP + k8), v1 = ld4(yg + row * MP + k8 + 4);
+      unsigned mx = 0u;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int n = t * TILE + 16 * w + 4 * lg + i;
-    if (n < N) {
-      const size_t o = (static_cast<size_t>(bh) * N + n) * D + lr;
+      for (int i = 0; i < 4; ++i)
+        mx = max(mx, max(__float_as_uint(v0[i]) & 0x7fffffffu, __float_as_uint(v1[i]) & 0x7fffffffu));
+      const int ew = fp16_scale(__uint_as_float(max8_u(mx)));
+      u32x4 hv, lv;
+      split8h(v0, v1, ew, hv, lv);
+      *reinterpret_cast<u32x4*>(YH + row * WLD + k8) = hv;
+      *reinterpret_cast<u32x4*>(YL + row * WLD + k8) = lv;
+      if (k8 == 0) EW[row] = ew;
+    }
+  }
+  __syncthreads();
+  if (!active) return;
 #pragma unroll
-      for (int cb = 0; cb < CBN; ++cb) {
-        if (bf16) {
-          static_cast<uint16_t*>(O)[o + 16 * cb] = f32_to_bf16_rne(acc[cb][i]);
-        } else {
-          static_cast<float*>(O)[o + 16 * cb] = acc[cb][i];
+  for (int tb = 0; tb < 4; ++tb) {
+    u32x4 kh[2], kl[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) split8h(av[tb][p][0], av[tb][p][1], 14, kh[p], kl[p]);
+#pragma unroll
+    for (int cb = 0; cb < CBN; ++cb) {
+      f4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int o = (16 * cb + lr) * WLD + 32 * p + 8 * lg;
+        const u32x4 yh = *reinterpret_cast<const u32x4*>(YH + o);
+        const u32x4 yl = *reinterpret_cast<const u32x4*>(YL + o);
+        c = mfma_h(kh[p], yh, c);
+        c = mfma_h(kl[p], yh, c);
+        c = mfma_h(kh[p], yl, c);
+      }
+      const int sc = -14 - EW[16 * cb + lr];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = t * TILE + 16 * tb + 4 * lg + i;
+        if (n < N) {
+          const size_t o = (static_cast<size_t>(bh) * N + n) * D + 16 * cb + lr;
+          const float val = ldexpf(c[i], sc);
+          if (bf16) static_cast<uint16_t*>(O)[o] = f32_to_bf16_rne(val);
+          else static_cast<float*>(O)[o] = val;
         }
       }
     }
@@ -1711,19 +1776,34 @@ inline float exp2_scale(float lambda) {
   return static_cast<float>(-1.4426950408889634 / static_cast<double>(lambda));
 }
 
+template <int D, int LPW>
+hipError_t launch_pool_dl(const Plan& p, const Args& a, const Buffers& b, hipStream_t s, Ev ev) {
+  const dim3 grid((p.m + LPW - 1) / LPW, p.BH);
+  if (p.bf16)
+    return launch(pool_kernel<D, true, LPW>, grid, dim3(WGS), s, ev, a.k, b.L, a.st_L, b.sync,
+                  p.gw, p.ph, p.pw, p.m, p.N);
+  return launch(pool_kernel<D, false, LPW>, grid, dim3(WGS), s, ev, a.k, b.L, a.st_L, b.sync,
+                p.gw, p.ph, p.pw, p.m, p.N);
+}
+
 template <int D>
 hipError_t launch_pool_d(const Plan& p, const Args& a, const Buffers& b, hipStream_t s, Ev ev) {
-  const dim3 grid(p.m, p.BH);
-  if (p.bf16)
-    return launch(pool_kernel<D, true>, grid, dim3(WGS), s, ev, a.k, b.L, a.st_L, b.sync, p.gw,
-                  p.ph, p.pw, p.m, p.N);
-  return launch(pool_kernel<D, false>, grid, dim3(WGS), s, ev, a.k, b.L, a.st_L, b.sync, p.gw,
-                p.ph, p.pw, p.m, p.N);
+  // one landmark per workgroup while that grid is resident at once (8
+  // workgroups of 256 threads per CU), else four
+  if (static_cast<long>(p.m) * p.BH <= 2048) return launch_pool_dl<D, 1>(p, a, b, s, ev);
+  return launch_pool_dl<D, 4>(p, a, b, s, ev);
 }
 
 template <int D, int MB>
 hipError_t launch_main_dm(const MainArgs& ma, unsigned grid, hipStream_t s, Ev ev) {
-  return launch(main_kernel<D, MB>, dim3(grid), dim3(WGM), s, ev, ma, ma.q, ma.k, ma.v, ma.L);
+  if (ma.kind == 0) {
+    if (ma.bf16)
+      return launch(main_kernel<D, MB, 0, true>, dim3(grid), dim3(WGM), s, ev, ma, ma.q, ma.k, ma.v, ma.L);
+    return launch(main_kernel<D, MB, 0, false>, dim3(grid), dim3(WGM), s, ev, ma, ma.q, ma.k, ma.v, ma.L);
+  }
+  if (ma.bf16)
+    return launch(main_kernel<D, MB, 1, true>, dim3(grid), dim3(WGM), s, ev, ma, ma.q, ma.k, ma.v, ma.L);
+  return launch(main_kernel<D, MB, 1, false>, dim3(grid), dim3(WGM), s, ev, ma, ma.q, ma.k, ma.v, ma.L);
 }
 
 template <int D>
@@ -1739,21 +1819,10 @@ hipError_t launch_main_d(const Plan& p, const MainArgs& ma, unsigned grid, hipSt
 
 template <int D>
 hipError_t launch_out_d(const Plan& p, const Args& a, const Buffers& b, hipStream_t s, Ev ev) {
-  const dim3 grid(p.BH * p.nT);
-  switch (p.mpad / 16) {
-    case 1:
-      return launch(out_kernel<D, 4>, grid, dim3(WGS), s, ev, b.kql, b.yt, a.out, p.bf16, p.N,
-                    p.mpad, p.nT);
-    case 2:
-      return launch(out_kernel<D, 8>, grid, dim3(WGS), s, ev, b.kql, b.yt, a.out, p.bf16, p.N,
-                    p.mpad, p.nT);
-    case 3:
-      return launch(out_kernel<D, 12>, grid, dim3(WGS), s, ev, b.kql, b.yt, a.out, p.bf16, p.N,
-                    p.mpad, p.nT);
-    default:
-      return launch(out_kernel<D, 16>, grid, dim3(WGS), s, ev, b.kql, b.yt, a.out, p.bf16, p.N,
-                    p.mpad, p.nT);
-  }
+  const int nWo = (p.nT + OUT_TILES - 1) / OUT_TILES;
+  const dim3 grid(p.BH * nWo);
+  return launch(out_kernel<D>, grid, dim3(WGS), s, ev, b.kql, b.yt, a.out, p.bf16, p.N, p.mpad,
+                nWo);
 }
 
 }  // namespace
