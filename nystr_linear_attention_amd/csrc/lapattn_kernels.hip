@@ -486,9 +486,12 @@ struct NsGeom {
   static constexpr int RSW = 8 * MB + 4;
   static constexpr int RSH = 2 * RSW;          // row stride in halves
   static constexpr int ARR = N16 * RSW;        // words per array
-  // X_t in half precision, column major: line k holds X_t[0..N16)[k], lines
-  // of XSW words (8 mod 32, so the 8-byte reads of 16 lines x 4 chunks and
-  // the 8-byte writes of 16 lines x 4 row groups spread over the banks).
+  // X_t in half precision, column major: line k holds X_t[0..N16)[k] in
+  // 8-byte chunks of 4 rows, chunk c of line k stored at position
+  // c ^ ((k >> 2) & 3) (xchunk); lines of XSW words (8 mod 32).  The reads of
+  // 4 chunks of 4 lines per 16 lanes and the writes of one chunk of 16
+  // consecutive lines per 16 lanes then both fall on distinct banks (without
+  // the swizzle the writes were 4-way bank conflicts).
   static constexpr int XSW = 40;
   static constexpr int XSH = 2 * XSW;          // line stride in halves
   static constexpr int XARR = N16 * XSW;       // words per array
@@ -544,6 +547,10 @@ __device__ __forceinline__ void load_op(const float* smem, int offh, int offl, i
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
+// Position of 8-byte chunk c (rows 4c .. 4c + 3) within line k of the
+// half-precision X_t arrays (see NsGeom).
+__device__ __forceinline__ int xchunk(int k, int c) { return c ^ ((k >> 2) & 3); }
+
 // A operand of one 16-row block of X_t (rows r0 .. r0 + 15) from the column-
 // major arrays at word offsets offh / offl, with transposing LDS reads: in
 // each 16-lane group, lane i receives half i % 4 of the 8 bytes read by lane
@@ -555,8 +562,9 @@ __device__ __forceinline__ void load_xop(float* smem, int offh, int offl, int r0
                                          u32x4* h, u32x4* l) {
   using G = NsGeom<MB, D>;
   const int lg = lane >> 4, j = (lane >> 2) & 3, q = lane & 3;
-  // halves offset of (line 4 g + j, row r0 + 4 q)
-  const int base = (4 * lg + j) * G::XSH + r0 + 4 * q;
+  // halves offset of (line 4 g + j, rows r0 + 4 q ..): r0 is a multiple of
+  // 16 and lines 16 (2p + h) + 4 g + j all have (k >> 2) & 3 = g
+  const int base = (4 * lg + j) * G::XSH + 4 * xchunk(4 * lg + j, r0 / 4 + q);
   uint16_t* H = reinterpret_cast<uint16_t*>(smem + offh);
   uint16_t* L = reinterpret_cast<uint16_t*>(smem + offl);
 #pragma unroll
@@ -718,7 +726,7 @@ __device__ __forceinline__ void ns_wave(const MainArgs& a, float* smem, int c, i
         if (!LAST) {
           split_block(xs[ip], ip, xh, xl);
           // rows 16 ip + 4 g .. + 3 of line col: one 8-byte store per part
-          const int o = col * XSH + 16 * ip + 4 * lg;
+          const int o = col * XSH + 4 * xchunk(col, 4 * ip + lg);
           *reinterpret_cast<u32x2*>(H + o) =
               u32x2{xh[ip >> 1][2 * (ip & 1)], xh[ip >> 1][2 * (ip & 1) + 1]};
           *reinterpret_cast<u32x2*>(L + o) =
@@ -916,8 +924,8 @@ __device__ __forceinline__ void solver_role(const MainArgs& a, int bh, float* sm
         // X_0 is exactly symmetric: its line i (column i) is its row i
         split2(ldexpf(xv[0], e0), ldexpf(xv[1], e0), h0w, l0w);
         split2(ldexpf(xv[2], e0), ldexpf(xv[3], e0), h1w, l1w);
-        *reinterpret_cast<u32x2*>(XH + i * G::XSH + 4 * q) = u32x2{h0w, h1w};
-        *reinterpret_cast<u32x2*>(XL + i * G::XSH + 4 * q) = u32x2{l0w, l1w};
+        *reinterpret_cast<u32x2*>(XH + i * G::XSH + 4 * xchunk(i, q)) = u32x2{h0w, h1w};
+        *reinterpret_cast<u32x2*>(XL + i * G::XSH + 4 * xchunk(i, q)) = u32x2{l0w, l1w};
       } else {
         st4(smem + G::OFF_X + i * SX + 4 * q, xv);
       }
