@@ -3,7 +3,8 @@
 // Two launches per forward call (three when Q and K are the same tensor, or
 // when the main grid cannot be resident at once), back to back on the
 // caller's stream:
-//   pool : landmarks L = window means of K                         (HBM stream)
+//   pool : landmarks L = window means of K (one or four landmarks per
+//          workgroup)                                             (HBM stream)
 //   main : role-split workgroups
 //          - solver WGs (one per head, first in the grid, raised wave
 //            priority): A = k(L, L) + eps I, alpha, then the Newton-Schulz
@@ -17,7 +18,8 @@
 //            write O = K_QL Y (fp16 MFMA, scaled two-part operands); on the
 //            output-launch plan the last key WG reduces and the second of
 //            (W^T, X) forms Y^T for the output launch
-//   out  : O = K_QL Y on fp32 MFMA from K_QL stored by the map WGs.
+//   out  : O = K_QL Y from K_QL stored by the map WGs, on fp16 MFMA with
+//          scaled two-part operands (4 tiles per workgroup).
 // Outputs are fp32 or bf16 (RNE).
 //
 // Pages behind each step: average-pool landmarks (SOFT review, "method";
