@@ -63,6 +63,12 @@ __device__ __forceinline__ f4 mfma4(float a, float b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// 2^x on the hardware exponential.  Kernel values are exp2 of
+// -dist / lambda * log2(e) <= 0; for arguments down to -126 this is exactly
+// what exp2f returns (exp2f adds only a rescaling for results below the
+// normal range, ~1e-38, where the map value is zero for any purpose here).
+__device__ __forceinline__ float exp2_map(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }
@@ -1333,7 +1339,7 @@ __device__ void gauss_tile(const MainArgs& a, const void* src, const float* Lh, 
       for (int i = 0; i < 4; ++i) {
         const int tt = 16 * tb + 4 * lg + i;
         const float d = fmaxf(fmaf(-2.0f, c[i], xx[tt] + pl), 0.0f);
-        const float kv = (j < m && t * TILE + tt < N) ? exp2f(d * a.c_exp2) : 0.f;
+        const float kv = (j < m && t * TILE + tt < N) ? exp2_map(d * a.c_exp2) : 0.f;
         PTt[tt * LS + j] = kv;
         if (key_role) PJ[j * LS + tt] = kv;
       }
@@ -1434,8 +1440,8 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
       for (; j + 1 < je; j += 2) {
         float d0, d1;
         dist_to2<D, KIND>(x, Lh + j * D, Lh + (j + 1) * D, d0, d1);
-        const float k0 = valid ? exp2f(d0 * a.c_exp2) : 0.f;
-        const float k1 = valid ? exp2f(d1 * a.c_exp2) : 0.f;
+        const float k0 = valid ? exp2_map(d0 * a.c_exp2) : 0.f;
+        const float k1 = valid ? exp2_map(d1 * a.c_exp2) : 0.f;
         if (key_role) {
           PJ[j * LS + lane] = k0;
           PJ[(j + 1) * LS + lane] = k1;
@@ -1444,7 +1450,7 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
         PTt[lane * LS + j + 1] = k1;
       }
       if (j < je) {
-        const float k0 = valid ? exp2f(dist_to<D, KIND>(x, Lh + j * D) * a.c_exp2) : 0.f;
+        const float k0 = valid ? exp2_map(dist_to<D, KIND>(x, Lh + j * D) * a.c_exp2) : 0.f;
         if (key_role) PJ[j * LS + lane] = k0;
         PTt[lane * LS + j] = k0;
       }
