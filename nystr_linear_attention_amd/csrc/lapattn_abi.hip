@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 
 #include "lapattn.h"
@@ -43,6 +44,26 @@ int check_params(float lambda, float eps, int32_t iters) {
   return LAPATTN_OK;
 }
 
+// Compute units of the current device, cached per device; 256 (MI355X) when
+// no device can be queried (host-only use such as sizing the workspace).
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  int cus = cache[dev].load(std::memory_order_relaxed);
+  if (cus > 0) return cus;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
 Plan make_plan(const lapattn_desc_t* d) {
   Plan p{};
   p.B = d->B;
@@ -68,12 +89,13 @@ Plan make_plan(const lapattn_desc_t* d) {
   // keep it resident, up to 128 partials per head; the plan assumes separate
   // Q and K (query workgroups present), which only sizes the workspace
   // larger when they are the same tensor.
+  p.resident = kResidentPerCU * device_cus() - kResidentMargin;
   p.S = (p.nT + 31) / 32;
   {
     const long nQ = (p.nT + kQueryTiles - 1) / kQueryTiles;
     for (int S = 1; S < p.S; ++S) {
       const long nP = (p.nT + S - 1) / S;
-      if (nP <= kMaxPartials && static_cast<long>(p.BH) * (1 + nP + nQ) <= kResidentWGs) {
+      if (nP <= kMaxPartials && static_cast<long>(p.BH) * (1 + nP + nQ) <= p.resident) {
         p.S = S;
         break;
       }

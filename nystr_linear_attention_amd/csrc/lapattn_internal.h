@@ -16,9 +16,10 @@ constexpr int kSyncHead = 256;
 constexpr int kQueryTiles = 2;
 // W partials per head at most (key ready flags per head).
 constexpr int kMaxPartials = 128;
-// Main-kernel workgroups that can be resident at once: 256 CUs x 2 (LDS and
-// registers allow two), with some margin.
-constexpr long kResidentWGs = 448;
+// Main-kernel workgroups taken to be resident at once: two per CU (LDS and
+// registers allow two) less a margin of 64; 448 on a 256-CU MI355X.
+constexpr long kResidentPerCU = 2;
+constexpr long kResidentMargin = 64;
 
 struct Plan {
   int B, H, gh, gw, D, ph, pw;
@@ -30,6 +31,7 @@ struct Plan {
   int nT;       // 64-token tiles per head
   int S;        // tiles per key-side workgroup
   int nP;       // key-side workgroups (= W partials) per head
+  long resident;  // main-kernel workgroups resident at once on the device
   // workspace byte offsets
   size_t off_L, off_kql, off_wpart, off_x, off_wt, off_yt, off_sync;
   size_t total;

@@ -1846,7 +1846,7 @@ hipError_t launch_out_d(const Plan& p, const Args& a, const Buffers& b, hipStrea
 bool out_in_main_launch(const Plan& p, int shared_qk) {
   if (shared_qk) return false;
   const long nQ = (p.nT + QT - 1) / QT;
-  return static_cast<long>(p.BH) * (1 + p.nP + nQ) <= kResidentWGs;
+  return static_cast<long>(p.BH) * (1 + p.nP + nQ) <= p.resident;
 }
 
 hipError_t launch_pool(const Plan& p, const Args& a, const Buffers& b, hipStream_t s, Ev ev) {
