@@ -1410,6 +1410,28 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
   const float* Lh = Lw + static_cast<size_t>(bh) * m * D;
   f4 wacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 
+  // V rows of the next key tile are loaded right after this tile's kernel
+  // values, before its stores and products: global loads and stores share
+  // one in-order counter, so loads issued after a tile's stores would wait
+  // for them too, and the load latency now overlaps the rest of the tile.
+  // (Token rows stay loaded at the start of their tile: held across the
+  // products they cost more in register pressure than they save.)
+  const int vc = tid % D, vtg = tid / D;
+  constexpr int TPT = TILE * D / WGM;
+  float vv[TPT];
+  auto load_v = [&](int t) {
+    if (key_role) {
+      // V rows: thread (c, group of TPT tokens); rows past N are clamped
+      // here and zeroed when staged
+#pragma unroll
+      for (int u = 0; u < TPT; ++u) {
+        const int nv = t * TILE + vtg * TPT + u;
+        vv[u] = load1_io(v, (static_cast<size_t>(bh) * N + (nv < N ? nv : N - 1)) * D + vc, BF16);
+      }
+    }
+  };
+  if (t_beg < t_end) load_v(t_beg);
+
   for (int t = t_beg; t < t_end; ++t) {
     float* PTt = (key_role || t == t_beg) ? PT : VT;  // this tile's K_QL rows
     const int n = t * TILE + lane;
@@ -1417,20 +1439,12 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
     float x[KIND == 0 ? D : 1];
     if constexpr (KIND == 0) load_row<D>(src, static_cast<size_t>(bh) * N + (valid ? n : N - 1), BF16, x);
     if (key_role) {
-      // V tile -> VT[c][token]; thread (c, group of TPT tokens); all loads
-      // are issued before the LDS writes (rows past N are clamped, then zeroed)
-      const int c = tid % D, tg = tid / D;
-      constexpr int TPT = TILE * D / WGM;
-      float vv[TPT];
+      // V tile -> VT[c][token] (VT is free: the previous tile's products
+      // finished before the barrier that ended its iteration)
 #pragma unroll
       for (int u = 0; u < TPT; ++u) {
-        const int nv = t * TILE + tg * TPT + u;
-        vv[u] = load1_io(v, (static_cast<size_t>(bh) * N + (nv < N ? nv : N - 1)) * D + c, BF16);
-      }
-#pragma unroll
-      for (int u = 0; u < TPT; ++u) {
-        const int tok = tg * TPT + u;
-        VT[c * LS + tok] = t * TILE + tok < N ? vv[u] : 0.f;
+        const int tok = vtg * TPT + u;
+        VT[vc * LS + tok] = t * TILE + tok < N ? vv[u] : 0.f;
       }
     }
     if constexpr (KIND == 0) {
@@ -1457,6 +1471,7 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
     } else {
       gauss_tile<D, BF16>(a, src, Lh, bh, t, PTt, PJ, xx, key_role);
     }
+    if (t + 1 < t_end) load_v(t + 1);
     __syncthreads();
     if (store_kql) {
       // 64 rows of mpad floats, contiguous in global memory
