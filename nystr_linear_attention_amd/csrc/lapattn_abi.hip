@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 
@@ -98,6 +99,25 @@ Plan make_plan(const lapattn_desc_t* d) {
       if (nP <= kMaxPartials && static_cast<long>(p.BH) * (1 + nP + nQ) <= p.resident) {
         p.S = S;
         break;
+      }
+    }
+  }
+  // A grid that cannot be resident at once runs in rounds of workgroups
+  // (output-launch plan), each workgroup paying its fixed latency (set-up,
+  // first loads) once.  When up to 4 tiles per key workgroup let the key
+  // workgroups and the solvers all be resident at once (one round, as for
+  // Q == K, which has no query workgroups), take the fewest such tiles;
+  // otherwise the rounds are unavoidable and short workgroups balance best.
+  {
+    const long nQ = (p.nT + kQueryTiles - 1) / kQueryTiles;
+    const long nP = (p.nT + p.S - 1) / p.S;
+    if (static_cast<long>(p.BH) * (1 + nP + nQ) > p.resident) {
+      for (int S = p.S + 1; S <= kMaxKeyTilesOut; ++S) {
+        const long nPS = (p.nT + S - 1) / S;
+        if (static_cast<long>(p.BH) * (1 + nPS) <= p.resident) {
+          p.S = S;
+          break;
+        }
       }
     }
   }

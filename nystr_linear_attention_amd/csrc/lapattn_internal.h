@@ -14,6 +14,9 @@ constexpr int MP = 64;
 constexpr int kSyncHead = 256;
 // 64-token tiles per query workgroup.
 constexpr int kQueryTiles = 2;
+// Tiles per key workgroup at most when the output-launch plan lengthens key
+// workgroups so that they are all resident at once.
+constexpr int kMaxKeyTilesOut = 4;
 // W partials per head at most (key ready flags per head).
 constexpr int kMaxPartials = 128;
 // Main-kernel workgroups taken to be resident at once: two per CU (LDS and

@@ -49,6 +49,7 @@ SMALL = [
     wl.small_case(10, 14, 32, 2, 2, H=2, shared_qk=True),         # Q = K, m=35 (mpad 48), ragged tiles
     wl.small_case(10, 10, 64, 2, 2, kernel=wl.GAUSSIAN, dtype=wl.BF16, B=2, shared_qk=True),
     wl.small_case(7, 7, 32, 1, 1, B=64),                          # 64 heads: pool takes 4 landmarks per WG
+    wl.small_case(10, 14, 32, 2, 2, B=150),                       # grid not resident: output launch, key WGs take 3 tiles
 ]
 
 
