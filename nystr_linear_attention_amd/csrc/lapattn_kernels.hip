@@ -1689,16 +1689,19 @@ __global__ __launch_bounds__(WGS) void pool_kernel(const void* __restrict__ K,
 
 // ---------------------------------------------------------------------------
 // out: O = K_QL Y for the output-launch plan.  Workgroup = (head, 4 tiles of
-// 64 tokens); Y^T (from compute_y, columns >= m zero) is scaled per row into
-// fp16 range and split in LDS once per workgroup; wave w forms the output
-// rows of tile w on fp16 MFMA with two-part operands, K_QL scaled by 2^14 and
-// split in registers (the arithmetic of out_tile in the main launch).
-// Contraction chunks of 32 landmarks past mpad read as zero.
+// 64 tokens) with 16 waves; Y^T (from compute_y, columns >= m zero) is scaled
+// per row into fp16 range and split in LDS once per workgroup; wave w forms
+// the output rows of token block w % 4 of tile w / 4 on fp16 MFMA with
+// two-part operands, K_QL scaled by 2^14 and split in registers (the
+// arithmetic of out_tile in the main launch).  One 16-token block per wave
+// keeps each wave's load -> product -> store chain short and many waves in
+// flight.  Contraction chunks of 32 landmarks past mpad read as zero.
 // ---------------------------------------------------------------------------
-constexpr int OUT_TILES = WGS / 64;  // tiles per output workgroup (one per wave)
+constexpr int WGO = 1024;             // output workgroup: 16 waves
+constexpr int OUT_TILES = WGO / 256;  // tiles per output workgroup (4 waves each)
 
 template <int D>
-__global__ __launch_bounds__(WGS) void out_kernel(const float* __restrict__ kql,
+__global__ __launch_bounds__(WGO) void out_kernel(const float* __restrict__ kql,
                                                   const float* __restrict__ yt,
                                                   void* __restrict__ O, int bf16, int N,
                                                   int mpad, int nWo) {
@@ -1709,24 +1712,24 @@ __global__ __launch_bounds__(WGS) void out_kernel(const float* __restrict__ kql,
   const int bh = blockIdx.x / nWo, wo = blockIdx.x % nWo;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int lr = lane & 15, lg = lane >> 4;
-  const int t = wo * OUT_TILES + w;  // this wave's tile
-  const bool active = t * TILE < N;
-  // K_QL operands of the tile's 4 token blocks, loads issued before the Y^T
-  // split so that the two memory latencies overlap
+  const int t = wo * OUT_TILES + (w >> 2), tb = w & 3;  // this wave's tile and block
+  const int n0 = t * TILE + 16 * tb;
+  const bool active = n0 < N;
+  // K_QL operands of the block, loads issued before the Y^T split so that
+  // the two memory latencies overlap
   const float* kb = kql + static_cast<size_t>(bh) * N * mpad;
-  f4 av[4][2][2];
-#pragma unroll
-  for (int tb = 0; tb < 4; ++tb) {
-    const int n = t * TILE + 16 * tb + lr;
+  f4 av[2][2];
+  {
+    const int n = n0 + lr;
     const float* ar = kb + static_cast<size_t>(n < N ? n : N - 1) * mpad;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       const int k = 32 * p + 8 * lg;
       if (active && k < mpad) {
-        av[tb][p][0] = ld4(ar + k);
-        av[tb][p][1] = ld4(ar + k + 4);
+        av[p][0] = ld4(ar + k);
+        av[p][1] = ld4(ar + k + 4);
       } else {
-        av[tb][p][0] = av[tb][p][1] = f4{0.f, 0.f, 0.f, 0.f};
+        av[p][0] = av[p][1] = f4{0.f, 0.f, 0.f, 0.f};
       }
     }
   }
@@ -1734,7 +1737,7 @@ __global__ __launch_bounds__(WGS) void out_kernel(const float* __restrict__ kql,
   // into fp16 range and split
   {
     const float* yg = yt + static_cast<size_t>(bh) * D * MP;
-    for (int e = tid; e < D * (MP / 8); e += WGS) {
+    for (int e = tid; e < D * (MP / 8); e += WGO) {
       const int row = e / (MP / 8), k8 = 8 * (e % (MP / 8));
       const f4 v0 = ld4(yg + row * MP + k8), v1 = ld4(yg + row * MP + k8 + 4);
       unsigned mx = 0u;
@@ -1751,33 +1754,30 @@ __global__ __launch_bounds__(WGS) void out_kernel(const float* __restrict__ kql,
   }
   __syncthreads();
   if (!active) return;
+  u32x4 kh[2], kl[2];
 #pragma unroll
-  for (int tb = 0; tb < 4; ++tb) {
-    u32x4 kh[2], kl[2];
+  for (int p = 0; p < 2; ++p) split8h(av[p][0], av[p][1], 14, kh[p], kl[p]);
 #pragma unroll
-    for (int p = 0; p < 2; ++p) split8h(av[tb][p][0], av[tb][p][1], 14, kh[p], kl[p]);
+  for (int cb = 0; cb < CBN; ++cb) {
+    f4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int cb = 0; cb < CBN; ++cb) {
-      f4 c = {0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < 2; ++p) {
+      const int o = (16 * cb + lr) * WLD + 32 * p + 8 * lg;
+      const u32x4 yh = *reinterpret_cast<const u32x4*>(YH + o);
+      const u32x4 yl = *reinterpret_cast<const u32x4*>(YL + o);
+      c = mfma_h(kh[p], yh, c);
+      c = mfma_h(kl[p], yh, c);
+      c = mfma_h(kh[p], yl, c);
+    }
+    const int sc = -14 - EW[16 * cb + lr];
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const int o = (16 * cb + lr) * WLD + 32 * p + 8 * lg;
-        const u32x4 yh = *reinterpret_cast<const u32x4*>(YH + o);
-        const u32x4 yl = *reinterpret_cast<const u32x4*>(YL + o);
-        c = mfma_h(kh[p], yh, c);
-        c = mfma_h(kl[p], yh, c);
-        c = mfma_h(kh[p], yl, c);
-      }
-      const int sc = -14 - EW[16 * cb + lr];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int n = t * TILE + 16 * tb + 4 * lg + i;
-        if (n < N) {
-          const size_t o = (static_cast<size_t>(bh) * N + n) * D + 16 * cb + lr;
-          const float val = ldexpf(c[i], sc);
-          if (bf16) static_cast<uint16_t*>(O)[o] = f32_to_bf16_rne(val);
-          else static_cast<float*>(O)[o] = val;
-        }
+    for (int i = 0; i < 4; ++i) {
+      const int n = n0 + 4 * lg + i;
+      if (n < N) {
+        const size_t o = (static_cast<size_t>(bh) * N + n) * D + 16 * cb + lr;
+        const float val = ldexpf(c[i], sc);
+        if (bf16) static_cast<uint16_t*>(O)[o] = f32_to_bf16_rne(val);
+        else static_cast<float*>(O)[o] = val;
       }
     }
   }
@@ -1852,7 +1852,7 @@ template <int D>
 hipError_t launch_out_d(const Plan& p, const Args& a, const Buffers& b, hipStream_t s, Ev ev) {
   const int nWo = (p.nT + OUT_TILES - 1) / OUT_TILES;
   const dim3 grid(p.BH * nWo);
-  return launch(out_kernel<D>, grid, dim3(WGS), s, ev, b.kql, b.yt, a.out, p.bf16, p.N, p.mpad,
+  return launch(out_kernel<D>, grid, dim3(WGO), s, ev, b.kql, b.yt, a.out, p.bf16, p.N, p.mpad,
                 nWo);
 }
 
