@@ -1248,7 +1248,9 @@ __device__ __forceinline__ void store_o_block(const MainArgs& a, int bh, int t, 
 // O rows of one 64-token tile: K_QL tile (PT, LDS, zero beyond m) times Y on
 // fp16 MFMA, with Y^T split in LDS (row c scaled by 2^(EW[c] + ex - 22),
 // y_in_lds) and the tile's K_QL rows scaled by 2^14 and split here, once per
-// tile.  Wave w: tokens 16 (w % 4) .. +15, column blocks w / 4, w / 4 + 2, ...
+// tile.  Wave w: tokens 16 (w % 4) .. +15; waves 0-3 take the first half of
+// the column blocks, waves 4-7 the second, so that each 128-byte line of an O
+// row is written by one wave (whole lines leave L2 under streaming stores).
 template <int D>
 __device__ void out_tile(const MainArgs& a, int bh, int t, const float* PT, const float* Q, int ex) {
   using QG = QGeom<D>;
@@ -1265,8 +1267,11 @@ __device__ void out_tile(const MainArgs& a, int bh, int t, const float* PT, cons
     const float* ar = PT + (16 * tb + lr) * LS + 32 * p + 8 * lg;
     split8h(ld4(ar), ld4(ar + 4), 14, kh[p], kl[p]);
   }
+  constexpr int CBW = (CBN + 1) / 2;  // column blocks per wave
 #pragma unroll
-  for (int cb = ch; cb < CBN; cb += 2) {
+  for (int k = 0; k < CBW; ++k) {
+    const int cb = CBW * ch + k;
+    if (cb >= CBN) break;
     f4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
