@@ -759,10 +759,15 @@ __device__ __forceinline__ void ns_wave(const MainArgs& a, float* smem, int c, i
       if (q + 2 < 2 * MB) load_block(q + 2, xoh, xol, bh[(q + 2) % 3], bl[(q + 2) % 3]);
       __builtin_amdgcn_sched_barrier(0);
       f4 acc = mfmas(q, 0, 1, f4{0.f, 0.f, 0.f, 0.f});
-      __builtin_amdgcn_sched_barrier(0);
       if (q > 0 && !(q == MB && !DEFER_LAST_T)) epilogue(q - 1, prev);
-      __builtin_amdgcn_sched_barrier(0);
       acc = mfmas(q, 1, NC, acc);
+      // the epilogue's vector instructions go into the shadows of this
+      // block's dependent MFMAs: one MFMA, then up to 4 VALU, in turn
+#pragma unroll
+      for (int i = 0; i < 3 * NC; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
       prev = acc;
       if (q == MB - 1 && !DEFER_LAST_T) epilogue(q, prev);
