@@ -762,11 +762,11 @@ __device__ __forceinline__ void ns_wave(const MainArgs& a, float* smem, int c, i
       if (q > 0 && !(q == MB && !DEFER_LAST_T)) epilogue(q - 1, prev);
       acc = mfmas(q, 1, NC, acc);
       // the epilogue's vector instructions go into the shadows of this
-      // block's dependent MFMAs: one MFMA, then up to 4 VALU, in turn
+      // block's dependent MFMAs: one MFMA, then up to 6 VALU, in turn
 #pragma unroll
       for (int i = 0; i < 3 * NC; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
       prev = acc;
