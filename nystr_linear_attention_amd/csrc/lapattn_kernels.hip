@@ -748,10 +748,11 @@ __device__ __forceinline__ void ns_wave(const MainArgs& a, float* smem, int c, i
     };
 
     // Software pipeline: block q's operand reads go out 2 blocks ahead, and
-    // block q - 1's epilogue runs between block q's first-chunk MFMAs and the
-    // rest (scheduling fences keep that order).  The last phase-1 block feeds
-    // the phase-2 operand's chunk (MB - 1) / 2: deferring its epilogue into
-    // the first phase-2 block works only when that is not chunk 0.
+    // block q - 1's epilogue, which needs only block q - 1's results, is
+    // interleaved with block q's MFMAs so that it runs in their shadows.  The
+    // last phase-1 block feeds the phase-2 operand's chunk (MB - 1) / 2:
+    // deferring its epilogue into the first phase-2 block works only when
+    // that is not chunk 0.
     constexpr bool DEFER_LAST_T = (MB - 1) / 2 > 0;
     f4 prev = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
