@@ -976,7 +976,7 @@ __device__ __forceinline__ void solver_role(const MainArgs& a, int bh, float* sm
           if (lane == 0) red[1] = 1.0f;
           state = 2;
         }
-        if (state == 0 && polled && __builtin_amdgcn_readfirstlane(cnt) >= 1u) {
+        if (state == 0 && polled && static_cast<unsigned>(__builtin_amdgcn_readfirstlane(cnt)) >= 1u) {
 #pragma unroll
           for (int u = 0; u < NW; ++u) {
             const int e = lane + 64 * u, row = e / (MP / 4), c4 = e % (MP / 4);
