@@ -1300,22 +1300,19 @@ __device__ void out_tile(const MainArgs& a, int bh, int t, const float* PT, cons
 // at zero: the expanded form can round slightly below it).  Wave w computes
 // the 16x16 blocks (tokens 16 (w % 4) .., landmarks 16 jb ..) for
 // jb = w / 4, w / 4 + 2; lane (g, r) supplies coordinates
-// (D/4) g .. (D/4) g + D/4 - 1 of token / landmark r of its blocks, read
-// straight from global memory.  Writes PTt[token][j] and, for key tiles,
-// PJ[j][token]; landmarks j in [m, 16 ceil(m/16)) get exact zeros.
+// (D/4) g .. (D/4) g + D/4 - 1 of token / landmark r of its blocks: the
+// token's come in av (gauss_rows), the landmark's are read from global
+// memory.  Writes PTt[token][j] and, for key tiles, PJ[j][token]; landmarks
+// j in [m, 16 ceil(m/16)) get exact zeros.
 template <int D, bool BF16>
-__device__ void gauss_tile(const MainArgs& a, const void* src, const float* Lh, int bh, int t,
-                           float* PTt, float* PJ, float* xx, bool key_role) {
-  constexpr int KS = D / 4;  // MFMA sub-steps; floats per lane per operand
+__device__ __forceinline__ void gauss_rows(const MainArgs& a, const void* src, int bh, int t,
+                                           float (&av)[D / 4]) {
+  constexpr int KS = D / 4;
   const int lane = threadIdx.x & 63, w = wave_id();
   const int lr = lane & 15, lg = lane >> 4;
-  const int tb = w & 3;
-  const int m = a.m, N = a.N;
-  const int mby = (m + 15) >> 4;
-  // token operand: KS coordinates of token 16 tb + lr
-  const int n = t * TILE + 16 * tb + lr;
-  const size_t row = static_cast<size_t>(bh) * N + (n < N ? n : N - 1);
-  float av[KS];
+  // token operand: KS coordinates of token 16 (w % 4) + lr (clamped past N)
+  const int n = t * TILE + 16 * (w & 3) + lr;
+  const size_t row = static_cast<size_t>(bh) * a.N + (n < a.N ? n : a.N - 1);
 #pragma unroll
   for (int q = 0; q < KS / 4; ++q) {
     const f4 u = load4_io(src, row * D + KS * lg + 4 * q, BF16);
@@ -1324,6 +1321,17 @@ __device__ void gauss_tile(const MainArgs& a, const void* src, const float* Lh, 
     av[4 * q + 2] = u[2];
     av[4 * q + 3] = u[3];
   }
+}
+
+template <int D, bool BF16>
+__device__ __forceinline__ void gauss_tile(const MainArgs& a, const float (&av)[D / 4], const float* Lh,
+                                           int t, float* PTt, float* PJ, float* xx, bool key_role) {
+  constexpr int KS = D / 4;  // MFMA sub-steps; floats per lane per operand
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int lr = lane & 15, lg = lane >> 4;
+  const int tb = w & 3;
+  const int m = a.m, N = a.N;
+  const int mby = (m + 15) >> 4;
   float px = 0.f;
 #pragma unroll
   for (int s = 0; s < KS; ++s) px = fmaf(av[s], av[s], px);
@@ -1430,8 +1438,10 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
   // values, before its stores and products: global loads and stores share
   // one in-order counter, so loads issued after a tile's stores would wait
   // for them too, and the load latency now overlaps the rest of the tile.
-  // (Token rows stay loaded at the start of their tile: held across the
-  // products they cost more in register pressure than they save.)
+  // Gaussian tiles load the next tile's token operand (D/4 floats per lane)
+  // at the same point.  (Laplacian token rows, D floats per lane, stay loaded
+  // at the start of their tile: held across the products they cost more in
+  // register pressure than they save.)
   const int vc = tid % D, vtg = tid / D;
   constexpr int TPT = TILE * D / WGM;
   float vv[TPT];
@@ -1446,7 +1456,11 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
       }
     }
   };
-  if (t_beg < t_end) load_v(t_beg);
+  float ga[KIND == 1 ? D / 4 : 1];
+  if (t_beg < t_end) {
+    load_v(t_beg);
+    if constexpr (KIND == 1) gauss_rows<D, BF16>(a, src, bh, t_beg, ga);
+  }
 
   for (int t = t_beg; t < t_end; ++t) {
     float* PTt = (key_role || t == t_beg) ? PT : VT;  // this tile's K_QL rows
@@ -1485,9 +1499,12 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
         PTt[lane * LS + j] = k0;
       }
     } else {
-      gauss_tile<D, BF16>(a, src, Lh, bh, t, PTt, PJ, xx, key_role);
+      gauss_tile<D, BF16>(a, ga, Lh, t, PTt, PJ, xx, key_role);
     }
-    if (t + 1 < t_end) load_v(t + 1);
+    if (t + 1 < t_end) {
+      load_v(t + 1);
+      if constexpr (KIND == 1) gauss_rows<D, BF16>(a, src, bh, t + 1, ga);
+    }
     __syncthreads();
     if (store_kql) {
       // 64 rows of mpad floats, contiguous in global memory
