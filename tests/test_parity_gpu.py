@@ -50,6 +50,8 @@ SMALL = [
     wl.small_case(10, 10, 64, 2, 2, kernel=wl.GAUSSIAN, dtype=wl.BF16, B=2, shared_qk=True),
     wl.small_case(7, 7, 32, 1, 1, B=64),                          # 64 heads: pool takes 4 landmarks per WG
     wl.small_case(10, 14, 32, 2, 2, B=150),                       # grid not resident: output launch, key WGs take 3 tiles
+    wl.small_case(12, 16, 32, 2, 2, B=2, eps=0.0),                # no diagonal perturbation (kernel matrix alone is PD)
+    wl.small_case(8, 12, 64, 2, 2, B=2, iters=1),                 # a single Newton-Schulz step
 ]
 
 
