@@ -8,7 +8,11 @@ synthetic seeded inputs N(0,1)/sqrt(d)*4 already resident in HBM.
 
 One step = one lapattn_forward call over the whole batch (landmark pool,
 solver, kernel maps, W reduction, output).  Prints one JSON line on stdout;
-progress goes to stderr.
+progress goes to stderr.  `value` is the warm rate (the same buffers every
+step); `cold` repeats the steps rotating over copies of the buffers larger
+than the Infinity Cache, so that every step reads its inputs from HBM.
+Per-kernel times carry the 10th, 50th and 90th percentiles over the launches
+of the kernel-event pass.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 """
@@ -188,6 +192,10 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-other-plan", action="store_true",
                     help="skip the pass over the other launch plan (its fields become null)")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache pass (steps rotating over copies of the inputs)")
+    ap.add_argument("--cold-mib", type=int, default=640,
+                    help="total size of the input copies the cold pass rotates over")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args(argv)
@@ -226,28 +234,36 @@ def main(argv=None):
     api.init()
     stream = torch.cuda.current_stream().cuda_stream
 
-    def make_step(serial):
+    def make_step(serial, bufs=None):
+        qq, kk, vv, oo = bufs if bufs is not None else (q, k, v, out)
         desc = api.make_desc(w.B, w.H, w.grid_h, w.grid_w, w.d, w.pool_h, w.pool_w,
                              w.kernel, q.dtype, serial=serial)
         ws = api.alloc_workspace(desc, dev)
-        call = (ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(), w.lam, w.eps,
-                w.iters, out.data_ptr(), ws.data_ptr(), ws.numel(), stream)
+        call = (ctypes.byref(desc), qq.data_ptr(), kk.data_ptr(), vv.data_ptr(), w.lam, w.eps,
+                w.iters, oo.data_ptr(), ws.data_ptr(), ws.numel(), stream)
 
         def step():
             st = lib.lapattn_forward(*call)
             if st != 0:
                 raise _lib.LapattnError(st, _lib.strerror(st))
-        step.keep = (desc, ws)
+        step.keep = (desc, ws, qq, kk, vv, oo)
+        step.nbytes = ws.numel() + sum(t.numel() * t.element_size()
+                                       for t in {id(t): t for t in (qq, kk, vv, oo)}.values())
         return step
 
     hip = HipEvents()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
 
+    pct = {}  # slot -> (p10, p50, p90) kernel ms of the last kernel-event pass
+
     def timed(step, steps, kernel_events, unused=()):
         """Times `steps` calls; with kernel_events, also every kernel's own
         duration (start/stop events bound to each launch).  Returns
-        (ms per step, {slot: mean kernel ms})."""
+        (ms per step, {slot: mean kernel ms}); the kernel-event pass also
+        leaves each slot's 10th, 50th and 90th percentiles in `pct`.
+        `step` may be a list of steps, called in turn."""
+        steps_list = step if isinstance(step, list) else [step]
         nev = 2 * len(_lib.STAGES)
         evsets = [hip.create(nev) for _ in range(steps)] if kernel_events else []
         torch.cuda.synchronize()
@@ -255,7 +271,7 @@ def main(argv=None):
         for i in range(steps):
             if kernel_events:
                 lib.lapattn_set_stage_events(evsets[i], nev)
-            step()
+            steps_list[i % len(steps_list)]()
         t1.record()
         lib.lapattn_set_stage_events(None, 0)
         torch.cuda.synchronize()
@@ -265,6 +281,7 @@ def main(argv=None):
             if evsets and name not in unused:
                 vals = [hip.elapsed_ms(evs[2 * s], evs[2 * s + 1]) for evs in evsets]
                 per[name] = sum(vals) / len(vals)
+                pct[name] = tuple(float(np.percentile(vals, p)) for p in (10, 50, 90))
         return ms, per
 
     fused = make_step(serial=False)
@@ -290,6 +307,7 @@ def main(argv=None):
         return tuple(n for n in _lib.STAGES if n not in used)
     unused = unused_slots(args.serial)
     ms_ev, kern = timed(main_step, args.steps, True, unused)
+    pct_main = dict(pct)
     log(f"[bench] kernel-event pass: {ms_ev * 1e3:.2f} us/step; kernels (us): "
         + ", ".join(f"{n}={t * 1e3:.2f}" for n, t in kern.items()))
     # The other launch plan, for the L1 stage on its own (serial) or fused.
@@ -301,6 +319,29 @@ def main(argv=None):
         ms_other, kern_other = timed(other, args.steps, True, unused_slots(not args.serial))
         log(f"[bench] {'fused' if args.serial else 'serial'} plan: {ms_other * 1e3:.2f} us/step; "
             "kernels (us): " + ", ".join(f"{n}={t * 1e3:.2f}" for n, t in kern_other.items()))
+    # Cold caches: the same steps rotating over copies of the inputs, output
+    # and workspace that together exceed the 256 MB Infinity Cache, so that
+    # every step reads its inputs from HBM.  Reported beside `value`.
+    cold = None
+    if not args.no_cold:
+        nsets = max(2, -(-(args.cold_mib << 20) // main_step.nbytes))
+
+        def copy_set():
+            qq = q.clone()
+            return (qq, qq if w.shared_qk else k.clone(), v.clone(), torch.empty_like(out))
+        cold_steps = [make_step(args.serial, copy_set()) for _ in range(nsets)]
+        for st in cold_steps:
+            st()
+        csteps = max(args.steps, 2 * nsets)
+        ms_cold, _ = timed(cold_steps, csteps, False)
+        cold = {"ms_per_step": round(ms_cold, 5),
+                "value": round(w.B * w.N / (ms_cold * 1e-3), 1),
+                "unit": "tokens/s", "steps": csteps, "sets": nsets,
+                "MB_rotated": round(nsets * main_step.nbytes / 1e6, 1)}
+        log(f"[bench] cold pass ({nsets} copies, {cold['MB_rotated']} MB): "
+            f"{ms_cold * 1e3:.2f} us/step")
+        del cold_steps
+        torch.cuda.empty_cache()
     kf = kern_other if args.serial else kern      # fused-plan kernels (may be empty)
     ks = kern if args.serial else kern_other      # serial-plan kernels (may be empty)
 
@@ -350,6 +391,8 @@ def main(argv=None):
     kernels = {}
     for name, t in kern.items():
         e = {"us": round(t * 1e3, 3)}
+        if name in pct_main:
+            e.update({f"p{p}_us": round(t_ * 1e3, 3) for p, t_ in zip((10, 50, 90), pct_main[name])})
         if name in ("pool", "out") and name in wk:
             e["GB/s"] = round(wk[name]["bytes"] / (t * 1e-3) / 1e9, 1)
             e["hbm_frac"] = round(e["GB/s"] / PEAK_HBM_GBS, 4)
@@ -401,6 +444,7 @@ def main(argv=None):
         "solver_mfma": mfma,
         "kernels": kernels,
         "ms_per_step_kernel_event_pass": round(ms_ev, 5),
+        "cold": cold,
     }
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle for ~{args.cpu_seconds:.0f} s")
