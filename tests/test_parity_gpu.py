@@ -52,6 +52,7 @@ SMALL = [
     wl.small_case(10, 14, 32, 2, 2, B=150),                       # grid not resident: output launch, key WGs take 3 tiles
     wl.small_case(12, 16, 32, 2, 2, B=2, eps=0.0),                # no diagonal perturbation (kernel matrix alone is PD)
     wl.small_case(8, 12, 64, 2, 2, B=2, iters=1),                 # a single Newton-Schulz step
+    wl.small_case(20, 20, 32, 4, 4, B=300),                       # output launch of 600 workgroups, ragged last tile
 ]
 
 
