@@ -135,6 +135,47 @@ def cpu_baseline(w, inputs, seconds):
     }
 
 
+def _oracle_worker(job):
+    """Pool worker: the fp64 oracle with one BLAS thread over whole heads of a
+    workload (round-robin from `offset`) for `seconds`; returns (heads, s).
+    Imports no GPU code: only the input generator and the oracle."""
+    name, seconds, offset = job
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from nystr_linear_attention_amd import workloads as wl
+    w = wl.BY_NAME[name]
+    x = wl.make_inputs(w)
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while True:
+            oracle.forward_workload(w, x, heads=[heads[(offset + done) % len(heads)]])
+            done += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                return done, el
+
+
+def cpu_baseline_pool(w, seconds, workers):
+    """The same oracle in `workers` spawned processes at once (heads are
+    independent), each with one BLAS thread; the rate is the sum of the
+    workers' rates.  Run before the GPU is initialised."""
+    import multiprocessing as mp
+    with mp.get_context("spawn").Pool(workers) as pool:
+        res = pool.map(_oracle_worker, [(w.name, seconds, i) for i in range(workers)])
+    heads = sum(d for d, _ in res)
+    return {
+        "value": sum(d * w.N / el for d, el in res),
+        "unit": "tokens/s",
+        "cores": workers,
+        "kind": "oracle",
+        "sample": f"{heads} whole heads of {w.name} over {workers} processes "
+                  f"(one BLAS thread each), {seconds:.0f} s each",
+    }
+
+
 def source_digest():
     """sha256 of the kernel sources, to tie stored counter figures to a build."""
     import hashlib
@@ -190,6 +231,9 @@ def main(argv=None):
                     help="time the serial launch plan (solver, then maps) instead of the fused one")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-workers", type=int, default=0,
+                    help="processes of the pooled CPU baseline (default: the usable cores, "
+                         "at most 16; 1 skips it)")
     ap.add_argument("--no-other-plan", action="store_true",
                     help="skip the pass over the other launch plan (its fields become null)")
     ap.add_argument("--no-cold", action="store_true",
@@ -220,6 +264,13 @@ def main(argv=None):
     log(f"[bench] workload {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} m={w.m} "
         f"kernel={w.kernel} dtype={w.dtype} iters={w.iters}")
     x = wl.make_inputs(w)
+    # The pooled CPU baseline runs first, before anything touches the GPU.
+    pooled = None
+    if not args.no_cpu_baseline:
+        workers = args.cpu_workers or min(16, len(os.sched_getaffinity(0)))
+        if workers > 1:
+            log(f"[bench] cpu baseline: oracle in {workers} processes for ~{args.cpu_seconds:.0f} s")
+            pooled = cpu_baseline_pool(w, args.cpu_seconds, workers)
 
     def to_dev(a):
         if w.dtype == wl.BF16:
@@ -449,6 +500,7 @@ def main(argv=None):
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle for ~{args.cpu_seconds:.0f} s")
         res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
+        res["cpu_baseline"]["pooled"] = pooled
     hip.close()
     print(json.dumps(res), flush=True)
     return 0
