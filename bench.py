@@ -93,6 +93,8 @@ def work(w):
     return {
         "map_pairs": map_pairs,
         "amat_pairs": amat_pairs,
+        "ns": ns,
+        "klkv": klkv,
         "pool": {"bytes": BH * (N * d * e + m * d * 4)},
         # solver launch of the serial plan: A, alpha, Newton-Schulz
         "solver": {"flops": 3 * amat_pairs + ns},
@@ -174,6 +176,27 @@ def cpu_baseline_pool(w, seconds, workers):
         "sample": f"{heads} whole heads of {w.name} over {workers} processes "
                   f"(one BLAS thread each), {seconds:.0f} s each",
     }
+
+
+def host_info():
+    """CPU model, usable cores and the BLAS NumPy calls (name, version,
+    threading layer) of the host the CPU baseline ran on."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = [{k: i.get(k) for k in ("internal_api", "version", "threading_layer",
+                                    "architecture", "num_threads")}
+            for i in threadpool_info() if i.get("user_api") == "blas"]
+    return {"cpu_model": model, "usable_cores": len(os.sched_getaffinity(0)),
+            "numpy": np.__version__, "blas": blas}
 
 
 def source_digest():
@@ -259,18 +282,19 @@ def main(argv=None):
     from nystr_linear_attention_amd import workloads as wl
 
     w = wl.BY_NAME[args.workload] if args.workload else wl.HEADLINE
-    torch.cuda.set_device(0)
-    dev = torch.device("cuda:0")
     log(f"[bench] workload {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} m={w.m} "
         f"kernel={w.kernel} dtype={w.dtype} iters={w.iters}")
     x = wl.make_inputs(w)
-    # The pooled CPU baseline runs first, before anything touches the GPU.
+    # The pooled CPU baseline runs first, before anything touches the GPU
+    # (torch.cuda.set_device already starts the runtime's initialisation).
     pooled = None
     if not args.no_cpu_baseline:
         workers = args.cpu_workers or min(16, len(os.sched_getaffinity(0)))
         if workers > 1:
             log(f"[bench] cpu baseline: oracle in {workers} processes for ~{args.cpu_seconds:.0f} s")
             pooled = cpu_baseline_pool(w, args.cpu_seconds, workers)
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
 
     def to_dev(a):
         if w.dtype == wl.BF16:
@@ -298,6 +322,7 @@ def main(argv=None):
             if st != 0:
                 raise _lib.LapattnError(st, _lib.strerror(st))
         step.keep = (desc, ws, qq, kk, vv, oo)
+        step.status = ws[api.status_offset(desc):api.status_offset(desc) + 4]
         step.nbytes = ws.numel() + sum(t.numel() * t.element_size()
                                        for t in {id(t): t for t in (qq, kk, vv, oo)}.values())
         return step
@@ -308,24 +333,40 @@ def main(argv=None):
 
     pct = {}  # slot -> (p10, p50, p90) kernel ms of the last kernel-event pass
 
+    timeouts = [0]  # timed-out in-launch waits seen in any checked call
+
+    def read_status(steps_list):
+        for st in steps_list:
+            timeouts[0] += int(st.status.cpu().view(torch.int32).item())
+
     def timed(step, steps, kernel_events, unused=()):
         """Times `steps` calls; with kernel_events, also every kernel's own
         duration (start/stop events bound to each launch).  Returns
         (ms per step, {slot: mean kernel ms}); the kernel-event pass also
         leaves each slot's 10th, 50th and 90th percentiles in `pct`.
-        `step` may be a list of steps, called in turn."""
+        `step` may be a list of steps, called in turn.  The status word of
+        the last call on each workspace is read afterwards; the kernel-event
+        pass (not used for `value`) also copies every call's status word to
+        the device right after the call, so that each of them is checked."""
         steps_list = step if isinstance(step, list) else [step]
         nev = 2 * len(_lib.STAGES)
         evsets = [hip.create(nev) for _ in range(steps)] if kernel_events else []
+        every = torch.zeros(steps, 4, dtype=torch.uint8, device=dev) if kernel_events else None
         torch.cuda.synchronize()
         t0.record()
         for i in range(steps):
             if kernel_events:
                 lib.lapattn_set_stage_events(evsets[i], nev)
-            steps_list[i % len(steps_list)]()
+            st = steps_list[i % len(steps_list)]
+            st()
+            if kernel_events:
+                every[i].copy_(st.status)
         t1.record()
         lib.lapattn_set_stage_events(None, 0)
         torch.cuda.synchronize()
+        read_status(steps_list)
+        if every is not None:
+            timeouts[0] += int(every.view(torch.int32).sum().item())
         ms = t0.elapsed_time(t1) / steps
         per = {}
         for s, name in enumerate(_lib.STAGES):
@@ -400,27 +441,40 @@ def main(argv=None):
     value = tokens / (ms_step * 1e-3)
     wk = work(w)
     peak = PEAK_FP32_VALU_TFLOPS
-    # dominant kernel of the timed plan
+    # Dominant kernel: main (the fused launch; in the serial plan, whichever
+    # of its two launches is longer).  Its roofline is the distance stage the
+    # metric names: the L1 map pairs (K_QL, K_LK) and the pairs of A, 3 flops
+    # per coordinate pair, on FP32 VALU; the Gaussian variant's distances
+    # run on fp32 MFMA instead (2 flops per multiply-add of X L^T).
     if args.serial:
-        dom, dom_ms, dom_flops = "maps", ks["maps"], wk["maps"]["flops"]
-        dom_desc = "main_kernel, map workgroups only (serial plan)"
-        if ks["main"] > ks["maps"]:
-            dom, dom_ms, dom_flops = "main", ks["main"], wk["solver"]["flops"]
-            dom_desc = "main_kernel, solver workgroups only (serial plan)"
+        dom_ms = max(ks["maps"], ks["main"])
+        dom_desc = ("main_kernel, map workgroups only (serial plan)" if ks["maps"] >= ks["main"]
+                    else "main_kernel, solver workgroups only (serial plan)")
     else:
-        dom, dom_ms, dom_flops = "main", kf["main"], wk["fused"]["flops"]
-        dom_desc = ("main_kernel (fused: Newton-Schulz workgroups on split-fp16 MFMA beside "
-                    "the L1 map workgroups on FP32 VALU, their K_LK V partials on fp32 MFMA "
-                    "and Y, O on scaled split-fp16 MFMA)")
+        dom_ms = kf["main"]
+        dom_desc = "main_kernel (fused: solver, map and output workgroups in one launch)"
+    l1_pairs = wk["map_pairs"] + wk["amat_pairs"]
+    if w.kernel == wl.GAUSSIAN:
+        dom_flops = 2 * wk["map_pairs"]
+        bound, dpeak, stage = "mfma", PEAK_FP32_MFMA_TFLOPS, (
+            "Gaussian distance stage: X L^T of K_QL (and K_LK when K != Q) on fp32 MFMA, "
+            "2 flops per multiply-add, over the launch's time")
+    else:
+        dom_flops = 3 * l1_pairs
+        bound, dpeak, stage = "alu", PEAK_FP32_VALU_TFLOPS, (
+            "L1 stage: |q - l| terms of K_QL, K_LK and A on FP32 VALU, 3 flops per "
+            "coordinate pair, over the launch's time")
     ach = dom_flops / (dom_ms * 1e-3) / 1e12
     traffic = stored_traffic(w.name, "main_kernel") if not args.serial else None
     roofline = {
         "kernel": dom_desc,
-        "bound": "alu",
+        "stage": stage,
+        "bound": bound,
+        "pipe": "FP32 MFMA" if bound == "mfma" else "FP32 VALU",
         "achieved": round(ach, 3),
-        "peak": peak,
+        "peak": dpeak,
         "unit": "TFLOP/s",
-        "frac": round(ach / peak, 4),
+        "frac": round(ach / dpeak, 4),
         "traffic": traffic,
         "kernel_us": round(dom_ms * 1e3, 3),
         "flops_per_launch": dom_flops,
@@ -428,14 +482,13 @@ def main(argv=None):
     # L1 stage: the distance maps and A, 3 flops per coordinate pair
     def frac_of(flops, t_ms):
         return round(flops / (t_ms * 1e-3) / 1e12 / peak, 4)
-    l1 = {"pairs": wk["map_pairs"] + wk["amat_pairs"],
+    l1 = {"pairs": l1_pairs,
           "note": "fused: maps and A over the whole fused main launch (conservative); "
                   "maps_only: the K_QL / K_LK pairs over the map launch of the serial plan "
                   "(which also forms W, Y and O)"}
     if kf:
         t = kf["main"]
-        l1.update(fused_us=round(t * 1e3, 3),
-                  frac_fused=frac_of(3 * (wk["map_pairs"] + wk["amat_pairs"]), t))
+        l1.update(fused_us=round(t * 1e3, 3), frac_fused=frac_of(3 * l1_pairs, t))
     if ks:
         t = ks["maps"]
         l1.update(maps_only_us=round(t * 1e3, 3), frac_maps_only=frac_of(3 * wk["map_pairs"], t))
@@ -448,23 +501,76 @@ def main(argv=None):
             e["GB/s"] = round(wk[name]["bytes"] / (t * 1e-3) / 1e9, 1)
             e["hbm_frac"] = round(e["GB/s"] / PEAK_HBM_GBS, 4)
         kernels[name] = e
+    # The main launch as an HBM stream: the bytes it must move (inputs once,
+    # output once, landmarks) and, when counters for these sources are
+    # stored, the bytes it did move.
+    if kf:
+        t = kf["main"]
+        e = 2 if w.dtype == wl.BF16 else 4
+        ins = (2 if w.shared_qk else 3) * w.heads * w.N * w.d * e
+        alg = ins + w.heads * w.N * w.d * e + w.heads * w.m * w.d * 4
+        hbm = {"algorithmic_bytes": alg,
+               "algorithmic_GB/s": round(alg / (t * 1e-3) / 1e9, 1)}
+        hbm["algorithmic_frac"] = round(hbm["algorithmic_GB/s"] / PEAK_HBM_GBS, 4)
+        if traffic:
+            hbm.update({"counter_bytes": traffic,
+                        "counter_GB/s": round(traffic / (t * 1e-3) / 1e9, 1),
+                        "counter_over_algorithmic": round(traffic / alg, 3)})
+        kernels.setdefault("main", {})["hbm"] = hbm
+    # Contractions, each against the peak of the matrix-core dtype it runs
+    # on, over the fused main launch that holds them all.
+    n16 = 16 * ((w.m + 15) // 16)
+    contractions = None
+    if kf:
+        t = kf["main"] * 1e-3
+        ns_issued = w.heads * w.iters * 2 * 3 * 2 * n16 ** 3
+        yo = 2 * w.m * w.m * w.d + 2 * w.N * w.m * w.d
+        mpad = 16 * ((w.m + 15) // 16)
+        yo_issued = 3 * w.heads * (2 * w.d * 64 * 64 + 2 * w.N * 64 * w.d)
+        klkv_issued = w.heads * 2 * w.d * mpad * 64 * -(-w.N // 64)
+        contractions = {
+            "note": "algorithmic flops (2 per multiply-add at the unpadded sizes) and the "
+                    "flops the matrix cores issue (split-fp16 products run 3 fp16 MFMAs; "
+                    "padding to 16-wide blocks), both over the fused main launch",
+            "newton_schulz": {
+                "unit": "fp16 MFMA (hi*hi + lo*hi + hi*lo)", "algorithmic_flops": wk["ns"],
+                "issued_flops": ns_issued, "peak_TFLOP/s": PEAK_FP16_MFMA_TFLOPS,
+                "issued_frac": round(ns_issued / t / 1e12 / PEAK_FP16_MFMA_TFLOPS, 5)},
+            "y_and_out": {
+                "unit": "fp16 MFMA (hi*hi + lo*hi + hi*lo)",
+                "algorithmic_flops": w.heads * yo, "issued_flops": yo_issued,
+                "peak_TFLOP/s": PEAK_FP16_MFMA_TFLOPS,
+                "issued_frac": round(yo_issued / t / 1e12 / PEAK_FP16_MFMA_TFLOPS, 5)},
+            "klk_v": {
+                "unit": "fp32 MFMA 16x16x4", "algorithmic_flops": wk["klkv"],
+                "issued_flops": klkv_issued, "peak_TFLOP/s": PEAK_FP32_MFMA_TFLOPS,
+                "issued_frac": round(klkv_issued / t / 1e12 / PEAK_FP32_MFMA_TFLOPS, 5)},
+        }
     mfma = None
     if ks:
         # The solver launch of the serial plan: one workgroup (one CU) per
-        # head.  Its Newton-Schulz steps issue 3 fp16 products (hi*hi, lo*hi,
-        # hi*lo) for each of the 2 matrix products per step, on the matrix
-        # zero padded to n = 16 ceil(m / 16).
+        # head.  MFMA utilisation of the Newton-Schulz stage as 4 m^3 iters
+        # flops per head at the unpadded m over that launch, against the
+        # fp32 matrix peak, device-wide and per CU that holds a solver; and
+        # the fp16 work its steps issue (3 fp16 products, hi*hi, lo*hi,
+        # hi*lo, for each of the 2 matrix products per step, on the matrix
+        # zero padded to n = 16 ceil(m / 16)) against the fp16 peak per CU.
         solver_ms = ks["main"]
-        n16 = 16 * ((w.m + 15) // 16)
+        f32eq = wk["ns"]
+        dev_frac = f32eq / (solver_ms * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS
         f16 = w.heads * w.iters * 2 * 3 * 2 * n16 ** 3
         tf = f16 / (solver_ms * 1e-3) / 1e12
         per_cu_peak = PEAK_FP16_MFMA_TFLOPS / 256
         mfma = {"solver_only_us": round(solver_ms * 1e3, 3),
+                "ns_flops": f32eq,
+                "utilisation_device": round(dev_frac, 5),
+                "utilisation_per_active_cu": round(dev_frac * 256 / min(256, w.heads), 4),
                 "fp16_mfma_flops_issued": f16,
-                "TFLOP/s": round(tf, 3),
-                "per_active_cu_frac_of_fp16_peak": round(tf / (per_cu_peak * w.heads), 4),
-                "note": "whole solver launch (A, alpha, set-up and the steps) per active CU "
-                        "against 1/256 of the dense fp16 MFMA peak"}
+                "fp16_TFLOP/s": round(tf, 3),
+                "fp16_per_active_cu_frac": round(tf / (per_cu_peak * min(256, w.heads)), 4),
+                "note": "utilisation = 4 m^3 iters B H / t(solver launch) / 157.3 TFLOP/s "
+                        "(unpadded m; device-wide, and per CU that holds a solver); the fp16 "
+                        "figures count the split products the steps issue on the padded matrix"}
 
     res = {
         "metric": "attention-layer tokens/sec (fwd) at N=3136,d=64,m=49; % FP32 VALU peak of L1 stage",
@@ -492,17 +598,23 @@ def main(argv=None):
         },
         "roofline": roofline,
         "l1_stage": l1,
+        "contractions": contractions,
         "solver_mfma": mfma,
         "kernels": kernels,
         "ms_per_step_kernel_event_pass": round(ms_ev, 5),
         "cold": cold,
     }
+    res["timeouts"] = timeouts[0]
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle for ~{args.cpu_seconds:.0f} s")
         res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
         res["cpu_baseline"]["pooled"] = pooled
+        res["cpu_baseline"]["host"] = host_info()
     hip.close()
     print(json.dumps(res), flush=True)
+    if timeouts[0]:
+        log(f"[bench] ERROR: {timeouts[0]} in-launch wait(s) timed out: outputs were invalid")
+        return 3
     return 0
 
 

@@ -103,7 +103,10 @@ enum {
                                     output rows                                */
 #define LAPATTN_STAGE_MAPS 2     /* LAPATTN_FLAG_SERIAL only: the map roles as
                                     a launch of their own                      */
-#define LAPATTN_STAGE_OUT 3      /* Q == K only: O = K_QL Y as its own launch  */
+#define LAPATTN_STAGE_OUT 3      /* O = K_QL Y as its own launch: when K == Q,
+                                    or when the main grid cannot be resident
+                                    on the device at once (lapattn_launches
+                                    reports which)                             */
 #define LAPATTN_NUM_STAGES 4
 
 typedef struct {
@@ -129,11 +132,27 @@ int lapattn_check(const lapattn_desc_t* desc, float lambda, float eps, int32_t i
 
 /* Bytes of device workspace lapattn_forward needs for `desc` (256-byte
  * aligned base required); 0 if the descriptor is invalid.  The size is linear
- * in B*H*N. */
+ * in B*H*N.
+ * The launch plan (tiles per key workgroup, hence the workspace size, the
+ * order in which W's partial sums are added and so the bitwise result) is
+ * derived from the compute-unit count of the device that is current on the
+ * calling thread (256 is assumed when no device can be queried).  Size the
+ * workspace, and call lapattn_forward, with the same device current. */
 size_t lapattn_workspace_bytes(const lapattn_desc_t* desc);
 
-/* Checks that a HIP device is current.  The library keeps no per-device
- * state, so this is optional; it exists so that callers can fail early. */
+/* Byte offset, inside the workspace of a call with this descriptor, of the
+ * call's status word (uint32, 4-byte aligned; (size_t)-1 if the descriptor is
+ * invalid).  Every forward call sets it to 0 in its first launch; afterwards
+ * it holds the number of in-launch waits of that call that ran out of time
+ * (see lapattn_forward).  A nonzero value means the call's output is INVALID.
+ * Read it (e.g. a 4-byte device-to-host copy ordered after the call on the
+ * same stream) before the workspace is used by another call. */
+size_t lapattn_status_offset(const lapattn_desc_t* desc);
+
+/* Checks that a HIP device is current and caches its compute-unit count (the
+ * only per-device state the library keeps: one int per device, written once,
+ * read by the launch plan).  Optional; it exists so that callers can fail
+ * early. */
 int lapattn_init(void);
 
 /* O = K_QL (X (K_LK V)) per head, as defined at the top of this file.
@@ -145,11 +164,13 @@ int lapattn_init(void);
  *   workspace device scratch of lapattn_workspace_bytes(desc) bytes, 256-byte
  *             aligned; its contents on entry are ignored
  *   stream    hipStream_t (as void*) the work is ordered on
- * Concurrent calls that share a workspace race; calls on different streams
- * with different workspaces are independent.  Within a call, workgroups of
- * one launch hand per-head results to each other through the workspace
- * (device-scope stores, then a per-workgroup flag); every such wait is
- * bounded in time. */
+ * Concurrent calls that share a workspace race.  Within a call, workgroups
+ * of one launch hand per-head results to each other through the workspace
+ * (device-scope stores, then a per-workgroup flag).  Every such wait is
+ * bounded (20 ms of the device clock); a wait that runs out counts one in the
+ * call's status word (lapattn_status_offset) and the call's output is then
+ * invalid, although the call itself has returned LAPATTN_OK (the library
+ * never synchronises, so it cannot report it as a return value). */
 int lapattn_forward(const lapattn_desc_t* desc, const void* q, const void* k,
                     const void* v, float lambda, float eps, int32_t iters,
                     void* out, void* workspace, size_t workspace_bytes,
@@ -181,7 +202,8 @@ int lapattn_launches(const lapattn_desc_t* desc, int q_is_k);
  * events: hipEventElapsedTime(events[2*s], events[2*s+1]) is then that
  * kernel's own execution time.  Slots without a launch in the call are left
  * unrecorded: LAPATTN_STAGE_MAPS outside LAPATTN_FLAG_SERIAL, and
- * LAPATTN_STAGE_OUT unless K is the same pointer as Q.
+ * LAPATTN_STAGE_OUT unless K is the same pointer as Q or the main grid cannot
+ * be resident at once (lapattn_launches tells which slots a call uses).
  * `events` holds 2 * LAPATTN_NUM_STAGES hipEvent_t handles (as void*) created
  * by the caller with timing enabled, and must stay valid until the hook is
  * cleared with (NULL, 0).  n must be 0 or 2 * LAPATTN_NUM_STAGES. */

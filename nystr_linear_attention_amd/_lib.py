@@ -30,7 +30,8 @@ FLAG_SERIAL = 1
 
 # Names of every entry point declared in include/lapattn.h.
 EXPORTS = ("lapattn_version", "lapattn_strerror", "lapattn_check",
-           "lapattn_workspace_bytes", "lapattn_init", "lapattn_forward",
+           "lapattn_workspace_bytes", "lapattn_status_offset", "lapattn_init",
+           "lapattn_forward",
            "lapattn_forward_stages", "lapattn_set_stage_events", "lapattn_launches")
 
 STAGES = ("pool", "main", "maps", "out")
@@ -57,6 +58,14 @@ class LapattnError(RuntimeError):
         self.status = status
 
 
+class LapattnTimeout(RuntimeError):
+    """A forward call's in-launch waits ran out of time: its output is invalid."""
+
+    def __init__(self, count: int):
+        super().__init__(f"lapattn: {count} in-launch wait(s) timed out; the output is invalid")
+        self.count = count
+
+
 _lib = None
 _lock = threading.Lock()
 
@@ -73,6 +82,8 @@ def _declare(lib):
     lib.lapattn_check.restype = ctypes.c_int
     lib.lapattn_workspace_bytes.argtypes = [dp]
     lib.lapattn_workspace_bytes.restype = sz
+    lib.lapattn_status_offset.argtypes = [dp]
+    lib.lapattn_status_offset.restype = sz
     lib.lapattn_init.argtypes = []
     lib.lapattn_init.restype = ctypes.c_int
     lib.lapattn_forward.argtypes = [dp, vp, vp, vp, f32, f32, i32, vp, vp, sz, vp]

@@ -71,6 +71,44 @@ def _check_io(q, k, v):
             raise ValueError("q, k and v must share shape and dtype")
 
 
+def _check_out(out, q):
+    """The library writes B*H*N*d elements of q's dtype through out's pointer:
+    anything but a contiguous tensor of q's shape, dtype and device would be
+    written out of bounds or in the wrong layout."""
+    if not isinstance(out, torch.Tensor):
+        raise ValueError("out must be a tensor")
+    if out.shape != q.shape or out.dtype != q.dtype or out.device != q.device:
+        raise ValueError(f"out must match q: shape {tuple(q.shape)}, dtype {q.dtype}, "
+                         f"device {q.device} (got {tuple(out.shape)}, {out.dtype}, {out.device})")
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
+
+
+def _check_workspace(ws, desc, device):
+    if not isinstance(ws, torch.Tensor) or ws.dtype != torch.uint8:
+        raise ValueError("workspace must be a torch.uint8 tensor (its numel is the byte count)")
+    if ws.device != device or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+    need = workspace_bytes(desc)
+    if ws.numel() < need:
+        raise ValueError(f"workspace holds {ws.numel()} bytes, {need} needed")
+
+
+def status_offset(desc: Desc) -> int:
+    off = int(_lib.lib().lapattn_status_offset(ctypes.byref(desc)))
+    if off == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid descriptor")
+    return off
+
+
+def status(desc: Desc, workspace: torch.Tensor) -> int:
+    """Timed-out in-launch waits of the last call on `workspace` (0 when its
+    output is valid).  Synchronises with the device."""
+    off = status_offset(desc)
+    word = workspace[off:off + 4].cpu()
+    return int(word.view(torch.int32).item())
+
+
 def _stream_ptr(stream) -> int:
     s = torch.cuda.current_stream() if stream is None else stream
     return s.cuda_stream
@@ -80,19 +118,42 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, grid_h: int,
             grid_w: int, pool_h: int, pool_w: int, lam: float, eps: float,
             iters: int, kernel: str = "laplacian", out: Optional[torch.Tensor] = None,
             workspace: Optional[torch.Tensor] = None, serial: bool = False,
-            stream=None) -> torch.Tensor:
-    """O = K_QL (X (K_LK V)) per head; see include/lapattn.h."""
+            stream=None, check: bool = True) -> torch.Tensor:
+    """O = K_QL (X (K_LK V)) per head; see include/lapattn.h.
+
+    With `check` (the default) the call's status word is read back after the
+    launch, which waits for the call to finish, and LapattnTimeout is raised
+    if any of its in-launch waits ran out of time.  With check=False nothing
+    synchronises; read `status(desc, workspace)` before reusing the workspace.
+    """
     _check_io(q, k, v)
     desc = _desc_for(q, grid_h, grid_w, pool_h, pool_w, kernel, serial)
     if out is None:
         out = torch.empty_like(q)
+    else:
+        _check_out(out, q)
     if workspace is None:
         workspace = alloc_workspace(desc, q.device)
+    else:
+        _check_workspace(workspace, desc, q.device)
     st = _lib.lib().lapattn_forward(
         ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(), lam, eps, iters,
         out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream_ptr(stream))
     _lib.check(st)
+    if check:
+        with torch.cuda.stream(stream) if stream is not None else _nullctx():
+            n = status(desc, workspace)
+        if n:
+            raise _lib.LapattnTimeout(n)
     return out
+
+
+class _nullctx:
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *a):
+        return False
 
 
 def forward_stages(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, grid_h: int,
@@ -122,6 +183,10 @@ def forward_stages(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, grid_h:
         res["L"].data_ptr(), res["KQL"].data_ptr(), res["KLK"].data_ptr(),
         res["A"].data_ptr(), res["X"].data_ptr(), res["W"].data_ptr())
     _lib.check(st)
+    with torch.cuda.stream(stream) if stream is not None else _nullctx():
+        n = status(desc, ws)
+    if n:
+        raise _lib.LapattnTimeout(n)
     return res
 
 

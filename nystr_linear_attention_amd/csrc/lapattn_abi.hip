@@ -265,6 +265,12 @@ size_t lapattn_workspace_bytes(const lapattn_desc_t* desc) {
   return lapattn::make_plan(desc).total;
 }
 
+size_t lapattn_status_offset(const lapattn_desc_t* desc) {
+  if (lapattn::check_desc(desc) != LAPATTN_OK) return static_cast<size_t>(-1);
+  // word 0 of the hand-off words: timed-out waits of the call
+  return lapattn::make_plan(desc).off_sync;
+}
+
 int lapattn_launches(const lapattn_desc_t* desc, int q_is_k) {
   const int st = lapattn::check_desc(desc);
   if (st != LAPATTN_OK) return st;
@@ -285,6 +291,7 @@ int lapattn_set_stage_events(void* const* events, int n) {
 int lapattn_init(void) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return LAPATTN_ERR_HIP;
+  (void)lapattn::device_cus();
   return LAPATTN_OK;
 }
 

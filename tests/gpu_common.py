@@ -29,14 +29,30 @@ def device_inputs(w, x):
     return q, k, v
 
 
+def poisoned_workspace(desc):
+    """A fresh workspace filled with 0xff bytes (NaN as fp32): the library
+    promises to ignore the workspace's contents on entry, and a read of
+    anything it did not write first shows up as NaN in the output."""
+    ws = api.alloc_workspace(desc, torch.device("cuda"))
+    ws.fill_(0xFF)
+    return ws
+
+
 def run_gpu(w, x, serial=False, stages=False):
+    """One forward through the C ABI.  api.forward / forward_stages read the
+    call's status word back and raise if any in-launch wait timed out, so
+    every GPU test that runs through here asserts it is zero."""
     q, k, v = device_inputs(w, x)
     kw = dict(grid_h=w.grid_h, grid_w=w.grid_w, pool_h=w.pool_h, pool_w=w.pool_w,
               lam=w.lam, eps=w.eps, iters=w.iters, kernel=w.kernel, serial=serial)
     if stages:
         res = api.forward_stages(q, k, v, **kw)
     else:
-        res = {"O": api.forward(q, k, v, **kw)}
+        desc = api.make_desc(w.B, w.H, w.grid_h, w.grid_w, w.d, w.pool_h, w.pool_w, w.kernel,
+                             q.dtype, serial=serial)
+        ws = poisoned_workspace(desc)
+        res = {"O": api.forward(q, k, v, workspace=ws, **kw)}
+        assert api.status(desc, ws) == 0
     torch.cuda.synchronize()
     return {key: t.float().cpu().numpy().astype(np.float64) for key, t in res.items()}
 

@@ -227,15 +227,44 @@ def pin_nystrom_exact_all_landmarks(o):
     v = r.standard_normal((n, d))
     lam = 2.0 * math.sqrt(d)
     for kern in ("laplacian", "gaussian"):
-        def kv(a, b):
-            diff = [a[c] - b[c] for c in range(d)]
-            dist = sum(abs(x) for x in diff) if kern == "laplacian" else sum(x * x for x in diff)
-            return math.exp(-dist / lam)
-        ref = np.array([[sum(kv(q[i], k[j]) * v[j, c] for j in range(n))
-                         for c in range(d)] for i in range(n)])
+        ref = _brute_full_attention(q, k, v, lam, kern)
         res = o.nystrom_head(q, k, v, grid_h=gh, grid_w=gw, pool_h=1, pool_w=1,
                              lam=lam, eps=0.0, iters=80, kernel=kern)
         _close(res["O"], ref, 1e-9, f"Nystrom exactness ({kern})")
+
+
+def _brute_full_attention(q, k, v, lam, kern):
+    """sum_j k(q_i, k_j) v_j with scalar loops only (no oracle code)."""
+    n, d = len(q), len(q[0])
+
+    def kv(a, b):
+        diff = [a[c] - b[c] for c in range(d)]
+        dist = sum(abs(x) for x in diff) if kern == "laplacian" else sum(x * x for x in diff)
+        return math.exp(-dist / lam)
+    return np.array([[sum(kv(q[i], k[j]) * v[j][c] for j in range(len(k)))
+                      for c in range(len(v[0]))] for i in range(n)])
+
+
+def pin_full_kernel_attention_brute_force(o):
+    """Exact kernel attention k(Q, K) V against loops-only brute force, with
+    Q != K, different query and key counts and d_v != d, so a transposed
+    kernel matrix, swapped arguments or a wrong contraction fails."""
+    r = _rng(19)
+    nq, nk, d, dv = 7, 11, 5, 3
+    q = r.standard_normal((nq, d))
+    k = r.standard_normal((nk, d)) + 0.3
+    v = r.standard_normal((nk, dv))
+    for kern, lam in (("laplacian", 3.0), ("gaussian", 4.5)):
+        got = o.full_kernel_attention(q, k, v, lam, kern)
+        _close(got, _brute_full_attention(q, k, v, lam, kern), 1e-13,
+               f"full kernel attention ({kern})")
+    # square and Q != K: the reversed map k(K, Q) has the same shape
+    qs = r.standard_normal((9, d))
+    ks = r.standard_normal((9, d)) - 0.2
+    vs = r.standard_normal((9, dv))
+    _close(o.full_kernel_attention(qs, ks, vs, 3.0, "laplacian"),
+           _brute_full_attention(qs, ks, vs, 3.0, "laplacian"), 1e-13,
+           "full kernel attention (square)")
 
 
 def _pure_python_head(q, k, v, gh, gw, ph, pw, lam, eps, iters, kern):
@@ -336,6 +365,7 @@ def pin_heads_independent(o):
 
 
 ALL_PINS = [
+    pin_full_kernel_attention_brute_force,
     pin_pool_identity,
     pin_pool_raster_geometry,
     pin_pool_reshape_mean,

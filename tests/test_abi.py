@@ -165,3 +165,17 @@ def test_launch_slots():
     bad = api.make_desc(8, 1, 56, 55, 64, 8, 8, "laplacian", torch.float32)
     with pytest.raises(_lib.LapattnError):
         api.launches(bad, False)
+
+
+def test_status_offset():
+    """The status word sits inside the workspace, 4-byte aligned, for every
+    valid descriptor; an invalid descriptor gives (size_t)-1."""
+    lib = _lib.lib()
+    for kw in (dict(), dict(B=8, H=1, grid_h=56, grid_w=56, d=64, pool_h=8, pool_w=8),
+               dict(B=32, H=5, grid_h=28, grid_w=28, d=64, pool_h=4, pool_w=4, dtype=1)):
+        d = good_desc(**kw)
+        off = lib.lapattn_status_offset(ctypes.byref(d))
+        need = lib.lapattn_workspace_bytes(ctypes.byref(d))
+        assert off % 4 == 0 and off + 4 <= need, (kw, off, need)
+    assert lib.lapattn_status_offset(ctypes.byref(good_desc(d=48))) == ctypes.c_size_t(-1).value
+    assert lib.lapattn_status_offset(None) == ctypes.c_size_t(-1).value

@@ -39,3 +39,22 @@ def test_source_digest_covers_the_kernel_sources():
     d = bench.source_digest()
     assert len(d) == 16 and int(d, 16) >= 0
     assert d == bench.source_digest()
+
+
+def test_work_matches_the_algorithmic_counts():
+    """The headline's algorithmic work: L1 pairs B*H*(2 N m + m^2)*d (maps
+    and A), 4 m^3 iters per head for Newton-Schulz, 2 m N d for K_LK V."""
+    from nystr_linear_attention_amd import workloads as wl
+    w = wl.HEADLINE
+    wk = bench.work(w)
+    assert wk["map_pairs"] + wk["amat_pairs"] == 8 * (2 * 3136 * 49 + 49 * 49) * 64 == 158581248
+    assert wk["ns"] == 8 * 4 * 49 ** 3 * 20
+    assert wk["klkv"] == 8 * 2 * 49 * 3136 * 64
+    g = bench.work(wl.BY_NAME["gauss_f32_b16h2_n3136_d64_m49_qk"])
+    assert g["map_pairs"] == 32 * 3136 * 49 * 64      # K = Q: one map
+
+
+def test_host_info_names_cpu_and_blas():
+    info = bench.host_info()
+    assert info["usable_cores"] >= 1
+    assert isinstance(info["blas"], list)

@@ -129,7 +129,22 @@ def widen_bf16_as_f16(x, dtype):
     return np.asarray(x, dtype=np.float32).astype(np.float64)
 
 
+def full_attention_reversed(q, k, v, lam, kernel="laplacian"):
+    # k(K, Q) V only type-checks when there are as many queries as keys;
+    # elsewhere the mutant computes the right thing, so only a square case
+    # can catch it
+    if q.shape[0] != k.shape[0]:
+        return o.kernel_map(q, k, lam, kernel) @ v
+    return o.kernel_map(k, q, lam, kernel) @ v
+
+
+def full_attention_no_v(q, k, v, lam, kernel="laplacian"):
+    return o.kernel_map(q, k, lam, kernel).sum(axis=1, keepdims=True) * v.mean(axis=0)
+
+
 MUTATIONS = {
+    "full attention uses k(K, Q)": ("full_kernel_attention", full_attention_reversed),
+    "full attention drops V's rows": ("full_kernel_attention", full_attention_no_v),
     "pool raster order column-major": ("landmarks_avg_pool", pool_column_major),
     "pool sums instead of averaging": ("landmarks_avg_pool", pool_sum),
     "pool window height/width swapped": ("landmarks_avg_pool", pool_swapped_window),

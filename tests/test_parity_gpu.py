@@ -21,11 +21,17 @@ def _print_case(w, extra=""):
           f"kernel={w.kernel} dtype={w.dtype} iters={w.iters} {extra}", flush=True)
 
 
+# Each workload at its own seed (1000 + position) and two more.
+SEED_OFFSETS = (0, 1, 2)
+
+
+@pytest.mark.parametrize("off", SEED_OFFSETS, ids=[f"seed+{o}" for o in SEED_OFFSETS])
 @pytest.mark.parametrize("idx", range(len(wl.WORKLOADS)), ids=[w.name for w in wl.WORKLOADS])
-def test_full_size_workloads(idx):
+def test_full_size_workloads(idx, off):
     """All heads of every reference workload, default (overlapped) launch plan."""
     w = wl.WORKLOADS[idx]
-    _print_case(w)
+    w = w.replace(seed=w.seed + 100 * off)
+    _print_case(w, f"seed={w.seed}")
     x = wl.make_inputs(w)
     got = run_gpu(w, x)
     worst = compare_output(w, x, got["O"])
@@ -109,6 +115,50 @@ def test_device_errors_are_reported():
         api.forward(q, q, q, grid_h=14, grid_w=14, pool_h=2, pool_w=2, lam=1.0, eps=0.0,
                     iters=1, out=q)
     assert e.value.status == api._lib.ERR_ALIAS
+
+
+def test_bad_out_and_workspace_are_rejected_before_launch():
+    """A caller-supplied out or workspace that the library would write out of
+    bounds or in the wrong layout raises ValueError before any launch."""
+    q = torch.randn(1, 2, 196, 32, device="cuda")
+    kw = dict(grid_h=14, grid_w=14, pool_h=2, pool_w=2, lam=32.0, eps=1e-3, iters=3)
+    bad_outs = {
+        "undersized": torch.empty(1, 1, 196, 32, device="cuda"),
+        "flat": torch.empty(2 * 196 * 32, device="cuda"),
+        "fp64": torch.empty(1, 2, 196, 32, device="cuda", dtype=torch.float64),
+        "bf16": torch.empty(1, 2, 196, 32, device="cuda", dtype=torch.bfloat16),
+        "host": torch.empty(1, 2, 196, 32),
+        "strided": torch.empty(1, 2, 32, 196, device="cuda").transpose(2, 3),
+    }
+    for name, o in bad_outs.items():
+        o.fill_(7.0)
+        with pytest.raises(ValueError):
+            api.forward(q, q.clone(), q.clone(), out=o, **kw)
+        assert bool((o == 7.0).all()), f"{name}: written although rejected"
+    desc = api.make_desc(1, 2, 14, 14, 32, 2, 2)
+    n = api.workspace_bytes(desc)
+    for ws in (torch.empty(n - 256, dtype=torch.uint8, device="cuda"),
+               torch.empty(n // 4 + 1, dtype=torch.float32, device="cuda"),
+               torch.empty(n, dtype=torch.uint8)):
+        with pytest.raises(ValueError):
+            api.forward(q, q.clone(), q.clone(), workspace=ws, **kw)
+    torch.cuda.synchronize()
+
+
+def test_status_word_is_cleared_by_every_call():
+    """The status word reads zero after a call even when the workspace held
+    garbage on entry (it is set by the call's first launch)."""
+    w = wl.WORKLOADS[0].replace(B=2, H=2)
+    x = wl.make_inputs(w)
+    q, k, v = (torch.from_numpy(x[n]).cuda() for n in "qkv")
+    desc = api.make_desc(w.B, w.H, w.grid_h, w.grid_w, w.d, w.pool_h, w.pool_w)
+    ws = api.alloc_workspace(desc, q.device)
+    off = api.status_offset(desc)
+    assert off % 4 == 0 and off + 4 <= ws.numel()
+    ws.fill_(0xA5)
+    api.forward(q, k, v, grid_h=w.grid_h, grid_w=w.grid_w, pool_h=w.pool_h, pool_w=w.pool_w,
+                lam=w.lam, eps=w.eps, iters=w.iters, workspace=ws, check=False)
+    assert api.status(desc, ws) == 0
 
 
 @pytest.mark.parametrize("serial", [False, True], ids=["fused", "serial"])
