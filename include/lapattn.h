@@ -91,8 +91,13 @@ enum {
   LAPATTN_ERR_ALIAS = -6,        /* O overlaps an input or the workspace      */
   LAPATTN_ERR_WORKSPACE = -7,    /* workspace smaller than required / unaligned*/
   LAPATTN_ERR_HIP = -8,          /* a HIP runtime call or launch failed       */
-  LAPATTN_ERR_ALIGN = -9         /* q, k, v or out not 16-byte aligned        */
+  LAPATTN_ERR_ALIGN = -9,        /* q, k, v or out not 16-byte aligned        */
+  LAPATTN_ERR_SCRATCH = -10      /* lapattn_forward_noalloc: the call needs
+                                    more workspace than the static scratch   */
 };
+
+/* Size of the static device scratch behind lapattn_forward_noalloc. */
+#define LAPATTN_NOALLOC_SCRATCH_BYTES (128u << 20)
 
 /* Launch slots of one forward call, in launch order (for
  * lapattn_set_stage_events). */
@@ -175,6 +180,27 @@ int lapattn_forward(const lapattn_desc_t* desc, const void* q, const void* k,
                     const void* v, float lambda, float eps, int32_t iters,
                     void* out, void* workspace, size_t workspace_bytes,
                     void* stream);
+
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * forward as lapattn_forward (same arguments, plan, kernels and bitwise
+ * result), with the workspace taken from a static device array of
+ * LAPATTN_NOALLOC_SCRATCH_BYTES (128 MiB) that the library holds on each
+ * device it runs on until the process ends.  The call allocates and frees
+ * nothing; its first call on a device (or lapattn_init with that device
+ * current) looks the array's device address up once.
+ *   status  device pointer to a uint32 (4-byte aligned) that the call sets
+ *           to its count of timed-out in-launch waits (nonzero: the output
+ *           is invalid); NULL: not reported
+ * Returns LAPATTN_ERR_SCRATCH when lapattn_workspace_bytes(desc) exceeds the
+ * scratch (nothing is enqueued), else what lapattn_forward returns.  Every
+ * call on a device shares that device's scratch, which keeps the last call's
+ * contents: calls that overlap on one device (other streams, other host
+ * threads) race and must be serialised by the caller. */
+int lapattn_forward_noalloc(const lapattn_desc_t* desc, const void* q,
+                            const void* k, const void* v, float lambda,
+                            float eps, int32_t iters, void* out,
+                            uint32_t* status, void* stream);
 
 /* lapattn_forward plus device copies of every intermediate, for stage-wise
  * checking.  Each stage pointer may be NULL (not written).  All fp32:

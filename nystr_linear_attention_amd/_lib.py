@@ -21,6 +21,8 @@ ERR_ALIAS = -6
 ERR_WORKSPACE = -7
 ERR_HIP = -8
 ERR_ALIGN = -9
+ERR_SCRATCH = -10
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 KERNEL_LAPLACIAN = 0
 KERNEL_GAUSSIAN = 1
@@ -31,7 +33,7 @@ FLAG_SERIAL = 1
 # Names of every entry point declared in include/lapattn.h.
 EXPORTS = ("lapattn_version", "lapattn_strerror", "lapattn_check",
            "lapattn_workspace_bytes", "lapattn_status_offset", "lapattn_init",
-           "lapattn_forward",
+           "lapattn_forward", "lapattn_forward_noalloc",
            "lapattn_forward_stages", "lapattn_set_stage_events", "lapattn_launches")
 
 STAGES = ("pool", "main", "maps", "out")
@@ -88,6 +90,8 @@ def _declare(lib):
     lib.lapattn_init.restype = ctypes.c_int
     lib.lapattn_forward.argtypes = [dp, vp, vp, vp, f32, f32, i32, vp, vp, sz, vp]
     lib.lapattn_forward.restype = ctypes.c_int
+    lib.lapattn_forward_noalloc.argtypes = [dp, vp, vp, vp, f32, f32, i32, vp, vp, vp]
+    lib.lapattn_forward_noalloc.restype = ctypes.c_int
     lib.lapattn_forward_stages.argtypes = [dp, vp, vp, vp, f32, f32, i32, vp, vp, sz, vp,
                                            vp, vp, vp, vp, vp, vp]
     lib.lapattn_forward_stages.restype = ctypes.c_int

@@ -15,6 +15,36 @@ namespace {
 
 constexpr size_t kAlign = 256;
 
+// Workspace of lapattn_forward_noalloc: a static device array that each
+// device the library runs on holds until the process ends.  In host code its
+// name is a host-side stand-in, never a device address: kernels and copies
+// get the per-device address that hipGetSymbolAddress returns (scratch_ptr).
+static __device__ __align__(256) unsigned char scratch[LAPATTN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+
+// Device address of `scratch` on the current device, looked up once per
+// device (lapattn_init, or the first no-alloc call on the device); null with
+// *err set when no device is current or the lookup fails.
+void* scratch_ptr(int* err) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    *err = LAPATTN_ERR_HIP;
+    return nullptr;
+  }
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+    (void)hipGetLastError();
+    *err = LAPATTN_ERR_HIP;
+    return nullptr;
+  }
+  g_scratch[dev].store(p, std::memory_order_release);
+  return p;
+}
+
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 int check_desc(const lapattn_desc_t* d) {
@@ -174,6 +204,11 @@ int run(const lapattn_desc_t* desc, const Args& args, void* workspace, size_t ws
   if (overlaps(a.out, io, a.q, io) || overlaps(a.out, io, a.k, io) ||
       overlaps(a.out, io, a.v, io) || overlaps(a.out, io, workspace, ws_bytes))
     return LAPATTN_ERR_ALIAS;
+  if (a.status && (reinterpret_cast<uintptr_t>(a.status) % 4 ||
+                   overlaps(a.status, 4, a.out, io) || overlaps(a.status, 4, a.q, io) ||
+                   overlaps(a.status, 4, a.k, io) || overlaps(a.status, 4, a.v, io) ||
+                   overlaps(a.status, 4, workspace, ws_bytes)))
+    return LAPATTN_ERR_ALIAS;
 
   char* ws = static_cast<char*>(workspace);
   Buffers b;
@@ -184,6 +219,7 @@ int run(const lapattn_desc_t* desc, const Args& args, void* workspace, size_t ws
   b.wt = reinterpret_cast<float*>(ws + p.off_wt);
   b.yt = reinterpret_cast<float*>(ws + p.off_yt);
   b.sync = reinterpret_cast<unsigned*>(ws + p.off_sync);
+  b.timeouts = a.status ? a.status : b.sync;
 
   if (launch_pool(p, a, b, stream, slot(LAPATTN_STAGE_POOL)) != hipSuccess) return LAPATTN_ERR_HIP;
   if (desc->flags & LAPATTN_FLAG_SERIAL) {
@@ -206,7 +242,7 @@ int run(const lapattn_desc_t* desc, const Args& args, void* workspace, size_t ws
 int forward_common(const lapattn_desc_t* desc, const void* q, const void* k, const void* v,
                    float lambda, float eps, int32_t iters, void* out, void* workspace,
                    size_t workspace_bytes, void* stream, float* L, float* kql, float* klk,
-                   float* am, float* x, float* w) {
+                   float* am, float* x, float* w, unsigned* status = nullptr) {
   int st = check_desc(desc);
   if (st != LAPATTN_OK) return st;
   st = check_params(lambda, eps, iters);
@@ -227,6 +263,7 @@ int forward_common(const lapattn_desc_t* desc, const void* q, const void* k, con
   a.st_a = am;
   a.st_x = x;
   a.st_w = w;
+  a.status = status;
   return run(desc, a, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
@@ -250,6 +287,8 @@ const char* lapattn_strerror(int status) {
     case LAPATTN_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
     case LAPATTN_ERR_HIP: return "HIP runtime or kernel launch failure";
     case LAPATTN_ERR_ALIGN: return "q, k, v or out is not 16-byte aligned";
+    case LAPATTN_ERR_SCRATCH:
+      return "the call needs more workspace than the no-alloc entry point's static scratch holds";
   }
   return "unknown status";
 }
@@ -292,6 +331,8 @@ int lapattn_init(void) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return LAPATTN_ERR_HIP;
   (void)lapattn::device_cus();
+  int err = LAPATTN_OK;
+  if (!lapattn::scratch_ptr(&err)) return err;
   return LAPATTN_OK;
 }
 
@@ -301,6 +342,24 @@ int lapattn_forward(const lapattn_desc_t* desc, const void* q, const void* k, co
   return lapattn::forward_common(desc, q, k, v, lambda, eps, iters, out, workspace,
                                  workspace_bytes, stream, nullptr, nullptr, nullptr, nullptr,
                                  nullptr, nullptr);
+}
+
+int lapattn_forward_noalloc(const lapattn_desc_t* desc, const void* q, const void* k,
+                            const void* v, float lambda, float eps, int32_t iters, void* out,
+                            uint32_t* status, void* stream) {
+  // every argument check first: nothing is looked up or enqueued on an error
+  int st = lapattn::check_desc(desc);
+  if (st != LAPATTN_OK) return st;
+  st = lapattn::check_params(lambda, eps, iters);
+  if (st != LAPATTN_OK) return st;
+  if (!q || !k || !v || !out) return LAPATTN_ERR_NULL;
+  if (lapattn::make_plan(desc).total > LAPATTN_NOALLOC_SCRATCH_BYTES) return LAPATTN_ERR_SCRATCH;
+  int err = LAPATTN_OK;
+  void* ws = lapattn::scratch_ptr(&err);
+  if (!ws) return err;
+  return lapattn::forward_common(desc, q, k, v, lambda, eps, iters, out, ws,
+                                 LAPATTN_NOALLOC_SCRATCH_BYTES, stream, nullptr, nullptr,
+                                 nullptr, nullptr, nullptr, nullptr, status);
 }
 
 int lapattn_forward_stages(const lapattn_desc_t* desc, const void* q, const void* k,

@@ -48,6 +48,8 @@ struct Buffers {
   float* wt;     // [BH][D][MP]    W^T = (K_LK V)^T, zero for columns >= m
   float* yt;     // [BH][D][MP]    Y^T = (X W)^T
   unsigned* sync;  // [kSyncHead (BH + 1)] hand-off words (see the main kernel)
+  unsigned* timeouts;  // the call's count of timed-out waits (word 0 of sync,
+                       // or a word the caller owns)
 };
 
 struct Args {
@@ -59,6 +61,8 @@ struct Args {
   int iters;
   int shared_qk;
   int out_in_main;  // query workgroups form O inside the main launch
+  unsigned* status;  // where the timeout count goes (null: word 0 of the
+                     // workspace's hand-off words)
   // optional fp32 stage copies (may be null)
   float* st_L;
   float* st_kql;

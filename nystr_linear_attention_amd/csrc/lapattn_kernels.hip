@@ -184,9 +184,11 @@ struct MainArgs {
   float* wt;          // [BH][D][MP]  W^T (reduced partials)
   float* yt;          // [BH][D][MP]  Y^T = (X W)^T
   void* out;          // [BH][N][D]   O (query workgroups write it)
-  unsigned* sync;     // hand-off words, zeroed by the pool launch: [0] counts
-                      // bounded waits that timed out; head bh owns the
-                      // kSyncHead words from kSyncHead (bh + 1) (see below)
+  unsigned* sync;     // hand-off words, zeroed by the pool launch; head bh
+                      // owns the kSyncHead words from kSyncHead (bh + 1)
+                      // (see below)
+  unsigned* timeouts; // counts bounded waits that timed out (zeroed by the
+                      // pool launch)
   float* st_a;
   float* st_x;
   float* st_kql;
@@ -237,7 +239,7 @@ struct MainArgs {
 // Forward progress: solver workgroups come first in the grid and each head's
 // key workgroups precede its query workgroups, so with in-order dispatch
 // every producer has started before a consumer can wait on it.  The wait is
-// bounded in time regardless (it then counts a timeout in sync[0] and goes
+// bounded in time regardless (it then counts a timeout in *timeouts and goes
 // on), so no wave can spin forever.
 // ---------------------------------------------------------------------------
 constexpr long long kWaitTicks = 2000000;  // 20 ms of the 100 MHz device clock
@@ -1563,14 +1565,14 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
     const int lps = (LINES + R - 1) / R;
     const int nslice = (LINES + lps - 1) / lps;
     if (u < nslice) {
-      wait_flags(key_flags(a, bh), nK, a.sync);
+      wait_flags(key_flags(a, bh), nK, a.timeouts);
       reduce_w_lines<D>(a, bh, u * lps, min((u + 1) * lps, LINES), PJ);
       raise_flag(slice_flags(a, bh) + u);
     }
     // W^T complete: copy it to LDS (PJ is unused by query tiles) while the
     // solver may still be running; then Y^T = W^T X^T in place, then the
     // output rows of the tiles (K_QL rows in LDS)
-    wait_flags(slice_flags(a, bh), nslice, a.sync);
+    wait_flags(slice_flags(a, bh), nslice, a.timeouts);
     {
       // row c of W^T (8 threads, consecutive lanes) scaled by 2^EW[c] into
       // fp16 range, split
@@ -1595,7 +1597,7 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
         if (k8 == 0) EW[row] = ew;
       }
     }
-    const int ex = static_cast<int16_t>(wait_flag(flag_x(a, bh), a.sync) & 0xffffu);
+    const int ex = static_cast<int16_t>(wait_flag(flag_x(a, bh), a.timeouts) & 0xffffu);
     {
       const uint16_t* xh = reinterpret_cast<const uint16_t*>(a.xw + static_cast<size_t>(bh) * MP * MP);
       y_in_lds<D>(PJ, xh, xh + MP * MP);
@@ -1665,8 +1667,9 @@ template <int D, bool BF16, int LPW>
 __global__ __launch_bounds__(WGS) void pool_kernel(const void* __restrict__ K,
                                                    float* __restrict__ L,
                                                    float* __restrict__ st_L,
-                                                   unsigned* __restrict__ sync, int gw, int ph,
-                                                   int pw, int m, int N) {
+                                                   unsigned* __restrict__ sync,
+                                                   unsigned* __restrict__ timeouts, int gw,
+                                                   int ph, int pw, int m, int N) {
   constexpr int C4 = D / 4;
   constexpr int G = WGS / C4;
   constexpr int U = 4;  // loads in flight per thread and window
@@ -1676,7 +1679,7 @@ __global__ __launch_bounds__(WGS) void pool_kernel(const void* __restrict__ K,
   // hand-off words of the main launch start at zero every call
   if (blockIdx.x == 0) {
     for (int e = tid; e < kSyncHead; e += WGS) sync[kSyncHead * (bh + 1) + e] = 0u;
-    if (bh == 0 && tid == 0) sync[0] = 0u;
+    if (bh == 0 && tid == 0) *timeouts = 0u;
   }
   const int mw = gw / pw;
   const int cnt = ph * pw;
@@ -1845,9 +1848,9 @@ hipError_t launch_pool_dl(const Plan& p, const Args& a, const Buffers& b, hipStr
   const dim3 grid((p.m + LPW - 1) / LPW, p.BH);
   if (p.bf16)
     return launch(pool_kernel<D, true, LPW>, grid, dim3(WGS), s, ev, a.k, b.L, a.st_L, b.sync,
-                  p.gw, p.ph, p.pw, p.m, p.N);
+                  b.timeouts, p.gw, p.ph, p.pw, p.m, p.N);
   return launch(pool_kernel<D, false, LPW>, grid, dim3(WGS), s, ev, a.k, b.L, a.st_L, b.sync,
-                p.gw, p.ph, p.pw, p.m, p.N);
+                b.timeouts, p.gw, p.ph, p.pw, p.m, p.N);
 }
 
 template <int D>
@@ -1920,6 +1923,7 @@ hipError_t launch_main(const Plan& p, const Args& a, const Buffers& b, bool with
   ma.yt = b.yt;
   ma.out = a.out;
   ma.sync = b.sync;
+  ma.timeouts = b.timeouts;
   ma.st_a = a.st_a;
   ma.st_x = a.st_x;
   ma.st_kql = a.st_kql;

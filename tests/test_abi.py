@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol():
 def test_version_and_strerror():
     lib = _lib.lib()
     assert lib.lapattn_version() == 1
-    for code in range(-9, 1):
+    for code in range(-10, 1):
         s = _lib.strerror(code)
         assert s and s != "unknown status"
     assert _lib.strerror(-99) == "unknown status"
@@ -179,3 +179,24 @@ def test_status_offset():
         assert off % 4 == 0 and off + 4 <= need, (kw, off, need)
     assert lib.lapattn_status_offset(ctypes.byref(good_desc(d=48))) == ctypes.c_size_t(-1).value
     assert lib.lapattn_status_offset(None) == ctypes.c_size_t(-1).value
+
+
+def test_noalloc_rejects_before_any_device_work():
+    """Argument errors and an oversize call come back before the scratch is
+    looked up (no device is touched on the CPU)."""
+    lib = _lib.lib()
+    d = good_desc()
+
+    def call(desc, q=FAKE, out=FAKE + 0x3000000, lam=4.0, iters=20):
+        return lib.lapattn_forward_noalloc(ctypes.byref(desc) if desc is not None else None,
+                                           q, FAKE + 0x1000000, FAKE + 0x2000000, lam, 1e-3,
+                                           iters, out, None, None)
+    assert call(None) == _lib.ERR_NULL
+    assert call(good_desc(B=0)) == _lib.ERR_SHAPE
+    assert call(d, lam=0.0) == _lib.ERR_PARAM
+    assert call(d, iters=65) == _lib.ERR_PARAM
+    assert call(d, q=None) == _lib.ERR_NULL
+    assert call(d, out=None) == _lib.ERR_NULL
+    big = good_desc(B=1024, H=8, grid_h=56, grid_w=56, d=64, pool_h=8, pool_w=8)
+    assert lib.lapattn_workspace_bytes(ctypes.byref(big)) > _lib.NOALLOC_SCRATCH_BYTES
+    assert call(big) == _lib.ERR_SCRATCH
