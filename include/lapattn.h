@@ -77,6 +77,15 @@ typedef enum {
                                    both as separate workgroup roles, so the
                                    solver overlaps the map stage.  Results are
                                    bitwise identical either way. */
+#define LAPATTN_FLAG_TICKETS 2u /* hand the main launch's workgroup roles out
+                                   by ticket, in the order workgroups start,
+                                   instead of by workgroup index.  By default
+                                   each XCD dispatching its workgroups in
+                                   index order guarantees that producers run
+                                   before their consumers wait; tickets drop
+                                   that assumption, at the cost of a few us of
+                                   contended counters per launch.  Results are
+                                   bitwise identical either way. */
 
 enum {
   LAPATTN_OK = 0,

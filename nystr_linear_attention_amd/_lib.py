@@ -29,6 +29,7 @@ KERNEL_GAUSSIAN = 1
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
 FLAG_SERIAL = 1
+FLAG_TICKETS = 2
 
 # Names of every entry point declared in include/lapattn.h.
 EXPORTS = ("lapattn_version", "lapattn_strerror", "lapattn_check",

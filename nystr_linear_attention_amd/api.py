@@ -19,13 +19,14 @@ _DTYPES = {torch.float32: _lib.DTYPE_F32, torch.bfloat16: _lib.DTYPE_BF16}
 
 def make_desc(B: int, H: int, grid_h: int, grid_w: int, d: int, pool_h: int,
               pool_w: int, kernel: str = "laplacian", dtype=torch.float32,
-              serial: bool = False) -> Desc:
+              serial: bool = False, tickets: bool = False) -> Desc:
     if kernel not in _KERNELS:
         raise ValueError(f"kernel must be one of {sorted(_KERNELS)}")
     if dtype not in _DTYPES:
         raise ValueError("dtype must be torch.float32 or torch.bfloat16")
+    flags = (_lib.FLAG_SERIAL if serial else 0) | (_lib.FLAG_TICKETS if tickets else 0)
     return Desc(B, H, grid_h, grid_w, d, pool_h, pool_w, _KERNELS[kernel],
-                _DTYPES[dtype], _lib.FLAG_SERIAL if serial else 0)
+                _DTYPES[dtype], flags)
 
 
 def version() -> int:
@@ -52,13 +53,13 @@ def alloc_workspace(desc: Desc, device) -> torch.Tensor:
 
 
 def _desc_for(q: torch.Tensor, grid_h: int, grid_w: int, pool_h: int, pool_w: int,
-              kernel: str, serial: bool) -> Desc:
+              kernel: str, serial: bool, tickets: bool = False) -> Desc:
     if q.dim() != 4:
         raise ValueError("q, k, v must be [B, H, N, d]")
     B, H, N, d = q.shape
     if N != grid_h * grid_w:
         raise ValueError(f"N={N} does not match the {grid_h}x{grid_w} grid")
-    return make_desc(B, H, grid_h, grid_w, d, pool_h, pool_w, kernel, q.dtype, serial)
+    return make_desc(B, H, grid_h, grid_w, d, pool_h, pool_w, kernel, q.dtype, serial, tickets)
 
 
 def _check_io(q, k, v):
@@ -118,7 +119,7 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, grid_h: int,
             grid_w: int, pool_h: int, pool_w: int, lam: float, eps: float,
             iters: int, kernel: str = "laplacian", out: Optional[torch.Tensor] = None,
             workspace: Optional[torch.Tensor] = None, serial: bool = False,
-            stream=None, check: bool = True) -> torch.Tensor:
+            tickets: bool = False, stream=None, check: bool = True) -> torch.Tensor:
     """O = K_QL (X (K_LK V)) per head; see include/lapattn.h.
 
     With `check` (the default) the call's status word is read back after the
@@ -127,7 +128,7 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, grid_h: int,
     synchronises; read `status(desc, workspace)` before reusing the workspace.
     """
     _check_io(q, k, v)
-    desc = _desc_for(q, grid_h, grid_w, pool_h, pool_w, kernel, serial)
+    desc = _desc_for(q, grid_h, grid_w, pool_h, pool_w, kernel, serial, tickets)
     if out is None:
         out = torch.empty_like(q)
     else:

@@ -64,7 +64,7 @@ int check_desc(const lapattn_desc_t* d) {
   if (d->kernel != LAPATTN_KERNEL_LAPLACIAN && d->kernel != LAPATTN_KERNEL_GAUSSIAN)
     return LAPATTN_ERR_PARAM;
   if (d->dtype != LAPATTN_F32 && d->dtype != LAPATTN_BF16) return LAPATTN_ERR_DTYPE;
-  if (d->flags & ~LAPATTN_FLAG_SERIAL) return LAPATTN_ERR_PARAM;
+  if (d->flags & ~(LAPATTN_FLAG_SERIAL | LAPATTN_FLAG_TICKETS)) return LAPATTN_ERR_PARAM;
   return LAPATTN_OK;
 }
 
@@ -264,6 +264,7 @@ int forward_common(const lapattn_desc_t* desc, const void* q, const void* k, con
   a.st_x = x;
   a.st_w = w;
   a.status = status;
+  a.tickets = (desc->flags & LAPATTN_FLAG_TICKETS) ? 1 : 0;
   return run(desc, a, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 

@@ -20,7 +20,9 @@ constexpr int kMaxKeyTilesOut = 4;
 // W partials per head at most (key ready flags per head).
 constexpr int kMaxPartials = 128;
 // Main-kernel workgroups taken to be resident at once: two per CU (LDS and
-// registers allow two) less a margin of 64; 448 on a 256-CU MI355X.
+// registers allow two) less a margin of 64; 448 on a 256-CU MI355X.  This
+// only chooses the faster plan: no plan depends on the whole grid being
+// resident for its hand-offs (see take_role in the kernels).
 constexpr long kResidentPerCU = 2;
 constexpr long kResidentMargin = 64;
 
@@ -63,6 +65,7 @@ struct Args {
   int out_in_main;  // query workgroups form O inside the main launch
   unsigned* status;  // where the timeout count goes (null: word 0 of the
                      // workspace's hand-off words)
+  int tickets;       // main-launch roles by ticket (LAPATTN_FLAG_TICKETS)
   // optional fp32 stage copies (may be null)
   float* st_L;
   float* st_kql;
@@ -92,8 +95,9 @@ hipError_t launch_out(const Plan& p, const Args& a, const Buffers& b, hipStream_
 
 // Whether query workgroups form O inside the main launch: only when there are
 // query workgroups (Q != K) and every workgroup of the launch can be resident
-// at once, so that the ones waiting for Y never keep key workgroups of the
-// same head from starting.
+// at once.  (Larger grids would be correct too, but query workgroups waiting
+// for X would hold CUs that later heads' map workgroups could use; they
+// store K_QL and an output launch forms O.)
 bool out_in_main_launch(const Plan& p, int shared_qk);
 
 }  // namespace lapattn

@@ -195,7 +195,10 @@ struct MainArgs {
   float* st_klk;
   float* st_w;
   int N, m, BH, nT, S, nP, mpad;
-  int ns_blocks;      // workgroups [0, ns_blocks) are solver workgroups
+  int ns_blocks;      // solver workgroups in the launch (0 or BH)
+  int tickets;        // roles come from per-queue tickets (else workgroup b
+                      // of a solver-only launch solves head b)
+  int nq;             // ticket queues (8 when 8 divides BH, else min(BH, 8))
   int nQ;             // query workgroups per head, QT tiles each (0 when Q == K)
   int shared_qk;      // Q and K are the same tensor
   int out_in_main;    // query workgroups wait for Y and write O (else they
@@ -236,11 +239,10 @@ struct MainArgs {
 // and evicts what the map workgroups stream; device-scope loads of the data
 // itself are several times slower than plain misses.)
 //
-// Forward progress: solver workgroups come first in the grid and each head's
-// key workgroups precede its query workgroups, so with in-order dispatch
-// every producer has started before a consumer can wait on it.  The wait is
-// bounded in time regardless (it then counts a timeout in *timeouts and goes
-// on), so no wave can spin forever.
+// Forward progress: see take_role (producers of a head are dispatched, or by
+// ticket start, before its consumers).  Every wait is bounded in time
+// regardless (it then counts a timeout in *timeouts and goes on), so no wave
+// can spin forever.
 // ---------------------------------------------------------------------------
 constexpr long long kWaitTicks = 2000000;  // 20 ms of the 100 MHz device clock
 
@@ -1375,8 +1377,8 @@ __device__ __forceinline__ void gauss_tile(const MainArgs& a, const float (&av)[
 
 template <int D, int KIND, bool BF16>
 __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restrict__ q, const void* __restrict__ k,
-                         const void* __restrict__ v, const float* __restrict__ Lw, int b,
-                         float* smem) {
+                         const void* __restrict__ v, const float* __restrict__ Lw, int bh,
+                         bool key_role, int unit, float* smem) {
   constexpr int CBN = D / 16;
   // PJ also holds the split W^T / Y^T copies of query workgroups
   constexpr int PJS = map_pj_size<D>();
@@ -1388,32 +1390,14 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
   const int lr = lane & 15, lg = lane >> 4;
   const int m = a.m, N = a.N;
   const int nK = a.nP;
-  // Workgroups are dispatched round-robin over the 8 XCDs.  When the heads
-  // divide evenly, renumber so that XCD x (= b % 8) works through heads
-  // x, x + 8, ... in order: each XCD's L2 and scalar caches then hold the
-  // landmarks of only 1/8 of the heads.
-  if (a.BH % 8 == 0) {
-    const int per_head = nK + a.nQ;
-    const int per_xcd = (a.BH / 8) * per_head;
-    const int x = b % 8, i = b / 8;
-    const int hh = i / per_head, u = i % per_head;  // head slot within the XCD, unit
-    const int head = 8 * hh + x;
-    b = u < nK ? head * nK + u : a.BH * nK + head * a.nQ + (u - nK);
-    (void)per_xcd;
-  }
-  const bool key_role = b < a.BH * nK;
-  int bh, t_beg, t_end;
+  int t_beg, t_end;
   if (key_role) {
-    bh = b / nK;
-    const int kw = b % nK;
-    t_beg = kw * a.S;
+    t_beg = unit * a.S;
     t_end = min(t_beg + a.S, a.nT);
   } else {
     // QT tiles per query workgroup (their K_QL rows stay in LDS until Y is
     // ready, in PT and in the V^T area, which query tiles do not use)
-    const int bq = b - a.BH * nK;
-    bh = bq / a.nQ;
-    t_beg = QT * (bq % a.nQ);
+    t_beg = QT * unit;
     t_end = min(t_beg + QT, a.nT);
   }
   // K_QL goes to global memory only when Q == K (the output launch reads
@@ -1607,7 +1591,7 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
     return;
   }
 
-  const int kw = b % nK;
+  const int kw = unit;
   float* part = a.wpart + (static_cast<size_t>(bh) * nK + kw) * D * MP;
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
@@ -1630,6 +1614,90 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
   }
 }
 
+// ---------------------------------------------------------------------------
+// Roles of the main launch.  Every wait inside the launch is on a producer of
+// the same head: query workgroups wait for the key workgroups' W^T partials,
+// for the W^T slices of the head's first R <= 32 query workgroups and for the
+// solver's X.  Solvers and key workgroups never wait.
+//
+// Default (static roles, by workgroup index): the solvers come first, then
+// the map units.  When 8 divides BH, workgroup index x (mod 8) -- which the
+// dispatcher places round-robin on the 8 XCDs -- works through heads
+// x, x + 8, ... in order, each head's key units before its query units: a
+// head's workgroups share one XCD's L2 and scalar caches (landmarks, X, W^T)
+// and every producer has a lower index than its consumers on the same XCD.
+// Otherwise all key units precede all query units.  Either way, with each
+// XCD dispatching its workgroups in index order, a consumer is dispatched
+// only after every producer it waits for on its XCD, or (heads spread over
+// XCDs) after every producer-class workgroup of that XCD, and producers run
+// to completion without waiting; so no residency beyond the slice exchange
+// (at most 32 workgroups of one head at once) is needed, whatever else runs
+// on the device.
+//
+// LAPATTN_FLAG_TICKETS drops the dispatch-order assumption: roles are handed
+// out by ticket, in the order in which workgroups start running.  The heads
+// are split into queues (queue x: heads x, x + nq, ...), each with its own
+// counter, and a queue's tickets run through its solvers, then per head its
+// key units, then its query units, so every producer a workgroup waits for
+// has already started.  The counters cost time: 50 to 215 workgroups take
+// their tickets from one word at the start of the launch, and those read-
+// modify-writes serialise at memory.  With 8 queues, queue x takes the
+// workgroups with index = x (mod 8) (the same XCD placement as above);
+// otherwise the queues take consecutive ranges of workgroup indices.
+// Both give bitwise identical results: the arithmetic of a unit does not
+// depend on which workgroup runs it.
+// ---------------------------------------------------------------------------
+struct Role {
+  int kind;  // 0 solver, 1 key unit, 2 query unit
+  int bh;    // head
+  int u;     // unit index within the head (key: partial index; query: tile pair)
+};
+
+__device__ __forceinline__ Role static_role(const MainArgs& a, int b) {
+  if (b < a.ns_blocks) return Role{0, b, 0};
+  b -= a.ns_blocks;
+  const int nK = a.nP;
+  if (a.BH % 8 == 0) {
+    const int per_head = nK + a.nQ;
+    const int x = b % 8, i = b / 8;
+    const int hh = i / per_head, u = i % per_head;  // head slot within the XCD, unit
+    const int head = 8 * hh + x;
+    return u < nK ? Role{1, head, u} : Role{2, head, u - nK};
+  }
+  if (b < a.BH * nK) return Role{1, b / nK, b % nK};
+  const int bq = b - a.BH * nK;
+  return Role{2, bq / a.nQ, bq % a.nQ};
+}
+
+__device__ __forceinline__ Role take_role(const MainArgs& a, int b) {
+  if (!a.tickets) return static_role(a, b);
+  const int nq = a.nq;
+  const int per = (a.ns_blocks ? 1 : 0) + a.nP + a.nQ;  // units per head
+  int x;
+  if (nq == 8 && a.BH % 8 == 0) {
+    x = b & 7;
+  } else {
+    int start = 0;
+    for (x = 0; x + 1 < nq; ++x) {
+      const int size = ((a.BH - x + nq - 1) / nq) * per;
+      if (b < start + size) break;
+      start += size;
+    }
+  }
+  __shared__ unsigned ticket_s;
+  if (threadIdx.x == 0)
+    ticket_s = __hip_atomic_fetch_add(a.sync + 32 * x + 1, 1u, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int t = static_cast<int>(ticket_s);
+  const int nh = (a.BH - x + nq - 1) / nq;  // heads of queue x
+  const int ns = a.ns_blocks ? nh : 0;
+  if (t < ns) return Role{0, x + nq * t, 0};
+  const int i = t - ns, np = a.nP + a.nQ;
+  const int head = x + nq * (i / np), u = i % np;
+  return u < a.nP ? Role{1, head, u} : Role{2, head, u - a.nP};
+}
+
 // Read-only inputs are separate __restrict__ parameters so that wave-uniform
 // reads of them (the landmark coordinates) compile to scalar loads.  At least
 // 4 waves per SIMD (at most 128 VGPRs): two workgroups per CU, which the
@@ -1647,11 +1715,11 @@ __global__ __launch_bounds__(WGM, 4) void main_kernel(MainArgs a, const void* __
   constexpr int SOLVER_SMEM = NsGeom<MB, D>::SMEM;
   __shared__ __attribute__((aligned(16)))
   float smem[MAP_SMEM > SOLVER_SMEM ? MAP_SMEM : SOLVER_SMEM];
-  const int b = blockIdx.x;
-  if (b < a.ns_blocks) {
-    solver_role<D, MB, KIND>(a, b, smem);
+  const Role r = take_role(a, blockIdx.x);
+  if (r.kind == 0) {
+    solver_role<D, MB, KIND>(a, r.bh, smem);
   } else {
-    map_role<D, KIND, BF16>(a, q, k, v, L, b - a.ns_blocks, smem);
+    map_role<D, KIND, BF16>(a, q, k, v, L, r.bh, r.kind == 1, r.u, smem);
   }
 }
 
@@ -1679,7 +1747,12 @@ __global__ __launch_bounds__(WGS) void pool_kernel(const void* __restrict__ K,
   // hand-off words of the main launch start at zero every call
   if (blockIdx.x == 0) {
     for (int e = tid; e < kSyncHead; e += WGS) sync[kSyncHead * (bh + 1) + e] = 0u;
-    if (bh == 0 && tid == 0) *timeouts = 0u;
+    if (bh == 0) {
+      // the call's words: ticket counters of the main launch (word 32 x + 1
+      // of queue x, one cache line each) and the timeout count
+      for (int e = tid; e < kSyncHead; e += WGS) sync[e] = 0u;
+      if (tid == 0) *timeouts = 0u;
+    }
   }
   const int mw = gw / pw;
   const int cnt = ph * pw;
@@ -1945,6 +2018,10 @@ hipError_t launch_main(const Plan& p, const Args& a, const Buffers& b, bool with
   ma.c_exp2 = exp2_scale(a.lambda);
   ma.eps = a.eps;
   ma.ns_blocks = with_solver ? p.BH : 0;
+  // roles by ticket on request; a solver-only launch (serial plan) has no
+  // waits and keeps workgroup b on head b
+  ma.tickets = (with_maps && a.tickets) ? 1 : 0;
+  ma.nq = p.BH % 8 == 0 ? 8 : (p.BH < 8 ? p.BH : 8);
   const long map_wgs = with_maps ? static_cast<long>(p.BH) * (p.nP + ma.nQ) : 0;
   const unsigned grid = static_cast<unsigned>(ma.ns_blocks + map_wgs);
   if (grid == 0) return hipSuccess;

@@ -38,7 +38,7 @@ def poisoned_workspace(desc):
     return ws
 
 
-def run_gpu(w, x, serial=False, stages=False):
+def run_gpu(w, x, serial=False, stages=False, tickets=False):
     """One forward through the C ABI.  api.forward / forward_stages read the
     call's status word back and raise if any in-launch wait timed out, so
     every GPU test that runs through here asserts it is zero."""
@@ -49,9 +49,9 @@ def run_gpu(w, x, serial=False, stages=False):
         res = api.forward_stages(q, k, v, **kw)
     else:
         desc = api.make_desc(w.B, w.H, w.grid_h, w.grid_w, w.d, w.pool_h, w.pool_w, w.kernel,
-                             q.dtype, serial=serial)
+                             q.dtype, serial=serial, tickets=tickets)
         ws = poisoned_workspace(desc)
-        res = {"O": api.forward(q, k, v, workspace=ws, **kw)}
+        res = {"O": api.forward(q, k, v, workspace=ws, tickets=tickets, **kw)}
         assert api.status(desc, ws) == 0
     torch.cuda.synchronize()
     return {key: t.float().cpu().numpy().astype(np.float64) for key, t in res.items()}

@@ -104,6 +104,24 @@ def test_serial_and_fused_plans_are_bitwise_equal():
     assert np.array_equal(a, b) and np.array_equal(a, c)
 
 
+TICKET_CASES = [wl.HEADLINE, wl.WORKLOADS[3], wl.WORKLOADS[4],
+                wl.small_case(10, 14, 32, 2, 2, B=3, H=1),     # BH % 8 != 0: three queues
+                wl.small_case(10, 14, 32, 2, 2, B=150),        # output-launch plan, 8 queues
+                wl.small_case(20, 20, 32, 4, 4, B=9)]          # 9 heads over 8 queues
+
+
+@pytest.mark.parametrize("w", TICKET_CASES, ids=[w.name for w in TICKET_CASES])
+def test_ticket_roles_are_bitwise_equal(w):
+    """Roles handed out by ticket (LAPATTN_FLAG_TICKETS) give the same bits as
+    roles by workgroup index, and pass the parity bar."""
+    _print_case(w, "tickets")
+    x = wl.make_inputs(w)
+    a = run_gpu(w, x)["O"]
+    b = run_gpu(w, x, tickets=True)["O"]
+    assert np.array_equal(a, b)
+    compare_output(w, x, b, heads=[(0, 0), (w.B - 1, w.H - 1)])
+
+
 def test_device_errors_are_reported():
     q = torch.zeros(1, 1, 196, 32, device="cuda")
     with pytest.raises(ValueError):
