@@ -190,6 +190,38 @@ int lapattn_forward(const lapattn_desc_t* desc, const void* q, const void* k,
                     void* out, void* workspace, size_t workspace_bytes,
                     void* stream);
 
+/* Backward pass: gradients of a scalar loss with respect to Q, K and V given
+ * dO, its gradient with respect to O = lapattn_forward(Q, K, V).  The
+ * LaplacianFormer summaries say the method's custom kernels serve the
+ * backward pass as well as the forward pass (Dutch summary, "Methodologie"
+ * item 3; Arabic summary, section 2(c) item 3) without giving formulas; this
+ * is the exact reverse-mode derivative of the forward defined at the top of
+ * this file, step by step (the Newton-Schulz steps, alpha's maxima and the
+ * landmark pool included).  Where the forward is not differentiable the
+ * subgradient is: d|t|/dt = sign(t) with sign(0) = 0; alpha's derivative
+ * through the first column (= row, A being exactly symmetric) of largest
+ * abs-sum.
+ *   q, k, v, dout   device, [B, H, N, d], element type desc->dtype (k may
+ *                   equal q: the shared projection's gradient is dq + dk)
+ *   lambda, eps, iters  as for lapattn_forward
+ *   dq, dk, dv      device, [B, H, N, d], element type desc->dtype; written
+ *                   in full; they must not overlap each other, an input or
+ *                   the workspace
+ *   workspace       device scratch of lapattn_backward_workspace_bytes(desc,
+ *                   iters) bytes, 256-byte aligned; contents on entry ignored
+ * The forward quantities it needs (landmarks, kernel maps, every
+ * Newton-Schulz iterate, W, Y) are recomputed, not taken from a forward call.
+ * desc->flags is ignored.  Compute is fp32 (MFMA for the products, FP32 VALU
+ * for the distance derivatives); bf16 outputs are rounded to nearest even.
+ * Five launches on `stream`; no waits across workgroups, no allocation, no
+ * synchronisation.  Returns LAPATTN_OK or the argument errors of
+ * lapattn_forward. */
+size_t lapattn_backward_workspace_bytes(const lapattn_desc_t* desc, int32_t iters);
+int lapattn_backward(const lapattn_desc_t* desc, const void* q, const void* k,
+                     const void* v, const void* dout, float lambda, float eps,
+                     int32_t iters, void* dq, void* dk, void* dv,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
 /* For callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
  * forward as lapattn_forward (same arguments, plan, kernels and bitwise

@@ -35,6 +35,7 @@ FLAG_TICKETS = 2
 EXPORTS = ("lapattn_version", "lapattn_strerror", "lapattn_check",
            "lapattn_workspace_bytes", "lapattn_status_offset", "lapattn_init",
            "lapattn_forward", "lapattn_forward_noalloc",
+           "lapattn_backward_workspace_bytes", "lapattn_backward",
            "lapattn_forward_stages", "lapattn_set_stage_events", "lapattn_launches")
 
 STAGES = ("pool", "main", "maps", "out")
@@ -91,6 +92,10 @@ def _declare(lib):
     lib.lapattn_init.restype = ctypes.c_int
     lib.lapattn_forward.argtypes = [dp, vp, vp, vp, f32, f32, i32, vp, vp, sz, vp]
     lib.lapattn_forward.restype = ctypes.c_int
+    lib.lapattn_backward_workspace_bytes.argtypes = [dp, i32]
+    lib.lapattn_backward_workspace_bytes.restype = sz
+    lib.lapattn_backward.argtypes = [dp, vp, vp, vp, vp, f32, f32, i32, vp, vp, vp, vp, sz, vp]
+    lib.lapattn_backward.restype = ctypes.c_int
     lib.lapattn_forward_noalloc.argtypes = [dp, vp, vp, vp, f32, f32, i32, vp, vp, vp]
     lib.lapattn_forward_noalloc.restype = ctypes.c_int
     lib.lapattn_forward_stages.argtypes = [dp, vp, vp, vp, f32, f32, i32, vp, vp, sz, vp,

@@ -197,3 +197,34 @@ def launches(desc: Desc, q_is_k: bool) -> tuple:
     if mask < 0:
         raise _lib.LapattnError(mask, _lib.strerror(mask))
     return tuple(name for s, name in enumerate(_lib.STAGES) if mask >> s & 1)
+
+
+def backward_workspace_bytes(desc: Desc, iters: int) -> int:
+    return int(_lib.lib().lapattn_backward_workspace_bytes(ctypes.byref(desc), iters))
+
+
+def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor, *,
+             grid_h: int, grid_w: int, pool_h: int, pool_w: int, lam: float, eps: float,
+             iters: int, kernel: str = "laplacian", workspace: Optional[torch.Tensor] = None,
+             stream=None):
+    """(dQ, dK, dV) of a loss with gradient dout at O = forward(q, k, v, ...);
+    see include/lapattn.h.  With k the same tensor as q, the gradient with
+    respect to that tensor is dQ + dK."""
+    _check_io(q, k, v)
+    _check_out(dout, q)
+    desc = _desc_for(q, grid_h, grid_w, pool_h, pool_w, kernel, False)
+    n = backward_workspace_bytes(desc, iters)
+    if n == 0:
+        raise ValueError("invalid descriptor or iters")
+    if workspace is None:
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    elif (workspace.dtype != torch.uint8 or workspace.device != q.device
+          or not workspace.is_contiguous() or workspace.numel() < n):
+        raise ValueError(f"workspace must be a contiguous uint8 tensor of >= {n} bytes on q's device")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    st = _lib.lib().lapattn_backward(
+        ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), lam, eps,
+        iters, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+        workspace.numel(), _stream_ptr(stream))
+    _lib.check(st)
+    return dq, dk, dv

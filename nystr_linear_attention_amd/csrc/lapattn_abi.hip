@@ -174,6 +174,57 @@ Plan make_plan(const lapattn_desc_t* d) {
   return p;
 }
 
+// Backward pass: tiles per workgroup of the partial launch so that each head
+// has at most 64 partials per side; every buffer 256-byte aligned.
+BwdPlan make_bwd_plan(const lapattn_desc_t* d, int32_t iters) {
+  BwdPlan p{};
+  p.B = d->B;
+  p.H = d->H;
+  p.gh = d->grid_h;
+  p.gw = d->grid_w;
+  p.D = d->d;
+  p.ph = d->pool_h;
+  p.pw = d->pool_w;
+  p.kernel = d->kernel;
+  p.bf16 = d->dtype == LAPATTN_BF16;
+  p.N = p.gh * p.gw;
+  p.m = (p.gh / p.ph) * (p.gw / p.pw);
+  p.BH = p.B * p.H;
+  p.ns_mb = (p.m + 15) / 16;
+  p.nT = (p.N + 63) / 64;
+  p.S = (p.nT + 63) / 64;
+  p.nP = (p.nT + p.S - 1) / p.S;
+  p.iters = iters < 0 ? 0 : iters;
+  const size_t BH = static_cast<size_t>(p.BH), f = sizeof(float);
+  size_t off = 0;
+  p.off_L = off;
+  off = align_up(off + BH * p.m * p.D * f);
+  p.off_xiter = off;
+  off = align_up(off + BH * (p.iters + 1) * MP * MP * f);
+  p.off_amat = off;
+  off = align_up(off + BH * MP * MP * f);
+  p.off_hscal = off;
+  off = align_up(off + BH * 4 * f);
+  p.off_wpart = off;
+  off = align_up(off + BH * p.nP * p.D * MP * f);
+  p.off_dypart = off;
+  off = align_up(off + BH * p.nP * p.D * MP * f);
+  p.off_ymat = off;
+  off = align_up(off + BH * MP * p.D * f);
+  p.off_dwmat = off;
+  off = align_up(off + BH * MP * p.D * f);
+  p.off_dla = off;
+  off = align_up(off + BH * MP * p.D * f);
+  p.off_dlpart = off;
+  off = align_up(off + BH * 2 * p.nT * MP * p.D * f);
+  p.off_dkd = off;
+  off = align_up(off + BH * p.N * p.D * f);
+  p.off_sync = off;
+  off = align_up(off + kSyncHead * (BH + 1) * sizeof(unsigned));
+  p.total = off;
+  return p;
+}
+
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
   return x < y + nb && y < x + na;
@@ -303,6 +354,53 @@ int lapattn_check(const lapattn_desc_t* desc, float lambda, float eps, int32_t i
 size_t lapattn_workspace_bytes(const lapattn_desc_t* desc) {
   if (lapattn::check_desc(desc) != LAPATTN_OK) return 0;
   return lapattn::make_plan(desc).total;
+}
+
+size_t lapattn_backward_workspace_bytes(const lapattn_desc_t* desc, int32_t iters) {
+  if (lapattn::check_desc(desc) != LAPATTN_OK) return 0;
+  if (iters < 0 || iters > LAPATTN_MAX_ITERS) return 0;
+  return lapattn::make_bwd_plan(desc, iters).total;
+}
+
+int lapattn_backward(const lapattn_desc_t* desc, const void* q, const void* k, const void* v,
+                     const void* dout, float lambda, float eps, int32_t iters, void* dq, void* dk,
+                     void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+  using namespace lapattn;
+  int st = check_desc(desc);
+  if (st != LAPATTN_OK) return st;
+  st = check_params(lambda, eps, iters);
+  if (st != LAPATTN_OK) return st;
+  if (!q || !k || !v || !dout || !dq || !dk || !dv || !workspace) return LAPATTN_ERR_NULL;
+  const BwdPlan p = make_bwd_plan(desc, iters);
+  if (misaligned16(q) || misaligned16(k) || misaligned16(v) || misaligned16(dout) ||
+      misaligned16(dq) || misaligned16(dk) || misaligned16(dv))
+    return LAPATTN_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign || workspace_bytes < p.total)
+    return LAPATTN_ERR_WORKSPACE;
+  const size_t io = static_cast<size_t>(p.BH) * p.N * p.D * (p.bf16 ? 2 : 4);
+  const void* ins[4] = {q, k, v, dout};
+  void* outs[3] = {dq, dk, dv};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 4; ++j)
+      if (overlaps(outs[i], io, ins[j], io)) return LAPATTN_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i], io, outs[j], io)) return LAPATTN_ERR_ALIAS;
+    if (overlaps(outs[i], io, workspace, workspace_bytes)) return LAPATTN_ERR_ALIAS;
+  }
+  BwdCall c{};
+  c.q = q;
+  c.k = k;
+  c.v = v;
+  c.dout = dout;
+  c.dq = dq;
+  c.dk = dk;
+  c.dv = dv;
+  c.workspace = workspace;
+  c.lambda = lambda;
+  c.eps = eps;
+  c.iters = iters;
+  if (launch_backward(p, c, static_cast<hipStream_t>(stream)) != hipSuccess) return LAPATTN_ERR_HIP;
+  return LAPATTN_OK;
 }
 
 size_t lapattn_status_offset(const lapattn_desc_t* desc) {

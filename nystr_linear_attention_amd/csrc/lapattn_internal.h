@@ -93,6 +93,36 @@ hipError_t launch_main(const Plan& p, const Args& a, const Buffers& b, bool with
                        bool with_maps, hipStream_t s, Ev ev);
 hipError_t launch_out(const Plan& p, const Args& a, const Buffers& b, hipStream_t s, Ev ev);
 
+// Backward pass (lapattn_backward): launch plan and workspace layout.
+struct BwdPlan {
+  int B, H, gh, gw, D, ph, pw;
+  int kernel, bf16;
+  int N, m, BH;
+  int ns_mb;  // 16x16 blocks per side of the padded Newton-Schulz matrix
+  int nT;     // 64-token tiles per head
+  int S;      // tiles per workgroup of the partial launch
+  int nP;     // partials per head and side (= ceil(nT / S))
+  int iters;
+  size_t off_L, off_xiter, off_amat, off_hscal, off_wpart, off_dypart, off_ymat, off_dwmat,
+      off_dla, off_dlpart, off_dkd, off_sync;
+  size_t total;
+};
+
+struct BwdCall {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  void* workspace;
+  float lambda, eps;
+  int iters;
+};
+
+hipError_t launch_backward(const BwdPlan& p, const BwdCall& c, hipStream_t s);
+
 // Whether query workgroups form O inside the main launch: only when there are
 // query workgroups (Q != K) and every workgroup of the launch can be resident
 // at once.  (Larger grids would be correct too, but query workgroups waiting

@@ -200,3 +200,32 @@ def test_noalloc_rejects_before_any_device_work():
     big = good_desc(B=1024, H=8, grid_h=56, grid_w=56, d=64, pool_h=8, pool_w=8)
     assert lib.lapattn_workspace_bytes(ctypes.byref(big)) > _lib.NOALLOC_SCRATCH_BYTES
     assert call(big) == _lib.ERR_SCRATCH
+
+
+def test_backward_rejects_before_launch():
+    """Argument errors of lapattn_backward come back before any device work."""
+    lib = _lib.lib()
+    d = good_desc()
+    need = lib.lapattn_backward_workspace_bytes(ctypes.byref(d), 20)
+    assert need > lib.lapattn_workspace_bytes(ctypes.byref(d))
+    assert lib.lapattn_backward_workspace_bytes(ctypes.byref(d), 65) == 0
+    assert lib.lapattn_backward_workspace_bytes(ctypes.byref(good_desc(d=48)), 20) == 0
+    io = 2 * 3 * 196 * 32 * 4
+
+    def call(desc=d, q=FAKE, k=FAKE + 0x1000000, v=FAKE + 0x2000000, g=FAKE + 0x3000000,
+             dq=FAKE + 0x4000000, dk=FAKE + 0x5000000, dv=FAKE + 0x6000000,
+             ws=FAKE + 0x8000000, wsb=1 << 30, lam=4.0, iters=20):
+        return lib.lapattn_backward(ctypes.byref(desc), q, k, v, g, lam, 1e-3, iters, dq, dk, dv,
+                                    ws, wsb, None)
+    assert call(good_desc(B=0)) == _lib.ERR_SHAPE
+    assert call(lam=0.0) == _lib.ERR_PARAM
+    assert call(iters=-1) == _lib.ERR_PARAM
+    assert call(g=None) == _lib.ERR_NULL
+    assert call(dv=None) == _lib.ERR_NULL
+    assert call(dq=FAKE + 4) == _lib.ERR_ALIGN
+    assert call(wsb=need - 1) == _lib.ERR_WORKSPACE
+    assert call(ws=FAKE + 0x8000000 + 64) == _lib.ERR_WORKSPACE
+    assert call(dq=FAKE + io // 2) == _lib.ERR_ALIAS                  # overlaps q
+    assert call(dk=FAKE + 0x3000000 + 16) == _lib.ERR_ALIAS           # overlaps dO
+    assert call(dv=FAKE + 0x4000000 + 256) == _lib.ERR_ALIAS          # overlaps dq
+    assert call(dk=FAKE + 0x8000000 + 256, wsb=need) == _lib.ERR_ALIAS  # inside the workspace
