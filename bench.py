@@ -105,6 +105,27 @@ def work(w):
     }
 
 
+def backward_work(w):
+    """Algorithmic work of the backward launches of one call (per the
+    definitions of `work`).  Distance stages count 3 flops per coordinate
+    pair for the kernel map recomputed and 6 for its derivative (difference,
+    sign, two multiply-adds: one into dQ or dK, one into dL); the
+    Newton-Schulz backward counts the 6 products per step of its definition
+    (X_t^T G X_t^T, G (A X_t)^T, (X_t A)^T G), 2 m^3 flops each."""
+    BH, N, d, m, T = w.heads, w.N, w.d, w.m, w.iters
+    e = 2 if w.dtype == "bf16" else 4
+    pairs = BH * 2 * N * m * d                    # K_QL and K_LK
+    return {
+        "part": {"flops": 3 * pairs + BH * 4 * m ** 3 * T + BH * 2 * 2 * m * N * d,
+                 "bound": "alu"},
+        "head": {"flops": BH * (12 * m ** 3 * T + 3 * 2 * m * m * d), "bound": "mfma"},
+        "grad": {"flops": 9 * pairs + BH * 3 * 2 * N * m * d, "bound": "alu",
+                 "pairs": pairs},
+        "dk": {"bytes": BH * (N * d * 4 + 2 * ((N + 63) // 64) * 64 * d * 4 + N * d * e),
+               "bound": "hbm"},
+    }
+
+
 def cpu_baseline(w, inputs, seconds):
     """The fp64 oracle on the host, one thread, over whole heads of the same
     workload until `seconds` of CPU time have been spent."""
@@ -244,6 +265,77 @@ def copy_calibration(mib):
     return 0
 
 
+def bench_backward(w, x, q, k, v, dev, stream, lib, hip, timed, pct, args):
+    """lapattn_backward on the same inputs and a seeded dO: K warm steps for
+    the step time, K more with events bound to each launch for the kernels'
+    own durations, each against the roofline of the unit that bounds it."""
+    import numpy as np
+    import torch
+
+    from nystr_linear_attention_amd import _lib, api
+    from nystr_linear_attention_amd import workloads as wl
+    rng = np.random.default_rng(w.seed + 7000)
+    g = rng.standard_normal((w.B, w.H, w.N, w.d))
+    if w.dtype == wl.BF16:
+        dout = torch.from_numpy(wl.f32_to_bf16_bits(g.astype(np.float32)).view(np.int16)).to(dev)
+        dout = dout.view(torch.bfloat16)
+    else:
+        dout = torch.from_numpy(g.astype(np.float32)).to(dev)
+    desc = api.make_desc(w.B, w.H, w.grid_h, w.grid_w, w.d, w.pool_h, w.pool_w, w.kernel, q.dtype)
+    ws = torch.empty(api.backward_workspace_bytes(desc, w.iters), dtype=torch.uint8, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    call = (ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), w.lam,
+            w.eps, w.iters, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), ws.numel(),
+            stream)
+
+    def step():
+        st = lib.lapattn_backward(*call)
+        if st != 0:
+            raise _lib.LapattnError(st, _lib.strerror(st))
+    # the status word of the forward steps does not exist here: nothing waits
+    step.status = torch.zeros(4, dtype=torch.uint8, device=dev)
+    for _ in range(max(2, args.warmup // 2)):
+        step()
+    torch.cuda.synchronize()
+    ms, _ = timed(step, args.steps, False)
+    used = ("bwd_part", "bwd_head", "bwd_grad", "bwd_dk", "pool")
+    ms_ev, kern = timed(step, args.steps, True, tuple(n for n in _lib.STAGES if n not in used))
+    log(f"[bench] backward: {ms * 1e3:.2f} us/step; kernels (us): "
+        + ", ".join(f"{n}={t * 1e3:.2f}" for n, t in kern.items()))
+    bw = backward_work(w)
+    peaks = {"alu": (PEAK_FP32_VALU_TFLOPS, "TFLOP/s", "FP32 VALU"),
+             "mfma": (PEAK_FP32_MFMA_TFLOPS, "TFLOP/s", "fp32 MFMA"),
+             "hbm": (PEAK_HBM_GBS, "GB/s", "HBM")}
+    kernels = {}
+    for name, t in kern.items():
+        e = {"us": round(t * 1e3, 3)}
+        if name in pct:
+            e.update({f"p{p}_us": round(t_ * 1e3, 3) for p, t_ in zip((10, 50, 90), pct[name])})
+        key = name[4:] if name.startswith("bwd_") else None
+        if key in bw:
+            b = bw[key]
+            peak, unit, pipe = peaks[b["bound"]]
+            amount = b.get("flops", b.get("bytes"))
+            rate = amount / (t * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
+            e.update({"bound": b["bound"], "pipe": pipe, "algorithmic": amount,
+                      "achieved": round(rate, 3), "unit": unit, "frac": round(rate / peak, 4)})
+        kernels[name] = e
+    dom = max((n for n in kern if n.startswith("bwd_")), key=lambda n: kern[n])
+    d = kernels[dom]
+    return {
+        "ms_per_step": round(ms, 5),
+        "value": round(w.B * w.N / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "ms_per_step_kernel_event_pass": round(ms_ev, 5),
+        "kernels": kernels,
+        "roofline": {"kernel": dom, "bound": d["bound"], "pipe": d["pipe"],
+                     "achieved": d["achieved"], "peak": peaks[d["bound"]][0], "unit": d["unit"],
+                     "frac": d["frac"], "traffic": None},
+        "note": "dO seeded N(0,1); dQ, dK, dV written; flops and bytes are algorithmic "
+                "(see backward_work in bench.py)",
+    }
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -263,6 +355,8 @@ def main(argv=None):
                     help="skip the cold-cache pass (steps rotating over copies of the inputs)")
     ap.add_argument("--cold-mib", type=int, default=640,
                     help="total size of the input copies the cold pass rotates over")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward pass measurement")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args(argv)
@@ -604,6 +698,8 @@ def main(argv=None):
         "ms_per_step_kernel_event_pass": round(ms_ev, 5),
         "cold": cold,
     }
+    if not args.no_backward:
+        res["backward"] = bench_backward(w, x, q, k, v, dev, stream, lib, hip, timed, pct, args)
     res["timeouts"] = timeouts[0]
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle for ~{args.cpu_seconds:.0f} s")

@@ -108,7 +108,7 @@ enum {
 /* Size of the static device scratch behind lapattn_forward_noalloc. */
 #define LAPATTN_NOALLOC_SCRATCH_BYTES (128u << 20)
 
-/* Launch slots of one forward call, in launch order (for
+/* Launch slots of one forward or backward call, in launch order (for
  * lapattn_set_stage_events). */
 #define LAPATTN_STAGE_POOL 0     /* landmark average pool                      */
 #define LAPATTN_STAGE_MAIN 1     /* A = k(L,L) + eps I, alpha and Newton-Schulz;
@@ -121,7 +121,15 @@ enum {
                                     or when the main grid cannot be resident
                                     on the device at once (lapattn_launches
                                     reports which)                             */
-#define LAPATTN_NUM_STAGES 4
+/* lapattn_backward's launches (the pool of slot 0 comes first) */
+#define LAPATTN_STAGE_BWD_PART 4 /* A, alpha and Newton-Schulz with every iterate
+                                    stored, beside the W^T and dY^T partials  */
+#define LAPATTN_STAGE_BWD_HEAD 5 /* per head: W, dY, Y, dX, dW             */
+#define LAPATTN_STAGE_BWD_GRAD 6 /* the Newton-Schulz backward and dL from A,
+                                    beside per token tile: dQ, direct dK, dV
+                                    and the dL partials                       */
+#define LAPATTN_STAGE_BWD_DK 7   /* dK += pool backward of dL                 */
+#define LAPATTN_NUM_STAGES 8
 
 typedef struct {
   int32_t B, H;            /* batch and heads; every (b, h) is independent   */
@@ -270,7 +278,8 @@ int lapattn_launches(const lapattn_desc_t* desc, int q_is_k);
  * kernel's own execution time.  Slots without a launch in the call are left
  * unrecorded: LAPATTN_STAGE_MAPS outside LAPATTN_FLAG_SERIAL, and
  * LAPATTN_STAGE_OUT unless K is the same pointer as Q or the main grid cannot
- * be resident at once (lapattn_launches tells which slots a call uses).
+ * be resident at once (lapattn_launches tells which slots a call uses); a
+ * backward call records slot 0 and the LAPATTN_STAGE_BWD_* slots.
  * `events` holds 2 * LAPATTN_NUM_STAGES hipEvent_t handles (as void*) created
  * by the caller with timing enabled, and must stay valid until the hook is
  * cleared with (NULL, 0).  n must be 0 or 2 * LAPATTN_NUM_STAGES. */

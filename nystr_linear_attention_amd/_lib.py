@@ -38,7 +38,7 @@ EXPORTS = ("lapattn_version", "lapattn_strerror", "lapattn_check",
            "lapattn_backward_workspace_bytes", "lapattn_backward",
            "lapattn_forward_stages", "lapattn_set_stage_events", "lapattn_launches")
 
-STAGES = ("pool", "main", "maps", "out")
+STAGES = ("pool", "main", "maps", "out", "bwd_part", "bwd_head", "bwd_grad", "bwd_dk")
 
 
 class Desc(ctypes.Structure):

@@ -213,6 +213,8 @@ BwdPlan make_bwd_plan(const lapattn_desc_t* d, int32_t iters) {
   off = align_up(off + BH * MP * p.D * f);
   p.off_dwmat = off;
   off = align_up(off + BH * MP * p.D * f);
+  p.off_dxmat = off;
+  off = align_up(off + BH * MP * MP * f);
   p.off_dla = off;
   off = align_up(off + BH * MP * p.D * f);
   p.off_dlpart = off;
@@ -399,6 +401,11 @@ int lapattn_backward(const lapattn_desc_t* desc, const void* q, const void* k, c
   c.lambda = lambda;
   c.eps = eps;
   c.iters = iters;
+  c.ev[0] = slot(LAPATTN_STAGE_POOL);
+  c.ev[1] = slot(LAPATTN_STAGE_BWD_PART);
+  c.ev[2] = slot(LAPATTN_STAGE_BWD_HEAD);
+  c.ev[3] = slot(LAPATTN_STAGE_BWD_GRAD);
+  c.ev[4] = slot(LAPATTN_STAGE_BWD_DK);
   if (launch_backward(p, c, static_cast<hipStream_t>(stream)) != hipSuccess) return LAPATTN_ERR_HIP;
   return LAPATTN_OK;
 }

@@ -29,12 +29,14 @@
 //         iterate X_0 .. X_T stored in fp32);  key tiles: W^T partials
 //         (K_LK V, the forward's key path);  query tiles: dY^T partials
 //         (K_QL dO, the same path with Q for K and dO for V)
-//   head  one workgroup per head: W, dY; Y = X W; dX, dW; the Newton-Schulz
-//         backward on fp32 MFMA in LDS; dA; dL from A
-//   grad  one workgroup per 64-token tile of Q or K: the kernel map again,
-//         dK_QL = dO Y^T (or dK_LK^T = V dW^T) on fp32 MFMA, the gradient
-//         map on FP32 VALU (dQ or the direct dK rows, and the tile's dL
-//         partial), and for key tiles dV = K_LK^T dW
+//   head  one workgroup per head: W, dY (partials summed in order); Y = X W,
+//         dW = X^T dY, dX = dY W^T
+//   grad  Newton-Schulz backward workgroups (one per head, fp32 MFMA in LDS,
+//         then dA and dL from A) beside one workgroup per 64-token tile of Q
+//         or K: the kernel map again, dK_QL = dO Y^T (or dK_LK^T = V dW^T)
+//         on fp32 MFMA, the gradient map on FP32 VALU (dQ or the direct dK
+//         rows, and the tile's dL partial), and for key tiles dV = K_LK^T dW;
+//         the two roles do not wait for each other
 //   dk    one workgroup per landmark window: dL = its partials in fixed order,
 //         dK rows of the window = direct part + dL / (ph pw)
 // Every reduction runs in a fixed order, so results do not depend on timing.
@@ -62,6 +64,7 @@ struct BwdArgs {
   const float* dypart; // [BH][nP][D][MP]      dY^T partials
   float* ymat;         // [BH][MP][D]          Y = X W (rows >= m zero)
   float* dwmat;        // [BH][MP][D]          dW = X^T dY (rows >= m zero)
+  float* dxmat;        // [BH][MP][MP]         dX = dY W^T (rows, columns >= m zero)
   float* dla;          // [BH][MP][D]          dL from A (rows >= m zero)
   float* dlpart;       // [BH][2 nT][MP][D]    dL partials of the gradient tiles
   float* dkd;          // [BH][N][D]           direct part of dK
@@ -206,33 +209,47 @@ __device__ __forceinline__ void load_mm(float* dst, const float* src, int m) {
   }
 }
 
-template <int D, int KIND>
-__global__ __launch_bounds__(WGM) void bwd_head_kernel(BwdArgs a) {
+template <int D>
+__global__ __launch_bounds__(WGM) void bwd_heada_kernel(BwdArgs a) {
   constexpr int NB64 = 16;           // 16 x 16 blocks of a 64 x 64 product
   constexpr int NBD = 4 * (D / 16);  // blocks of a 64 x D product
-  __shared__ __attribute__((aligned(16))) float sm[6 * MP * BS + 8];
+  __shared__ __attribute__((aligned(16))) float sm[3 * MP * BS];
   float* M0 = sm;
   float* M1 = sm + MP * BS;
   float* M2 = sm + 2 * MP * BS;
-  float* M3 = sm + 3 * MP * BS;
-  float* M4 = sm + 4 * MP * BS;
-  float* M5 = sm + 5 * MP * BS;
-  float* red = sm + 6 * MP * BS;
   const int bh = blockIdx.x, tid = threadIdx.x;
   const int m = a.m, nP = a.nP, T = a.iters;
   const size_t ps = static_cast<size_t>(D) * MP;
+  const int lane = tid & 63, w = wave_id(), lr = lane & 15, lg = lane >> 4;
 
-  // W[j][c] and dY[j][c] (row stride BS), the partials summed in order
+  // W[j][c] and dY[j][c] (row stride BS), the partials summed in order;
+  // a partial is W^T [D][MP], so consecutive threads take consecutive j, and
+  // the loads of 8 partials are in flight at once
   {
     const float* wp = a.wpart + static_cast<size_t>(bh) * nP * ps;
     const float* dp = a.dypart + static_cast<size_t>(bh) * nP * ps;
     for (int e = tid; e < MP * MP; e += WGM) {
-      const int j = e / MP, c = e % MP;
+      const int c = e / MP, j = e % MP;
       float sw = 0.f, sd = 0.f;
       if (j < m && c < D) {
-        for (int p = 0; p < nP; ++p) {
-          sw += wp[p * ps + c * MP + j];
-          sd += dp[p * ps + c * MP + j];
+        const size_t o = static_cast<size_t>(c) * MP + j;
+        int p = 0;
+        for (; p + 8 <= nP; p += 8) {
+          float vw[8], vd[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            vw[u] = wp[(p + u) * ps + o];
+            vd[u] = dp[(p + u) * ps + o];
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            sw += vw[u];
+            sd += vd[u];
+          }
+        }
+        for (; p < nP; ++p) {
+          sw += wp[p * ps + o];
+          sd += dp[p * ps + o];
         }
       }
       M0[j * BS + c] = sw;
@@ -241,69 +258,166 @@ __global__ __launch_bounds__(WGM) void bwd_head_kernel(BwdArgs a) {
   }
   load_mm(M2, a.xiter + (static_cast<size_t>(bh) * (T + 1) + T) * MP * MP, m);  // X = X_T
   __syncthreads();
-  {
-    // Y = X W; dW = X^T dY  (m x D) to global memory
-    f4 acc[(NBD + 7) / 8];
-    lds_mm<NBD>(M2, BS, 1, M0, BS, 1, D / 16, acc);
-    const int lane = tid & 63, w = wave_id(), lr = lane & 15, lg = lane >> 4;
+  // Y = X W and dW = X^T dY (64 x D, rows >= m zero) to global memory
+  f4 acc[(NBD + 7) / 8];
+  for (int pass = 0; pass < 2; ++pass) {
+    if (pass == 0) lds_mm<NBD>(M2, BS, 1, M0, BS, 1, D / 16, acc);
+    else lds_mm<NBD>(M2, 1, BS, M1, BS, 1, D / 16, acc);
+    float* dst = (pass == 0 ? a.ymat : a.dwmat) + static_cast<size_t>(bh) * MP * D;
 #pragma unroll
     for (int s = 0; s < (NBD + 7) / 8; ++s) {
       const int blk = w + 8 * s;
       if (blk < NBD) {
         const int bi = blk / (D / 16), bj = blk % (D / 16);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          a.ymat[(static_cast<size_t>(bh) * MP + 16 * bi + 4 * lg + i) * D + 16 * bj + lr] = acc[s][i];
+        for (int i = 0; i < 4; ++i) dst[(16 * bi + 4 * lg + i) * D + 16 * bj + lr] = acc[s][i];
       }
     }
-    lds_mm<NBD>(M2, 1, BS, M1, BS, 1, D / 16, acc);
-#pragma unroll
-    for (int s = 0; s < (NBD + 7) / 8; ++s) {
-      const int blk = w + 8 * s;
-      if (blk < NBD) {
-        const int bi = blk / (D / 16), bj = blk % (D / 16);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          a.dwmat[(static_cast<size_t>(bh) * MP + 16 * bi + 4 * lg + i) * D + 16 * bj + lr] = acc[s][i];
-      }
-    }
-    // G = dX = dY W^T  (m x m): rows of dY against rows of W
-    f4 g[2];
-    lds_mm<NB64>(M1, BS, 1, M0, 1, BS, 4, g);
-    lds_store<NB64>(M3, 4, g, 1.f, 0.f);
   }
-  load_mm(M4, a.amat + static_cast<size_t>(bh) * MP * MP, m);  // A
-  for (int e = tid; e < MP * BS; e += WGM) M5[e] = 0.f;       // dA
-  __syncthreads();
+  // dX = dY W^T (64 x 64): rows of dY against rows of W
+  f4 g[2];
+  lds_mm<NB64>(M1, BS, 1, M0, 1, BS, 4, g);
+  float* dx = a.dxmat + static_cast<size_t>(bh) * MP * MP;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int blk = w + 8 * s, bi = blk / 4, bj = blk % 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dx[(16 * bi + 4 * lg + i) * MP + 16 * bj + lr] = g[s][i];
+  }
+}
 
-  // Newton-Schulz backward, t = T-1 .. 0.  X_t commutes with A and is
-  // symmetric in exact arithmetic, so (X_t A)^T is taken as A X_t (the
-  // difference is rounding of X_t, and the recursion is linear in G).
+// ---------------------------------------------------------------------------
+// The fused launch: Newton-Schulz backward workgroups (one per head, first in
+// the grid) beside the gradient tiles; neither waits for the other.
+// ---------------------------------------------------------------------------
+constexpr int WGG = 256;
+
+// One 16 x 16 block of sum over k < 64 of A[i][k] B^T[j][k], both operands
+// rows of 64 floats in LDS (row stride BS): lane (g, r) reads 16 consecutive
+// k = 16 g .. 16 g + 15 of row 16 bi + r of A and row 16 bj + r of B^T.
+__device__ __forceinline__ f4 rows_mm(const float* A, const float* BT, int bi, int bj, f4 c) {
+  const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const float* ap = A + (16 * bi + lr) * BS + 16 * lg;
+  const float* bp = BT + (16 * bj + lr) * BS + 16 * lg;
+  f4 av[4], bv[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    av[q] = ld4(ap + 4 * q);
+    bv[q] = ld4(bp + 4 * q);
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int h = 0; h < 4; ++h) c = mfma4(av[q][h], bv[q][h], c);
+  return c;
+}
+
+// Writes block (bi, bj) of accumulator c to M (row-major) and, with MT, its
+// transpose.
+__device__ __forceinline__ void put_block(float* M, float* MT, int bi, int bj, f4 c) {
+  const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * bi + 4 * lg + i, col = 16 * bj + lr;
+    M[r * BS + col] = c[i];
+    if (MT) MT[col * BS + r] = c[i];
+  }
+}
+
+constexpr int NSB_SMEM = 7 * MP * BS + 8;
+
+// Newton-Schulz backward of one head (4 waves).  LDS holds A, X_t and X_t^T,
+// G and G^T, Q1 = A X_t and P1 = X_t^T G, so that every product reads rows
+// of both operands.  Wave w owns the blocks w, w + 4, w + 8, w + 12 of dA
+// (kept in registers across the steps) and of the new G.  X_{t-1} is read
+// from global memory during step t.
+template <int D, int KIND>
+__device__ void nsb_role(const BwdArgs& a, int bh, float* sm) {
+  float* MA = sm;
+  float* MX = sm + MP * BS;
+  float* MXT = sm + 2 * MP * BS;
+  float* MG = sm + 3 * MP * BS;
+  float* MGT = sm + 4 * MP * BS;
+  float* MQ = sm + 5 * MP * BS;
+  float* MP1 = sm + 6 * MP * BS;
+  float* red = sm + 7 * MP * BS;
+  const int tid = threadIdx.x, w = wave_id();
+  const int m = a.m, T = a.iters;
+  const float* xi = a.xiter + static_cast<size_t>(bh) * (T + 1) * MP * MP;
+  constexpr int PER = MP * MP / WGG;  // elements per thread of a 64 x 64 matrix
+  // A, G = dX and X_{T-1} (or nothing to do when T == 0) into LDS
+  {
+    const float* ag = a.amat + static_cast<size_t>(bh) * MP * MP;
+    const float* dg = a.dxmat + static_cast<size_t>(bh) * MP * MP;
+    const float* xg = xi + static_cast<size_t>(T > 0 ? T - 1 : 0) * MP * MP;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid + WGG * u, r = e / MP, c = e % MP;
+      const bool in = r < m && c < m;
+      MA[r * BS + c] = ag[e];
+      const float gv = dg[e];
+      MG[r * BS + c] = gv;
+      MGT[c * BS + r] = gv;
+      const float xv = in ? xg[e] : 0.f;
+      MX[r * BS + c] = xv;
+      MXT[c * BS + r] = xv;
+    }
+  }
+  __syncthreads();
+  f4 da[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) da[s] = f4{0.f, 0.f, 0.f, 0.f};
   for (int t = T - 1; t >= 0; --t) {
-    load_mm(M2, a.xiter + (static_cast<size_t>(bh) * (T + 1) + t) * MP * MP, m);  // X_t
-    __syncthreads();
-    f4 acc[2];
-    lds_mm<NB64>(M4, BS, 1, M2, BS, 1, 4, acc);  // Q1 = A X_t
-    lds_store<NB64>(M0, 4, acc, 1.f, 0.f);
-    lds_mm<NB64>(M2, 1, BS, M3, BS, 1, 4, acc);  // P1 = X_t^T G
-    lds_store<NB64>(M1, 4, acc, 1.f, 0.f);
-    __syncthreads();
-    lds_mm<NB64>(M1, BS, 1, M2, 1, BS, 4, acc);  // P1 X_t^T
-    lds_store<NB64>(M5, 4, acc, -1.f, 1.f);      // dA -= P1 X_t^T
-    f4 gq[2], qg[2];
-    lds_mm<NB64>(M3, BS, 1, M0, 1, BS, 4, gq);   // G Q1^T
-    lds_mm<NB64>(M0, BS, 1, M3, BS, 1, 4, qg);   // Q1 G
-    __syncthreads();                             // every read of G is done
-    {
-      const int lane = tid & 63, w = wave_id(), lr = lane & 15, lg = lane >> 4;
+    // X_{t-1} for the next step, read now (consumed after the step's last
+    // barrier)
+    float nx[PER];
+    if (t > 0) {
+      const float* xg = xi + static_cast<size_t>(t - 1) * MP * MP;
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int blk = w + 8 * s, bi = blk / 4, bj = blk % 4;
+      for (int u = 0; u < PER; ++u) {
+        const int e = tid + WGG * u, r = e / MP, c = e % MP;
+        nx[u] = (r < m && c < m) ? xg[e] : 0.f;
+      }
+    }
+    // Q1 = A X_t (rows of A, rows of X_t^T); P1 = X_t^T G (rows of X_t^T,
+    // rows of G^T)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float* p = M3 + (16 * bi + 4 * lg + i) * BS + 16 * bj + lr;
-          *p = 2.f * *p - gq[s][i] - qg[s][i];
-        }
+    for (int s = 0; s < 4; ++s) {
+      const int blk = w + 4 * s, bi = blk >> 2, bj = blk & 3;
+      put_block(MQ, nullptr, bi, bj, rows_mm(MA, MXT, bi, bj, f4{0.f, 0.f, 0.f, 0.f}));
+      put_block(MP1, nullptr, bi, bj, rows_mm(MXT, MGT, bi, bj, f4{0.f, 0.f, 0.f, 0.f}));
+    }
+    __syncthreads();
+    // dA -= P1 X_t^T (rows of P1, rows of X_t); G' = 2 G - G Q1^T - Q1 G,
+    // with (X_t A)^T taken as A X_t: X_t commutes with A and is symmetric in
+    // exact arithmetic, and the recursion is linear in G, so the rounding
+    // difference of the two stays at rounding level
+    f4 gn[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int blk = w + 4 * s, bi = blk >> 2, bj = blk & 3;
+      const f4 pd = rows_mm(MP1, MX, bi, bj, f4{0.f, 0.f, 0.f, 0.f});
+      f4 gq = rows_mm(MG, MQ, bi, bj, f4{0.f, 0.f, 0.f, 0.f});
+      gq = rows_mm(MQ, MGT, bi, bj, gq);
+      const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        da[s][i] -= pd[i];
+        gn[s][i] = 2.f * MG[(16 * bi + 4 * lg + i) * BS + 16 * bj + lr] - gq[i];
+      }
+    }
+    __syncthreads();  // every read of G, X_t, Q1, P1 is done
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int blk = w + 4 * s;
+      put_block(MG, MGT, blk >> 2, blk & 3, gn[s]);
+    }
+    if (t > 0) {
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int e = tid + WGG * u, r = e / MP, c = e % MP;
+        MX[r * BS + c] = nx[u];
+        MXT[c * BS + r] = nx[u];
       }
     }
     __syncthreads();
@@ -316,68 +430,65 @@ __global__ __launch_bounds__(WGM) void bwd_head_kernel(BwdArgs a) {
   const int jc = __float_as_int(hs[1]);
   {
     float part = 0.f;
-    for (int e = tid; e < MP * MP; e += WGM) {
+    for (int e = tid; e < MP * MP; e += WGG) {
       const int r = e / MP, c = e % MP;
-      part = fmaf(M3[r * BS + c], M4[r * BS + c], part);
+      part = fmaf(MG[r * BS + c], MA[r * BS + c], part);
     }
     // fixed-order sum: per wave, then over waves
     for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o);
-    if ((tid & 63) == 0) red[wave_id()] = part;
+    if ((tid & 63) == 0) red[w] = part;
     __syncthreads();
     float dalpha = 0.f;
-    for (int i = 0; i < WGM / 64; ++i) dalpha += red[i];
+    for (int i = 0; i < WGG / 64; ++i) dalpha += red[i];
     const float dc = -dalpha * alpha / csum;
-    for (int e = tid; e < MP * MP; e += WGM) {
-      const int r = e / MP, c = e % MP;
-      float v = fmaf(alpha, M3[r * BS + c], M5[r * BS + c]);
-      if (r < m && c < m) {
-        const float av = M4[r * BS + c];
-        const float sg = av > 0.f ? 1.f : (av < 0.f ? -1.f : 0.f);
-        if (c == jc) v = fmaf(dc, sg, v);
-        if (r == jc) v = fmaf(dc, sg, v);
+    const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    const float il = 1.0f / a.lambda;
+    // dd = -dA k(L, L) / lambda into MP1 (k(L, L) = A - eps I inside m x m)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int blk = w + 4 * s, bi = blk >> 2, bj = blk & 3;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * bi + 4 * lg + i, c = 16 * bj + lr;
+        float v = fmaf(alpha, MG[r * BS + c], da[s][i]);
+        float dd = 0.f;
+        if (r < m && c < m) {
+          const float av = MA[r * BS + c];
+          const float sg = av > 0.f ? 1.f : (av < 0.f ? -1.f : 0.f);
+          if (c == jc) v = fmaf(dc, sg, v);
+          if (r == jc) v = fmaf(dc, sg, v);
+          dd = -v * (av - (r == c ? a.eps : 0.f)) * il;
+        }
+        MP1[r * BS + c] = dd;
       }
-      M5[r * BS + c] = v;
     }
   }
-  __syncthreads();
-  // dL from A = k(L, L) + eps I: dd = -dA k(L, L) / lambda, and for landmark
-  // p: sum_j (dd[p][j] + dd[j][p]) s(l_p - l_j), s = sign (Laplacian) or 2 x
-  // (Gaussian).  Landmarks in M0 (rows of D floats, stride BS).
+  // dL from A: for landmark p, sum_j (dd[p][j] + dd[j][p]) s(l_p - l_j),
+  // s = sign (Laplacian) or 2 x (Gaussian).  Landmarks in MQ (rows of D).
   {
     const float* Lg = a.L + static_cast<size_t>(bh) * m * D;
-    for (int e = tid; e < MP * D; e += WGM) {
+    for (int e = tid; e < MP * D; e += WGG) {
       const int r = e / D, c = e % D;
-      M0[r * BS + c] = r < m ? Lg[r * D + c] : 0.f;
-    }
-    const float il = 1.0f / a.lambda;
-    for (int e = tid; e < MP * MP; e += WGM) {
-      const int r = e / MP, c = e % MP;
-      const float kv = (r < m && c < m) ? M4[r * BS + c] - (r == c ? a.eps : 0.f) : 0.f;
-      M1[r * BS + c] = -M5[r * BS + c] * kv * il;
+      MQ[r * BS + c] = r < m ? Lg[r * D + c] : 0.f;
     }
     __syncthreads();
-    for (int e = tid; e < MP * D; e += WGM) {
+    for (int e = tid; e < MP * D; e += WGG) {
       const int p = e / D, c = e % D;
       float acc = 0.f;
       if (p < m) {
-        const float lp = M0[p * BS + c];
+        const float lp = MQ[p * BS + c];
         for (int j = 0; j < m; ++j) {
-          const float x = lp - M0[j * BS + c];
-          float s;
-          if constexpr (KIND == 0) s = x > 0.f ? 1.f : (x < 0.f ? -1.f : 0.f);
-          else s = 2.f * x;
-          acc = fmaf(M1[p * BS + j] + M1[j * BS + p], s, acc);
+          const float x = lp - MQ[j * BS + c];
+          float sv;
+          if constexpr (KIND == 0) sv = x > 0.f ? 1.f : (x < 0.f ? -1.f : 0.f);
+          else sv = 2.f * x;
+          acc = fmaf(MP1[p * BS + j] + MP1[j * BS + p], sv, acc);
         }
       }
       a.dla[(static_cast<size_t>(bh) * MP + p) * D + c] = acc;
     }
   }
 }
-
-// ---------------------------------------------------------------------------
-// grad: one workgroup (4 waves) per 64-token tile of Q (side 0) or K (side 1).
-// ---------------------------------------------------------------------------
-constexpr int WGG = 256;
 
 // sign(x) with sign(0) = 0 (Laplacian) or 2 x (Gaussian): the derivative of
 // the coordinate's distance term.  For the sign, x is scaled by 2^252 in two
@@ -391,8 +502,18 @@ __device__ __forceinline__ float dterm(float x) {
     return x + x;
 }
 
+// LDS floats of one gradient tile (see grad_tile).
+template <int D>
+constexpr int grad_smem() {
+  constexpr int XS = D + 4, R = 64 / D;
+  constexpr int U1 = TILE * BS + TILE * XS + MP * XS;
+  constexpr int U2 = 4 * R * MP * D;
+  return TILE * XS + MP * XS + MP * BS + (U1 > U2 ? U1 : U2);
+}
+
+// One workgroup (4 waves) per 64-token tile of Q (side 0) or K (side 1).
 template <int D, int KIND, bool BF16>
-__global__ __launch_bounds__(WGG) void bwd_grad_kernel(BwdArgs a) {
+__device__ void grad_tile(const BwdArgs& a, int tile, float* sm) {
   constexpr int XS = D + 4;     // row stride of token / landmark rows
   constexpr int R = 64 / D;     // tokens per wave row (lane = r D + k)
   constexpr int TPW = TILE / 4; // tokens per wave
@@ -407,10 +528,6 @@ __global__ __launch_bounds__(WGG) void bwd_grad_kernel(BwdArgs a) {
   constexpr int OFF_P = OFF_U;
   constexpr int OFF_VO = OFF_P + TILE * BS;
   constexpr int OFF_YB = OFF_VO + TILE * XS;
-  constexpr int U1 = TILE * BS + TILE * XS + MP * XS;
-  constexpr int U2 = 4 * R * MP * D;
-  constexpr int SMEM = OFF_U + (U1 > U2 ? U1 : U2);
-  __shared__ __attribute__((aligned(16))) float sm[SMEM];
   float* XT = sm + OFF_XT;
   float* LM = sm + OFF_LM;
   float* WT = sm + OFF_WT;
@@ -420,9 +537,9 @@ __global__ __launch_bounds__(WGG) void bwd_grad_kernel(BwdArgs a) {
   float* PL = sm + OFF_U;
 
   const int nT = a.nT, N = a.N, m = a.m;
-  const int bh = blockIdx.x / (2 * nT);
-  const int side = (blockIdx.x / nT) & 1;  // 0: query tile, 1: key tile
-  const int t = blockIdx.x % nT;
+  const int bh = tile / (2 * nT);
+  const int side = (tile / nT) & 1;  // 0: query tile, 1: key tile
+  const int t = tile % nT;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const void* xsrc = side ? a.k : a.q;
   const void* osrc = side ? a.v : a.dout;
@@ -575,6 +692,14 @@ __global__ __launch_bounds__(WGG) void bwd_grad_kernel(BwdArgs a) {
   }
 }
 
+template <int D, int KIND, bool BF16>
+__global__ __launch_bounds__(WGG) void bwd_fused_kernel(BwdArgs a) {
+  constexpr int G = grad_smem<D>();
+  __shared__ __attribute__((aligned(16))) float sm[G > NSB_SMEM ? G : NSB_SMEM];
+  if (static_cast<int>(blockIdx.x) < a.BH) nsb_role<D, KIND>(a, blockIdx.x, sm);
+  else grad_tile<D, KIND, BF16>(a, blockIdx.x - a.BH, sm);
+}
+
 // ---------------------------------------------------------------------------
 // dk: one workgroup per (landmark window j, head): dL[j] = dL_A[j] + its
 // 2 nT tile partials (query tiles, then key tiles, in order); the window's
@@ -613,8 +738,7 @@ __global__ __launch_bounds__(WGG) void bwd_dk_kernel(BwdArgs a) {
 
 template <int D, int MB>
 hipError_t launch_part_dm(const MainArgs& ma, const void* dout, float* dypart, float* xiter, float* amat,
-                          float* hscal, unsigned grid, hipStream_t s) {
-  const Ev ev{};
+                          float* hscal, unsigned grid, hipStream_t s, Ev ev) {
   if (ma.kind == 0) {
     if (ma.bf16)
       return launch(bwd_part_kernel<D, MB, 0, true>, dim3(grid), dim3(WGM), s, ev, ma, ma.q, ma.k, ma.v,
@@ -631,31 +755,30 @@ hipError_t launch_part_dm(const MainArgs& ma, const void* dout, float* dypart, f
 
 template <int D>
 hipError_t launch_bwd_d(const BwdPlan& p, const BwdArgs& ba, const MainArgs& ma, float* dypart,
-                        float* xiter, float* amat, float* hscal, hipStream_t s) {
+                        float* xiter, float* amat, float* hscal, hipStream_t s, const Ev* ev) {
   const unsigned gpart = static_cast<unsigned>(p.BH + 2 * p.BH * p.nP);
   hipError_t e = hipErrorInvalidValue;
   switch (p.ns_mb) {
-    case 1: e = launch_part_dm<D, 1>(ma, ba.dout, dypart, xiter, amat, hscal, gpart, s); break;
-    case 2: e = launch_part_dm<D, 2>(ma, ba.dout, dypart, xiter, amat, hscal, gpart, s); break;
-    case 3: e = launch_part_dm<D, 3>(ma, ba.dout, dypart, xiter, amat, hscal, gpart, s); break;
-    case 4: e = launch_part_dm<D, 4>(ma, ba.dout, dypart, xiter, amat, hscal, gpart, s); break;
+    case 1: e = launch_part_dm<D, 1>(ma, ba.dout, dypart, xiter, amat, hscal, gpart, s, ev[1]); break;
+    case 2: e = launch_part_dm<D, 2>(ma, ba.dout, dypart, xiter, amat, hscal, gpart, s, ev[1]); break;
+    case 3: e = launch_part_dm<D, 3>(ma, ba.dout, dypart, xiter, amat, hscal, gpart, s, ev[1]); break;
+    case 4: e = launch_part_dm<D, 4>(ma, ba.dout, dypart, xiter, amat, hscal, gpart, s, ev[1]); break;
   }
   if (e != hipSuccess) return e;
-  const Ev ev{};
-  e = p.kernel == 0 ? launch(bwd_head_kernel<D, 0>, dim3(p.BH), dim3(WGM), s, ev, ba)
-                    : launch(bwd_head_kernel<D, 1>, dim3(p.BH), dim3(WGM), s, ev, ba);
+  e = launch(bwd_heada_kernel<D>, dim3(p.BH), dim3(WGM), s, ev[2], ba);
   if (e != hipSuccess) return e;
-  const dim3 gg(static_cast<unsigned>(p.BH * 2 * p.nT));
+  // Newton-Schulz backward workgroups first, then the gradient tiles
+  const dim3 gg(static_cast<unsigned>(p.BH + p.BH * 2 * p.nT));
   if (p.kernel == 0)
-    e = p.bf16 ? launch(bwd_grad_kernel<D, 0, true>, gg, dim3(WGG), s, ev, ba)
-               : launch(bwd_grad_kernel<D, 0, false>, gg, dim3(WGG), s, ev, ba);
+    e = p.bf16 ? launch(bwd_fused_kernel<D, 0, true>, gg, dim3(WGG), s, ev[3], ba)
+               : launch(bwd_fused_kernel<D, 0, false>, gg, dim3(WGG), s, ev[3], ba);
   else
-    e = p.bf16 ? launch(bwd_grad_kernel<D, 1, true>, gg, dim3(WGG), s, ev, ba)
-               : launch(bwd_grad_kernel<D, 1, false>, gg, dim3(WGG), s, ev, ba);
+    e = p.bf16 ? launch(bwd_fused_kernel<D, 1, true>, gg, dim3(WGG), s, ev[3], ba)
+               : launch(bwd_fused_kernel<D, 1, false>, gg, dim3(WGG), s, ev[3], ba);
   if (e != hipSuccess) return e;
   const dim3 gk(static_cast<unsigned>(p.m), static_cast<unsigned>(p.BH));
-  return p.bf16 ? launch(bwd_dk_kernel<D, true>, gk, dim3(WGG), s, ev, ba)
-                : launch(bwd_dk_kernel<D, false>, gk, dim3(WGG), s, ev, ba);
+  return p.bf16 ? launch(bwd_dk_kernel<D, true>, gk, dim3(WGG), s, ev[4], ba)
+                : launch(bwd_dk_kernel<D, false>, gk, dim3(WGG), s, ev[4], ba);
 }
 
 }  // namespace
@@ -692,7 +815,7 @@ hipError_t launch_backward(const BwdPlan& p, const BwdCall& c, hipStream_t s) {
     fb.L = L;
     fb.sync = sync;
     fb.timeouts = sync;
-    const hipError_t e = launch_pool(fp, fa, fb, s, Ev{});
+    const hipError_t e = launch_pool(fp, fa, fb, s, c.ev[0]);
     if (e != hipSuccess) return e;
   }
   MainArgs ma{};
@@ -734,6 +857,7 @@ hipError_t launch_backward(const BwdPlan& p, const BwdCall& c, hipStream_t s) {
   ba.dypart = dypart;
   ba.ymat = reinterpret_cast<float*>(ws + p.off_ymat);
   ba.dwmat = reinterpret_cast<float*>(ws + p.off_dwmat);
+  ba.dxmat = reinterpret_cast<float*>(ws + p.off_dxmat);
   ba.dla = reinterpret_cast<float*>(ws + p.off_dla);
   ba.dlpart = reinterpret_cast<float*>(ws + p.off_dlpart);
   ba.dkd = reinterpret_cast<float*>(ws + p.off_dkd);
@@ -752,9 +876,9 @@ hipError_t launch_backward(const BwdPlan& p, const BwdCall& c, hipStream_t s) {
   ba.eps = c.eps;
   ba.c_exp2 = ma.c_exp2;
   switch (p.D) {
-    case 16: return launch_bwd_d<16>(p, ba, ma, dypart, xiter, amat, hscal, s);
-    case 32: return launch_bwd_d<32>(p, ba, ma, dypart, xiter, amat, hscal, s);
-    case 64: return launch_bwd_d<64>(p, ba, ma, dypart, xiter, amat, hscal, s);
+    case 16: return launch_bwd_d<16>(p, ba, ma, dypart, xiter, amat, hscal, s, c.ev);
+    case 32: return launch_bwd_d<32>(p, ba, ma, dypart, xiter, amat, hscal, s, c.ev);
+    case 64: return launch_bwd_d<64>(p, ba, ma, dypart, xiter, amat, hscal, s, c.ev);
   }
   return hipErrorInvalidValue;
 }

@@ -104,7 +104,7 @@ struct BwdPlan {
   int nP;     // partials per head and side (= ceil(nT / S))
   int iters;
   size_t off_L, off_xiter, off_amat, off_hscal, off_wpart, off_dypart, off_ymat, off_dwmat,
-      off_dla, off_dlpart, off_dkd, off_sync;
+      off_dxmat, off_dla, off_dlpart, off_dkd, off_sync;
   size_t total;
 };
 
@@ -119,6 +119,7 @@ struct BwdCall {
   void* workspace;
   float lambda, eps;
   int iters;
+  Ev ev[5];  // profiling events of the pool, part, head, grad and dk launches
 };
 
 hipError_t launch_backward(const BwdPlan& p, const BwdCall& c, hipStream_t s);
