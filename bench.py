@@ -336,6 +336,81 @@ def bench_backward(w, x, q, k, v, dev, stream, lib, hip, timed, pct, args):
     }
 
 
+def solver_compare(args):
+    """Newton-Schulz against conjugate gradient on the landmark systems of
+    the workloads: for each step count, the relative residual
+    ||A Y - W|| / ||W|| and the error max|Y - Y*| / max|Y*| against LAPACK's
+    solve Y* of the same fp32 A and W (the GPU's own, from
+    lapattn_forward_stages), median and worst over the heads; and the GPU time
+    of one solve launch over all heads at the workload's step count."""
+    import numpy as np
+    import torch
+
+    from nystr_linear_attention_amd import api
+    from nystr_linear_attention_amd import workloads as wl
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    out = {"metric": "landmark solve Y = A^-1 W: Newton-Schulz vs conjugate gradient",
+           "unit": "relative residual / error vs LAPACK solve; us per solve launch",
+           "workloads": {}}
+    names = args.solver_workloads.split(",")
+    for name in names:
+        w = wl.BY_NAME[name]
+        x = wl.make_inputs(w)
+
+        def to_dev(a):
+            if w.dtype == wl.BF16:
+                return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+            return torch.from_numpy(a).to(dev)
+        q = to_dev(x["q"])
+        k = q if w.shared_qk else to_dev(x["k"])
+        v = to_dev(x["v"])
+        kw = dict(grid_h=w.grid_h, grid_w=w.grid_w, pool_h=w.pool_h, pool_w=w.pool_w,
+                  lam=w.lam, eps=w.eps, kernel=w.kernel)
+        st = api.forward_stages(q, k, v, iters=w.iters, **kw)
+        L, W = st["L"].contiguous(), st["W"].contiguous()
+        A = st["A"].double().cpu().numpy().reshape(w.heads, w.m, w.m)
+        Wn = W.double().cpu().numpy().reshape(w.heads, w.m, w.d)
+        ystar = np.stack([np.linalg.solve(A[i], Wn[i]) for i in range(w.heads)])
+        kappa = [float(np.linalg.cond(A[i])) for i in range(w.heads)]
+        rows = []
+        for T in (5, 10, 15, 20, 25, 30, 40, 64):
+            row = {"iters": T}
+            for solver in ("ns", "cg"):
+                y = api.landmark_solve(L, W, iters=T, solver=solver, **kw)
+                y = y.double().cpu().numpy().reshape(w.heads, w.m, w.d)
+                res = [float(np.linalg.norm(A[i] @ y[i] - Wn[i]) / np.linalg.norm(Wn[i]))
+                       for i in range(w.heads)]
+                err = [float(np.abs(y[i] - ystar[i]).max() / np.abs(ystar[i]).max())
+                       for i in range(w.heads)]
+                row[solver] = {"residual_median": float(np.median(res)), "residual_max": max(res),
+                               "error_median": float(np.median(err)), "error_max": max(err)}
+            rows.append(row)
+        times = {}
+        for solver in ("ns", "cg"):
+            for _ in range(5):
+                api.landmark_solve(L, W, iters=w.iters, solver=solver, **kw)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(50):
+                api.landmark_solve(L, W, iters=w.iters, solver=solver, **kw)
+            e1.record()
+            torch.cuda.synchronize()
+            times[solver] = round(e0.elapsed_time(e1) / 50 * 1e3, 2)
+        out["workloads"][name] = {"heads": w.heads, "m": w.m, "d": w.d, "iters": w.iters,
+                                  "kappa_median": float(np.median(kappa)),
+                                  "kappa_max": max(kappa), "steps": rows,
+                                  "us_per_launch_at_iters": times}
+        log(f"[solver] {name}: kappa {np.median(kappa):.3g}; us per launch {times}")
+        for r in rows:
+            log(f"[solver]   T={r['iters']:3d}  ns res {r['ns']['residual_median']:.2e} "
+                f"err {r['ns']['error_median']:.2e}   cg res {r['cg']['residual_median']:.2e} "
+                f"err {r['cg']['error_median']:.2e}")
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -355,6 +430,11 @@ def main(argv=None):
                     help="skip the cold-cache pass (steps rotating over copies of the inputs)")
     ap.add_argument("--cold-mib", type=int, default=640,
                     help="total size of the input copies the cold pass rotates over")
+    ap.add_argument("--solver-compare", action="store_true",
+                    help="only compare Newton-Schulz and conjugate gradient on the landmark "
+                         "systems (its own JSON line)")
+    ap.add_argument("--solver-workloads", default="lap_f32_pvt1_b8_n3136_d64_m49,"
+                    "gauss_f32_b16h2_n3136_d64_m49_qk,lap_f32_h2_n16384_d64_m64_t3")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward pass measurement")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -368,6 +448,8 @@ def main(argv=None):
         return 2
     if args.copy_calibration:
         return copy_calibration(args.copy_calibration)
+    if args.solver_compare:
+        return solver_compare(args)
 
     import numpy as np
     import torch

@@ -230,6 +230,27 @@ int lapattn_backward(const lapattn_desc_t* desc, const void* q, const void* k,
                      int32_t iters, void* dq, void* dk, void* dv,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* The landmark solve on its own: Y = A^{-1} W per head, A = k(L, L) + eps I
+ * built as in lapattn_forward, by one of two solvers, for the comparison the
+ * LaplacianFormer summaries draw between them (Arabic summary, section 4,
+ * efficiency analysis: Newton-Schulz more stable and better converging than
+ * conjugate-gradient solvers, above all on ill-conditioned matrices):
+ *   LAPATTN_SOLVER_NEWTON_SCHULZ  Y = X_iters W, X_iters from the forward's
+ *                                 solver (same arithmetic)
+ *   LAPATTN_SOLVER_CG             `iters` steps of conjugate gradient
+ *                                 (Hestenes-Stiefel) on A y = w for every
+ *                                 column w of W, from y = 0, fp32
+ *   landmarks  device, fp32 [B, H, m, d] (the pool of lapattn_forward_stages)
+ *   w          device, fp32 [B, H, m, d]
+ *   y          device, fp32 [B, H, m, d], written
+ * One launch, one workgroup per head, no workspace; errors as for
+ * lapattn_forward (LAPATTN_ERR_PARAM for an unknown solver). */
+#define LAPATTN_SOLVER_NEWTON_SCHULZ 0
+#define LAPATTN_SOLVER_CG 1
+int lapattn_landmark_solve(const lapattn_desc_t* desc, const float* landmarks,
+                           const float* w, float lambda, float eps, int32_t iters,
+                           int32_t solver, float* y, void* stream);
+
 /* For callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
  * forward as lapattn_forward (same arguments, plan, kernels and bitwise

@@ -30,12 +30,14 @@ DTYPE_F32 = 0
 DTYPE_BF16 = 1
 FLAG_SERIAL = 1
 FLAG_TICKETS = 2
+SOLVER_NEWTON_SCHULZ = 0
+SOLVER_CG = 1
 
 # Names of every entry point declared in include/lapattn.h.
 EXPORTS = ("lapattn_version", "lapattn_strerror", "lapattn_check",
            "lapattn_workspace_bytes", "lapattn_status_offset", "lapattn_init",
            "lapattn_forward", "lapattn_forward_noalloc",
-           "lapattn_backward_workspace_bytes", "lapattn_backward",
+           "lapattn_backward_workspace_bytes", "lapattn_backward", "lapattn_landmark_solve",
            "lapattn_forward_stages", "lapattn_set_stage_events", "lapattn_launches")
 
 STAGES = ("pool", "main", "maps", "out", "bwd_part", "bwd_head", "bwd_grad", "bwd_dk")
@@ -96,6 +98,8 @@ def _declare(lib):
     lib.lapattn_backward_workspace_bytes.restype = sz
     lib.lapattn_backward.argtypes = [dp, vp, vp, vp, vp, f32, f32, i32, vp, vp, vp, vp, sz, vp]
     lib.lapattn_backward.restype = ctypes.c_int
+    lib.lapattn_landmark_solve.argtypes = [dp, vp, vp, f32, f32, i32, i32, vp, vp]
+    lib.lapattn_landmark_solve.restype = ctypes.c_int
     lib.lapattn_forward_noalloc.argtypes = [dp, vp, vp, vp, f32, f32, i32, vp, vp, vp]
     lib.lapattn_forward_noalloc.restype = ctypes.c_int
     lib.lapattn_forward_stages.argtypes = [dp, vp, vp, vp, f32, f32, i32, vp, vp, sz, vp,

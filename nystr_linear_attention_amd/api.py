@@ -228,3 +228,26 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tens
         workspace.numel(), _stream_ptr(stream))
     _lib.check(st)
     return dq, dk, dv
+
+
+def landmark_solve(L: torch.Tensor, W: torch.Tensor, *, grid_h: int, grid_w: int, pool_h: int,
+                   pool_w: int, lam: float, eps: float, iters: int, solver: str = "ns",
+                   kernel: str = "laplacian", stream=None) -> torch.Tensor:
+    """Y = A^{-1} W per head, A = k(L, L) + eps I, by Newton-Schulz ("ns") or
+    conjugate gradient ("cg"); L and W fp32 [B, H, m, d] on the GPU."""
+    if solver not in ("ns", "cg"):
+        raise ValueError("solver must be 'ns' or 'cg'")
+    for name, t in (("L", L), ("W", W)):
+        if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError(f"{name} must be a contiguous fp32 [B, H, m, d] GPU tensor")
+    B, H, m, d = L.shape
+    if W.shape != L.shape or m != (grid_h // pool_h) * (grid_w // pool_w):
+        raise ValueError("L and W must be [B, H, m, d] with m the landmark count of the grid")
+    desc = make_desc(B, H, grid_h, grid_w, d, pool_h, pool_w, kernel, torch.float32)
+    y = torch.empty_like(W)
+    st = _lib.lib().lapattn_landmark_solve(
+        ctypes.byref(desc), L.data_ptr(), W.data_ptr(), lam, eps, iters,
+        _lib.SOLVER_CG if solver == "cg" else _lib.SOLVER_NEWTON_SCHULZ, y.data_ptr(),
+        _stream_ptr(stream))
+    _lib.check(st)
+    return y

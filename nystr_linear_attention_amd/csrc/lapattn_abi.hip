@@ -410,6 +410,26 @@ int lapattn_backward(const lapattn_desc_t* desc, const void* q, const void* k, c
   return LAPATTN_OK;
 }
 
+int lapattn_landmark_solve(const lapattn_desc_t* desc, const float* landmarks, const float* w,
+                           float lambda, float eps, int32_t iters, int32_t solver, float* y,
+                           void* stream) {
+  using namespace lapattn;
+  int st = check_desc(desc);
+  if (st != LAPATTN_OK) return st;
+  st = check_params(lambda, eps, iters);
+  if (st != LAPATTN_OK) return st;
+  if (solver != LAPATTN_SOLVER_NEWTON_SCHULZ && solver != LAPATTN_SOLVER_CG) return LAPATTN_ERR_PARAM;
+  if (!landmarks || !w || !y) return LAPATTN_ERR_NULL;
+  if (misaligned16(landmarks) || misaligned16(w) || misaligned16(y)) return LAPATTN_ERR_ALIGN;
+  const Plan p = make_plan(desc);
+  const size_t n = static_cast<size_t>(p.BH) * p.m * p.D * sizeof(float);
+  if (overlaps(y, n, landmarks, n) || overlaps(y, n, w, n)) return LAPATTN_ERR_ALIAS;
+  if (launch_landmark_solve(p, landmarks, w, lambda, eps, iters, solver, y,
+                            static_cast<hipStream_t>(stream)) != hipSuccess)
+    return LAPATTN_ERR_HIP;
+  return LAPATTN_OK;
+}
+
 size_t lapattn_status_offset(const lapattn_desc_t* desc) {
   if (lapattn::check_desc(desc) != LAPATTN_OK) return static_cast<size_t>(-1);
   // word 0 of the hand-off words: timed-out waits of the call

@@ -124,6 +124,11 @@ struct BwdCall {
 
 hipError_t launch_backward(const BwdPlan& p, const BwdCall& c, hipStream_t s);
 
+// The landmark solve Y = A^{-1} W alone (lapattn_landmark_solve): Newton-
+// Schulz (cg = 0) or conjugate gradient (cg = 1), one workgroup per head.
+hipError_t launch_landmark_solve(const Plan& p, const float* L, const float* W, float lambda, float eps,
+                                 int iters, int cg, float* Y, hipStream_t s);
+
 // Whether query workgroups form O inside the main launch: only when there are
 // query workgroups (Q != K) and every workgroup of the launch can be resident
 // at once.  (Larger grids would be correct too, but query workgroups waiting

@@ -229,3 +229,20 @@ def test_backward_rejects_before_launch():
     assert call(dk=FAKE + 0x3000000 + 16) == _lib.ERR_ALIAS           # overlaps dO
     assert call(dv=FAKE + 0x4000000 + 256) == _lib.ERR_ALIAS          # overlaps dq
     assert call(dk=FAKE + 0x8000000 + 256, wsb=need) == _lib.ERR_ALIAS  # inside the workspace
+
+
+def test_landmark_solve_rejects_before_launch():
+    lib = _lib.lib()
+    d = good_desc()
+
+    def call(desc=d, L=FAKE, W=FAKE + 0x1000000, Y=FAKE + 0x2000000, lam=4.0, iters=20, solver=0):
+        return lib.lapattn_landmark_solve(ctypes.byref(desc), L, W, lam, 1e-3, iters, solver, Y,
+                                          None)
+    assert call(good_desc(B=0)) == _lib.ERR_SHAPE
+    assert call(lam=-1.0) == _lib.ERR_PARAM
+    assert call(iters=65) == _lib.ERR_PARAM
+    assert call(solver=2) == _lib.ERR_PARAM
+    assert call(L=None) == _lib.ERR_NULL
+    assert call(Y=None) == _lib.ERR_NULL
+    assert call(W=FAKE + 8) == _lib.ERR_ALIGN
+    assert call(Y=FAKE + 0x1000000 + 256) == _lib.ERR_ALIAS
