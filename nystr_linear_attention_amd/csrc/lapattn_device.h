@@ -1241,6 +1241,13 @@ __device__ void reduce_w_lines(const MainArgs& a, int bh, int l0, int l1, float*
   }
 }
 
+// Offset of K_QL[token][j] in a tile's token-major rows (row stride LS).  The
+// row of token t starts (t >> 3) & 3 floats in, so that the map waves' stores
+// of one landmark column for 64 tokens (lane = token) fall on distinct banks
+// (with no offset, 32 lanes at stride LS = 68 share 8 banks); readers use
+// scalar loads, since the rows are no longer 16-byte aligned.
+__device__ __forceinline__ int ptj(int tok, int j) { return tok * LS + j + ((tok >> 3) & 3); }
+
 // Stores output block (tokens 16 tb + 4 g + i, columns 16 cb + lr) of tile t
 // from accumulator c (lane (g, lr)), fp32 or bf16 (round to nearest even).
 template <int D>
@@ -1281,8 +1288,8 @@ __device__ void out_tile(const MainArgs& a, int bh, int t, const float* PT, cons
   u32x4 kh[2], kl[2];
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
-    const float* ar = PT + (16 * tb + lr) * LS + 32 * p + 8 * lg;
-    split8h(ld4(ar), ld4(ar + 4), 14, kh[p], kl[p]);
+    const float* ar = PT + ptj(16 * tb + lr, 32 * p + 8 * lg);
+    split8h(f4{ar[0], ar[1], ar[2], ar[3]}, f4{ar[4], ar[5], ar[6], ar[7]}, 14, kh[p], kl[p]);
   }
   constexpr int CBW = (CBN + 1) / 2;  // column blocks per wave
 #pragma unroll
@@ -1336,7 +1343,8 @@ __device__ __forceinline__ void gauss_rows(const MainArgs& a, const void* src, i
 
 template <int D, bool BF16>
 __device__ __forceinline__ void gauss_tile(const MainArgs& a, const float (&av)[D / 4], const float* Lh,
-                                           int t, float* PTt, float* PJ, float* xx, bool key_role) {
+                                           int t, float* PTt, float* PJ, float* xx, bool key_role,
+                                           bool write_pt) {
   constexpr int KS = D / 4;  // MFMA sub-steps; floats per lane per operand
   const int lane = threadIdx.x & 63, w = wave_id();
   const int lr = lane & 15, lg = lane >> 4;
@@ -1375,7 +1383,7 @@ __device__ __forceinline__ void gauss_tile(const MainArgs& a, const float (&av)[
         const int tt = 16 * tb + 4 * lg + i;
         const float d = fmaxf(fmaf(-2.0f, c[i], xx[tt] + pl), 0.0f);
         const float kv = (j < m && t * TILE + tt < N) ? exp2_map(d * a.c_exp2) : 0.f;
-        PTt[tt * LS + j] = kv;
+        if (write_pt) PTt[ptj(tt, j)] = kv;
         if (key_role) PJ[j * LS + tt] = kv;
       }
     }
@@ -1411,6 +1419,10 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
   // it); query tiles keep theirs in LDS and form their output rows here.
   const bool store_kql = key_role ? a.shared_qk != 0 : a.out_in_main == 0;
   const bool stage_kql = a.st_kql && (!key_role || a.shared_qk);
+  // token-major K_QL rows: query tiles (their output rows) and key tiles
+  // whose K_QL is stored or staged (Q == K); other key tiles need only the
+  // landmark-major rows of the W^T product
+  const bool write_pt = !key_role || store_kql || stage_kql;
   const void* src = key_role ? k : q;
   const int mby = (m + 15) >> 4;
   const int nwb = CBN * mby;  // W output blocks
@@ -1483,16 +1495,18 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
           PJ[j * LS + lane] = k0;
           PJ[(j + 1) * LS + lane] = k1;
         }
-        PTt[lane * LS + j] = k0;
-        PTt[lane * LS + j + 1] = k1;
+        if (write_pt) {
+          PTt[ptj(lane, j)] = k0;
+          PTt[ptj(lane, j + 1)] = k1;
+        }
       }
       if (j < je) {
         const float k0 = valid ? exp2_map(dist_to<D, KIND>(x, Lh + j * D) * a.c_exp2) : 0.f;
         if (key_role) PJ[j * LS + lane] = k0;
-        PTt[lane * LS + j] = k0;
+        if (write_pt) PTt[ptj(lane, j)] = k0;
       }
     } else {
-      gauss_tile<D, BF16>(a, ga, Lh, t, PTt, PJ, xx, key_role);
+      gauss_tile<D, BF16>(a, ga, Lh, t, PTt, PJ, xx, key_role, write_pt);
     }
     if (t + 1 < t_end) {
       load_v(t + 1);
@@ -1505,14 +1519,15 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
       float* dst = a.kql + (static_cast<size_t>(bh) * N + t * TILE) * a.mpad;
       for (int e = tid; e < TILE * q4; e += WGM) {
         const int tok = e / q4, c4 = e % q4;
-        if (t * TILE + tok < N) st4(dst + tok * a.mpad + 4 * c4, ld4(PTt + tok * LS + 4 * c4));
+        const float* src4 = PTt + ptj(tok, 4 * c4);
+        if (t * TILE + tok < N) st4(dst + tok * a.mpad + 4 * c4, f4{src4[0], src4[1], src4[2], src4[3]});
       }
     }
     if (stage_kql) {
       for (int e = tid; e < TILE * m; e += WGM) {
         const int tok = e / m, j = e % m;
         if (t * TILE + tok < N)
-          a.st_kql[(static_cast<size_t>(bh) * N + t * TILE + tok) * m + j] = PTt[tok * LS + j];
+          a.st_kql[(static_cast<size_t>(bh) * N + t * TILE + tok) * m + j] = PTt[ptj(tok, j)];
       }
     }
     if (key_role) {
