@@ -411,6 +411,61 @@ def solver_compare(args):
     return 0
 
 
+def bench_block(bw, steps, warmup):
+    """One attention block (lapattn_block_forward: the projections into the
+    heads, the Nystrom attention, the projection back) on seeded tokens and
+    weights resident in HBM: mean time of `steps` calls after `warmup`."""
+    import numpy as np
+    import torch
+
+    from nystr_linear_attention_amd import _lib, api
+    from nystr_linear_attention_amd import workloads as wl
+    dev = torch.device("cuda:0")
+    inp = wl.make_block_inputs(bw)
+
+    def to_dev(a):
+        if a is None:
+            return None
+        if bw.dtype == wl.BF16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+    t = {k: to_dev(v) for k, v in inp.items()}
+    desc = api.make_desc(bw.B, bw.H, bw.grid_h, bw.grid_w, bw.d, bw.pool_h, bw.pool_w, bw.kernel,
+                         t["x"].dtype)
+    lib = _lib.lib()
+    ws = torch.empty(lib.lapattn_block_workspace_bytes(ctypes.byref(desc), bw.C),
+                     dtype=torch.uint8, device=dev)
+    y = torch.empty_like(t["x"])
+    stream = torch.cuda.current_stream().cuda_stream
+    call = (ctypes.byref(desc), bw.C, t["x"].data_ptr(), t["wq"].data_ptr(),
+            None if t["wk"] is None else t["wk"].data_ptr(), t["wv"].data_ptr(),
+            t["wo"].data_ptr(), bw.lam, bw.eps, bw.iters, y.data_ptr(), ws.data_ptr(),
+            ws.numel(), stream)
+
+    def step():
+        st = lib.lapattn_block_forward(*call)
+        if st != 0:
+            raise _lib.LapattnError(st, _lib.strerror(st))
+    for _ in range(warmup):
+        step()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    timeouts = int(ws[:4].cpu().view(torch.int32).item())
+    hd = bw.H * bw.d
+    proj_flops = 2 * bw.B * bw.N * bw.C * hd * (3 if not bw.shared_qk else 2) \
+        + 2 * bw.B * bw.N * hd * bw.C
+    return {"workload": bw.name, "B": bw.B, "N": bw.N, "C": bw.C, "H": bw.H, "d": bw.d,
+            "m": bw.m, "kernel": bw.kernel, "shared_qk": bw.shared_qk,
+            "ms_per_step": round(ms, 5), "value": round(bw.B * bw.N / (ms * 1e-3), 1),
+            "unit": "tokens/s", "projection_flops": proj_flops, "timeouts": timeouts}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -435,6 +490,10 @@ def main(argv=None):
                          "systems (its own JSON line)")
     ap.add_argument("--solver-workloads", default="lap_f32_pvt1_b8_n3136_d64_m49,"
                     "gauss_f32_b16h2_n3136_d64_m49_qk,lap_f32_h2_n16384_d64_m64_t3")
+    ap.add_argument("--blocks", action="store_true",
+                    help="only time the attention block of every pyramid stage (its own JSON line)")
+    ap.add_argument("--no-block", action="store_true",
+                    help="skip the stage-1 attention block measurement")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward pass measurement")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -450,6 +509,17 @@ def main(argv=None):
         return copy_calibration(args.copy_calibration)
     if args.solver_compare:
         return solver_compare(args)
+    if args.blocks:
+        import torch
+        from nystr_linear_attention_amd import workloads as wl
+        torch.cuda.set_device(0)
+        rows = [bench_block(bw, args.steps, args.warmup) for bw in wl.BLOCKS]
+        for r in rows:
+            log(f"[bench] block {r['workload']}: {r['ms_per_step'] * 1e3:.2f} us/step, "
+                f"{r['value']:.3g} tokens/s")
+        print(json.dumps({"metric": "attention-block tokens/sec (fwd) per pyramid stage",
+                          "unit": "tokens/s", "blocks": rows}), flush=True)
+        return 3 if any(r["timeouts"] for r in rows) else 0
 
     import numpy as np
     import torch
@@ -782,6 +852,10 @@ def main(argv=None):
     }
     if not args.no_backward:
         res["backward"] = bench_backward(w, x, q, k, v, dev, stream, lib, hip, timed, pct, args)
+    if not args.no_block:
+        res["block"] = bench_block(wl.BLOCKS[0], args.steps, args.warmup)
+        timeouts[0] += res["block"]["timeouts"]
+        log(f"[bench] block {wl.BLOCKS[0].name}: {res['block']['ms_per_step'] * 1e3:.2f} us/step")
     res["timeouts"] = timeouts[0]
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle for ~{args.cpu_seconds:.0f} s")

@@ -251,6 +251,31 @@ int lapattn_landmark_solve(const lapattn_desc_t* desc, const float* landmarks,
                            const float* w, float lambda, float eps, int32_t iters,
                            int32_t solver, float* y, void* stream);
 
+/* One attention block around the Nystrom attention, on the tokens of one
+ * stage of a pyramid backbone (the SOFT review instantiates SOFT as one
+ * layer of such a backbone, "proposed method", last bullet; its symmetric
+ * kernel S = exp(Q (-) K) shares the query and key projection):
+ *   Q = X Wq, K = X Wk (wk == NULL: K = Q), V = X Wv, each split into the
+ *   desc->H heads of desc->d columns (columns h d .. h d + d - 1 are head h),
+ *   O_h = lapattn_forward(Q_h, K_h, V_h), Y = concat_h(O_h) Wo.
+ *   x        device, [B, N, C] (N = grid_h grid_w, tokens in raster order)
+ *   wq, wk, wv  device, [C, H d] row-major, no bias
+ *   wo       device, [H d, C] row-major
+ *   y        device, [B, N, C]
+ * All in desc->dtype; Q, K, V and O are stored in that type in the
+ * workspace (rounded to nearest even for bf16); every product accumulates in
+ * fp32 (the projections on fp32 MFMA).  C and H d must be multiples of 32
+ * (LAPATTN_ERR_SHAPE).  The workspace (lapattn_block_workspace_bytes,
+ * 256-byte aligned) starts with the call's status word (uint32 at offset 0,
+ * as lapattn_status_offset describes for lapattn_forward).  Three or four
+ * launches on `stream`; errors as for lapattn_forward. */
+size_t lapattn_block_workspace_bytes(const lapattn_desc_t* desc, int32_t C);
+int lapattn_block_forward(const lapattn_desc_t* desc, int32_t C, const void* x,
+                          const void* wq, const void* wk, const void* wv,
+                          const void* wo, float lambda, float eps, int32_t iters,
+                          void* y, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
 /* For callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
  * forward as lapattn_forward (same arguments, plan, kernels and bitwise

@@ -251,3 +251,45 @@ def landmark_solve(L: torch.Tensor, W: torch.Tensor, *, grid_h: int, grid_w: int
         _stream_ptr(stream))
     _lib.check(st)
     return y
+
+
+def block_forward(x: torch.Tensor, wq: torch.Tensor, wk: Optional[torch.Tensor], wv: torch.Tensor,
+                  wo: torch.Tensor, *, H: int, d: int, grid_h: int, grid_w: int, pool_h: int,
+                  pool_w: int, lam: float, eps: float, iters: int, kernel: str = "laplacian",
+                  workspace: Optional[torch.Tensor] = None, stream=None,
+                  check: bool = True) -> torch.Tensor:
+    """Y = concat_h(attention(X Wq, X Wk or X Wq, X Wv)_h) Wo; see
+    include/lapattn.h.  x [B, N, C]; wq, wk, wv [C, H d]; wo [H d, C]."""
+    if x.dim() != 3 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [B, N, C] GPU tensor")
+    B, N, C = x.shape
+    if N != grid_h * grid_w:
+        raise ValueError(f"N={N} does not match the {grid_h}x{grid_w} grid")
+    for name, t, shape in (("wq", wq, (C, H * d)), ("wk", wk, (C, H * d)),
+                           ("wv", wv, (C, H * d)), ("wo", wo, (H * d, C))):
+        if t is None and name == "wk":
+            continue
+        if tuple(t.shape) != shape or t.dtype != x.dtype or t.device != x.device \
+                or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {shape} tensor like x")
+    desc = make_desc(B, H, grid_h, grid_w, d, pool_h, pool_w, kernel, x.dtype)
+    n = int(_lib.lib().lapattn_block_workspace_bytes(ctypes.byref(desc), C))
+    if n == 0:
+        raise ValueError("invalid descriptor (C and H d must be multiples of 32)")
+    if workspace is None:
+        workspace = torch.empty(n, dtype=torch.uint8, device=x.device)
+    elif (workspace.dtype != torch.uint8 or workspace.device != x.device
+          or not workspace.is_contiguous() or workspace.numel() < n):
+        raise ValueError(f"workspace must be a contiguous uint8 tensor of >= {n} bytes on x's device")
+    y = torch.empty_like(x)
+    st = _lib.lib().lapattn_block_forward(
+        ctypes.byref(desc), C, x.data_ptr(), wq.data_ptr(), None if wk is None else wk.data_ptr(),
+        wv.data_ptr(), wo.data_ptr(), lam, eps, iters, y.data_ptr(), workspace.data_ptr(),
+        workspace.numel(), _stream_ptr(stream))
+    _lib.check(st)
+    if check:
+        with torch.cuda.stream(stream) if stream is not None else _nullctx():
+            cnt = int(workspace[:4].cpu().view(torch.int32).item())
+        if cnt:
+            raise _lib.LapattnTimeout(cnt)
+    return y

@@ -430,6 +430,89 @@ int lapattn_landmark_solve(const lapattn_desc_t* desc, const float* landmarks, c
   return LAPATTN_OK;
 }
 
+// Block workspace: the status word (256 bytes), Q, K, V, O in the heads'
+// layout and I/O type, then the attention's workspace.
+namespace lapattn {
+namespace {
+int check_block(const lapattn_desc_t* desc, int32_t C) {
+  const int st = check_desc(desc);
+  if (st != LAPATTN_OK) return st;
+  if (C <= 0 || C % 32 || (desc->H * desc->d) % 32) return LAPATTN_ERR_SHAPE;
+  return LAPATTN_OK;
+}
+size_t block_io_bytes(const lapattn_desc_t* d) {
+  return align_up(static_cast<size_t>(d->B) * d->H * d->grid_h * d->grid_w * d->d *
+                  (d->dtype == LAPATTN_BF16 ? 2 : 4));
+}
+}  // namespace
+}  // namespace lapattn
+
+size_t lapattn_block_workspace_bytes(const lapattn_desc_t* desc, int32_t C) {
+  if (lapattn::check_block(desc, C) != LAPATTN_OK) return 0;
+  return lapattn::kAlign + 4 * lapattn::block_io_bytes(desc) + lapattn::make_plan(desc).total;
+}
+
+int lapattn_block_forward(const lapattn_desc_t* desc, int32_t C, const void* x, const void* wq,
+                          const void* wk, const void* wv, const void* wo, float lambda, float eps,
+                          int32_t iters, void* y, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  using namespace lapattn;
+  int st = check_block(desc, C);
+  if (st != LAPATTN_OK) return st;
+  st = check_params(lambda, eps, iters);
+  if (st != LAPATTN_OK) return st;
+  if (!x || !wq || !wv || !wo || !y || !workspace) return LAPATTN_ERR_NULL;
+  if (misaligned16(x) || misaligned16(wq) || (wk && misaligned16(wk)) || misaligned16(wv) ||
+      misaligned16(wo) || misaligned16(y))
+    return LAPATTN_ERR_ALIGN;
+  const Plan p = make_plan(desc);
+  const size_t io = block_io_bytes(desc);
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign ||
+      workspace_bytes < kAlign + 4 * io + p.total)
+    return LAPATTN_ERR_WORKSPACE;
+  const size_t es = p.bf16 ? 2 : 4;
+  const size_t xb = static_cast<size_t>(p.B) * p.N * C * es;
+  const size_t wb = static_cast<size_t>(C) * p.H * p.D * es;
+  if (overlaps(y, xb, x, xb) || overlaps(y, xb, wq, wb) || (wk && overlaps(y, xb, wk, wb)) ||
+      overlaps(y, xb, wv, wb) || overlaps(y, xb, wo, wb) || overlaps(y, xb, workspace, workspace_bytes))
+    return LAPATTN_ERR_ALIAS;
+  char* ws = static_cast<char*>(workspace);
+  unsigned* status = reinterpret_cast<unsigned*>(ws);
+  void* Q = ws + kAlign;
+  void* K = ws + kAlign + io;
+  void* V = ws + kAlign + 2 * io;
+  void* O = ws + kAlign + 3 * io;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int M = p.B * p.N, HD = p.H * p.D;
+  // Q (and K unless shared) and V, one launch
+  {
+    const void* w3[3] = {wq, wk ? wk : wv, wv};
+    void* o3[3] = {Q, wk ? K : V, V};
+    if (launch_block_proj(0, x, w3, o3, wk ? 3 : 2, M, C, HD, p.N, p.H, p.D, p.bf16, s) != hipSuccess)
+      return LAPATTN_ERR_HIP;
+  }
+  Args a{};
+  a.q = Q;
+  a.k = wk ? K : Q;
+  a.v = V;
+  a.out = O;
+  a.lambda = lambda;
+  a.eps = eps;
+  a.iters = iters;
+  a.shared_qk = wk ? 0 : 1;
+  a.status = status;
+  a.tickets = (desc->flags & LAPATTN_FLAG_TICKETS) ? 1 : 0;
+  st = run(desc, a, ws + kAlign + 4 * io, p.total, s);
+  if (st != LAPATTN_OK) return st;
+  {
+    const void* w1[1] = {wo};
+    void* o1[1] = {y};
+    if (launch_block_proj(1, O, w1, o1, 1, M, HD, C, p.N, p.H, p.D, p.bf16, s) != hipSuccess)
+      return LAPATTN_ERR_HIP;
+  }
+  return LAPATTN_OK;
+}
+
 size_t lapattn_status_offset(const lapattn_desc_t* desc) {
   if (lapattn::check_desc(desc) != LAPATTN_OK) return static_cast<size_t>(-1);
   // word 0 of the hand-off words: timed-out waits of the call

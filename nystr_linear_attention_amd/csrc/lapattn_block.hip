@@ -1,0 +1,173 @@
+// The attention block around the Nystrom attention: the projections of
+// tokens X [B, N, C] into the heads' Q, K, V and of the heads' outputs back,
+// as one SOFT layer of a pyramid backbone (SOFT review, "proposed method",
+// last bullet; the symmetric kernel S = exp(Q (-) K) shares the query and key
+// projection).
+//
+//   in  : Q = X Wq, K = X Wk (or Q), V = X Wv, weights [C, H d], written
+//         straight into the heads' [B, H, N, d] layout (head h = columns
+//         h d .. h d + d - 1) in the I/O type
+//   attn: lapattn_forward on (Q, K, V)
+//   out : Y = concat_h(O_h) Wo, Wo [H d, C], the heads gathered from
+//         [B, H, N, d] while the tiles load
+//
+// One GEMM kernel for both: 64 x 64 output tiles, 4 waves of 32 x 32, the
+// contraction in chunks of 32 staged in LDS as fp32 rows of both operands,
+// fp32 MFMA (16x16x4, k = 8 g + s for lane group g at sub-step s), fp32
+// accumulation; bf16 operands are widened exactly, bf16 outputs rounded to
+// nearest even.
+
+#include "lapattn_device.h"
+
+namespace lapattn {
+namespace {
+
+constexpr int GT = 64;      // output tile side
+constexpr int GK = 32;      // contraction chunk
+constexpr int GS = GK + 4;  // LDS row stride of the staged chunks
+constexpr int WGP = 256;    // 4 waves
+
+struct ProjArgs {
+  const void* a;      // MODE 0: X [M][Kd]; MODE 1: O [B][H][N][d]
+  const void* w[3];   // weights [Kd][Nc], row-major
+  void* out[3];       // MODE 0: [B][H][N][d]; MODE 1: Y [M][Nc]
+  int M, Kd, Nc;      // rows (B N), contraction, columns
+  int N, H, d;
+  int bf16;
+};
+
+// Eight consecutive elements (fp32 or bf16, 16-byte aligned) as fp32.
+__device__ __forceinline__ void load8(const void* base, size_t idx, int bf16, float* v) {
+  if (bf16) {
+    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
+    const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      v[2 * h] = __uint_as_float(w4[h] << 16);
+      v[2 * h + 1] = __uint_as_float(w4[h] & 0xffff0000u);
+    }
+  } else {
+    const f4 x0 = ld4(static_cast<const float*>(base) + idx), x1 = ld4(static_cast<const float*>(base) + idx + 4);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      v[h] = x0[h];
+      v[4 + h] = x1[h];
+    }
+  }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(WGP) void proj_kernel(ProjArgs p) {
+  __shared__ __attribute__((aligned(16))) float As[GT * GS];  // [row][k]
+  __shared__ __attribute__((aligned(16))) float Bs[GT * GS];  // [col][k]
+  const int z = blockIdx.z;
+  const void* w = p.w[z];
+  void* out = p.out[z];
+  const int r0 = blockIdx.x * GT, c0 = blockIdx.y * GT;
+  const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
+  const int lr = lane & 15, lg = lane >> 4;
+  const int wr = 32 * (wv >> 1), wc = 32 * (wv & 1);  // this wave's 32 x 32 quadrant
+  f4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+
+  // thread's slots of a chunk: A rows ar (8 consecutive k at ak), B row bk
+  // (8 consecutive columns at bc)
+  const int ar = tid >> 2, ak = 8 * (tid & 3);
+  const int bk = tid >> 3, bc = 8 * (tid & 7);
+  for (int k0 = 0; k0 < p.Kd; k0 += GK) {
+    float va[8], vb[8];
+    {
+      const int row = r0 + ar, k = k0 + ak;
+      if (row < p.M) {
+        size_t idx;
+        if constexpr (MODE == 0) {
+          idx = static_cast<size_t>(row) * p.Kd + k;
+        } else {
+          // row = b N + n, k = h d + c  ->  O[b][h][n][c]
+          const int b = row / p.N, n = row % p.N, h = k / p.d, c = k % p.d;
+          idx = ((static_cast<size_t>(b) * p.H + h) * p.N + n) * p.d + c;
+        }
+        load8(p.a, idx, p.bf16, va);
+      } else {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) va[u] = 0.f;
+      }
+      const int col = c0 + bc;
+      if (col < p.Nc) {
+        load8(w, static_cast<size_t>(k0 + bk) * p.Nc + col, p.bf16, vb);
+      } else {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) vb[u] = 0.f;
+      }
+    }
+    __syncthreads();  // the previous chunk's products are done with As, Bs
+    st4(As + ar * GS + ak, f4{va[0], va[1], va[2], va[3]});
+    st4(As + ar * GS + ak + 4, f4{va[4], va[5], va[6], va[7]});
+#pragma unroll
+    for (int u = 0; u < 8; ++u) Bs[(bc + u) * GS + bk] = vb[u];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float* ap = As + (wr + 16 * i + lr) * GS + 8 * lg;
+      const f4 a0 = ld4(ap), a1 = ld4(ap + 4);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float* bp = Bs + (wc + 16 * j + lr) * GS + 8 * lg;
+        const f4 b0 = ld4(bp), b1 = ld4(bp + 4);
+        f4 c = acc[i][j];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) c = mfma4(a0[s], b0[s], c);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) c = mfma4(a1[s], b1[s], c);
+        acc[i][j] = c;
+      }
+    }
+  }
+  // accumulator of block (i, j): element (wr + 16 i + 4 lg + e, wc + 16 j + lr)
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = r0 + wr + 16 * i + 4 * lg + e, col = c0 + wc + 16 * j + lr;
+        if (row >= p.M || col >= p.Nc) continue;
+        size_t o;
+        if constexpr (MODE == 0) {
+          const int b = row / p.N, n = row % p.N, h = col / p.d, c = col % p.d;
+          o = ((static_cast<size_t>(b) * p.H + h) * p.N + n) * p.d + c;
+        } else {
+          o = static_cast<size_t>(row) * p.Nc + col;
+        }
+        const float v = acc[i][j][e];
+        if (p.bf16) static_cast<uint16_t*>(out)[o] = f32_to_bf16_rne(v);
+        else static_cast<float*>(out)[o] = v;
+      }
+}
+
+}  // namespace
+
+hipError_t launch_block_proj(int mode, const void* a, const void* const* w, void* const* out, int nz, int M,
+                             int Kd, int Nc, int N, int H, int d, int bf16, hipStream_t s) {
+  ProjArgs p{};
+  p.a = a;
+  for (int z = 0; z < nz; ++z) {
+    p.w[z] = w[z];
+    p.out[z] = out[z];
+  }
+  p.M = M;
+  p.Kd = Kd;
+  p.Nc = Nc;
+  p.N = N;
+  p.H = H;
+  p.d = d;
+  p.bf16 = bf16;
+  const dim3 grid((M + GT - 1) / GT, (Nc + GT - 1) / GT, nz);
+  if (mode == 0) return launch(proj_kernel<0>, grid, dim3(WGP), s, Ev{}, p);
+  return launch(proj_kernel<1>, grid, dim3(WGP), s, Ev{}, p);
+}
+
+}  // namespace lapattn

@@ -129,6 +129,12 @@ hipError_t launch_backward(const BwdPlan& p, const BwdCall& c, hipStream_t s);
 hipError_t launch_landmark_solve(const Plan& p, const float* L, const float* W, float lambda, float eps,
                                  int iters, int cg, float* Y, hipStream_t s);
 
+// The block's projection GEMM: mode 0 = tokens [M][Kd] times nz weights
+// [Kd][Nc] into the heads' [B][H][N][d] layouts; mode 1 = heads [B][H][N][d]
+// gathered as rows of H d, times one weight [Kd][Nc] into [M][Nc].
+hipError_t launch_block_proj(int mode, const void* a, const void* const* w, void* const* out, int nz, int M,
+                             int Kd, int Nc, int N, int H, int d, int bf16, hipStream_t s);
+
 // Whether query workgroups form O inside the main launch: only when there are
 // query workgroups (Q != K) and every workgroup of the launch can be resident
 // at once.  (Larger grids would be correct too, but query workgroups waiting

@@ -182,3 +182,72 @@ def small_case(grid_h: int, grid_w: int, d: int, pool_h: int, pool_w: int,
         pool_w=pool_w, lam=lam, eps=eps, iters=iters, kernel=kernel,
         dtype=dtype, shared_qk=shared_qk, qk_dist=qk_dist, qk_scale=qk_scale,
         seed=seed)
+
+
+@dataclasses.dataclass(frozen=True)
+class BlockWorkload:
+    """One attention block on the tokens of a pyramid stage: x [B, N, C],
+    projections [C, H d] (query and key shared when ``shared_qk``) and
+    [H d, C], the Nystrom attention in between."""
+
+    name: str
+    B: int
+    H: int
+    d: int
+    C: int
+    grid_h: int
+    grid_w: int
+    pool_h: int
+    pool_w: int
+    lam: float
+    eps: float = 1e-3
+    iters: int = 20
+    kernel: str = LAPLACIAN
+    dtype: str = F32
+    shared_qk: bool = False
+    seed: int = 2000
+
+    @property
+    def N(self) -> int:
+        return self.grid_h * self.grid_w
+
+    @property
+    def m(self) -> int:
+        return (self.grid_h // self.pool_h) * (self.grid_w // self.pool_w)
+
+    def replace(self, **kw) -> "BlockWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+# The four stages of a PVT-small-like pyramid (tokens 56^2, 28^2, 14^2, 7^2;
+# widths 64, 128, 320, 512; heads of 64 columns), 49 landmarks each; the
+# first stage also as SOFT's Gaussian layer with the shared projection.
+BLOCKS: List[BlockWorkload] = [
+    BlockWorkload("block_lap_s1_b8_n3136_c64", B=8, H=1, d=64, C=64, grid_h=56, grid_w=56,
+                  pool_h=8, pool_w=8, lam=2.0 * _SQRT64, seed=2000),
+    BlockWorkload("block_lap_s2_b8_n784_c128", B=8, H=2, d=64, C=128, grid_h=28, grid_w=28,
+                  pool_h=4, pool_w=4, lam=2.0 * _SQRT64, seed=2001),
+    BlockWorkload("block_lap_s3_b8_n196_c320", B=8, H=5, d=64, C=320, grid_h=14, grid_w=14,
+                  pool_h=2, pool_w=2, lam=2.0 * _SQRT64, seed=2002),
+    BlockWorkload("block_lap_s4_b8_n49_c512", B=8, H=8, d=64, C=512, grid_h=7, grid_w=7,
+                  pool_h=1, pool_w=1, lam=2.0 * _SQRT64, seed=2003),
+    BlockWorkload("block_gauss_s1_b8_n3136_c64_qk", B=8, H=1, d=64, C=64, grid_h=56, grid_w=56,
+                  pool_h=8, pool_w=8, lam=2.0 * _SQRT64, kernel=GAUSSIAN, shared_qk=True,
+                  seed=2004),
+]
+BLOCK_BY_NAME: Dict[str, BlockWorkload] = {b.name: b for b in BLOCKS}
+
+
+def make_block_inputs(w: BlockWorkload, seed: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """x ~ N(0, 1) [B, N, C]; Wq, Wk, Wv ~ N(0, 1/C) [C, H d] (so projected
+    coordinates are about N(0, 1)); Wo ~ N(0, 1/(H d)) [H d, C]; drawn in that
+    order (Wk skipped when shared, the entry is then None) and cast to the
+    I/O type."""
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    hd = w.H * w.d
+    x = _cast(rng.standard_normal((w.B, w.N, w.C)), w.dtype)
+    wq = _cast(rng.standard_normal((w.C, hd)) / math.sqrt(w.C), w.dtype)
+    wk = None if w.shared_qk else _cast(rng.standard_normal((w.C, hd)) / math.sqrt(w.C), w.dtype)
+    wv = _cast(rng.standard_normal((w.C, hd)) / math.sqrt(w.C), w.dtype)
+    wo = _cast(rng.standard_normal((hd, w.C)) / math.sqrt(hd), w.dtype)
+    return {"x": x, "wq": wq, "wk": wk, "wv": wv, "wo": wo}
