@@ -852,6 +852,31 @@ def main(argv=None):
     }
     if not args.no_backward:
         res["backward"] = bench_backward(w, x, q, k, v, dev, stream, lib, hip, timed, pct, args)
+    if not args.no_backward:
+        # the normalised feature map variant on the same inputs (its own plan:
+        # K_QL stored, a statistics launch, the output launch)
+        ws_n = api.alloc_workspace(api.make_desc(w.B, w.H, w.grid_h, w.grid_w, w.d, w.pool_h,
+                                                 w.pool_w, w.kernel, q.dtype), dev)
+        out_n = torch.empty_like(q)
+        dn = api.make_desc(w.B, w.H, w.grid_h, w.grid_w, w.d, w.pool_h, w.pool_w, w.kernel, q.dtype)
+        calln = (ctypes.byref(dn), q.data_ptr(), k.data_ptr(), v.data_ptr(), w.lam, w.eps,
+                 w.iters, 1e-5, out_n.data_ptr(), ws_n.data_ptr(), ws_n.numel(), stream)
+
+        def step_n():
+            st = lib.lapattn_forward_normalized(*calln)
+            if st != 0:
+                raise _lib.LapattnError(st, _lib.strerror(st))
+        step_n.status = ws_n[api.status_offset(dn):api.status_offset(dn) + 4]
+        for _ in range(args.warmup):
+            step_n()
+        ms_n, _ = timed(step_n, args.steps, False)
+        res["normalized"] = {"ms_per_step": round(ms_n, 5),
+                             "value": round(w.B * w.N / (ms_n * 1e-3), 1), "unit": "tokens/s",
+                             "delta": 1e-5,
+                             "note": "normalised feature map Z = (K_QL - mu) / sqrt(var + delta) "
+                                     "in place of K_QL; output-launch plan plus a statistics "
+                                     "launch"}
+        log(f"[bench] normalized map: {ms_n * 1e3:.2f} us/step")
     if not args.no_block:
         res["block"] = bench_block(wl.BLOCKS[0], args.steps, args.warmup)
         timeouts[0] += res["block"]["timeouts"]

@@ -230,6 +230,25 @@ int lapattn_backward(const lapattn_desc_t* desc, const void* q, const void* k,
                      int32_t iters, void* dq, void* dk, void* dv,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* LaplacianFormer's normalised feature map in place of the raw query-side
+ * kernel values (Arabic summary, section 2(b); Dutch summary, "Methodologie"
+ * item 1: each query's similarity vector centred and whitened, with a
+ * diagonal estimator that normalises every feature dimension on its own
+ * across the batch instead of the covariance's inverse square root):
+ *   Z = (K_QL - mu) / sqrt(var + delta), mu_j and var_j the mean and the
+ *   population variance of column j (landmark j) of K_QL over the head's N
+ *   queries;  O = Z (X (K_LK V)).
+ * Readings (the pages print no formula): the similarity vector of query i is
+ * row i of K_QL; the batch is the head's N queries; delta >= 0 is the
+ * whitening's stabiliser.  Arguments and workspace as for lapattn_forward,
+ * plus delta (LAPATTN_ERR_PARAM when negative or not finite).  Takes the
+ * output-launch plan (K_QL stored), plus one statistics launch. */
+int lapattn_forward_normalized(const lapattn_desc_t* desc, const void* q,
+                               const void* k, const void* v, float lambda,
+                               float eps, int32_t iters, float delta, void* out,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream);
+
 /* The landmark solve on its own: Y = A^{-1} W per head, A = k(L, L) + eps I
  * built as in lapattn_forward, by one of two solvers, for the comparison the
  * LaplacianFormer summaries draw between them (Arabic summary, section 4,

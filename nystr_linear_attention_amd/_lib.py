@@ -39,6 +39,7 @@ EXPORTS = ("lapattn_version", "lapattn_strerror", "lapattn_check",
            "lapattn_forward", "lapattn_forward_noalloc",
            "lapattn_backward_workspace_bytes", "lapattn_backward", "lapattn_landmark_solve",
            "lapattn_block_workspace_bytes", "lapattn_block_forward",
+           "lapattn_forward_normalized",
            "lapattn_forward_stages", "lapattn_set_stage_events", "lapattn_launches")
 
 STAGES = ("pool", "main", "maps", "out", "bwd_part", "bwd_head", "bwd_grad", "bwd_dk")
@@ -105,6 +106,8 @@ def _declare(lib):
     lib.lapattn_block_workspace_bytes.restype = sz
     lib.lapattn_block_forward.argtypes = [dp, i32, vp, vp, vp, vp, vp, f32, f32, i32, vp, vp, sz, vp]
     lib.lapattn_block_forward.restype = ctypes.c_int
+    lib.lapattn_forward_normalized.argtypes = [dp, vp, vp, vp, f32, f32, i32, f32, vp, vp, sz, vp]
+    lib.lapattn_forward_normalized.restype = ctypes.c_int
     lib.lapattn_forward_noalloc.argtypes = [dp, vp, vp, vp, f32, f32, i32, vp, vp, vp]
     lib.lapattn_forward_noalloc.restype = ctypes.c_int
     lib.lapattn_forward_stages.argtypes = [dp, vp, vp, vp, f32, f32, i32, vp, vp, sz, vp,

@@ -293,3 +293,29 @@ def block_forward(x: torch.Tensor, wq: torch.Tensor, wk: Optional[torch.Tensor],
         if cnt:
             raise _lib.LapattnTimeout(cnt)
     return y
+
+
+def forward_normalized(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, grid_h: int,
+                       grid_w: int, pool_h: int, pool_w: int, lam: float, eps: float,
+                       iters: int, delta: float, kernel: str = "laplacian",
+                       workspace: Optional[torch.Tensor] = None, stream=None,
+                       check: bool = True) -> torch.Tensor:
+    """O = Z (X (K_LK V)) with the normalised feature map Z of K_QL; see
+    include/lapattn.h."""
+    _check_io(q, k, v)
+    desc = _desc_for(q, grid_h, grid_w, pool_h, pool_w, kernel, False)
+    out = torch.empty_like(q)
+    if workspace is None:
+        workspace = alloc_workspace(desc, q.device)
+    else:
+        _check_workspace(workspace, desc, q.device)
+    st = _lib.lib().lapattn_forward_normalized(
+        ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(), lam, eps, iters, delta,
+        out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream_ptr(stream))
+    _lib.check(st)
+    if check:
+        with torch.cuda.stream(stream) if stream is not None else _nullctx():
+            n = status(desc, workspace)
+        if n:
+            raise _lib.LapattnTimeout(n)
+    return out

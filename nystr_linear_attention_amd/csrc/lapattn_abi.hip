@@ -168,6 +168,8 @@ Plan make_plan(const lapattn_desc_t* d) {
   off = align_up(off + BH * p.D * MP * f);
   p.off_yt = off;
   off = align_up(off + BH * p.D * MP * f);
+  p.off_mu = off;
+  off = align_up(off + BH * MP * f);
   p.off_sync = off;
   off = align_up(off + kSyncHead * (BH + 1) * sizeof(unsigned));
   p.total = off;
@@ -247,7 +249,9 @@ int run(const lapattn_desc_t* desc, const Args& args, void* workspace, size_t ws
         hipStream_t stream) {
   const Plan p = make_plan(desc);
   Args a = args;
-  a.out_in_main = out_in_main_launch(p, a.shared_qk) ? 1 : 0;
+  // the normalised map needs every query's K_QL before any output row: it
+  // always takes the output-launch plan
+  a.out_in_main = (!a.normalized && out_in_main_launch(p, a.shared_qk)) ? 1 : 0;
   if (misaligned16(a.q) || misaligned16(a.k) || misaligned16(a.v) || misaligned16(a.out))
     return LAPATTN_ERR_ALIGN;
   if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return LAPATTN_ERR_WORKSPACE;
@@ -271,6 +275,7 @@ int run(const lapattn_desc_t* desc, const Args& args, void* workspace, size_t ws
   b.x = reinterpret_cast<float*>(ws + p.off_x);
   b.wt = reinterpret_cast<float*>(ws + p.off_wt);
   b.yt = reinterpret_cast<float*>(ws + p.off_yt);
+  b.mu = reinterpret_cast<float*>(ws + p.off_mu);
   b.sync = reinterpret_cast<unsigned*>(ws + p.off_sync);
   b.timeouts = a.status ? a.status : b.sync;
 
@@ -287,6 +292,7 @@ int run(const lapattn_desc_t* desc, const Args& args, void* workspace, size_t ws
   // W = K_LK V, Y = X W and (when Q != K) the output rows are formed inside the
   // main launch; with Q == K there are no query workgroups and the output
   // product runs as its own launch.
+  if (a.normalized && launch_norm_stats(p, a, b, stream) != hipSuccess) return LAPATTN_ERR_HIP;
   if (!a.out_in_main && launch_out(p, a, b, stream, slot(LAPATTN_STAGE_OUT)) != hipSuccess)
     return LAPATTN_ERR_HIP;
   return LAPATTN_OK;
@@ -551,6 +557,31 @@ int lapattn_forward(const lapattn_desc_t* desc, const void* q, const void* k, co
   return lapattn::forward_common(desc, q, k, v, lambda, eps, iters, out, workspace,
                                  workspace_bytes, stream, nullptr, nullptr, nullptr, nullptr,
                                  nullptr, nullptr);
+}
+
+int lapattn_forward_normalized(const lapattn_desc_t* desc, const void* q, const void* k,
+                               const void* v, float lambda, float eps, int32_t iters, float delta,
+                               void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  using namespace lapattn;
+  int st = check_desc(desc);
+  if (st != LAPATTN_OK) return st;
+  st = check_params(lambda, eps, iters);
+  if (st != LAPATTN_OK) return st;
+  if (!std::isfinite(delta) || delta < 0.f) return LAPATTN_ERR_PARAM;
+  if (!q || !k || !v || !out || !workspace) return LAPATTN_ERR_NULL;
+  Args a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lambda = lambda;
+  a.eps = eps;
+  a.iters = iters;
+  a.shared_qk = (q == k) ? 1 : 0;
+  a.tickets = (desc->flags & LAPATTN_FLAG_TICKETS) ? 1 : 0;
+  a.normalized = 1;
+  a.delta = delta;
+  return run(desc, a, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 int lapattn_forward_noalloc(const lapattn_desc_t* desc, const void* q, const void* k,

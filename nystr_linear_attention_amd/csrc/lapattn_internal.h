@@ -38,7 +38,7 @@ struct Plan {
   int nP;       // key-side workgroups (= W partials) per head
   long resident;  // main-kernel workgroups resident at once on the device
   // workspace byte offsets
-  size_t off_L, off_kql, off_wpart, off_x, off_wt, off_yt, off_sync;
+  size_t off_L, off_kql, off_wpart, off_x, off_wt, off_yt, off_mu, off_sync;
   size_t total;
 };
 
@@ -49,6 +49,7 @@ struct Buffers {
   float* x;      // [BH][MP][MP]   Newton-Schulz result
   float* wt;     // [BH][D][MP]    W^T = (K_LK V)^T, zero for columns >= m
   float* yt;     // [BH][D][MP]    Y^T = (X W)^T
+  float* mu;     // [BH][MP]       column means of K_QL (normalised map only)
   unsigned* sync;  // [kSyncHead (BH + 1)] hand-off words (see the main kernel)
   unsigned* timeouts;  // the call's count of timed-out waits (word 0 of sync,
                        // or a word the caller owns)
@@ -66,6 +67,8 @@ struct Args {
   unsigned* status;  // where the timeout count goes (null: word 0 of the
                      // workspace's hand-off words)
   int tickets;       // main-launch roles by ticket (LAPATTN_FLAG_TICKETS)
+  int normalized;    // the normalised feature map in place of K_QL
+  float delta;       // its whitening stabiliser
   // optional fp32 stage copies (may be null)
   float* st_L;
   float* st_kql;
@@ -92,6 +95,9 @@ hipError_t launch_pool(const Plan& p, const Args& a, const Buffers& b, hipStream
 hipError_t launch_main(const Plan& p, const Args& a, const Buffers& b, bool with_solver,
                        bool with_maps, hipStream_t s, Ev ev);
 hipError_t launch_out(const Plan& p, const Args& a, const Buffers& b, hipStream_t s, Ev ev);
+// Normalised feature map: per head, the column means mu and variances of the
+// stored K_QL, and Y^T scaled in place by 1 / sqrt(var + delta) per column.
+hipError_t launch_norm_stats(const Plan& p, const Args& a, const Buffers& b, hipStream_t s);
 
 // Backward pass (lapattn_backward): launch plan and workspace layout.
 struct BwdPlan {

@@ -237,7 +237,8 @@ template <int D>
 __global__ __launch_bounds__(WGO) void out_kernel(const float* __restrict__ kql,
                                                   const float* __restrict__ yt,
                                                   void* __restrict__ O, int bf16, int N,
-                                                  int mpad, int nWo) {
+                                                  int mpad, int nWo,
+                                                  const float* __restrict__ mu) {
   constexpr int CBN = D / 16;
   __shared__ __attribute__((aligned(16))) uint16_t YH[D * WLD];
   __shared__ __attribute__((aligned(16))) uint16_t YL[D * WLD];
@@ -287,6 +288,18 @@ __global__ __launch_bounds__(WGO) void out_kernel(const float* __restrict__ kql,
   }
   __syncthreads();
   if (!active) return;
+  if (mu) {
+    // normalised map: K_QL centred per column (the column scales are in Y)
+    const float* mh = mu + static_cast<size_t>(bh) * MP;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int k = 32 * p + 8 * lg;
+      if (active && k < mpad) {
+        av[p][0] -= ld4(mh + k);
+        av[p][1] -= ld4(mh + k + 4);
+      }
+    }
+  }
   u32x4 kh[2], kl[2];
 #pragma unroll
   for (int p = 0; p < 2; ++p) split8h(av[p][0], av[p][1], 14, kh[p], kl[p]);
@@ -367,7 +380,62 @@ hipError_t launch_out_d(const Plan& p, const Args& a, const Buffers& b, hipStrea
   const int nWo = (p.nT + OUT_TILES - 1) / OUT_TILES;
   const dim3 grid(p.BH * nWo);
   return launch(out_kernel<D>, grid, dim3(WGO), s, ev, b.kql, b.yt, a.out, p.bf16, p.N, p.mpad,
-                nWo);
+                nWo, a.normalized ? static_cast<const float*>(b.mu) : nullptr);
+}
+
+// ---------------------------------------------------------------------------
+// Normalised feature map (LaplacianFormer summaries: Arabic summary, section
+// 2(b); Dutch summary, "Methodologie" item 1): Z = (K_QL - mu) / sqrt(var +
+// delta) per column, mu and var over the head's N queries.  One workgroup
+// per head reads the stored K_QL once: thread (column j, row group g) sums
+// k - s and (k - s)^2 over rows g, g + 8, ... with s = K_QL[0][j] (a shift
+// that keeps the variance free of cancellation), the 8 groups are added in
+// order; mu = s + S1 / N, var = S2 / N - (S1 / N)^2.  mu goes to the
+// workspace (the output launch centres K_QL with it) and Y^T's column j is
+// scaled by 1 / sqrt(var + delta), so O = (K_QL - mu) (Y / sqrt(var + delta))
+// = Z Y.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(WGM) void norm_stats_kernel(const float* __restrict__ kql, float* yt,
+                                                         float* mu, int N, int m, int mpad,
+                                                         float delta) {
+  __shared__ float s1[WGM], s2[WGM];
+  __shared__ float rs[MP];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const int j = tid % MP, g = tid / MP;  // 8 row groups
+  const float* kb = kql + static_cast<size_t>(bh) * N * mpad;
+  float a1 = 0.f, a2 = 0.f;
+  if (j < m) {
+    const float sh = kb[j];
+    for (int i = g; i < N; i += WGM / MP) {
+      const float t = kb[static_cast<size_t>(i) * mpad + j] - sh;
+      a1 += t;
+      a2 = fmaf(t, t, a2);
+    }
+  }
+  s1[tid] = a1;
+  s2[tid] = a2;
+  __syncthreads();
+  if (tid < MP) {
+    float t1 = 0.f, t2 = 0.f;
+    for (int u = 0; u < WGM / MP; ++u) {
+      t1 += s1[u * MP + tid];
+      t2 += s2[u * MP + tid];
+    }
+    float mean = 0.f, r = 0.f;
+    if (tid < m) {
+      const float inv = 1.0f / static_cast<float>(N);
+      const float d1 = t1 * inv;
+      const float var = fmaxf(t2 * inv - d1 * d1, 0.f);
+      mean = kb[tid] + d1;
+      r = 1.0f / sqrtf(var + delta);
+    }
+    mu[static_cast<size_t>(bh) * MP + tid] = mean;
+    rs[tid] = r;
+  }
+  __syncthreads();
+  float* y = yt + static_cast<size_t>(bh) * D * MP;
+  for (int e = tid; e < D * MP; e += WGM) y[e] *= rs[e % MP];
 }
 
 }  // namespace
@@ -434,6 +502,15 @@ hipError_t launch_main(const Plan& p, const Args& a, const Buffers& b, bool with
     case 16: return launch_main_d<16>(p, ma, grid, s, ev);
     case 32: return launch_main_d<32>(p, ma, grid, s, ev);
     case 64: return launch_main_d<64>(p, ma, grid, s, ev);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_norm_stats(const Plan& p, const Args& a, const Buffers& b, hipStream_t s) {
+  switch (p.D) {
+    case 16: return launch(norm_stats_kernel<16>, dim3(p.BH), dim3(WGM), s, Ev{}, b.kql, b.yt, b.mu, p.N, p.m, p.mpad, a.delta);
+    case 32: return launch(norm_stats_kernel<32>, dim3(p.BH), dim3(WGM), s, Ev{}, b.kql, b.yt, b.mu, p.N, p.m, p.mpad, a.delta);
+    case 64: return launch(norm_stats_kernel<64>, dim3(p.BH), dim3(WGM), s, Ev{}, b.kql, b.yt, b.mu, p.N, p.m, p.mpad, a.delta);
   }
   return hipErrorInvalidValue;
 }

@@ -180,3 +180,44 @@ def full_kernel_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     Used only as a sanity reference for approximation quality.
     """
     return kernel_map(q, k, lam, kernel) @ v
+
+
+def normalized_feature_map(kql: np.ndarray, delta: float) -> np.ndarray:
+    """Z = (K_QL - mu) / sqrt(var + delta), per column j (landmark): mu_j and
+    var_j the mean and the population variance of column j over the queries.
+
+    LaplacianFormer summaries (Arabic summary, section 2(b); Dutch summary,
+    "Methodologie" item 1): each query's similarity vector is centred and
+    whitened, the covariance's inverse square root replaced by a diagonal
+    estimator that normalises each feature dimension on its own across the
+    batch of queries.  Reading: the similarity vector of query i is row i of
+    K_QL (its kernel values against the landmarks); the batch is the head's
+    N queries; delta is the whitening's stabiliser (not printed on the pages).
+    """
+    mu = kql.mean(axis=0)
+    var = ((kql - mu) ** 2).mean(axis=0)
+    return (kql - mu) / np.sqrt(var + delta)
+
+
+def nystrom_head_normalized(q, k, v, *, grid_h, grid_w, pool_h, pool_w, lam, eps,
+                            iters, delta, kernel=LAPLACIAN):
+    """One head with the normalised feature map in place of K_QL:
+    O = Z (X (K_LK V)), Z = normalized_feature_map(K_QL, delta)."""
+    res = nystrom_head(q, k, v, grid_h=grid_h, grid_w=grid_w, pool_h=pool_h,
+                       pool_w=pool_w, lam=lam, eps=eps, iters=iters, kernel=kernel)
+    Z = normalized_feature_map(res["KQL"], delta)
+    res["Z"] = Z
+    res["O"] = Z @ res["Y"]
+    return res
+
+
+def forward_normalized(q, k, v, *, grid_h, grid_w, pool_h, pool_w, lam, eps, iters,
+                       delta, kernel=LAPLACIAN, dtype="f32", heads=None):
+    """forward() with the normalised feature map; returns {(b, h): O}."""
+    B, H = q.shape[0], q.shape[1]
+    if heads is None:
+        heads = [(b, h) for b in range(B) for h in range(H)]
+    return {(b, h): nystrom_head_normalized(
+        widen(q[b, h], dtype), widen(k[b, h], dtype), widen(v[b, h], dtype),
+        grid_h=grid_h, grid_w=grid_w, pool_h=pool_h, pool_w=pool_w, lam=lam, eps=eps,
+        iters=iters, delta=delta, kernel=kernel)["O"] for (b, h) in heads}
