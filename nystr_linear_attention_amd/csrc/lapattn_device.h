@@ -1248,33 +1248,31 @@ __device__ void reduce_w_lines(const MainArgs& a, int bh, int l0, int l1, float*
 // scalar loads, since the rows are no longer 16-byte aligned.
 __device__ __forceinline__ int ptj(int tok, int j) { return tok * LS + j + ((tok >> 3) & 3); }
 
-// Stores output block (tokens 16 tb + 4 g + i, columns 16 cb + lr) of tile t
-// from accumulator c (lane (g, lr)), fp32 or bf16 (round to nearest even).
-template <int D>
-// fp32 O rows are written with streaming (non-temporal) stores: nothing in
-// the launch reads them again, and the end-of-kernel write-back of O is
-// shorter (about 0.5 us of a 35 us forward on 8 heads of 3136 tokens).  bf16
-// rows keep ordinary stores: 2-byte streaming stores made the output launch
-// slower (15 -> 19 us for 160 heads of 784 tokens).
-__device__ __forceinline__ void store_o_block(const MainArgs& a, int bh, int t, int tb, int cb, f4 c) {
-  const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int n = t * TILE + 16 * tb + 4 * lg + i;
-    if (n < a.N) {
-      const size_t o = (static_cast<size_t>(bh) * a.N + n) * D + 16 * cb + lr;
-      if (a.bf16) static_cast<uint16_t*>(a.out)[o] = f32_to_bf16_rne(c[i]);
-      else __builtin_nontemporal_store(c[i], static_cast<float*>(a.out) + o);
-    }
+// Four consecutive output columns of one token at element offset o: one
+// 16-byte streaming store (fp32) or one 8-byte store (bf16, round to nearest
+// even).  fp32 O rows are written with streaming (non-temporal) stores:
+// nothing in the launch reads them again, and the end-of-kernel write-back of
+// O is shorter.
+__device__ __forceinline__ void store_o4(void* out, int bf16, size_t o, f4 v) {
+  if (bf16) {
+    const uint2 u = {static_cast<uint32_t>(f32_to_bf16_rne(v[0])) |
+                         (static_cast<uint32_t>(f32_to_bf16_rne(v[1])) << 16),
+                     static_cast<uint32_t>(f32_to_bf16_rne(v[2])) |
+                         (static_cast<uint32_t>(f32_to_bf16_rne(v[3])) << 16)};
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + o) = u;
+  } else {
+    __builtin_nontemporal_store(v, reinterpret_cast<f4*>(static_cast<float*>(out) + o));
   }
 }
 
 // O rows of one 64-token tile: K_QL tile (PT, LDS, zero beyond m) times Y on
 // fp16 MFMA, with Y^T split in LDS (row c scaled by 2^(EW[c] + ex - 22),
 // y_in_lds) and the tile's K_QL rows scaled by 2^14 and split here, once per
-// tile.  Wave w: tokens 16 (w % 4) .. +15; waves 0-3 take the first half of
-// the column blocks, waves 4-7 the second, so that each 128-byte line of an O
-// row is written by one wave (whole lines leave L2 under streaming stores).
+// tile.  Each product forms a block of O^T (Y^T rows as the first operand),
+// so that lane (g, r) holds four consecutive columns 16 cb + 4 g .. + 3 of
+// token 16 tb + r: one 16-byte store.  Wave w: tokens 16 (w % 4) .. +15;
+// waves 0-3 take the first half of the column blocks, waves 4-7 the second,
+// so that each 128-byte line of an O row is written by one wave.
 template <int D>
 __device__ void out_tile(const MainArgs& a, int bh, int t, const float* PT, const float* Q, int ex) {
   using QG = QGeom<D>;
@@ -1302,14 +1300,16 @@ __device__ void out_tile(const MainArgs& a, int bh, int t, const float* PT, cons
       const int o = (16 * cb + lr) * WLD + 32 * p + 8 * lg;
       const u32x4 yh = *reinterpret_cast<const u32x4*>(YH + o);
       const u32x4 yl = *reinterpret_cast<const u32x4*>(YL + o);
-      c = mfma_h(kh[p], yh, c);
-      c = mfma_h(kl[p], yh, c);
-      c = mfma_h(kh[p], yl, c);
+      c = mfma_h(yh, kh[p], c);
+      c = mfma_h(yh, kl[p], c);
+      c = mfma_h(yl, kh[p], c);
     }
-    const int sc = 8 - ex - EW[16 * cb + lr];  // 22 - 14 - (EW + ex)
+    // lane (g, lr): O[token 16 tb + lr][16 cb + 4 g + i]; scale
+    // 2^(22 - 14 - (EW + ex)) per column
 #pragma unroll
-    for (int i = 0; i < 4; ++i) c[i] = ldexpf(c[i], sc);
-    store_o_block<D>(a, bh, t, tb, cb, c);
+    for (int i = 0; i < 4; ++i) c[i] = ldexpf(c[i], 8 - ex - EW[16 * cb + 4 * lg + i]);
+    const int n = t * TILE + 16 * tb + lr;
+    if (n < a.N) store_o4(a.out, a.bf16, (static_cast<size_t>(bh) * a.N + n) * D + 16 * cb + 4 * lg, c);
   }
 }
 

@@ -311,21 +311,16 @@ __global__ __launch_bounds__(WGO) void out_kernel(const float* __restrict__ kql,
       const int o = (16 * cb + lr) * WLD + 32 * p + 8 * lg;
       const u32x4 yh = *reinterpret_cast<const u32x4*>(YH + o);
       const u32x4 yl = *reinterpret_cast<const u32x4*>(YL + o);
-      c = mfma_h(kh[p], yh, c);
-      c = mfma_h(kl[p], yh, c);
-      c = mfma_h(kh[p], yl, c);
+      c = mfma_h(yh, kh[p], c);
+      c = mfma_h(yh, kl[p], c);
+      c = mfma_h(yl, kh[p], c);
     }
-    const int sc = -14 - EW[16 * cb + lr];
+    // a block of O^T: lane (g, lr) holds columns 16 cb + 4 g .. + 3 of token
+    // n0 + lr
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int n = n0 + 4 * lg + i;
-      if (n < N) {
-        const size_t o = (static_cast<size_t>(bh) * N + n) * D + 16 * cb + lr;
-        const float val = ldexpf(c[i], sc);
-        if (bf16) static_cast<uint16_t*>(O)[o] = f32_to_bf16_rne(val);
-        else __builtin_nontemporal_store(val, static_cast<float*>(O) + o);  // as store_o_block
-      }
-    }
+    for (int i = 0; i < 4; ++i) c[i] = ldexpf(c[i], -14 - EW[16 * cb + 4 * lg + i]);
+    const int n = n0 + lr;
+    if (n < N) store_o4(O, bf16, (static_cast<size_t>(bh) * N + n) * D + 16 * cb + 4 * lg, c);
   }
 }
 
