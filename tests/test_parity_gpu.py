@@ -59,6 +59,15 @@ SMALL = [
     wl.small_case(12, 16, 32, 2, 2, B=2, eps=0.0),                # no diagonal perturbation (kernel matrix alone is PD)
     wl.small_case(8, 12, 64, 2, 2, B=2, iters=1),                 # a single Newton-Schulz step
     wl.small_case(20, 20, 32, 4, 4, B=300),                       # output launch of 600 workgroups, ragged last tile
+    # m = 16 k + 1: Newton-Schulz on a 16 k interior plus a border row / column
+    wl.small_case(17, 8, 32, 1, 8, B=2),                          # m=17, ragged tiles
+    wl.small_case(6, 22, 32, 2, 2, H=2),                          # m=33
+    wl.small_case(14, 14, 16, 2, 2),                              # m=49, d=16
+    wl.small_case(14, 14, 32, 2, 2, iters=0),                     # m=49, no steps (X_0 with its border)
+    wl.small_case(14, 14, 32, 2, 2, iters=1),                     # m=49, one step
+    wl.small_case(14, 14, 64, 2, 2, kernel=wl.GAUSSIAN, shared_qk=True, B=2),  # m=49, output launch
+    wl.small_case(14, 14, 32, 2, 2, B=150),                       # m=49, grid not resident
+    wl.small_case(17, 4, 64, 1, 4, eps=1e-5, iters=30),           # m=17, nearly singular A
 ]
 
 
@@ -74,7 +83,10 @@ STAGE_CASES = [wl.WORKLOADS[0], wl.small_case(10, 14, 32, 2, 2, B=2, H=1),
                wl.small_case(12, 20, 32, 3, 4, kernel=wl.GAUSSIAN),
                wl.small_case(8, 8, 64, 1, 1),
                wl.small_case(64, 128, 64, 16, 16),
-               wl.small_case(7, 7, 32, 1, 1, B=64)]
+               wl.small_case(7, 7, 32, 1, 1, B=64),
+               wl.small_case(17, 8, 32, 1, 8, B=2),                # border: m = 17, 33, 49
+               wl.small_case(6, 22, 32, 2, 2),
+               wl.small_case(14, 14, 64, 2, 2, iters=7)]
 
 
 @pytest.mark.parametrize("w", STAGE_CASES, ids=[w.name for w in STAGE_CASES])
