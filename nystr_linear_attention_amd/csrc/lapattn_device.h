@@ -199,7 +199,8 @@ struct MainArgs {
 // Words of head bh (kSyncHead from kSyncHead (bh + 1), each group on its own
 // cache lines): [0, 128) key ready flags, [128, 160) W^T slice flags, [192]
 // X ready (its value carries the scale exponent of the published X), [224]
-// key arrivals, [225] arrivals of W and X, [226] Y ready.
+// key arrivals, [225] arrivals of W and X, [226] Y ready, [227] chunks of
+// the normalised map's statistics (a later launch).
 // Flags are plain device-scope stores (no read-modify-write on a shared word,
 // which serialises at memory when many workgroups arrive at once).
 //
@@ -232,6 +233,8 @@ __device__ __forceinline__ unsigned* flag_x(const MainArgs& a, int bh) { return 
 __device__ __forceinline__ unsigned* cnt_w(const MainArgs& a, int bh) { return head_sync(a, bh) + 224; }
 __device__ __forceinline__ unsigned* cnt_y(const MainArgs& a, int bh) { return head_sync(a, bh) + 225; }
 __device__ __forceinline__ unsigned* flag_y(const MainArgs& a, int bh) { return head_sync(a, bh) + 226; }
+// word of head bh counting the chunks of the normalised map's statistics
+constexpr int kNormCount = 227;
 
 __device__ __forceinline__ void st_dev(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

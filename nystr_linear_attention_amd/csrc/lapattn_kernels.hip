@@ -33,6 +33,8 @@
 // Device code shared with the backward pass (solver and map roles, helpers)
 // is in lapattn_device.h.
 
+#include <algorithm>
+
 #include "lapattn_device.h"
 
 namespace lapattn {
@@ -381,41 +383,69 @@ hipError_t launch_out_d(const Plan& p, const Args& a, const Buffers& b, hipStrea
 // ---------------------------------------------------------------------------
 // Normalised feature map (LaplacianFormer summaries: Arabic summary, section
 // 2(b); Dutch summary, "Methodologie" item 1): Z = (K_QL - mu) / sqrt(var +
-// delta) per column, mu and var over the head's N queries.  One workgroup
-// per head reads the stored K_QL once: thread (column j, row group g) sums
-// k - s and (k - s)^2 over rows g, g + 8, ... with s = K_QL[0][j] (a shift
-// that keeps the variance free of cancellation), the 8 groups are added in
-// order; mu = s + S1 / N, var = S2 / N - (S1 / N)^2.  mu goes to the
-// workspace (the output launch centres K_QL with it) and Y^T's column j is
-// scaled by 1 / sqrt(var + delta), so O = (K_QL - mu) (Y / sqrt(var + delta))
-// = Z Y.
+// delta) per column, mu and var over the head's N queries.  Workgroup (head,
+// chunk c) reads rows [c R, (c + 1) R) of the stored K_QL: thread (column j,
+// row group g) sums k - s and (k - s)^2 over rows g, g + 8, ... of the chunk
+// (8 loads in flight) with s = K_QL[0][j] (a shift that keeps the variance
+// free of cancellation); the 8 groups are added in order and the chunk's
+// sums published; the last chunk of the head to arrive adds the chunks' sums
+// in chunk order (so the result does not depend on timing): mu = s + S1 / N,
+// var = S2 / N - (S1 / N)^2.  mu goes to the workspace (the output launch
+// centres K_QL with it) and Y^T's column j is scaled by 1 / sqrt(var +
+// delta), so O = (K_QL - mu) (Y / sqrt(var + delta)) = Z Y.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(WGM) void norm_stats_kernel(const float* __restrict__ kql, float* yt,
-                                                         float* mu, int N, int m, int mpad,
+                                                         float* mu, float* part, unsigned* sync,
+                                                         int N, int m, int mpad, int R,
                                                          float delta) {
+  constexpr int G = WGM / MP;  // row groups
+  constexpr int U = 8;         // loads in flight per thread
   __shared__ float s1[WGM], s2[WGM];
   __shared__ float rs[MP];
-  const int bh = blockIdx.x, tid = threadIdx.x;
-  const int j = tid % MP, g = tid / MP;  // 8 row groups
+  const int bh = blockIdx.x, c = blockIdx.y, nc = gridDim.y, tid = threadIdx.x;
+  const int j = tid % MP, g = tid / MP;
   const float* kb = kql + static_cast<size_t>(bh) * N * mpad;
+  const int r0 = c * R, r1 = min(N, r0 + R);
   float a1 = 0.f, a2 = 0.f;
   if (j < m) {
     const float sh = kb[j];
-    for (int i = g; i < N; i += WGM / MP) {
-      const float t = kb[static_cast<size_t>(i) * mpad + j] - sh;
-      a1 += t;
-      a2 = fmaf(t, t, a2);
+    for (int i0 = r0 + g; i0 < r1; i0 += U * G) {
+      float v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * G;
+        v[u] = i < r1 ? kb[static_cast<size_t>(i) * mpad + j] - sh : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        a1 += v[u];
+        a2 = fmaf(v[u], v[u], a2);
+      }
     }
   }
   s1[tid] = a1;
   s2[tid] = a2;
   __syncthreads();
+  // this chunk's sums, published for the head's last chunk
+  float* pc = part + (static_cast<size_t>(bh) * nc + c) * 2 * MP;
   if (tid < MP) {
     float t1 = 0.f, t2 = 0.f;
-    for (int u = 0; u < WGM / MP; ++u) {
+    for (int u = 0; u < G; ++u) {
       t1 += s1[u * MP + tid];
       t2 += s2[u * MP + tid];
+    }
+    st_dev(pc + tid, t1);
+    st_dev(pc + MP + tid, t2);
+  }
+  unsigned* cnt = sync + kSyncHead * (bh + 1) + kNormCount;
+  if (publish_arrive(cnt) != static_cast<unsigned>(nc - 1)) return;
+  if (tid < MP) {
+    const float* ph = part + static_cast<size_t>(bh) * nc * 2 * MP;
+    float t1 = 0.f, t2 = 0.f;
+    for (int u = 0; u < nc; ++u) {
+      t1 += ph[u * 2 * MP + tid];
+      t2 += ph[u * 2 * MP + MP + tid];
     }
     float mean = 0.f, r = 0.f;
     if (tid < m) {
@@ -502,13 +532,23 @@ hipError_t launch_main(const Plan& p, const Args& a, const Buffers& b, bool with
 }
 
 hipError_t launch_norm_stats(const Plan& p, const Args& a, const Buffers& b, hipStream_t s) {
+  // chunks of rows per head: enough workgroups to spread over the device, at
+  // least 64 rows each, and their sums (2 MP floats per chunk) within the W^T
+  // partials buffer, which the output-launch plan has consumed by now
+  const int want = std::max(1, std::min((p.N + 63) / 64, (512 + p.BH - 1) / p.BH));
+  const int cap = std::max(1, p.nP * p.D / 2);
+  const int nc0 = std::min(want, cap);
+  const int R = (p.N + nc0 - 1) / nc0;
+  const int nc = (p.N + R - 1) / R;
+  const dim3 grid(p.BH, nc);
   switch (p.D) {
-    case 16: return launch(norm_stats_kernel<16>, dim3(p.BH), dim3(WGM), s, Ev{}, b.kql, b.yt, b.mu, p.N, p.m, p.mpad, a.delta);
-    case 32: return launch(norm_stats_kernel<32>, dim3(p.BH), dim3(WGM), s, Ev{}, b.kql, b.yt, b.mu, p.N, p.m, p.mpad, a.delta);
-    case 64: return launch(norm_stats_kernel<64>, dim3(p.BH), dim3(WGM), s, Ev{}, b.kql, b.yt, b.mu, p.N, p.m, p.mpad, a.delta);
+    case 16: return launch(norm_stats_kernel<16>, grid, dim3(WGM), s, Ev{}, b.kql, b.yt, b.mu, b.wpart, b.sync, p.N, p.m, p.mpad, R, a.delta);
+    case 32: return launch(norm_stats_kernel<32>, grid, dim3(WGM), s, Ev{}, b.kql, b.yt, b.mu, b.wpart, b.sync, p.N, p.m, p.mpad, R, a.delta);
+    case 64: return launch(norm_stats_kernel<64>, grid, dim3(WGM), s, Ev{}, b.kql, b.yt, b.mu, b.wpart, b.sync, p.N, p.m, p.mpad, R, a.delta);
   }
   return hipErrorInvalidValue;
 }
+
 
 hipError_t launch_out(const Plan& p, const Args& a, const Buffers& b, hipStream_t s, Ev ev) {
   switch (p.D) {
