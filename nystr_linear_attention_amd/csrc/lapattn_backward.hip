@@ -129,7 +129,7 @@ __global__ __launch_bounds__(WGM, 4) void bwd_part_kernel(MainArgs a, const void
                                                         const void* __restrict__ dout,
                                                         const float* __restrict__ L, float* dypart,
                                                         float* xiter, float* amat, float* hscal) {
-  constexpr int MAP_SMEM = map_pj_size<D>() + 2 * MP * LS + TILE;
+  constexpr int MAP_SMEM = map_smem<D, KIND>();
   constexpr int SOLVER_SMEM = NsGeom<MB, D>::SMEM;
   __shared__ __attribute__((aligned(16)))
   float smem[MAP_SMEM > SOLVER_SMEM ? MAP_SMEM : SOLVER_SMEM];

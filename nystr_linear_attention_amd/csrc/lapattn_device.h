@@ -73,34 +73,6 @@ __device__ __forceinline__ float load1_io(const void* base, size_t idx, int bf16
   return static_cast<const float*>(base)[idx];
 }
 
-// One token row of D elements into registers.
-template <int D>
-__device__ __forceinline__ void load_row(const void* base, size_t row, int bf16, float* x) {
-  if (bf16) {
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + row * D);
-#pragma unroll
-    for (int i = 0; i < D / 8; ++i) {
-      const uint4 u = p[i];
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        x[8 * i + 2 * h] = __uint_as_float(w[h] << 16);
-        x[8 * i + 2 * h + 1] = __uint_as_float(w[h] & 0xffff0000u);
-      }
-    }
-  } else {
-    const f4* p = reinterpret_cast<const f4*>(static_cast<const float*>(base) + row * D);
-#pragma unroll
-    for (int i = 0; i < D / 4; ++i) {
-      const f4 u = p[i];
-      x[4 * i] = u[0];
-      x[4 * i + 1] = u[1];
-      x[4 * i + 2] = u[2];
-      x[4 * i + 3] = u[3];
-    }
-  }
-}
-
 // Distances of a register-resident point to two wave-uniform points l0, l1
 // (scalar loads issued together, so their latencies overlap).  Holding more
 // landmark coordinates in flight than this spills scalar registers.
@@ -1128,6 +1100,19 @@ constexpr int map_pj_size() {
   return MP * LS > QGeom<D>::SIZE ? MP * LS : QGeom<D>::SIZE;
 }
 
+// Row stride (floats) of the Laplacian tiles' staged token rows: 16-byte
+// reads of one row per lane fall on distinct banks for D = 16, 32, 64.
+template <int D>
+constexpr int row_stride() { return D + 4; }
+
+// Floats of LDS the map role uses: P, the token-major K_QL rows, V^T (or the
+// query workgroups' second K_QL tile), the Gaussian tiles' squared norms and
+// the Laplacian tiles' staged token rows.
+template <int D, int KIND>
+constexpr int map_smem() {
+  return map_pj_size<D>() + 2 * MP * LS + TILE + (KIND == 0 ? TILE * row_stride<D>() : 0);
+}
+
 // Y^T = W^T X^T in place: the split, row-scaled W^T in LDS (row c scaled by
 // 2^EW[c]) is replaced by the split Y^T with the same row scales times
 // 2^(ex - 22); X comes split from global memory (hi then lo, rows of MP
@@ -1404,6 +1389,7 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
   float* PT = smem + PJS;                // [64 tokens][LS]:    P[j] of token at [token][j]
   float* VT = smem + PJS + MP * LS;      // [D][LS]:            V[token][c] at [c][token]
   float* xx = smem + PJS + 2 * MP * LS;  // [64]: squared norms of a tile's tokens (Gaussian)
+  float* XR = xx + TILE;                 // [64 tokens][XS]: token rows (Laplacian)
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int lr = lane & 15, lg = lane >> 4;
   const int m = a.m, N = a.N;
@@ -1430,14 +1416,6 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
   const int mby = (m + 15) >> 4;
   const int nwb = CBN * mby;  // W output blocks
 
-  // padding rows / columns j in [m, 64) stay zero for the whole workgroup
-  for (int e = tid; e < MP * LS; e += WGM) {
-    PJ[e] = 0.f;
-    PT[e] = 0.f;
-    if (!key_role) VT[e] = 0.f;
-  }
-  __syncthreads();
-
   const int jb = (w * m) / NGRP, je = ((w + 1) * m) / NGRP;
   const float* Lh = Lw + static_cast<size_t>(bh) * m * D;
   f4 wacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
@@ -1447,9 +1425,7 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
   // one in-order counter, so loads issued after a tile's stores would wait
   // for them too, and the load latency now overlaps the rest of the tile.
   // Gaussian tiles load the next tile's token operand (D/4 floats per lane)
-  // at the same point.  (Laplacian token rows, D floats per lane, stay loaded
-  // at the start of their tile: held across the products they cost more in
-  // register pressure than they save.)
+  // at the same point, and Laplacian tiles the runs of their token rows.
   const int vc = tid % D, vtg = tid / D;
   constexpr int TPT = TILE * D / WGM;
   float vv[TPT];
@@ -1465,17 +1441,74 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
     }
   };
   float ga[KIND == 1 ? D / 4 : 1];
+
+  // Laplacian token rows pass through LDS: thread i < 8 D loads the i-th run
+  // of 8 elements of the tile (16-byte loads, consecutive threads on
+  // consecutive addresses), and every wave then reads one row per lane from
+  // LDS.  Read straight from global memory, each of the 8 waves fetched all
+  // 64 rows with one cache line per lane and load.  The next tile's runs are
+  // loaded after this tile's distances and stored after its products.
+  constexpr int XS = row_stride<D>();
+  const bool row_thread = KIND == 0 && tid < TILE * D / 8;
+  const int rtok = tid / (D / 8), rcol = 8 * (tid % (D / 8));
+  f4 rf0, rf1;  // fp32 rows: the run
+  u32x4 rbv;    // bf16 rows: the run, widened when stored
+  auto fetch_rows = [&](int t) {
+    if (row_thread) {
+      const int nt = t * TILE + rtok;
+      const size_t e = (static_cast<size_t>(bh) * N + (nt < N ? nt : N - 1)) * D + rcol;
+      if constexpr (BF16) {
+        rbv = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(src) + e);
+      } else {
+        const f4* p = reinterpret_cast<const f4*>(static_cast<const float*>(src) + e);
+        rf0 = p[0];
+        rf1 = p[1];
+      }
+    }
+  };
+  auto stage_rows = [&]() {
+    if (row_thread) {
+      float* dst = XR + rtok * XS + rcol;
+      if constexpr (BF16) {
+        st4(dst, f4{__uint_as_float(rbv[0] << 16), __uint_as_float(rbv[0] & 0xffff0000u),
+                    __uint_as_float(rbv[1] << 16), __uint_as_float(rbv[1] & 0xffff0000u)});
+        st4(dst + 4, f4{__uint_as_float(rbv[2] << 16), __uint_as_float(rbv[2] & 0xffff0000u),
+                        __uint_as_float(rbv[3] << 16), __uint_as_float(rbv[3] & 0xffff0000u)});
+      } else {
+        st4(dst, rf0);
+        st4(dst + 4, rf1);
+      }
+    }
+  };
   if (t_beg < t_end) {
     load_v(t_beg);
     if constexpr (KIND == 1) gauss_rows<D, BF16>(a, src, bh, t_beg, ga);
+    if constexpr (KIND == 0) fetch_rows(t_beg);
   }
+  // padding rows / columns j in [m, 64) stay zero for the whole workgroup
+  for (int e = tid; e < MP * LS; e += WGM) {
+    PJ[e] = 0.f;
+    PT[e] = 0.f;
+    if (!key_role) VT[e] = 0.f;
+  }
+  if (KIND == 0 && t_beg < t_end) stage_rows();
+  __syncthreads();
 
   for (int t = t_beg; t < t_end; ++t) {
     float* PTt = (key_role || t == t_beg) ? PT : VT;  // this tile's K_QL rows
     const int n = t * TILE + lane;
     const bool valid = n < N;
     float x[KIND == 0 ? D : 1];
-    if constexpr (KIND == 0) load_row<D>(src, static_cast<size_t>(bh) * N + (valid ? n : N - 1), BF16, x);
+    if constexpr (KIND == 0) {
+#pragma unroll
+      for (int i = 0; i < D / 4; ++i) {
+        const f4 u = ld4(XR + lane * XS + 4 * i);
+        x[4 * i] = u[0];
+        x[4 * i + 1] = u[1];
+        x[4 * i + 2] = u[2];
+        x[4 * i + 3] = u[3];
+      }
+    }
     if (key_role) {
       // V tile -> VT[c][token] (VT is free: the previous tile's products
       // finished before the barrier that ended its iteration)
@@ -1514,6 +1547,7 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
     if (t + 1 < t_end) {
       load_v(t + 1);
       if constexpr (KIND == 1) gauss_rows<D, BF16>(a, src, bh, t + 1, ga);
+      if constexpr (KIND == 0) fetch_rows(t + 1);
     }
     __syncthreads();
     if (store_kql) {
@@ -1562,6 +1596,8 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
         }
       }
     }
+    // every wave read this tile's rows before the barrier above
+    if (KIND == 0 && t + 1 < t_end) stage_rows();
     __syncthreads();
   }
   if (!key_role) {

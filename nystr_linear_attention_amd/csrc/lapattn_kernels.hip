@@ -135,7 +135,7 @@ __global__ __launch_bounds__(WGM, 4) void main_kernel(MainArgs a, const void* __
                                                     const void* __restrict__ k,
                                                     const void* __restrict__ v,
                                                     const float* __restrict__ L) {
-  constexpr int MAP_SMEM = map_pj_size<D>() + 2 * MP * LS + TILE;
+  constexpr int MAP_SMEM = map_smem<D, KIND>();
   // solver: the Newton-Schulz arrays plus a W^T copy (landmarks while A is
   // built)
   constexpr int SOLVER_SMEM = NsGeom<MB, D>::SMEM;
