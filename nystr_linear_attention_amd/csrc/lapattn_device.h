@@ -391,6 +391,26 @@ __device__ __forceinline__ void split2(float x0, float x1, unsigned& hi, unsigne
   lo = __builtin_bit_cast(unsigned, __builtin_convertvector(f2{r0, r1}, h2));
 }
 
+// split2 with the remainders formed in fp32 by mixed-precision FMAs,
+// r = fma(x, one, -hi) with hi in fp16 (exact, as x - hi is), then one
+// packed conversion: the same bits as split2 in 4 instructions instead of
+// 6.  `one` must be 1.0 in a register (a literal lets the compiler fold the
+// FMA back into a conversion and a subtraction).
+__device__ __forceinline__ void split2_mix(float x0, float x1, float one, unsigned& hi, unsigned& lo) {
+  const h2 h = __builtin_convertvector(f2{x0, x1}, h2);
+  const float r0 = __builtin_fmaf(x0, one, -static_cast<float>(h[0]));
+  const float r1 = __builtin_fmaf(x1, one, -static_cast<float>(h[1]));
+  hi = __builtin_bit_cast(unsigned, h);
+  lo = __builtin_bit_cast(unsigned, __builtin_convertvector(f2{r0, r1}, h2));
+}
+
+// 1.0 in a register the compiler cannot see through (for split2_mix).
+__device__ __forceinline__ float opaque_one() {
+  float one = 1.0f;
+  asm("" : "+v"(one));
+  return one;
+}
+
 // Sum over the 4 lanes (g = 0..3) that share lr, on VALU: a lane-half swap
 // with itself leaves v[l] + v[l ^ 32] as the sum of the two results (and
 // likewise for 16-lane rows).
@@ -551,6 +571,17 @@ __device__ __forceinline__ void load_xop(float* smem, int offh, int offl, int r0
   }
 }
 
+// split_block with split2_mix.
+__device__ __forceinline__ void split_block_mix(f4 x, int i, float one, u32x4* h, u32x4* l) {
+  unsigned h0, l0, h1, l1;
+  split2_mix(x[0], x[1], one, h0, l0);
+  split2_mix(x[2], x[3], one, h1, l1);
+  h[i >> 1][2 * (i & 1)] = h0;
+  h[i >> 1][2 * (i & 1) + 1] = h1;
+  l[i >> 1][2 * (i & 1)] = l0;
+  l[i >> 1][2 * (i & 1) + 1] = l1;
+}
+
 // Splits accumulator block i into the B operand registers of its chunk.
 __device__ __forceinline__ void split_block(f4 x, int i, u32x4* h, u32x4* l) {
   unsigned h0, l0, h1, l1;
@@ -594,6 +625,7 @@ __device__ __forceinline__ void ns_wave(const MainArgs& a, float* smem, int c, i
   __syncthreads();  // the fp32 A (in the parity-1 X halves) is dead from here
 
   int ep = e0, ec = e0;  // scale exponents of X_{t-1} and X_t
+  const float one = opaque_one();
   // A step is 2 MB blocks: q < MB is phase-1 block q (operand: rows 16 q ..
   // of A), q >= MB is phase-2 block q - MB (operand: rows of X_t).  Operands
   // go through a ring of 3 register slots, read 2 blocks ahead; the reads of
@@ -625,6 +657,7 @@ __device__ __forceinline__ void ns_wave(const MainArgs& a, float* smem, int c, i
     for (int q = NPRE; q < 2; ++q) load_block(q, xoh, xol, bh[q], bl[q]);
 
     const int sT = 14 - eA - ec;  // T-hat = 2^sT (A-hat X-hat_t)
+
     u32x4 th[NC], tl[NC];
 #pragma unroll
     for (int p = 0; p < NC; ++p) th[p] = tl[p] = u32x4{0u, 0u, 0u, 0u};
@@ -672,7 +705,7 @@ __device__ __forceinline__ void ns_wave(const MainArgs& a, float* smem, int c, i
         f4 tv;
 #pragma unroll
         for (int j = 0; j < 4; ++j) tv[j] = ldexpf(acc[j], sT);
-        split_block(tv, ip, th, tl);
+        split_block_mix(tv, ip, one, th, tl);
         if (ip == MB - 1) {
           // scale of X_{t+1}: max|X_{t-1}| 2^eN < 2^7 (the last X stays at
           // 2^ec); X-hat_{t+1} = 2^(eN - ec + 1) X-hat_t
@@ -696,7 +729,7 @@ __device__ __forceinline__ void ns_wave(const MainArgs& a, float* smem, int c, i
           for (int j = 0; j < 4; ++j) dst[(16 * ip + 4 * lg + j) * MP + col] = ldexpf(xs[ip][j], -eN);
         }
         if (!LAST) {
-          split_block(xs[ip], ip, xh, xl);
+          split_block_mix(xs[ip], ip, one, xh, xl);
           // rows 16 ip + 4 g .. + 3 of line col: one 8-byte store per part
           const int o = col * XSH + 4 * xchunk(col, 4 * ip + lg);
           *reinterpret_cast<u32x2*>(H + o) =
