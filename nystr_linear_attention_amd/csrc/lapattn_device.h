@@ -694,13 +694,14 @@ __device__ __forceinline__ void ns_wave(const MainArgs& a, float* smem, int c, i
         const int ip = q;
         if (!LAST && ip == 0) {
           // publish max|X-hat_t| of the own columns (units 2^ec), one copy per
-          // lane; magnitudes compare as unsigned bit patterns
-          unsigned mx = 0u;
+          // lane (across lanes, the non-negative maxima compare as unsigned
+          // bit patterns)
+          float mx = 0.f;
 #pragma unroll
           for (int i = 0; i < MB; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) mx = max(mx, __float_as_uint(xs[i][j]) & 0x7fffffffu);
-          slot[256 * cb + 64 * c + lane] = __uint_as_float(wave_max_u(mx));
+            for (int j = 0; j < 4; ++j) mx = fmaxf(mx, fabsf(xs[i][j]));
+          slot[256 * cb + 64 * c + lane] = __uint_as_float(wave_max_u(__float_as_uint(mx)));
         }
         f4 tv;
 #pragma unroll
@@ -794,7 +795,14 @@ __device__ __forceinline__ void ns_wave(const MainArgs& a, float* smem, int c, i
     }
   };
 
-  for (int t = 0; t + 1 < iters; ++t) step(t, std::false_type{});
+  // two steps per loop iteration: the registers carried from step to step
+  // then need no copies at the back edge (about 20 moves per step otherwise)
+  int t = 0;
+  for (; t + 2 < iters; t += 2) {
+    step(t, std::false_type{});
+    step(t + 1, std::false_type{});
+  }
+  if (t + 1 < iters) step(t, std::false_type{});
   if (iters > 0) step(iters - 1, std::true_type{});
   // the final iterate's scale: max|X| 2^ec < 2^15
   if (c == 0 && lane == 0) smem[G::OFF_RED + 3] = __int_as_float(ec);
