@@ -1552,11 +1552,20 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
     }
     if (key_role) {
       // V tile -> VT[c][token] (VT is free: the previous tile's products
-      // finished before the barrier that ended its iteration)
+      // finished before the barrier that ended its iteration).  A thread's
+      // TPT consecutive tokens of column c go out as 16-byte stores: lanes
+      // c = 0..15 of a store then cover all banks (single stores put lanes
+      // c and c + 16 on one bank).
+      float vz[TPT];
 #pragma unroll
-      for (int u = 0; u < TPT; ++u) {
-        const int tok = vtg * TPT + u;
-        VT[vc * LS + tok] = t * TILE + tok < N ? vv[u] : 0.f;
+      for (int u = 0; u < TPT; ++u) vz[u] = t * TILE + vtg * TPT + u < N ? vv[u] : 0.f;
+      float* vdst = VT + vc * LS + vtg * TPT;
+      if constexpr (TPT % 4 == 0) {
+#pragma unroll
+        for (int u = 0; u < TPT; u += 4) st4(vdst + u, f4{vz[u], vz[u + 1], vz[u + 2], vz[u + 3]});
+      } else {
+#pragma unroll
+        for (int u = 0; u < TPT; ++u) vdst[u] = vz[u];
       }
     }
     if constexpr (KIND == 0) {
