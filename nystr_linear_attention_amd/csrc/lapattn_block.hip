@@ -12,7 +12,8 @@
 //         [B, H, N, d] while the tiles load
 //
 // One GEMM kernel for both: 64 x 64 output tiles, 4 waves of 32 x 32, the
-// contraction in chunks of 32 staged in LDS as fp32 rows of both operands,
+// contraction in chunks of 32 staged in LDS as fp32 rows of both operands
+// (the next chunk's loads in flight during the current chunk's products),
 // fp32 MFMA (16x16x4, k = 8 g + s for lane group g at sub-step s), fp32
 // accumulation; bf16 operands are widened exactly, bf16 outputs rounded to
 // nearest even.
@@ -73,42 +74,52 @@ __global__ __launch_bounds__(WGP) void proj_kernel(ProjArgs p) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
 
-  // thread's slots of a chunk: A rows ar (8 consecutive k at ak), B row bk
-  // (8 consecutive columns at bc)
+  // thread's slots of a chunk: A row ar (8 consecutive k at ak); B row bk of
+  // the chunk (8 consecutive columns at bc; consecutive lanes take
+  // consecutive k, so the transposed LDS stores fall on distinct banks)
   const int ar = tid >> 2, ak = 8 * (tid & 3);
-  const int bk = tid >> 3, bc = 8 * (tid & 7);
-  for (int k0 = 0; k0 < p.Kd; k0 += GK) {
-    float va[8], vb[8];
-    {
-      const int row = r0 + ar, k = k0 + ak;
-      if (row < p.M) {
-        size_t idx;
-        if constexpr (MODE == 0) {
-          idx = static_cast<size_t>(row) * p.Kd + k;
-        } else {
-          // row = b N + n, k = h d + c  ->  O[b][h][n][c]
-          const int b = row / p.N, n = row % p.N, h = k / p.d, c = k % p.d;
-          idx = ((static_cast<size_t>(b) * p.H + h) * p.N + n) * p.d + c;
-        }
-        load8(p.a, idx, p.bf16, va);
+  const int bk = tid & 31, bc = 8 * (tid >> 5);
+  const int arow = r0 + ar, bcol = c0 + bc;
+  // MODE 1: the A row is token (b, n) of the heads' layout
+  size_t abase = 0;
+  if constexpr (MODE == 1) {
+    const int b = arow / p.N, n = arow % p.N;
+    abase = (static_cast<size_t>(b) * p.H * p.N + n) * p.d;
+  }
+  float va[8], vb[8];
+  auto fetch = [&](int k0) {
+    if (arow < p.M) {
+      size_t idx;
+      if constexpr (MODE == 0) {
+        idx = static_cast<size_t>(arow) * p.Kd + k0 + ak;
       } else {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) va[u] = 0.f;
+        // k = h d + c  ->  O[b][h][n][c]
+        const int k = k0 + ak, h = k / p.d, c = k - h * p.d;
+        idx = abase + static_cast<size_t>(h) * p.N * p.d + c;
       }
-      const int col = c0 + bc;
-      if (col < p.Nc) {
-        load8(w, static_cast<size_t>(k0 + bk) * p.Nc + col, p.bf16, vb);
-      } else {
+      load8(p.a, idx, p.bf16, va);
+    } else {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) vb[u] = 0.f;
-      }
+      for (int u = 0; u < 8; ++u) va[u] = 0.f;
     }
+    if (bcol < p.Nc) {
+      load8(w, static_cast<size_t>(k0 + bk) * p.Nc + bcol, p.bf16, vb);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) vb[u] = 0.f;
+    }
+  };
+  // software pipeline: the next chunk's loads are in flight during this
+  // chunk's products
+  fetch(0);
+  for (int k0 = 0; k0 < p.Kd; k0 += GK) {
     __syncthreads();  // the previous chunk's products are done with As, Bs
     st4(As + ar * GS + ak, f4{va[0], va[1], va[2], va[3]});
     st4(As + ar * GS + ak + 4, f4{va[4], va[5], va[6], va[7]});
 #pragma unroll
     for (int u = 0; u < 8; ++u) Bs[(bc + u) * GS + bk] = vb[u];
     __syncthreads();
+    if (k0 + GK < p.Kd) fetch(k0 + GK);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const float* ap = As + (wr + 16 * i + lr) * GS + 8 * lg;
@@ -126,22 +137,45 @@ __global__ __launch_bounds__(WGP) void proj_kernel(ProjArgs p) {
       }
     }
   }
-  // accumulator of block (i, j): element (wr + 16 i + 4 lg + e, wc + 16 j + lr)
+  // accumulator of block (i, j): element (wr + 16 i + 4 lg + e, wc + 16 j + lr).
+  // Output offsets separate into a row part and a column part: MODE 0,
+  // ((b H + h) N + n) d + c = (b H N + n) d + h N d + c; MODE 1, row Nc + col.
+  // One division per distinct row and column of the lane.
+  size_t roff[2][4];
+  size_t coff[2];
+  bool rin[2][4], cin[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = r0 + wr + 16 * i + 4 * lg + e;
+      rin[i][e] = row < p.M;
+      if constexpr (MODE == 0) {
+        const int b = row / p.N, n = row - b * p.N;
+        roff[i][e] = (static_cast<size_t>(b) * p.H * p.N + n) * p.d;
+      } else {
+        roff[i][e] = static_cast<size_t>(row) * p.Nc;
+      }
+    }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int col = c0 + wc + 16 * j + lr;
+    cin[j] = col < p.Nc;
+    if constexpr (MODE == 0) {
+      const int h = col / p.d, c = col - h * p.d;
+      coff[j] = static_cast<size_t>(h) * p.N * p.d + c;
+    } else {
+      coff[j] = col;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int row = r0 + wr + 16 * i + 4 * lg + e, col = c0 + wc + 16 * j + lr;
-        if (row >= p.M || col >= p.Nc) continue;
-        size_t o;
-        if constexpr (MODE == 0) {
-          const int b = row / p.N, n = row % p.N, h = col / p.d, c = col % p.d;
-          o = ((static_cast<size_t>(b) * p.H + h) * p.N + n) * p.d + c;
-        } else {
-          o = static_cast<size_t>(row) * p.Nc + col;
-        }
+        if (!rin[i][e] || !cin[j]) continue;
+        const size_t o = roff[i][e] + coff[j];
         const float v = acc[i][j][e];
         if (p.bf16) static_cast<uint16_t*>(out)[o] = f32_to_bf16_rne(v);
         else static_cast<float*>(out)[o] = v;
