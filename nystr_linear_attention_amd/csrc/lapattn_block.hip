@@ -59,8 +59,11 @@ __device__ __forceinline__ void load8(const void* base, size_t idx, int bf16, fl
 
 template <int MODE>
 __global__ __launch_bounds__(WGP) void proj_kernel(ProjArgs p) {
-  __shared__ __attribute__((aligned(16))) float As[GT * GS];  // [row][k]
-  __shared__ __attribute__((aligned(16))) float Bs[GT * GS];  // [col][k]
+  constexpr int OS = GT + 4;  // row stride of the staged output tile
+  static_assert(GT * OS <= 2 * GT * GS, "output tile fits the operand arrays");
+  __shared__ __attribute__((aligned(16))) float smem[2 * GT * GS];
+  float* As = smem;            // [row][k]
+  float* Bs = smem + GT * GS;  // [col][k]
   const int z = blockIdx.z;
   const void* w = p.w[z];
   void* out = p.out[z];
@@ -137,49 +140,51 @@ __global__ __launch_bounds__(WGP) void proj_kernel(ProjArgs p) {
       }
     }
   }
-  // accumulator of block (i, j): element (wr + 16 i + 4 lg + e, wc + 16 j + lr).
-  // Output offsets separate into a row part and a column part: MODE 0,
-  // ((b H + h) N + n) d + c = (b H N + n) d + h N d + c; MODE 1, row Nc + col.
-  // One division per distinct row and column of the lane.
-  size_t roff[2][4];
-  size_t coff[2];
-  bool rin[2][4], cin[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = r0 + wr + 16 * i + 4 * lg + e;
-      rin[i][e] = row < p.M;
-      if constexpr (MODE == 0) {
-        const int b = row / p.N, n = row - b * p.N;
-        roff[i][e] = (static_cast<size_t>(b) * p.H * p.N + n) * p.d;
-      } else {
-        roff[i][e] = static_cast<size_t>(row) * p.Nc;
-      }
-    }
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int col = c0 + wc + 16 * j + lr;
-    cin[j] = col < p.Nc;
-    if constexpr (MODE == 0) {
-      const int h = col / p.d, c = col - h * p.d;
-      coff[j] = static_cast<size_t>(h) * p.N * p.d + c;
-    } else {
-      coff[j] = col;
-    }
-  }
+  // The tile goes through LDS so that every row leaves as whole 16-byte
+  // chunks (4 consecutive columns, in one head for MODE 0 since 4 divides d).
+  // accumulator of block (i, j): element (wr + 16 i + 4 lg + e, wc + 16 j + lr)
+  __syncthreads();  // every wave is done with As, Bs
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (!rin[i][e] || !cin[j]) continue;
-        const size_t o = roff[i][e] + coff[j];
-        const float v = acc[i][j][e];
-        if (p.bf16) static_cast<uint16_t*>(out)[o] = f32_to_bf16_rne(v);
-        else static_cast<float*>(out)[o] = v;
-      }
+      for (int e = 0; e < 4; ++e) smem[(wr + 16 * i + 4 * lg + e) * OS + wc + 16 * j + lr] = acc[i][j][e];
+  __syncthreads();
+  // thread: chunk c4 = tid % 16 of rows tid / 16 + 16 q.  Output offsets
+  // separate into a row part and a column part: MODE 0,
+  // ((b H + h) N + n) d + c = (b H N + n) d + h N d + c; MODE 1, row Nc + col.
+  const int c4 = tid & 15;
+  const int col = c0 + 4 * c4;
+  size_t coff;
+  if constexpr (MODE == 0) {
+    const int h = col / p.d, c = col - h * p.d;
+    coff = static_cast<size_t>(h) * p.N * p.d + c;
+  } else {
+    coff = col;
+  }
+#pragma unroll
+  for (int q = 0; q < GT / 16; ++q) {
+    const int rl = (tid >> 4) + 16 * q, row = r0 + rl;
+    if (row >= p.M || col >= p.Nc) continue;
+    size_t roff;
+    if constexpr (MODE == 0) {
+      const int b = row / p.N, n = row - b * p.N;
+      roff = (static_cast<size_t>(b) * p.H * p.N + n) * p.d;
+    } else {
+      roff = static_cast<size_t>(row) * p.Nc;
+    }
+    // Nc is a multiple of 32 (checked at the entry point): whole chunks
+    const f4 v = ld4(smem + rl * OS + 4 * c4);
+    const size_t o = roff + coff;
+    if (p.bf16) {
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + o) =
+          uint2{static_cast<unsigned>(f32_to_bf16_rne(v[0])) | (static_cast<unsigned>(f32_to_bf16_rne(v[1])) << 16),
+                static_cast<unsigned>(f32_to_bf16_rne(v[2])) | (static_cast<unsigned>(f32_to_bf16_rne(v[3])) << 16)};
+    } else {
+      st4(static_cast<float*>(out) + o, v);
+    }
+  }
 }
 
 }  // namespace
