@@ -141,14 +141,23 @@ Plan make_plan(const lapattn_desc_t* d) {
   {
     const long nQ = (p.nT + kQueryTiles - 1) / kQueryTiles;
     const long nP = (p.nT + p.S - 1) / p.S;
+    p.qt = kQueryTiles;
     if (static_cast<long>(p.BH) * (1 + nP + nQ) > p.resident) {
+      bool one_round = false;
       for (int S = p.S + 1; S <= kMaxKeyTilesOut; ++S) {
         const long nPS = (p.nT + S - 1) / S;
         if (static_cast<long>(p.BH) * (1 + nPS) <= p.resident) {
           p.S = S;
+          one_round = true;
           break;
         }
       }
+      // Rounds either way: 2 key tiles and 4 query tiles per workgroup
+      // amortise each workgroup's fixed latency and still balance (160 heads
+      // of 784 bf16 tokens: main launch 104 -> 91 us; 1 / 2, 3 / 2, 7 / 7
+      // and 13 / 13 tiles were slower)
+      if (!one_round) p.S = p.S > 2 ? p.S : 2;
+      p.qt = kQueryTilesOut;
     }
   }
   p.nP = (p.nT + p.S - 1) / p.S;

@@ -146,7 +146,9 @@ struct MainArgs {
   int tickets;        // roles come from per-queue tickets (else workgroup b
                       // of a solver-only launch solves head b)
   int nq;             // ticket queues (8 when 8 divides BH, else min(BH, 8))
-  int nQ;             // query workgroups per head, QT tiles each (0 when Q == K)
+  int nQ;             // query workgroups per head, qt tiles each (0 when Q == K)
+  int qt;             // tiles per query workgroup (QT when the output rows are
+                      // formed here, which keeps the K_QL rows in LDS)
   int shared_qk;      // Q and K are the same tensor
   int out_in_main;    // query workgroups wait for Y and write O (else they
                       // store K_QL and the output launch forms O)
@@ -1436,10 +1438,12 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
     t_beg = unit * a.S;
     t_end = min(t_beg + a.S, a.nT);
   } else {
-    // QT tiles per query workgroup (their K_QL rows stay in LDS until Y is
-    // ready, in PT and in the V^T area, which query tiles do not use)
-    t_beg = QT * unit;
-    t_end = min(t_beg + QT, a.nT);
+    // qt tiles per query workgroup.  When they form their output rows here
+    // (qt = QT), the K_QL rows stay in LDS until Y is ready, in PT and in the
+    // V^T area, which query tiles do not use; otherwise every tile's rows are
+    // stored before the next tile reuses the V^T area.
+    t_beg = a.qt * unit;
+    t_end = min(t_beg + a.qt, a.nT);
   }
   // K_QL goes to global memory only when Q == K (the output launch reads
   // it); query tiles keep theirs in LDS and form their output rows here.
@@ -1650,7 +1654,7 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
     if (!a.out_in_main) return;  // K_QL stored; the output launch forms O
     // Query workgroup u < R reduces its slice of W^T once every key
     // workgroup of the head has published its partial.
-    const int u = t_beg / QT;
+    const int u = unit;
     constexpr int LINES = D * MP / 32;  // cache lines of W^T
     const int R = a.nQ < 32 ? a.nQ : 32;
     const int lps = (LINES + R - 1) / R;

@@ -12,8 +12,12 @@ namespace lapattn {
 constexpr int MP = 64;
 // Hand-off words per head (and once more for the words of the whole call).
 constexpr int kSyncHead = 256;
-// 64-token tiles per query workgroup.
+// 64-token tiles per query workgroup when it forms its output rows in the
+// main launch (their K_QL rows stay in LDS).
 constexpr int kQueryTiles = 2;
+// Query tiles per workgroup when the grid cannot be resident at once (the
+// output-launch plan stores K_QL, so a workgroup can take more tiles).
+constexpr int kQueryTilesOut = 4;
 // Tiles per key workgroup at most when the output-launch plan lengthens key
 // workgroups so that they are all resident at once.
 constexpr int kMaxKeyTilesOut = 4;
@@ -35,6 +39,8 @@ struct Plan {
   int ns_mb;    // 16x16 MFMA blocks per side in the solver interior
   int nT;       // 64-token tiles per head
   int S;        // tiles per key-side workgroup
+  int qt;       // tiles per query workgroup when K_QL is stored (output-launch
+                // plan); the main launch's output rows take kQueryTiles
   int nP;       // key-side workgroups (= W partials) per head
   long resident;  // main-kernel workgroups resident at once on the device
   // workspace byte offsets

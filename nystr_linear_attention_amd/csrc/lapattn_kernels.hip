@@ -509,7 +509,8 @@ hipError_t launch_main(const Plan& p, const Args& a, const Buffers& b, bool with
   ma.mpad = p.mpad;
   ma.shared_qk = a.shared_qk;
   ma.out_in_main = a.out_in_main;
-  ma.nQ = a.shared_qk ? 0 : (p.nT + QT - 1) / QT;
+  ma.qt = a.out_in_main ? QT : p.qt;
+  ma.nQ = a.shared_qk ? 0 : (p.nT + ma.qt - 1) / ma.qt;
   ma.kind = p.kernel;
   ma.bf16 = p.bf16;
   ma.iters = a.iters;
