@@ -226,8 +226,6 @@ BwdPlan make_bwd_plan(const lapattn_desc_t* d, int32_t iters) {
   off = align_up(off + BH * MP * p.D * f);
   p.off_dxmat = off;
   off = align_up(off + BH * MP * MP * f);
-  p.off_dla = off;
-  off = align_up(off + BH * MP * p.D * f);
   p.off_dlpart = off;
   off = align_up(off + BH * 2 * p.nT * MP * p.D * f);
   p.off_dkd = off;

@@ -31,14 +31,16 @@
 //         (K_QL dO, the same path with Q for K and dO for V)
 //   head  one workgroup per head: W, dY (partials summed in order); Y = X W,
 //         dW = X^T dY, dX = dY W^T
-//   grad  Newton-Schulz backward workgroups (one per head, fp32 MFMA in LDS,
-//         then dA and dL from A) beside one workgroup per 64-token tile of Q
+//   grad  Newton-Schulz backward workgroups (one per head, split fp16
+//         operands on fp16 MFMA in LDS, then dA and dd = -dA k(L, L) /
+//         lambda) beside one workgroup per 64-token tile of Q
 //         or K: the kernel map again, dK_QL = dO Y^T (or dK_LK^T = V dW^T)
 //         on fp32 MFMA, the gradient map on FP32 VALU (dQ or the direct dK
 //         rows, and the tile's dL partial), and for key tiles dV = K_LK^T dW;
 //         the two roles do not wait for each other
-//   dk    one workgroup per landmark window: dL = its partials in fixed order,
-//         dK rows of the window = direct part + dL / (ph pw)
+//   dk    one workgroup per landmark window: dL = its part from A (from dd)
+//         and its tile partials in fixed order, dK rows of the window =
+//         direct part + dL / (ph pw)
 // Every reduction runs in a fixed order, so results do not depend on timing.
 
 #include "lapattn_device.h"
@@ -64,8 +66,9 @@ struct BwdArgs {
   const float* dypart; // [BH][nP][D][MP]      dY^T partials
   float* ymat;         // [BH][MP][D]          Y = X W (rows >= m zero)
   float* dwmat;        // [BH][MP][D]          dW = X^T dY (rows >= m zero)
-  float* dxmat;        // [BH][MP][MP]         dX = dY W^T (rows, columns >= m zero)
-  float* dla;          // [BH][MP][D]          dL from A (rows >= m zero)
+  float* dxmat;        // [BH][MP][MP]         dX = dY W^T (rows, columns >= m zero);
+                       //                      then dd = -dA k(L, L) / lambda (from the
+                       //                      Newton-Schulz backward, for dk)
   float* dlpart;       // [BH][2 nT][MP][D]    dL partials of the gradient tiles
   float* dkd;          // [BH][N][D]           direct part of dK
   int N, m, BH, nT, nP, gw, ph, pw, iters, kind, bf16;
@@ -292,136 +295,290 @@ __global__ __launch_bounds__(WGM) void bwd_heada_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int WGG = 256;
 
-// One 16 x 16 block of sum over k < 64 of A[i][k] B^T[j][k], both operands
-// rows of 64 floats in LDS (row stride BS): lane (g, r) reads 16 consecutive
-// k = 16 g .. 16 g + 15 of row 16 bi + r of A and row 16 bj + r of B^T.
-__device__ __forceinline__ f4 rows_mm(const float* A, const float* BT, int bi, int bj, f4 c) {
+// Operands of the Newton-Schulz backward products: a 64 x 64 matrix M as
+// fp16 hi and lo parts of 2^s M (s keeps the magnitudes below 2^15), rows of
+// HSH halves; the 16-byte reads of 16 consecutive rows fall on distinct
+// banks.
+constexpr int HSH = 72;
+constexpr int HMAT = MP * HSH / 2;  // floats per part
+constexpr int NSB_HALVES = 14;      // A, X, X^T, G, G^T, Q1, P1: hi and lo
+constexpr int NSB_SLOTS = NSB_HALVES * HMAT;
+constexpr int NSB_SMEM = NSB_SLOTS + 16;
+static_assert(NSB_SLOTS >= 7 * MP * BS + 8, "the fp32 matrices of the last part fit");
+
+// Split operand rows 16 b + r (lane (g, r)), halves 32 p + 8 g .. + 7 of
+// both chunks, and the 6 MFMAs of one block of sum over k < 64 of
+// A[i][k] B^T[j][k] from the rows of A and of B^T (hi hi + lo hi + hi lo on
+// fp16 MFMA).
+struct HOp {
+  u32x4 h[2], l[2];
+};
+__device__ __forceinline__ HOp load_hop(const uint16_t* H, const uint16_t* L, int b) {
   const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
-  const float* ap = A + (16 * bi + lr) * BS + 16 * lg;
-  const float* bp = BT + (16 * bj + lr) * BS + 16 * lg;
-  f4 av[4], bv[4];
+  const int o = (16 * b + lr) * HSH + 8 * lg;
+  HOp r;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    av[q] = ld4(ap + 4 * q);
-    bv[q] = ld4(bp + 4 * q);
+  for (int p = 0; p < 2; ++p) {
+    r.h[p] = *reinterpret_cast<const u32x4*>(H + o + 32 * p);
+    r.l[p] = *reinterpret_cast<const u32x4*>(L + o + 32 * p);
   }
+  return r;
+}
+__device__ __forceinline__ f4 mm_hop(const HOp& a, const HOp& b, f4 c) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-#pragma unroll
-    for (int h = 0; h < 4; ++h) c = mfma4(av[q][h], bv[q][h], c);
+  for (int p = 0; p < 2; ++p) {
+    c = mfma_h(a.h[p], b.h[p], c);
+    c = mfma_h(a.l[p], b.h[p], c);
+    c = mfma_h(a.h[p], b.l[p], c);
+  }
   return c;
 }
 
-// Writes block (bi, bj) of accumulator c to M (row-major) and, with MT, its
-// transpose.
-__device__ __forceinline__ void put_block(float* M, float* MT, int bi, int bj, f4 c) {
+// Block (bi, bj) of accumulator c, times the power of two sc, split into
+// the half matrices (H, L) and, with HT, into the transposed ones too.
+__device__ __forceinline__ void put_block_h(uint16_t* H, uint16_t* L, uint16_t* HT, uint16_t* LT, int bi, int bj,
+                                            f4 c, float sc, float one) {
   const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  unsigned h01, l01, h23, l23;
+  split2_mix(c[0] * sc, c[1] * sc, one, h01, l01);
+  split2_mix(c[2] * sc, c[3] * sc, one, h23, l23);
+  const unsigned hv[4] = {h01 & 0xffffu, h01 >> 16, h23 & 0xffffu, h23 >> 16};
+  const unsigned lv[4] = {l01 & 0xffffu, l01 >> 16, l23 & 0xffffu, l23 >> 16};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = 16 * bi + 4 * lg + i, col = 16 * bj + lr;
-    M[r * BS + col] = c[i];
-    if (MT) MT[col * BS + r] = c[i];
+    const int o = (16 * bi + 4 * lg + i) * HSH + 16 * bj + lr;
+    H[o] = static_cast<uint16_t>(hv[i]);
+    L[o] = static_cast<uint16_t>(lv[i]);
+  }
+  if (HT) {
+    // row 16 bj + r, columns 16 bi + 4 g .. + 3: one 8-byte store per part
+    const int o = (16 * bj + lr) * HSH + 16 * bi + 4 * lg;
+    *reinterpret_cast<u32x2*>(HT + o) = u32x2{h01, h23};
+    *reinterpret_cast<u32x2*>(LT + o) = u32x2{l01, l23};
   }
 }
 
-constexpr int NSB_SMEM = 7 * MP * BS + 8;
+// Four consecutive elements (row r, columns 4 c4 ..) of a matrix, times sc,
+// split into the half matrices (H, L) and the transposed ones (HT, LT).
+__device__ __forceinline__ void put_row4_h(uint16_t* H, uint16_t* L, uint16_t* HT, uint16_t* LT, int r, int c4,
+                                           f4 v, float sc, float one) {
+  unsigned h01, l01, h23, l23;
+  split2_mix(v[0] * sc, v[1] * sc, one, h01, l01);
+  split2_mix(v[2] * sc, v[3] * sc, one, h23, l23);
+  const int o = r * HSH + 4 * c4;
+  *reinterpret_cast<u32x2*>(H + o) = u32x2{h01, h23};
+  *reinterpret_cast<u32x2*>(L + o) = u32x2{l01, l23};
+  if (HT) {
+    const unsigned hv[4] = {h01 & 0xffffu, h01 >> 16, h23 & 0xffffu, h23 >> 16};
+    const unsigned lv[4] = {l01 & 0xffffu, l01 >> 16, l23 & 0xffffu, l23 >> 16};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ot = (4 * c4 + i) * HSH + r;
+      HT[ot] = static_cast<uint16_t>(hv[i]);
+      LT[ot] = static_cast<uint16_t>(lv[i]);
+    }
+  }
+}
+
+// Scale exponent of a matrix with maximum mx for nsb_role: fp16_scale, at
+// most 40.  G shrinks by orders of magnitude per step once the forward has
+// converged (its step map is flat at the fixed point); the cap keeps every
+// scale and its inverse finite, and a G that small adds nothing measurable.
+__device__ __forceinline__ int nsb_scale(float mx) {
+  const int s = fp16_scale(mx);
+  return s < 40 ? s : 40;
+}
+
+// Maximum of non-negative v over the 4 waves of the workgroup: each wave's
+// maximum goes to slot[w]; every thread reads the four after the next
+// barrier (max4_slots).
+__device__ __forceinline__ void wave_max_to_slot(float* slot, float v) {
+  v = __uint_as_float(wave_max_u(__float_as_uint(v)));
+  if ((threadIdx.x & 63) == 0) slot[wave_id()] = v;
+}
+__device__ __forceinline__ float max4_slots(const float* slot) {
+  const f4 v = ld4(slot);
+  return fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+}
 
 // Newton-Schulz backward of one head (4 waves).  LDS holds A, X_t and X_t^T,
-// G and G^T, Q1 = A X_t and P1 = X_t^T G, so that every product reads rows
-// of both operands.  Wave w owns the blocks w, w + 4, w + 8, w + 12 of dA
-// (kept in registers across the steps) and of the new G.  X_{t-1} is read
-// from global memory during step t.
+// G and G^T, Q1 = A X_t and P1 = X_t^T G as split fp16 operands, so that
+// every product reads rows of both operands on fp16 MFMA (three products
+// per contraction chunk, about 22 significant bits, as in the forward).
+// Scales: A, X_t and G by their maxima (nsb_scale), Q1 and P1 by 2^-22 of
+// their products' scales (every term of a product is below 2^30 and there
+// are 64, so the accumulator is below 2^36).  Wave w owns the blocks w,
+// w + 4, w + 8, w + 12 of dA and of G (fp32, in registers across the
+// steps).  X_{t-1} is read from global memory during step t.
 template <int D, int KIND>
 __device__ void nsb_role(const BwdArgs& a, int bh, float* sm) {
   float* MA = sm;
-  float* MX = sm + MP * BS;
-  float* MXT = sm + 2 * MP * BS;
   float* MG = sm + 3 * MP * BS;
-  float* MGT = sm + 4 * MP * BS;
-  float* MQ = sm + 5 * MP * BS;
-  float* MP1 = sm + 6 * MP * BS;
   float* red = sm + 7 * MP * BS;
   const int tid = threadIdx.x, w = wave_id();
   const int m = a.m, T = a.iters;
   const float* xi = a.xiter + static_cast<size_t>(bh) * (T + 1) * MP * MP;
-  constexpr int PER = MP * MP / WGG;  // elements per thread of a 64 x 64 matrix
-  // A, G = dX and X_{T-1} (or nothing to do when T == 0) into LDS
+  // A, G = dX and X_{T-1} (or nothing to do when T == 0): their maxima,
+  // then their split parts into LDS; G of the own blocks into registers
+  uint16_t* hbase = reinterpret_cast<uint16_t*>(sm);
+  auto half = [&](int k) { return hbase + static_cast<size_t>(k) * HMAT * 2; };
+  uint16_t *AH = half(0), *AL = half(1), *XH = half(2), *XL = half(3), *XTH = half(4), *XTL = half(5);
+  uint16_t *GH = half(6), *GL = half(7), *GTH = half(8), *GTL = half(9), *QH = half(10), *QL = half(11);
+  uint16_t *PH = half(12), *PL = half(13);
+  float* slot = sm + NSB_SLOTS;  // [3][4]: maxima of A (or G'), X, G
+  const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const float one = opaque_one();
+  constexpr int R4 = MP * MP / 4 / WGG;  // rows-of-4 per thread of a 64 x 64 matrix
+  f4 av[R4], gv4[R4], xv[R4];
   {
     const float* ag = a.amat + static_cast<size_t>(bh) * MP * MP;
     const float* dg = a.dxmat + static_cast<size_t>(bh) * MP * MP;
     const float* xg = xi + static_cast<size_t>(T > 0 ? T - 1 : 0) * MP * MP;
+    float ma = 0.f, mg = 0.f, mx = 0.f;
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int e = tid + WGG * u, r = e / MP, c = e % MP;
-      const bool in = r < m && c < m;
-      MA[r * BS + c] = ag[e];
-      const float gv = dg[e];
-      MG[r * BS + c] = gv;
-      MGT[c * BS + r] = gv;
-      const float xv = in ? xg[e] : 0.f;
-      MX[r * BS + c] = xv;
-      MXT[c * BS + r] = xv;
+    for (int u = 0; u < R4; ++u) {
+      const int e4 = tid + WGG * u, r = e4 / 16, c4 = e4 % 16;
+      av[u] = ld4(ag + r * MP + 4 * c4);
+      gv4[u] = ld4(dg + r * MP + 4 * c4);
+      const f4 x = ld4(xg + r * MP + 4 * c4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xv[u][i] = (r < m && 4 * c4 + i < m) ? x[i] : 0.f;
+        ma = fmaxf(ma, fabsf(av[u][i]));
+        mg = fmaxf(mg, fabsf(gv4[u][i]));
+        mx = fmaxf(mx, fabsf(xv[u][i]));
+      }
     }
+    wave_max_to_slot(slot, ma);
+    wave_max_to_slot(slot + 4, mx);
+    wave_max_to_slot(slot + 8, mg);
+  }
+  f4 g[4];
+  {
+    const float* dg = a.dxmat + static_cast<size_t>(bh) * MP * MP;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int blk = w + 4 * s, bi = blk >> 2, bj = blk & 3;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) g[s][i] = dg[(16 * bi + 4 * lg + i) * MP + 16 * bj + lr];
+    }
+  }
+  __syncthreads();
+  const int sA = nsb_scale(max4_slots(slot));
+  int sX = nsb_scale(max4_slots(slot + 4));
+  int sG = nsb_scale(max4_slots(slot + 8));
+#pragma unroll
+  for (int u = 0; u < R4; ++u) {
+    const int e4 = tid + WGG * u, r = e4 / 16, c4 = e4 % 16;
+    put_row4_h(AH, AL, nullptr, nullptr, r, c4, av[u], ldexpf(1.0f, sA), one);
+    put_row4_h(GH, GL, GTH, GTL, r, c4, gv4[u], ldexpf(1.0f, sG), one);
+    put_row4_h(XH, XL, XTH, XTL, r, c4, xv[u], ldexpf(1.0f, sX), one);
   }
   __syncthreads();
   f4 da[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) da[s] = f4{0.f, 0.f, 0.f, 0.f};
-  for (int t = T - 1; t >= 0; --t) {
-    // X_{t-1} for the next step, read now (consumed after the step's last
-    // barrier)
-    float nx[PER];
-    if (t > 0) {
-      const float* xg = xi + static_cast<size_t>(t - 1) * MP * MP;
+  // X_{t-1} is consumed in step t (after its second barrier) and read two
+  // steps ahead: nx holds X_{t-1}, nn receives X_{t-2}
+  auto read_x = [&](int i, f4 (&dst)[R4]) {
+    const float* xg = xi + static_cast<size_t>(i) * MP * MP;
 #pragma unroll
-      for (int u = 0; u < PER; ++u) {
-        const int e = tid + WGG * u, r = e / MP, c = e % MP;
-        nx[u] = (r < m && c < m) ? xg[e] : 0.f;
-      }
+    for (int u = 0; u < R4; ++u) {
+      const int e4 = tid + WGG * u, r = e4 / 16, c4 = e4 % 16;
+      dst[u] = ld4(xg + r * MP + 4 * c4);
     }
+  };
+  f4 nx[R4], nn[R4];
+  if (T >= 2) read_x(T - 2, nx);
+  for (int t = T - 1; t >= 0; --t) {
+    if (t >= 2) read_x(t - 2, nn);
     // Q1 = A X_t (rows of A, rows of X_t^T); P1 = X_t^T G (rows of X_t^T,
-    // rows of G^T)
+    // rows of G^T), each stored at 2^-22 of its accumulator's scale
+    // (wave w owns column block w, row blocks 0..3: the second operand of
+    // every product is read once per phase; all products of a phase come
+    // before its stores, so that no operand read waits behind a store)
+    const int sQ = sA + sX - 22, sP = sX + sG - 22;
+    const HOp bxt = load_hop(XTH, XTL, w), bgt = load_hop(GTH, GTL, w);
+    {
+      f4 aq[4], ap[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int blk = w + 4 * s, bi = blk >> 2, bj = blk & 3;
-      put_block(MQ, nullptr, bi, bj, rows_mm(MA, MXT, bi, bj, f4{0.f, 0.f, 0.f, 0.f}));
-      put_block(MP1, nullptr, bi, bj, rows_mm(MXT, MGT, bi, bj, f4{0.f, 0.f, 0.f, 0.f}));
+      for (int s = 0; s < 4; ++s) {
+        aq[s] = mm_hop(load_hop(AH, AL, s), bxt, f4{0.f, 0.f, 0.f, 0.f});
+        ap[s] = mm_hop(load_hop(XTH, XTL, s), bgt, f4{0.f, 0.f, 0.f, 0.f});
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        put_block_h(QH, QL, nullptr, nullptr, s, w, aq[s], 0x1p-22f, one);
+        put_block_h(PH, PL, nullptr, nullptr, s, w, ap[s], 0x1p-22f, one);
+      }
     }
     __syncthreads();
     // dA -= P1 X_t^T (rows of P1, rows of X_t); G' = 2 G - G Q1^T - Q1 G,
     // with (X_t A)^T taken as A X_t: X_t commutes with A and is symmetric in
     // exact arithmetic, and the recursion is linear in G, so the rounding
     // difference of the two stays at rounding level
-    f4 gn[4];
+    const float upd = ldexpf(1.0f, -(sP + sX)), ugq = ldexpf(1.0f, -(sG + sQ));
+    float mg = 0.f;
+    const HOp bx = load_hop(XH, XL, w), bq = load_hop(QH, QL, w);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int blk = w + 4 * s, bi = blk >> 2, bj = blk & 3;
-      const f4 pd = rows_mm(MP1, MX, bi, bj, f4{0.f, 0.f, 0.f, 0.f});
-      f4 gq = rows_mm(MG, MQ, bi, bj, f4{0.f, 0.f, 0.f, 0.f});
-      gq = rows_mm(MQ, MGT, bi, bj, gq);
-      const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+      const f4 pd = mm_hop(load_hop(PH, PL, s), bx, f4{0.f, 0.f, 0.f, 0.f});
+      f4 gq = mm_hop(load_hop(GH, GL, s), bq, f4{0.f, 0.f, 0.f, 0.f});
+      gq = mm_hop(load_hop(QH, QL, s), bgt, gq);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        da[s][i] -= pd[i];
-        gn[s][i] = 2.f * MG[(16 * bi + 4 * lg + i) * BS + 16 * bj + lr] - gq[i];
+        da[s][i] = fmaf(-pd[i], upd, da[s][i]);
+        g[s][i] = fmaf(-gq[i], ugq, 2.f * g[s][i]);
+        mg = fmaxf(mg, fabsf(g[s][i]));
       }
     }
-    __syncthreads();  // every read of G, X_t, Q1, P1 is done
+    wave_max_to_slot(slot + 8, mg);
+    if (t > 0) {
+      float mx = 0.f;
+#pragma unroll
+      for (int u = 0; u < R4; ++u) {
+        const int e4 = tid + WGG * u, r = e4 / 16, c4 = e4 % 16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          nx[u][i] = (r < m && 4 * c4 + i < m) ? nx[u][i] : 0.f;
+          mx = fmaxf(mx, fabsf(nx[u][i]));
+        }
+      }
+      wave_max_to_slot(slot + 4, mx);
+    }
+    __syncthreads();  // every read of G, X_t, Q1, P1 is done; the maxima are in
+    sG = nsb_scale(max4_slots(slot + 8));
+    const float scg = ldexpf(1.0f, sG);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int blk = w + 4 * s;
-      put_block(MG, MGT, blk >> 2, blk & 3, gn[s]);
+      put_block_h(GH, GL, GTH, GTL, blk >> 2, blk & 3, g[s], scg, one);
     }
     if (t > 0) {
+      sX = nsb_scale(max4_slots(slot + 4));
+      const float scx = ldexpf(1.0f, sX);
 #pragma unroll
-      for (int u = 0; u < PER; ++u) {
-        const int e = tid + WGG * u, r = e / MP, c = e % MP;
-        MX[r * BS + c] = nx[u];
-        MXT[c * BS + r] = nx[u];
+      for (int u = 0; u < R4; ++u) {
+        const int e4 = tid + WGG * u, r = e4 / 16, c4 = e4 % 16;
+        put_row4_h(XH, XL, XTH, XTL, r, c4, nx[u], scx, one);
       }
     }
+#pragma unroll
+    for (int u = 0; u < R4; ++u) nx[u] = nn[u];
     __syncthreads();
   }
+  // the last part in fp32: A from global memory, G from the registers
+  {
+    const float* ag = a.amat + static_cast<size_t>(bh) * MP * MP;
+    for (int e = tid; e < MP * MP; e += WGG) MA[(e / MP) * BS + e % MP] = ag[e];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int blk = w + 4 * s, bi = blk >> 2, bj = blk & 3;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) MG[(16 * bi + 4 * lg + i) * BS + 16 * bj + lr] = g[s][i];
+    }
+  }
+  __syncthreads();
   // dA += alpha G; d alpha = <G, A> flows through alpha = 1 / (c r), c = r =
   // the largest column (row) abs-sum: dA[:, jc] and dA[jc, :] each gain
   // -d alpha alpha / c sign(A)
@@ -443,7 +600,8 @@ __device__ void nsb_role(const BwdArgs& a, int bh, float* sm) {
     const float dc = -dalpha * alpha / csum;
     const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
     const float il = 1.0f / a.lambda;
-    // dd = -dA k(L, L) / lambda into MP1 (k(L, L) = A - eps I inside m x m)
+    // dd = -dA k(L, L) / lambda (k(L, L) = A - eps I inside m x m)
+    float* ddg = a.dxmat + static_cast<size_t>(bh) * MP * MP;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int blk = w + 4 * s, bi = blk >> 2, bj = blk & 3;
@@ -459,33 +617,10 @@ __device__ void nsb_role(const BwdArgs& a, int bh, float* sm) {
           if (r == jc) v = fmaf(dc, sg, v);
           dd = -v * (av - (r == c ? a.eps : 0.f)) * il;
         }
-        MP1[r * BS + c] = dd;
+        // dX (read at the start) is dead: dd takes its place, and the dk
+        // launch forms dL from it, one landmark per workgroup
+        ddg[r * MP + c] = dd;
       }
-    }
-  }
-  // dL from A: for landmark p, sum_j (dd[p][j] + dd[j][p]) s(l_p - l_j),
-  // s = sign (Laplacian) or 2 x (Gaussian).  Landmarks in MQ (rows of D).
-  {
-    const float* Lg = a.L + static_cast<size_t>(bh) * m * D;
-    for (int e = tid; e < MP * D; e += WGG) {
-      const int r = e / D, c = e % D;
-      MQ[r * BS + c] = r < m ? Lg[r * D + c] : 0.f;
-    }
-    __syncthreads();
-    for (int e = tid; e < MP * D; e += WGG) {
-      const int p = e / D, c = e % D;
-      float acc = 0.f;
-      if (p < m) {
-        const float lp = MQ[p * BS + c];
-        for (int j = 0; j < m; ++j) {
-          const float x = lp - MQ[j * BS + c];
-          float sv;
-          if constexpr (KIND == 0) sv = x > 0.f ? 1.f : (x < 0.f ? -1.f : 0.f);
-          else sv = 2.f * x;
-          acc = fmaf(MP1[p * BS + j] + MP1[j * BS + p], sv, acc);
-        }
-      }
-      a.dla[(static_cast<size_t>(bh) * MP + p) * D + c] = acc;
     }
   }
 }
@@ -701,25 +836,52 @@ __global__ __launch_bounds__(WGG) void bwd_fused_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dk: one workgroup per (landmark window j, head): dL[j] = dL_A[j] + its
-// 2 nT tile partials (query tiles, then key tiles, in order); the window's
-// dK rows = direct part + dL[j] / (ph pw).
+// dk: one workgroup per (landmark window j, head): dL[j] = its part from A
+// plus its 2 nT tile partials (thread (g, c) takes partials and landmarks
+// g, g + G, ..., then the G sums are added in order); the window's dK rows =
+// direct part + dL[j] / (ph pw).
 // ---------------------------------------------------------------------------
 template <int D, bool BF16>
 __global__ __launch_bounds__(WGG) void bwd_dk_kernel(BwdArgs a) {
   constexpr int G = WGG / D;
   __shared__ float part[WGG];
   __shared__ float dl[D];
+  __shared__ float dds[MP];
   const int j = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   const int c = tid % D, g = tid / D;
-  const int np = 2 * a.nT;
+  const int np = 2 * a.nT, m = a.m;
+  // dd[j][p] + dd[p][j] for the part of dL from A (dd from the Newton-Schulz
+  // backward)
+  if (tid < MP) {
+    const float* dd = a.dxmat + static_cast<size_t>(bh) * MP * MP;
+    dds[tid] = tid < m ? dd[j * MP + tid] + dd[tid * MP + j] : 0.f;
+  }
   const float* pb = a.dlpart + static_cast<size_t>(bh) * np * MP * D + j * D + c;
   float s = 0.f;
   for (int p = g; p < np; p += G) s += pb[static_cast<size_t>(p) * MP * D];
+  // landmark coordinates l_p[c] of this thread's landmarks p = g, g + G, ...
+  const float* Lh = a.L + static_cast<size_t>(bh) * m * D;
+  const float lj = Lh[j * D + c];
+  float lp[MP / G];
+#pragma unroll
+  for (int k = 0; k < MP / G; ++k) {
+    const int p = g + G * k;
+    lp[k] = p < m ? Lh[p * D + c] : lj;
+  }
+  __syncthreads();
+  // dL from A: sum over landmarks p of (dd[j][p] + dd[p][j]) s(l_j - l_p),
+  // s = sign (Laplacian) or 2 x (Gaussian)
+#pragma unroll
+  for (int k = 0; k < MP / G; ++k) {
+    const int p = g + G * k;
+    const float x = lj - lp[k];
+    const float sv = a.kind == 0 ? (x > 0.f ? 1.f : (x < 0.f ? -1.f : 0.f)) : 2.f * x;
+    if (p < m) s = fmaf(dds[p], sv, s);
+  }
   part[tid] = s;
   __syncthreads();
   if (tid < D) {
-    float acc = a.dla[(static_cast<size_t>(bh) * MP + j) * D + tid];
+    float acc = 0.f;
     for (int u = 0; u < G; ++u) acc += part[u * D + tid];
     dl[tid] = acc / static_cast<float>(a.ph * a.pw);
   }
@@ -858,7 +1020,6 @@ hipError_t launch_backward(const BwdPlan& p, const BwdCall& c, hipStream_t s) {
   ba.ymat = reinterpret_cast<float*>(ws + p.off_ymat);
   ba.dwmat = reinterpret_cast<float*>(ws + p.off_dwmat);
   ba.dxmat = reinterpret_cast<float*>(ws + p.off_dxmat);
-  ba.dla = reinterpret_cast<float*>(ws + p.off_dla);
   ba.dlpart = reinterpret_cast<float*>(ws + p.off_dlpart);
   ba.dkd = reinterpret_cast<float*>(ws + p.off_dkd);
   ba.N = p.N;

@@ -116,7 +116,7 @@ struct BwdPlan {
   int nP;     // partials per head and side (= ceil(nT / S))
   int iters;
   size_t off_L, off_xiter, off_amat, off_hscal, off_wpart, off_dypart, off_ymat, off_dwmat,
-      off_dxmat, off_dla, off_dlpart, off_dkd, off_sync;
+      off_dxmat, off_dlpart, off_dkd, off_sync;
   size_t total;
 };
 
