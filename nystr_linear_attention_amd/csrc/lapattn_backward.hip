@@ -99,13 +99,7 @@ __device__ __forceinline__ void bwd_solver(const MainArgs& a, int bh, float* sme
     ag[e] = (r < m && c < m) ? Af[r * SX + c] : 0.f;
   }
   if (w == 0) {
-    float sum = 0.f;
-    if (lane < m) {
-      for (int q = 0; q < (m + 3) / 4; ++q) {
-        const f4 v = ld4(Af + lane * SX + 4 * q);  // zero beyond m
-        sum += fabsf(v[0]) + fabsf(v[1]) + fabsf(v[2]) + fabsf(v[3]);
-      }
-    }
+    const float sum = lane < m ? a_row_abs_sum<G::N16, SX>(Af, lane) : 0.f;
     const float mx = __uint_as_float(wave_max_u(__float_as_uint(sum)));
     const unsigned long long hit = __ballot(lane < m && sum == mx);
     const int jc = static_cast<int>(__builtin_ctzll(hit));

@@ -861,6 +861,19 @@ __device__ void build_a(const MainArgs& a, int bh, const float* Ls, float* A, in
   }
 }
 
+// Abs-sum of row `row` of the fp32 A in LDS (row stride SX, zero beyond m),
+// over all N16 columns (the zeros add nothing): all loads issued at once.
+template <int N16, int SX>
+__device__ __forceinline__ float a_row_abs_sum(const float* Af, int row) {
+  f4 v[N16 / 4];
+#pragma unroll
+  for (int q = 0; q < N16 / 4; ++q) v[q] = ld4(Af + row * SX + 4 * q);
+  float sum = 0.f;
+#pragma unroll
+  for (int q = 0; q < N16 / 4; ++q) sum += fabsf(v[q][0]) + fabsf(v[q][1]) + fabsf(v[q][2]) + fabsf(v[q][3]);
+  return sum;
+}
+
 // Set-up of a solver workgroup: A = k(L, L) + eps I in LDS (fp32, row stride
 // SX, at the parity-1 X halves, where it stays until the first step's
 // barrier), alpha, and the scaled split arrays of A and X_0 = alpha A.
@@ -900,27 +913,21 @@ __device__ __forceinline__ void solver_setup(const MainArgs& a, int bh, float* s
   // alpha = 1 / (max column abs-sum * max row abs-sum); A is symmetric, so
   // its largest column sum equals its largest row sum.  Also max|A|.
   if (w == 0) {
-    float sum = 0.f, amx = 0.f;
-    if (lane < m) {
-      for (int q = 0; q < (m + 3) / 4; ++q) {
-        const f4 v = ld4(Af + lane * SX + 4 * q);  // zero beyond m
-        sum += fabsf(v[0]) + fabsf(v[1]) + fabsf(v[2]) + fabsf(v[3]);
-        amx = fmaxf(amx, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
-      }
-    }
-    // both are non-negative, so they compare as unsigned bit patterns
-    sum = __uint_as_float(wave_max_u(__float_as_uint(sum)));
-    amx = __uint_as_float(wave_max_u(__float_as_uint(amx)));
+    const float sum = lane < N16 ? a_row_abs_sum<N16, SX>(Af, lane) : 0.f;
+    // non-negative, so it compares as an unsigned bit pattern
+    const float mx = __uint_as_float(wave_max_u(__float_as_uint(sum)));
     if (lane == 0) {
-      red[0] = sum;
+      red[0] = mx;
       red[1] = 0.f;  // set once W^T is in LDS
-      red[2] = amx;
     }
   }
   __syncthreads();
   const float alpha = 1.0f / (red[0] * red[0]);
-  const int eA = 14 - __builtin_amdgcn_frexp_expf(red[2]);
-  const float m0 = alpha * red[2];  // max|X_0|
+  // max|A| is the diagonal's 1 + eps: every other entry is exp2 of a
+  // non-positive argument (eps >= 0 is checked at the boundary)
+  const float amax = 1.0f + a.eps;
+  const int eA = 14 - __builtin_amdgcn_frexp_expf(amax);
+  const float m0 = alpha * amax;  // max|X_0|
   const int e0 = 7 - __builtin_amdgcn_frexp_expf(m0);
   // A and X_0 = alpha A, scaled and split, into the half-precision arrays
   // (four consecutive columns per thread: 8-byte stores); with no steps to
@@ -931,9 +938,20 @@ __device__ __forceinline__ void solver_setup(const MainArgs& a, int bh, float* s
     uint16_t* AL = reinterpret_cast<uint16_t*>(smem + G::OFF_AL);
     uint16_t* XH = reinterpret_cast<uint16_t*>(smem + G::OFF_X);
     uint16_t* XL = reinterpret_cast<uint16_t*>(smem + G::OFF_X + G::XARR);
-    for (int e = tid; e < N16 * Q4; e += WGM) {
+    // every row read issued before the first store
+    constexpr int NR = (N16 * Q4 + WGM - 1) / WGM;
+    f4 avs[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int e = tid + r * WGM;
+      if (e < N16 * Q4) avs[r] = ld4(Af + (e / Q4) * SX + 4 * (e % Q4));
+    }
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int e = tid + r * WGM;
+      if (e >= N16 * Q4) break;
       const int i = e / Q4, q = e % Q4;
-      const f4 av = ld4(Af + i * SX + 4 * q);
+      const f4 av = avs[r];
       const int h0 = i * RSH + hpos<MB>(4 * q);  // a multiple of 4
       unsigned h0w, l0w, h1w, l1w;
       split2(ldexpf(av[0], eA), ldexpf(av[1], eA), h0w, l0w);
