@@ -71,6 +71,7 @@ struct BwdArgs {
                        //                      Newton-Schulz backward, for dk)
   float* dlpart;       // [BH][2 nT][MP][D]    dL partials of the gradient tiles
   float* dkd;          // [BH][N][D]           direct part of dK
+  unsigned* sync;      // hand-off words (zeroed by the pool launch)
   int N, m, BH, nT, nP, gw, ph, pw, iters, kind, bf16;
   float lambda, eps, c_exp2;
 };
@@ -206,52 +207,63 @@ __device__ __forceinline__ void load_mm(float* dst, const float* src, int m) {
   }
 }
 
+// Head reduction, in kBwdHeadSlices workgroups per head: workgroup r sums
+// elements [r E, (r + 1) E) of the W^T and the dY^T partials (one thread per
+// element, partials in order, 32 loads in flight), stores the sums with
+// device-scope stores into Y's and dW's buffers (free until the products
+// below) and counts its arrival; the head's last workgroup to arrive reads
+// W and dY back and forms the products.  With one workgroup per head the
+// reduction ran at one CU's load latency (31 us for 8 heads of 25 partials).
+constexpr int kBwdHeadSlices = 16;
+
 template <int D>
 __global__ __launch_bounds__(WGM) void bwd_heada_kernel(BwdArgs a) {
   constexpr int NB64 = 16;           // 16 x 16 blocks of a 64 x 64 product
   constexpr int NBD = 4 * (D / 16);  // blocks of a 64 x D product
+  constexpr int E = D * MP / kBwdHeadSlices;
+  static_assert(2 * E <= WGM, "one thread per element of the slice");
   __shared__ __attribute__((aligned(16))) float sm[3 * MP * BS];
   float* M0 = sm;
   float* M1 = sm + MP * BS;
   float* M2 = sm + 2 * MP * BS;
-  const int bh = blockIdx.x, tid = threadIdx.x;
+  const int bh = blockIdx.y, tid = threadIdx.x;
   const int m = a.m, nP = a.nP, T = a.iters;
   const size_t ps = static_cast<size_t>(D) * MP;
   const int lane = tid & 63, w = wave_id(), lr = lane & 15, lg = lane >> 4;
+  float* wred = a.ymat + static_cast<size_t>(bh) * MP * D;    // W^T [D][MP] until the products
+  float* dyred = a.dwmat + static_cast<size_t>(bh) * MP * D;  // dY^T [D][MP] likewise
 
-  // W[j][c] and dY[j][c] (row stride BS), the partials summed in order;
-  // a partial is W^T [D][MP], so consecutive threads take consecutive j, and
-  // the loads of 8 partials are in flight at once
-  {
-    const float* wp = a.wpart + static_cast<size_t>(bh) * nP * ps;
-    const float* dp = a.dypart + static_cast<size_t>(bh) * nP * ps;
-    for (int e = tid; e < MP * MP; e += WGM) {
-      const int c = e / MP, j = e % MP;
-      float sw = 0.f, sd = 0.f;
-      if (j < m && c < D) {
-        const size_t o = static_cast<size_t>(c) * MP + j;
-        int p = 0;
-        for (; p + 8 <= nP; p += 8) {
-          float vw[8], vd[8];
+  if (tid < 2 * E) {
+    const bool isw = tid < E;
+    const int o = static_cast<int>(blockIdx.x) * E + (isw ? tid : tid - E);  // c MP + j
+    const float* src = (isw ? a.wpart : a.dypart) + static_cast<size_t>(bh) * nP * ps + o;
+    float sum = 0.f;
+    if (o % MP < m) {
+      for (int p0 = 0; p0 < nP; p0 += 32) {
+        float v[32];
 #pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            vw[u] = wp[(p + u) * ps + o];
-            vd[u] = dp[(p + u) * ps + o];
-          }
+        for (int u = 0; u < 32; ++u) v[u] = p0 + u < nP ? src[(p0 + u) * ps] : 0.f;
 #pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            sw += vw[u];
-            sd += vd[u];
-          }
-        }
-        for (; p < nP; ++p) {
-          sw += wp[p * ps + o];
-          sd += dp[p * ps + o];
-        }
+        for (int u = 0; u < 32; ++u)
+          if (p0 + u < nP) sum += v[u];
       }
-      M0[j * BS + c] = sw;
-      M1[j * BS + c] = sd;
     }
+    st_dev((isw ? wred : dyred) + o, sum);
+  }
+  unsigned* cnt = a.sync + kSyncHead * (bh + 1) + kBwdHeadCount;
+  if (publish_arrive(cnt) != static_cast<unsigned>(kBwdHeadSlices - 1)) return;
+
+  // the last workgroup: W[j][c] and dY[j][c] (row stride BS), zero beyond m
+  // and D
+  for (int e = tid; e < MP * MP; e += WGM) {
+    const int c = e / MP, j = e % MP;
+    float vw = 0.f, vd = 0.f;
+    if (c < D) {
+      vw = wred[e];
+      vd = dyred[e];
+    }
+    M0[j * BS + c] = vw;
+    M1[j * BS + c] = vd;
   }
   load_mm(M2, a.xiter + (static_cast<size_t>(bh) * (T + 1) + T) * MP * MP, m);  // X = X_T
   __syncthreads();
@@ -921,7 +933,7 @@ hipError_t launch_bwd_d(const BwdPlan& p, const BwdArgs& ba, const MainArgs& ma,
     case 4: e = launch_part_dm<D, 4>(ma, ba.dout, dypart, xiter, amat, hscal, gpart, s, ev[1]); break;
   }
   if (e != hipSuccess) return e;
-  e = launch(bwd_heada_kernel<D>, dim3(p.BH), dim3(WGM), s, ev[2], ba);
+  e = launch(bwd_heada_kernel<D>, dim3(kBwdHeadSlices, p.BH), dim3(WGM), s, ev[2], ba);
   if (e != hipSuccess) return e;
   // Newton-Schulz backward workgroups first, then the gradient tiles
   const dim3 gg(static_cast<unsigned>(p.BH + p.BH * 2 * p.nT));
@@ -1014,6 +1026,7 @@ hipError_t launch_backward(const BwdPlan& p, const BwdCall& c, hipStream_t s) {
   ba.ymat = reinterpret_cast<float*>(ws + p.off_ymat);
   ba.dwmat = reinterpret_cast<float*>(ws + p.off_dwmat);
   ba.dxmat = reinterpret_cast<float*>(ws + p.off_dxmat);
+  ba.sync = sync;
   ba.dlpart = reinterpret_cast<float*>(ws + p.off_dlpart);
   ba.dkd = reinterpret_cast<float*>(ws + p.off_dkd);
   ba.N = p.N;

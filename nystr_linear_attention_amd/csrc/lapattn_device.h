@@ -209,6 +209,8 @@ __device__ __forceinline__ unsigned* cnt_y(const MainArgs& a, int bh) { return h
 __device__ __forceinline__ unsigned* flag_y(const MainArgs& a, int bh) { return head_sync(a, bh) + 226; }
 // word of head bh counting the chunks of the normalised map's statistics
 constexpr int kNormCount = 227;
+// word of head bh counting the slices of the backward's head reduction
+constexpr int kBwdHeadCount = 228;
 
 __device__ __forceinline__ void st_dev(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
