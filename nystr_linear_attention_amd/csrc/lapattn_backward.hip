@@ -864,7 +864,18 @@ __global__ __launch_bounds__(WGG) void bwd_dk_kernel(BwdArgs a) {
   }
   const float* pb = a.dlpart + static_cast<size_t>(bh) * np * MP * D + j * D + c;
   float s = 0.f;
-  for (int p = g; p < np; p += G) s += pb[static_cast<size_t>(p) * MP * D];
+  // partials g, g + G, ... in order, 16 loads in flight
+  for (int p0 = g; p0 < np; p0 += 16 * G) {
+    float v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int p = p0 + G * u;
+      v[u] = p < np ? pb[static_cast<size_t>(p) * MP * D] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (p0 + G * u < np) s += v[u];
+  }
   // landmark coordinates l_p[c] of this thread's landmarks p = g, g + G, ...
   const float* Lh = a.L + static_cast<size_t>(bh) * m * D;
   const float lj = Lh[j * D + c];
@@ -894,13 +905,25 @@ __global__ __launch_bounds__(WGG) void bwd_dk_kernel(BwdArgs a) {
   __syncthreads();
   const int mw = a.gw / a.pw, R0 = j / mw, C0 = j % mw;
   const int cnt = a.ph * a.pw;
-  for (int e = tid; e < cnt * D; e += WGG) {
-    const int tk = e / D, cc = e % D;
-    const int n = (R0 * a.ph + tk / a.pw) * a.gw + C0 * a.pw + tk % a.pw;
-    const size_t o = (static_cast<size_t>(bh) * a.N + n) * D + cc;
-    const float v = a.dkd[o] + dl[cc];
-    if (BF16) static_cast<uint16_t*>(a.dk)[o] = f32_to_bf16_rne(v);
-    else static_cast<float*>(a.dk)[o] = v;
+  // 16 rows' loads in flight before their stores
+  for (int e0 = tid; e0 < cnt * D; e0 += 16 * WGG) {
+    float v[16];
+    size_t o[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int e = e0 + u * WGG;
+      const int ec = e < cnt * D ? e : cnt * D - 1;  // in bounds either way
+      const int tk = ec / D, cc = ec % D;
+      const int n = (R0 * a.ph + tk / a.pw) * a.gw + C0 * a.pw + tk % a.pw;
+      o[u] = (static_cast<size_t>(bh) * a.N + n) * D + cc;
+      v[u] = e < cnt * D ? a.dkd[o[u]] + dl[cc] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      if (e0 + u * WGG >= cnt * D) break;
+      if (BF16) static_cast<uint16_t*>(a.dk)[o[u]] = f32_to_bf16_rne(v[u]);
+      else static_cast<float*>(a.dk)[o[u]] = v[u];
+    }
   }
 }
 
