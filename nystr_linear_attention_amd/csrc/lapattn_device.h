@@ -1169,8 +1169,15 @@ constexpr int row_stride() { return D + 4; }
 // the Laplacian tiles' staged token rows.
 template <int D, int KIND>
 constexpr int map_smem() {
-  return map_pj_size<D>() + 2 * MP * LS + TILE + (KIND == 0 ? TILE * row_stride<D>() : 0);
+  return map_pj_size<D>() + 2 * MP * LS + TILE + (KIND == 0 ? TILE * row_stride<D>() : 0) + 8;
 }
+
+// Key tiles' operands of the W^T product as scaled fp16 parts (hi, lo):
+// rows of 64 halves (one per token), the 16-byte chunks of row r permuted
+// (chunk c at position c ^ (r & 7)) so that the operand reads of 16
+// consecutive rows spread over the banks.  Position (in halves) of token k
+// of row r:
+__device__ __forceinline__ int hsw(int r, int k) { return r * 64 + ((((k >> 3) ^ r) & 7) << 3) + (k & 7); }
 
 // Y^T = W^T X^T in place: the split, row-scaled W^T in LDS (row c scaled by
 // 2^EW[c]) is replaced by the split Y^T with the same row scales times
@@ -1390,8 +1397,8 @@ __device__ __forceinline__ void gauss_rows(const MainArgs& a, const void* src, i
 
 template <int D, bool BF16>
 __device__ __forceinline__ void gauss_tile(const MainArgs& a, const float (&av)[D / 4], const float* Lh,
-                                           int t, float* PTt, float* PJ, float* xx, bool key_role,
-                                           bool write_pt) {
+                                           int t, float* PTt, uint16_t* PJH, uint16_t* PJL, float* xx,
+                                           bool key_role, bool write_pt) {
   constexpr int KS = D / 4;  // MFMA sub-steps; floats per lane per operand
   const int lane = threadIdx.x & 63, w = wave_id();
   const int lr = lane & 15, lg = lane >> 4;
@@ -1425,13 +1432,23 @@ __device__ __forceinline__ void gauss_tile(const MainArgs& a, const float (&av)[
       f4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s) c = mfma4(av[s], bv[s], c);
+      f4 kq;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tt = 16 * tb + 4 * lg + i;
         const float d = fmaxf(fmaf(-2.0f, c[i], xx[tt] + pl), 0.0f);
         const float kv = (j < m && t * TILE + tt < N) ? exp2_map(d * a.c_exp2) : 0.f;
         if (write_pt) PTt[ptj(tt, j)] = kv;
-        if (key_role) PJ[j * LS + tt] = kv;
+        kq[i] = kv;
+      }
+      if (key_role) {
+        // 4 consecutive tokens of row j: half a chunk per part, 2^14 k
+        unsigned h0, l0, h1, l1;
+        split2(kq[0] * 16384.f, kq[1] * 16384.f, h0, l0);
+        split2(kq[2] * 16384.f, kq[3] * 16384.f, h1, l1);
+        const int o = hsw(j, 16 * tb + 4 * lg);
+        *reinterpret_cast<u32x2*>(PJH + o) = u32x2{h0, h1};
+        *reinterpret_cast<u32x2*>(PJL + o) = u32x2{l0, l1};
       }
     }
   }
@@ -1449,6 +1466,19 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
   float* VT = smem + PJS + MP * LS;      // [D][LS]:            V[token][c] at [c][token]
   float* xx = smem + PJS + 2 * MP * LS;  // [64]: squared norms of a tile's tokens (Gaussian)
   float* XR = xx + TILE;                 // [64 tokens][XS]: token rows (Laplacian)
+  // Gaussian key tiles: K_LK [landmark][token] and V^T [c][token] as fp16
+  // parts of 2^14 K_LK and 2^sv V (hsw layout) in the PJ and VT areas, and
+  // the per-wave maxima of |V| of the next tile (sv); their W^T product runs
+  // on fp16 MFMA.  Laplacian key tiles keep both in fp32 (fp32 MFMA): their
+  // maps write K_LK one token per lane, and splitting it there cost more
+  // VALU time than the product saved (160-head bf16: +1.7 us per forward;
+  // Gaussian Q = K: -3.6 us).
+  constexpr bool SPLIT_W = KIND == 1;
+  uint16_t* const PJH = reinterpret_cast<uint16_t*>(PJ);
+  uint16_t* const PJL = PJH + MP * 64;
+  uint16_t* const VTH = reinterpret_cast<uint16_t*>(VT);
+  uint16_t* const VTL = VTH + MP * 64;
+  float* const vmax = XR + (KIND == 0 ? TILE * row_stride<D>() : 0);
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int lr = lane & 15, lg = lane >> 4;
   const int m = a.m, N = a.N;
@@ -1499,6 +1529,19 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
         const int nv = t * TILE + vtg * TPT + u;
         vv[u] = load1_io(v, (static_cast<size_t>(bh) * N + (nv < N ? nv : N - 1)) * D + vc, BF16);
       }
+    }
+  };
+  // max|V| of the loaded tile over this wave's threads into vmax[w] (the
+  // clamped rows past N only make the scale conservative); read by every
+  // wave after the next barrier, when the tile is staged
+  auto publish_vmax = [&]() {
+    if (SPLIT_W && key_role) {
+      float mx = 0.f;
+#pragma unroll
+      for (int u = 0; u < TPT; ++u) mx = fmaxf(mx, fabsf(vv[u]));
+      // non-negative: compares as an unsigned bit pattern
+      mx = __uint_as_float(wave_max_u(__float_as_uint(mx)));
+      if (lane == 0) vmax[w] = mx;
     }
   };
   float ga[KIND == 1 ? D / 4 : 1];
@@ -1553,6 +1596,7 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
     if (!key_role) VT[e] = 0.f;
   }
   if (KIND == 0 && t_beg < t_end) stage_rows();
+  if (t_beg < t_end) publish_vmax();
   __syncthreads();
 
   for (int t = t_beg; t < t_end; ++t) {
@@ -1570,7 +1614,8 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
         x[4 * i + 3] = u[3];
       }
     }
-    if (key_role) {
+    int sv = 0;  // V^T scale of this tile: max|V| 2^sv < 2^15
+    if (key_role && !SPLIT_W) {
       // V tile -> VT[c][token] (VT is free: the previous tile's products
       // finished before the barrier that ended its iteration).  A thread's
       // TPT consecutive tokens of column c go out as 16-byte stores: lanes
@@ -1586,6 +1631,35 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
       } else {
 #pragma unroll
         for (int u = 0; u < TPT; ++u) vdst[u] = vz[u];
+      }
+    }
+    if (key_role && SPLIT_W) {
+      // V tile -> V^T as fp16 parts of 2^sv V (the VT area is free: the
+      // previous tile's products finished before the barrier that ended its
+      // iteration).  A thread's TPT consecutive tokens of column c are one
+      // run of a row: one store per part.
+      float mxv = vmax[0];
+#pragma unroll
+      for (int i = 1; i < WGM / 64; ++i) mxv = fmaxf(mxv, vmax[i]);
+      // (capped so that 2^-(sv + 14) stays a normal fp32 number)
+      sv = min(fp16_scale(mxv), 100);
+      float vz[TPT];
+#pragma unroll
+      for (int u = 0; u < TPT; ++u) vz[u] = t * TILE + vtg * TPT + u < N ? ldexpf(vv[u], sv) : 0.f;
+      unsigned hv[TPT / 2], lv[TPT / 2];
+#pragma unroll
+      for (int u = 0; u < TPT; u += 2) split2(vz[u], vz[u + 1], hv[u / 2], lv[u / 2]);
+      const int o = hsw(vc, vtg * TPT);
+      if constexpr (TPT == 8) {
+        *reinterpret_cast<u32x4*>(VTH + o) = u32x4{hv[0], hv[1], hv[2], hv[3]};
+        *reinterpret_cast<u32x4*>(VTL + o) = u32x4{lv[0], lv[1], lv[2], lv[3]};
+      } else if constexpr (TPT == 4) {
+        *reinterpret_cast<u32x2*>(VTH + o) = u32x2{hv[0], hv[1]};
+        *reinterpret_cast<u32x2*>(VTL + o) = u32x2{lv[0], lv[1]};
+      } else {
+        static_assert(TPT == 2, "runs of 2, 4 or 8 tokens");
+        *reinterpret_cast<unsigned*>(VTH + o) = hv[0];
+        *reinterpret_cast<unsigned*>(VTL + o) = lv[0];
       }
     }
     if constexpr (KIND == 0) {
@@ -1612,7 +1686,7 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
         if (write_pt) PTt[ptj(lane, j)] = k0;
       }
     } else {
-      gauss_tile<D, BF16>(a, ga, Lh, t, PTt, PJ, xx, key_role, write_pt);
+      gauss_tile<D, BF16>(a, ga, Lh, t, PTt, PJH, PJL, xx, key_role, write_pt);
     }
     if (t + 1 < t_end) {
       load_v(t + 1);
@@ -1641,15 +1715,23 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
       if (a.st_klk) {
         for (int e = tid; e < m * TILE; e += WGM) {
           const int j = e / TILE, tok = e % TILE;
-          if (t * TILE + tok < N)
-            a.st_klk[(static_cast<size_t>(bh) * m + j) * N + t * TILE + tok] = PJ[j * LS + tok];
+          float kv = PJ[j * LS + tok];
+          if constexpr (SPLIT_W) {
+            const int o = hsw(j, tok);
+            kv = (static_cast<float>(__builtin_bit_cast(_Float16, PJH[o])) +
+                  static_cast<float>(__builtin_bit_cast(_Float16, PJL[o]))) * 0x1p-14f;
+          }
+          if (t * TILE + tok < N) a.st_klk[(static_cast<size_t>(bh) * m + j) * N + t * TILE + tok] = kv;
         }
       }
-      // W^T[c][j] += sum_token V^T[c][token] P[j][token]
+      // W^T[c][j] += sum_token V^T[c][token] P[j][token]: on fp32 MFMA, or
+      // (Gaussian) on fp16 MFMA with the scaled two-part operands (hi hi +
+      // lo hi + hi lo), the tile's scale 2^(sv + 14) taken out as it is added
+      const float unscale = ldexpf(1.0f, -(sv + 14));
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const int blk = w + 8 * s;
-        if (blk < nwb) {
+        if (!SPLIT_W && blk < nwb) {
           const int cb = blk % CBN, jbk = blk / CBN;
           const float* ar = VT + (16 * cb + lr) * LS + 16 * lg;
           const float* br = PJ + (16 * jbk + lr) * LS + 16 * lg;
@@ -1664,10 +1746,29 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
           }
           wacc[s] = c;
         }
+        if (SPLIT_W && blk < nwb) {
+          const int cb = blk % CBN, jbk = blk / CBN;
+          const int ra = 16 * cb + lr, rb = 16 * jbk + lr;
+          f4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            const int k0 = 32 * p + 8 * lg;
+            const u32x4 ah = *reinterpret_cast<const u32x4*>(VTH + hsw(ra, k0));
+            const u32x4 al = *reinterpret_cast<const u32x4*>(VTL + hsw(ra, k0));
+            const u32x4 bh2 = *reinterpret_cast<const u32x4*>(PJH + hsw(rb, k0));
+            const u32x4 bl2 = *reinterpret_cast<const u32x4*>(PJL + hsw(rb, k0));
+            c = mfma_h(ah, bh2, c);
+            c = mfma_h(al, bh2, c);
+            c = mfma_h(ah, bl2, c);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) wacc[s][i] = fmaf(c[i], unscale, wacc[s][i]);
+        }
       }
     }
     // every wave read this tile's rows before the barrier above
     if (KIND == 0 && t + 1 < t_end) stage_rows();
+    if (t + 1 < t_end) publish_vmax();
     __syncthreads();
   }
   if (!key_role) {

@@ -139,6 +139,10 @@ __global__ __launch_bounds__(WGM, 4) void main_kernel(MainArgs a, const void* __
   // solver: the Newton-Schulz arrays plus a W^T copy (landmarks while A is
   // built)
   constexpr int SOLVER_SMEM = NsGeom<MB, D>::SMEM;
+  // two workgroups per CU (160 KB of LDS), which the in-launch hand-offs
+  // count on
+  static_assert(4 * (MAP_SMEM > SOLVER_SMEM ? MAP_SMEM : SOLVER_SMEM) <= 80 * 1024,
+                "LDS of two workgroups per CU");
   __shared__ __attribute__((aligned(16)))
   float smem[MAP_SMEM > SOLVER_SMEM ? MAP_SMEM : SOLVER_SMEM];
   const Role r = take_role(a, blockIdx.x);
