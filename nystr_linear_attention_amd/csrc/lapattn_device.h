@@ -1395,6 +1395,13 @@ __device__ __forceinline__ void gauss_rows(const MainArgs& a, const void* src, i
   }
 }
 
+// Scale exponent s of a vector with squared norm p: every coordinate times
+// 2^s is below 2^14 (|x_k| <= sqrt(p) < 2^ceil(e / 2) for p < 2^e).
+__device__ __forceinline__ int norm_scale(float p) {
+  const int e = p > 0.f ? __builtin_amdgcn_frexp_expf(p) : 0;
+  return 14 - ((e + 1) >> 1);
+}
+
 template <int D, bool BF16>
 __device__ __forceinline__ void gauss_tile(const MainArgs& a, const float (&av)[D / 4], const float* Lh,
                                            int t, float* PTt, uint16_t* PJH, uint16_t* PJL, float* xx,
@@ -1410,6 +1417,24 @@ __device__ __forceinline__ void gauss_tile(const MainArgs& a, const float (&av)[
   for (int s = 0; s < KS; ++s) px = fmaf(av[s], av[s], px);
   px = sum_over_g(px);
   if (w < 4 && lg == 0) xx[16 * tb + lr] = px;
+  // x.l on fp16 MFMA with scaled two-part operands (hi hi + lo hi + hi lo):
+  // lane (g, r) supplies its KS coordinates in chunks of 8 (any order of the
+  // k terms gives the same dot product, as long as both operands use it);
+  // the token's scale comes from its squared norm, so the epilogue can
+  // recompute it from xx
+  constexpr int NCH = (KS + 7) / 8;
+  u32x4 xh[NCH], xl[NCH];
+  {
+    const int sx = norm_scale(px);
+#pragma unroll
+    for (int p = 0; p < NCH; ++p) {
+      const f4 v0 = {av[8 * p], av[8 * p + 1], av[8 * p + 2], av[8 * p + 3]};
+      const f4 v1 = KS >= 8 ? f4{av[(8 * p + 4) % KS], av[(8 * p + 5) % KS], av[(8 * p + 6) % KS],
+                                 av[(8 * p + 7) % KS]}
+                            : f4{0.f, 0.f, 0.f, 0.f};
+      split8h(v0, v1, sx, xh[p], xl[p]);
+    }
+  }
   __syncthreads();
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -1429,14 +1454,27 @@ __device__ __forceinline__ void gauss_tile(const MainArgs& a, const float (&av)[
 #pragma unroll
       for (int s = 0; s < KS; ++s) pl = fmaf(bv[s], bv[s], pl);
       pl = sum_over_g(pl);
+      const int sl = norm_scale(pl);
       f4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < KS; ++s) c = mfma4(av[s], bv[s], c);
+      for (int p = 0; p < NCH; ++p) {
+        const f4 v0 = {bv[8 * p], bv[8 * p + 1], bv[8 * p + 2], bv[8 * p + 3]};
+        const f4 v1 = KS >= 8 ? f4{bv[(8 * p + 4) % KS], bv[(8 * p + 5) % KS], bv[(8 * p + 6) % KS],
+                                   bv[(8 * p + 7) % KS]}
+                              : f4{0.f, 0.f, 0.f, 0.f};
+        u32x4 lh, ll;
+        split8h(v0, v1, sl, lh, ll);
+        c = mfma_h(xh[p], lh, c);
+        c = mfma_h(xl[p], lh, c);
+        c = mfma_h(xh[p], ll, c);
+      }
       f4 kq;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tt = 16 * tb + 4 * lg + i;
-        const float d = fmaxf(fmaf(-2.0f, c[i], xx[tt] + pl), 0.0f);
+        const float xt = xx[tt];
+        const float dot = ldexpf(c[i], -(norm_scale(xt) + sl));
+        const float d = fmaxf(fmaf(-2.0f, dot, xt + pl), 0.0f);
         const float kv = (j < m && t * TILE + tt < N) ? exp2_map(d * a.c_exp2) : 0.f;
         if (write_pt) PTt[ptj(tt, j)] = kv;
         kq[i] = kv;
