@@ -691,7 +691,8 @@ def main(argv=None):
     # of its two launches is longer).  Its roofline is the distance stage the
     # metric names: the L1 map pairs (K_QL, K_LK) and the pairs of A, 3 flops
     # per coordinate pair, on FP32 VALU; the Gaussian variant's distances
-    # run on fp32 MFMA instead (2 flops per multiply-add of X L^T).
+    # run on fp16 MFMA instead (X L^T as scaled hi + lo parts, three products
+    # per block; 2 flops per multiply-add of X L^T, against the fp16 peak).
     if args.serial:
         dom_ms = max(ks["maps"], ks["main"])
         dom_desc = ("main_kernel, map workgroups only (serial plan)" if ks["maps"] >= ks["main"]
@@ -702,9 +703,9 @@ def main(argv=None):
     l1_pairs = wk["map_pairs"] + wk["amat_pairs"]
     if w.kernel == wl.GAUSSIAN:
         dom_flops = 2 * wk["map_pairs"]
-        bound, dpeak, stage = "mfma", PEAK_FP32_MFMA_TFLOPS, (
-            "Gaussian distance stage: X L^T of K_QL (and K_LK when K != Q) on fp32 MFMA, "
-            "2 flops per multiply-add, over the launch's time")
+        bound, dpeak, stage = "mfma", PEAK_FP16_MFMA_TFLOPS, (
+            "Gaussian distance stage: X L^T of K_QL (and K_LK when K != Q) on fp16 MFMA as "
+            "scaled hi + lo parts (3 products), 2 flops per multiply-add, over the launch's time")
     else:
         dom_flops = 3 * l1_pairs
         bound, dpeak, stage = "alu", PEAK_FP32_VALU_TFLOPS, (
@@ -716,7 +717,7 @@ def main(argv=None):
         "kernel": dom_desc,
         "stage": stage,
         "bound": bound,
-        "pipe": "FP32 MFMA" if bound == "mfma" else "FP32 VALU",
+        "pipe": "fp16 MFMA" if bound == "mfma" else "FP32 VALU",
         "achieved": round(ach, 3),
         "peak": dpeak,
         "unit": "TFLOP/s",
@@ -787,10 +788,14 @@ def main(argv=None):
                 "algorithmic_flops": w.heads * yo, "issued_flops": yo_issued,
                 "peak_TFLOP/s": PEAK_FP16_MFMA_TFLOPS,
                 "issued_frac": round(yo_issued / t / 1e12 / PEAK_FP16_MFMA_TFLOPS, 5)},
-            "klk_v": {
+            "klk_v": ({
+                "unit": "fp16 MFMA (hi*hi + lo*hi + hi*lo)", "algorithmic_flops": wk["klkv"],
+                "issued_flops": 3 * klkv_issued, "peak_TFLOP/s": PEAK_FP16_MFMA_TFLOPS,
+                "issued_frac": round(3 * klkv_issued / t / 1e12 / PEAK_FP16_MFMA_TFLOPS, 5)}
+                if w.kernel == wl.GAUSSIAN else {
                 "unit": "fp32 MFMA 16x16x4", "algorithmic_flops": wk["klkv"],
                 "issued_flops": klkv_issued, "peak_TFLOP/s": PEAK_FP32_MFMA_TFLOPS,
-                "issued_frac": round(klkv_issued / t / 1e12 / PEAK_FP32_MFMA_TFLOPS, 5)},
+                "issued_frac": round(klkv_issued / t / 1e12 / PEAK_FP32_MFMA_TFLOPS, 5)}),
         }
     mfma = None
     if ks:
@@ -830,10 +835,12 @@ def main(argv=None):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32" if w.dtype == wl.F32 else "bf16 I/O, f32 compute",
-        "arithmetic": "L1 / squared-L2 maps on FP32 VALU; Newton-Schulz products as fp16 "
-                      "hi+lo splits on fp16 MFMA (about 22 significant bits); Y and O as "
-                      "power-of-two scaled fp16 hi+lo splits on fp16 MFMA; K_LK V on fp32 MFMA; "
-                      "fp32 accumulation throughout",
+        "arithmetic": "L1 maps on FP32 VALU; squared-L2 maps as |x|^2 + |l|^2 - 2 x.l with "
+                      "x.l as power-of-two scaled fp16 hi+lo splits on fp16 MFMA; Newton-Schulz "
+                      "products as fp16 hi+lo splits on fp16 MFMA (about 22 significant bits); "
+                      "Y and O as scaled fp16 hi+lo splits on fp16 MFMA; K_LK V on fp32 MFMA "
+                      "(Laplacian) or as scaled fp16 hi+lo splits (Gaussian); fp32 accumulation "
+                      "throughout",
         "data": "synthetic (seeded, shapes and distributions of the workload; resident in HBM)",
         "config": {
             "workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "m": w.m,
