@@ -156,12 +156,12 @@ __global__ __launch_bounds__(WGM, 4) void main_kernel(MainArgs a, const void* __
 // ---------------------------------------------------------------------------
 // pool: one workgroup per (LPW consecutive landmarks, head).  Thread
 // (g, c4) sums a float4 column chunk over every G-th token of each window,
-// the loads of all LPW windows (4 tokens each per pass) issued together; a
+// the loads of all LPW windows (U tokens each per pass) issued together; a
 // fixed-order LDS reduction over g finishes each mean.  LPW > 1 when the
 // grid of one landmark per workgroup would not be resident at once: fewer,
 // longer workgroups with more loads in flight.
 // ---------------------------------------------------------------------------
-template <int D, bool BF16, int LPW>
+template <int D, bool BF16, int LPW, int U>
 __global__ __launch_bounds__(WGS) void pool_kernel(const void* __restrict__ K,
                                                    float* __restrict__ L,
                                                    float* __restrict__ st_L,
@@ -170,7 +170,6 @@ __global__ __launch_bounds__(WGS) void pool_kernel(const void* __restrict__ K,
                                                    int ph, int pw, int m, int N) {
   constexpr int C4 = D / 4;
   constexpr int G = WGS / C4;
-  constexpr int U = 4;  // loads in flight per thread and window
   __shared__ f4 part[LPW][WGS];
   const int j0 = blockIdx.x * LPW, bh = blockIdx.y;
   const int tid = threadIdx.x, c4 = tid % C4, g = tid / C4;
@@ -335,22 +334,28 @@ inline float exp2_scale(float lambda) {
   return static_cast<float>(-1.4426950408889634 / static_cast<double>(lambda));
 }
 
-template <int D, int LPW>
+template <int D, int LPW, int U>
 hipError_t launch_pool_dl(const Plan& p, const Args& a, const Buffers& b, hipStream_t s, Ev ev) {
   const dim3 grid((p.m + LPW - 1) / LPW, p.BH);
   if (p.bf16)
-    return launch(pool_kernel<D, true, LPW>, grid, dim3(WGS), s, ev, a.k, b.L, a.st_L, b.sync,
+    return launch(pool_kernel<D, true, LPW, U>, grid, dim3(WGS), s, ev, a.k, b.L, a.st_L, b.sync,
                   b.timeouts, p.gw, p.ph, p.pw, p.m, p.N);
-  return launch(pool_kernel<D, false, LPW>, grid, dim3(WGS), s, ev, a.k, b.L, a.st_L, b.sync,
+  return launch(pool_kernel<D, false, LPW, U>, grid, dim3(WGS), s, ev, a.k, b.L, a.st_L, b.sync,
                 b.timeouts, p.gw, p.ph, p.pw, p.m, p.N);
 }
 
 template <int D>
 hipError_t launch_pool_d(const Plan& p, const Args& a, const Buffers& b, hipStream_t s, Ev ev) {
-  // one landmark per workgroup while that grid is resident at once (8
-  // workgroups of 256 threads per CU), else four
-  if (static_cast<long>(p.m) * p.BH <= 2048) return launch_pool_dl<D, 1>(p, a, b, s, ev);
-  return launch_pool_dl<D, 4>(p, a, b, s, ev);
+  // One landmark per workgroup while that grid is resident at once (8
+  // workgroups of 256 threads per CU), else four, with all their loads in
+  // flight together.  A thread takes up to 4 tokens of a window, or one when
+  // the window has at most one token per thread group (160 heads of 4 x 4
+  // windows: the three clamped loads that no token needed made the launch
+  // 10.2 instead of 6.5 us).
+  const bool one = p.ph * p.pw <= WGS / (D / 4);
+  if (static_cast<long>(p.m) * p.BH <= 2048)
+    return one ? launch_pool_dl<D, 1, 1>(p, a, b, s, ev) : launch_pool_dl<D, 1, 4>(p, a, b, s, ev);
+  return one ? launch_pool_dl<D, 4, 1>(p, a, b, s, ev) : launch_pool_dl<D, 4, 4>(p, a, b, s, ev);
 }
 
 template <int D, int MB>
