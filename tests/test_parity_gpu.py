@@ -118,6 +118,33 @@ def test_serial_and_fused_plans_are_bitwise_equal():
     assert np.array_equal(a, b) and np.array_equal(a, c)
 
 
+LINEAR_CASES = [wl.HEADLINE, wl.WORKLOADS[4],
+                wl.small_case(10, 14, 64, 2, 2, dtype=wl.BF16, B=2, H=2),   # bf16 I/O
+                wl.small_case(12, 20, 32, 3, 4, kernel=wl.GAUSSIAN, B=2),    # Gaussian, Q != K
+                wl.small_case(10, 14, 32, 2, 2, B=150)]                      # output-launch plan
+
+
+@pytest.mark.parametrize("w", LINEAR_CASES, ids=[w.name for w in LINEAR_CASES])
+def test_output_scales_exactly_with_v(w):
+    """O is linear in V, and every scale the kernels choose (the split
+    operands' powers of two, the row scales of W^T and Y^T) follows a power of
+    two through exactly: O(2^k V) equals 2^k O(V) bit for bit (no value
+    leaves the normal range at k = +-40)."""
+    _print_case(w, "O(2^k V) = 2^k O(V)")
+    x = wl.make_inputs(w)
+    base = run_gpu(w, x)["O"]
+    for k in (40, -40):
+        xs = dict(x)
+        if w.dtype == wl.BF16:
+            # bf16 bits: scale the widened values and take the (exact) high half
+            f = (x["v"].astype(np.uint32) << 16).view(np.float32) * np.float32(2.0 ** k)
+            xs["v"] = (f.view(np.uint32) >> 16).astype(np.uint16)
+        else:
+            xs["v"] = x["v"] * np.float32(2.0 ** k)
+        got = run_gpu(w, xs)["O"]
+        assert np.array_equal(got, base * 2.0 ** k), f"k={k}: O does not scale exactly"
+
+
 TICKET_CASES = [wl.HEADLINE, wl.WORKLOADS[3], wl.WORKLOADS[4],
                 wl.small_case(10, 14, 32, 2, 2, B=3, H=1),     # BH % 8 != 0: three queues
                 wl.small_case(10, 14, 32, 2, 2, B=150),        # output-launch plan, 8 queues
