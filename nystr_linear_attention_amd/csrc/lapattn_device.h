@@ -1319,6 +1319,29 @@ __device__ __forceinline__ void store_o4(void* out, int bf16, size_t o, f4 v) {
   }
 }
 
+// fp32 O columns col .. col + 31 (one 128-byte line per row) of tokens n0 ..
+// n0 + 15, held as two 16x16 blocks of O^T: lane (g, r) has columns
+// col + 4 g .. + 3 (c0) and col + 16 + 4 g .. + 3 (c1) of token n0 + r.
+// Lanes r and r ^ 8 trade one block (DPP row rotation by 8) so that each of
+// the two stores writes whole lines (a streaming store of part of a line
+// can leave L2 as a partial line): first tokens n0 .. n0 + 7 (lanes r < 8
+// their c0, lanes r >= 8 the c1 of token r - 8), then n0 + 8 .. n0 + 15.
+// Rows from N on are not written; row n of the head is at rows + n.
+template <int D>
+__device__ __forceinline__ void store_o_lines(void* out, size_t rows, int n0, int N, int col, f4 c0, f4 c1) {
+  const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const bool lo = lr < 8;
+  const f4 x = lo ? c1 : c0;
+  f4 y;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    y[i] = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x[i]), 0x128, 0xF, 0xF, false));
+  const int c = col + (lo ? 0 : 16) + 4 * lg;
+  const int n1 = n0 + (lo ? lr : lr - 8), n2 = n1 + 8;
+  if (n1 < N) store_o4(out, 0, (rows + n1) * D + c, lo ? c0 : y);
+  if (n2 < N) store_o4(out, 0, (rows + n2) * D + c, lo ? y : c1);
+}
+
 // O rows of one 64-token tile: K_QL tile (PT, LDS, zero beyond m) times Y on
 // fp16 MFMA, with Y^T split in LDS (row c scaled by 2^(EW[c] + ex - 22),
 // y_in_lds) and the tile's K_QL rows scaled by 2^14 and split here, once per
@@ -1326,7 +1349,10 @@ __device__ __forceinline__ void store_o4(void* out, int bf16, size_t o, f4 v) {
 // so that lane (g, r) holds four consecutive columns 16 cb + 4 g .. + 3 of
 // token 16 tb + r: one 16-byte store.  Wave w: tokens 16 (w % 4) .. +15;
 // waves 0-3 take the first half of the column blocks, waves 4-7 the second,
-// so that each 128-byte line of an O row is written by one wave.
+// so that each 128-byte line of an O row is written by one wave.  (Trading
+// blocks between lanes so that one store writes whole lines, as the output
+// launch does, cut the written bytes by 1.3 MB on 8 heads of 3136 tokens but
+// put 0.5 us on the end of the launch, which this tail sets.)
 template <int D>
 __device__ void out_tile(const MainArgs& a, int bh, int t, const float* PT, const float* Q, int ex) {
   using QG = QGeom<D>;

@@ -21,6 +21,8 @@ constexpr int kQueryTilesOut = 4;
 // Tiles per key workgroup at most when the output-launch plan lengthens key
 // workgroups so that they are all resident at once.
 constexpr int kMaxKeyTilesOut = 4;
+// least tiles per key workgroup when the whole grid is resident
+constexpr int kMinKeyTiles = 3;
 // W partials per head at most (key ready flags per head).
 constexpr int kMaxPartials = 128;
 // Main-kernel workgroups taken to be resident at once: two per CU (LDS and

@@ -308,6 +308,7 @@ __global__ __launch_bounds__(WGO) void out_kernel(const float* __restrict__ kql,
   u32x4 kh[2], kl[2];
 #pragma unroll
   for (int p = 0; p < 2; ++p) split8h(av[p][0], av[p][1], 14, kh[p], kl[p]);
+  f4 cs[CBN];
 #pragma unroll
   for (int cb = 0; cb < CBN; ++cb) {
     f4 c = {0.f, 0.f, 0.f, 0.f};
@@ -324,8 +325,16 @@ __global__ __launch_bounds__(WGO) void out_kernel(const float* __restrict__ kql,
     // n0 + lr
 #pragma unroll
     for (int i = 0; i < 4; ++i) c[i] = ldexpf(c[i], -14 - EW[16 * cb + 4 * lg + i]);
+    cs[cb] = c;
+    if (CBN % 2 == 0 && !bf16) continue;
     const int n = n0 + lr;
     if (n < N) store_o4(O, bf16, (static_cast<size_t>(bh) * N + n) * D + 16 * cb + 4 * lg, c);
+  }
+  // fp32 rows of whole 128-byte lines: a line per store instruction
+  if (CBN % 2 == 0 && !bf16) {
+#pragma unroll
+    for (int cb = 0; cb < CBN; cb += 2)
+      store_o_lines<D>(O, static_cast<size_t>(bh) * N, n0, N, 16 * cb, cs[cb], cs[cb + 1]);
   }
 }
 

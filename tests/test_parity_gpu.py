@@ -52,7 +52,8 @@ SMALL = [
     wl.small_case(10, 14, 64, 2, 2, dtype=wl.BF16, B=2, H=2),     # bf16, ragged
     wl.small_case(24, 24, 64, 3, 3, qk_dist="student_t3", qk_scale=0.5, eps=1e-2, iters=30),
     wl.small_case(40, 40, 64, 5, 5, B=1, H=1, iters=64),          # N=1600, max iters
-    wl.small_case(64, 128, 64, 16, 16),                           # 128 tiles, 128 W partials
+    wl.small_case(64, 128, 64, 16, 16),                           # 128 tiles, 3 per key WG: 43 W partials
+    wl.small_case(128, 192, 32, 16, 32),                          # 384 tiles: 128 W partials (the most), m=48
     wl.small_case(9, 9, 16, 3, 3, B=2, shared_qk=True),           # Q = K: output launch, m=9 (mpad 16)
     wl.small_case(10, 14, 32, 2, 2, H=2, shared_qk=True),         # Q = K, m=35 (mpad 48), ragged tiles
     wl.small_case(10, 10, 64, 2, 2, kernel=wl.GAUSSIAN, dtype=wl.BF16, B=2, shared_qk=True),
