@@ -610,6 +610,11 @@ __device__ __forceinline__ void ns_wave(const MainArgs& a, float* smem, int c, i
   const int col = 16 * c + lr;
   const int iters = a.iters;
   float* slot = smem + G::OFF_SLOT;
+  // ITERS: X_1 .. X_T through a buffer resource over the head's iterates
+  // (stores outside it are dropped), lane offset of row 4 g, column col
+  const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+      xiter, static_cast<short>(0), ITERS ? (iters + 1) * MP * MP * 4 : 0, 0x00020000);
+  const int xoff = (4 * lg * MP + col) * 4;
 
   // X-hat_0 = 2^e0 alpha A on the own columns, fp32 and split (the same
   // arithmetic as the shared copy, so the two agree bit for bit)
@@ -729,9 +734,14 @@ __device__ __forceinline__ void ns_wave(const MainArgs& a, float* smem, int c, i
 #pragma unroll
         for (int j = 0; j < 4; ++j) xs[ip][j] = fmaf(acc[j], c2, c1 * xs[ip][j]);
         if constexpr (ITERS) {
-          float* dst = xiter + static_cast<size_t>(t + 1) * MP * MP;
+          // buffer stores: the iterate's offset in a scalar register, one
+          // 32-bit lane offset (64-bit lane addresses pushed the step loop
+          // into register spills)
+          const int so = ((t + 1) * MP * MP + 16 * ip * MP) * 4;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) dst[(16 * ip + 4 * lg + j) * MP + col] = ldexpf(xs[ip][j], -eN);
+          for (int j = 0; j < 4; ++j)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ldexpf(xs[ip][j], -eN)), xrs,
+                                                  xoff, so + j * MP * 4, 0);
         }
         if (!LAST) {
           split_block_mix(xs[ip], ip, one, xh, xl);
