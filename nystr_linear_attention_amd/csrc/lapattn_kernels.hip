@@ -407,7 +407,8 @@ hipError_t launch_out_d(const Plan& p, const Args& a, const Buffers& b, hipStrea
 // (8 loads in flight) with s = K_QL[0][j] (a shift that keeps the variance
 // free of cancellation); the 8 groups are added in order and the chunk's
 // sums published; the last chunk of the head to arrive adds the chunks' sums
-// in chunk order (so the result does not depend on timing): mu = s + S1 / N,
+// in a fixed order (8 contiguous runs of chunks, each in chunk order, then
+// the runs in order; so the result does not depend on timing): mu = s + S1 / N,
 // var = S2 / N - (S1 / N)^2.  mu goes to the workspace (the output launch
 // centres K_QL with it) and Y^T's column j is scaled by 1 / sqrt(var +
 // delta), so O = (K_QL - mu) (Y / sqrt(var + delta)) = Z Y.
@@ -458,12 +459,41 @@ __global__ __launch_bounds__(WGM) void norm_stats_kernel(const float* __restrict
   }
   unsigned* cnt = sync + kSyncHead * (bh + 1) + kNormCount;
   if (publish_arrive(cnt) != static_cast<unsigned>(nc - 1)) return;
-  if (tid < MP) {
+  {
+    // the head's chunk sums in chunk order: thread (j, g) sums chunks
+    // [g P, (g + 1) P) with up to 8 chunks' loads in flight, then the G
+    // group sums are added in order of g (one load in flight per chunk made
+    // this sum a chain of nc memory latencies)
     const float* ph = part + static_cast<size_t>(bh) * nc * 2 * MP;
+    const int P = (nc + G - 1) / G;
+    const int u1 = min(nc, (g + 1) * P);
     float t1 = 0.f, t2 = 0.f;
-    for (int u = 0; u < nc; ++u) {
-      t1 += ph[u * 2 * MP + tid];
-      t2 += ph[u * 2 * MP + MP + tid];
+    for (int p0 = g * P; p0 < u1; p0 += 8) {
+      float v1[8], v2[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const bool ok = p0 + q < u1;
+        v1[q] = ok ? ph[(p0 + q) * 2 * MP + j] : 0.f;
+        v2[q] = ok ? ph[(p0 + q) * 2 * MP + MP + j] : 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (p0 + q < u1) {
+          t1 += v1[q];
+          t2 += v2[q];
+        }
+      }
+    }
+    __syncthreads();  // s1 and s2 held this chunk's sums
+    s1[tid] = t1;
+    s2[tid] = t2;
+    __syncthreads();
+  }
+  if (tid < MP) {
+    float t1 = 0.f, t2 = 0.f;
+    for (int u = 0; u < G; ++u) {
+      t1 += s1[u * MP + tid];
+      t2 += s2[u * MP + tid];
     }
     float mean = 0.f, r = 0.f;
     if (tid < m) {
