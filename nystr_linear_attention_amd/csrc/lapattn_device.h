@@ -611,7 +611,8 @@ __device__ __forceinline__ void ns_wave(const MainArgs& a, float* smem, int c, i
   const int iters = a.iters;
   float* slot = smem + G::OFF_SLOT;
   // ITERS: X_1 .. X_T through a buffer resource over the head's iterates
-  // (stores outside it are dropped), lane offset of row 4 g, column col
+  // ((iters + 1) MP MP floats from xiter); the lane's byte offset of row
+  // 4 g, column col; the iterate and block rows go in the scalar offset
   const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
       xiter, static_cast<short>(0), ITERS ? (iters + 1) * MP * MP * 4 : 0, 0x00020000);
   const int xoff = (4 * lg * MP + col) * 4;
