@@ -72,7 +72,7 @@ def nslice(D, nQ):
 
 
 SHAPES = list(itertools.product((1, 3, 8, 9, 16, 150),
-                                (1, 25, 128),
+                                (1, 17, 25, 86, 128),
                                 (0, 1, 25, 128),
                                 (16, 64),
                                 (True, False)))
