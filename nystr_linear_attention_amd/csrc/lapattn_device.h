@@ -1442,7 +1442,7 @@ __device__ __forceinline__ int norm_scale(float p) {
 template <int D, bool BF16>
 __device__ __forceinline__ void gauss_tile(const MainArgs& a, const float (&av)[D / 4], const float* Lh,
                                            int t, float* PTt, uint16_t* PJH, uint16_t* PJL, float* xx,
-                                           bool key_role, bool write_pt) {
+                                           bool key_role, bool write_pt, float* kdst) {
   constexpr int KS = D / 4;  // MFMA sub-steps; floats per lane per operand
   const int lane = threadIdx.x & 63, w = wave_id();
   const int lr = lane & 15, lg = lane >> 4;
@@ -1514,6 +1514,9 @@ __device__ __forceinline__ void gauss_tile(const MainArgs& a, const float (&av)[
         const float d = fmaxf(fmaf(-2.0f, dot, xt + pl), 0.0f);
         const float kv = (j < m && t * TILE + tt < N) ? exp2_map(d * a.c_exp2) : 0.f;
         if (write_pt) PTt[ptj(tt, j)] = kv;
+        // K_QL row tt of the tile straight to global memory (zero columns
+        // j >= m included): no pass through LDS after the tile's barrier
+        if (kdst && t * TILE + tt < N) kdst[tt * a.mpad + j] = kv;
         kq[i] = kv;
       }
       if (key_role) {
@@ -1577,7 +1580,9 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
   // token-major K_QL rows: query tiles (their output rows) and key tiles
   // whose K_QL is stored or staged (Q == K); other key tiles need only the
   // landmark-major rows of the W^T product
-  const bool write_pt = !key_role || store_kql || stage_kql;
+  // Gaussian tiles write their stored K_QL rows from registers
+  const bool kql_direct = KIND == 1 && store_kql;
+  const bool write_pt = (!key_role && a.out_in_main) || (store_kql && !kql_direct) || stage_kql;
   const void* src = key_role ? k : q;
   const int mby = (m + 15) >> 4;
   const int nwb = CBN * mby;  // W output blocks
@@ -1761,7 +1766,8 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
         if (write_pt) PTt[ptj(lane, j)] = k0;
       }
     } else {
-      gauss_tile<D, BF16>(a, ga, Lh, t, PTt, PJH, PJL, xx, key_role, write_pt);
+      gauss_tile<D, BF16>(a, ga, Lh, t, PTt, PJH, PJL, xx, key_role, write_pt,
+                          kql_direct ? a.kql + (static_cast<size_t>(bh) * N + t * TILE) * a.mpad : nullptr);
     }
     if (t + 1 < t_end) {
       load_v(t + 1);
@@ -1769,7 +1775,7 @@ __device__ __forceinline__ void map_role(const MainArgs& a, const void* __restri
       if constexpr (KIND == 0) fetch_rows(t + 1);
     }
     __syncthreads();
-    if (store_kql) {
+    if (store_kql && !kql_direct) {
       // 64 rows of mpad floats, contiguous in global memory
       const int q4 = a.mpad / 4;
       float* dst = a.kql + (static_cast<size_t>(bh) * N + t * TILE) * a.mpad;
